@@ -1,0 +1,212 @@
+"""CPU oracle for Compressed PagedAttention (compression pass + paged decode).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this package; the product path never does.
+
+The arithmetic lives in ``zp_oracle.c`` (plain C, double precision, OpenMP
+over independent units).  This module only marshals NumPy arrays into it and
+strings the steps together in the pages' order: plan the target blocks,
+score every cached slot (observation-window importance and Lightning
+Redundancy Score), select the survivors per (layer, head), compact them in
+order into the first N_max-1 blocks, then append the pending token and run
+dense decode attention.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import List, Optional
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_f64p = ctypes.POINTER(ctypes.c_double)
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_build.LIB):
+        _build.build()
+    lib = ctypes.CDLL(_build.LIB)
+    lib.zpo_num_threads.restype = ctypes.c_int
+    lib.zpo_plan.restype = ctypes.c_int
+    lib.zpo_plan.argtypes = [ctypes.c_int32, _i32p, ctypes.c_int32, ctypes.c_int32, _i32p,
+                             _i32p, _i32p, _i32p, _i32p]
+    lib.zpo_scores.restype = None
+    lib.zpo_scores.argtypes = [ctypes.c_int32] * 8 + [ctypes.c_void_p, ctypes.c_void_p, _i32p,
+                                                      _f64p, _f64p, _f64p]
+    lib.zpo_select.restype = None
+    lib.zpo_select.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                               _f64p, _i32p]
+    lib.zpo_compact.restype = None
+    lib.zpo_compact.argtypes = [ctypes.c_int64] + [ctypes.c_int32] * 7 + [
+        ctypes.c_void_p, ctypes.c_void_p, _i32p, _i32p, _i32p]
+    lib.zpo_append.restype = None
+    lib.zpo_append.argtypes = [ctypes.c_int32] * 5 + [ctypes.c_void_p] * 4 + [_i32p]
+    lib.zpo_decode.restype = None
+    lib.zpo_decode.argtypes = [ctypes.c_int32] * 6 + [ctypes.c_void_p] * 3 + [
+        _i32p, ctypes.c_int32, _i32p, ctypes.c_double, _f64p]
+    _lib = lib
+    return lib
+
+
+def _i32(a: np.ndarray):
+    assert a.dtype == np.int32 and a.flags.c_contiguous
+    return a.ctypes.data_as(_i32p)
+
+
+def _f64(a: np.ndarray):
+    assert a.dtype == np.float64 and a.flags.c_contiguous
+    return a.ctypes.data_as(_f64p)
+
+
+def _vp(a: np.ndarray):
+    assert a.flags.c_contiguous
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def num_threads() -> int:
+    return int(_load().zpo_num_threads())
+
+
+OK, INVALID, NO_BLOCKS = 0, 1, 2
+
+
+@dataclass
+class Plan:
+    status: int
+    tables: np.ndarray      # new tables [R][n_max]
+    refcounts: np.ndarray   # new refcounts
+    src: np.ndarray         # [R][n_max]
+    dst: np.ndarray         # [R][n_max-1]
+    freed: np.ndarray       # freed ids in order
+
+
+def plan(refcounts: np.ndarray, tables: np.ndarray, n_max: int) -> Plan:
+    """Target-block plan of one compression call (inputs are not modified)."""
+    lib = _load()
+    rc = np.ascontiguousarray(refcounts, dtype=np.int32).copy()
+    tab = np.ascontiguousarray(tables, dtype=np.int32).copy()
+    R = int(tab.shape[0])
+    src = np.zeros((R, n_max), dtype=np.int32)
+    dst = np.zeros((R, max(n_max - 1, 1)), dtype=np.int32)
+    freed = np.zeros(max(R * n_max, 1), dtype=np.int32)
+    nfreed = np.zeros(1, dtype=np.int32)
+    st = lib.zpo_plan(int(rc.shape[0]), _i32(rc), R, n_max, _i32(tab), _i32(src), _i32(dst),
+                      _i32(freed), _i32(nfreed))
+    return Plan(int(st), tab, rc, src, dst, freed[: int(nfreed[0])].copy())
+
+
+def scores(kpool: np.ndarray, window_q: np.ndarray, src: np.ndarray, *, num_kv_heads: int,
+           num_q_heads: int, head_dim: int, block_size: int, n_max: int, window: int):
+    """Importance A, redundancy R and combined score s, each [R][H][T] float64."""
+    lib = _load()
+    is_bf16 = int(kpool.dtype == np.uint16)
+    R = int(src.shape[0])
+    T = n_max * block_size
+    A = np.zeros((R, num_kv_heads, T))
+    Rr = np.zeros((R, num_kv_heads, T))
+    s = np.zeros((R, num_kv_heads, T))
+    lib.zpo_scores(num_kv_heads, num_q_heads, head_dim, block_size, is_bf16, n_max, window, R,
+                   _vp(np.ascontiguousarray(kpool)), _vp(np.ascontiguousarray(window_q)),
+                   _i32(np.ascontiguousarray(src, dtype=np.int32)), _f64(A), _f64(Rr), _f64(s))
+    return A, Rr, s
+
+
+def select(s: np.ndarray, window: int, k_sel: int) -> np.ndarray:
+    """Ascending kept slots per unit: s [..., T] float64 -> int32 [..., k_sel + w]."""
+    lib = _load()
+    T = int(s.shape[-1])
+    lead = s.shape[:-1]
+    flat = np.ascontiguousarray(s.reshape(-1, T), dtype=np.float64)
+    kept = np.zeros((flat.shape[0], k_sel + window), dtype=np.int32)
+    lib.zpo_select(int(flat.shape[0]), T, window, k_sel, _f64(flat), _i32(kept))
+    return kept.reshape(*lead, k_sel + window)
+
+
+def compact(pool: np.ndarray, src: np.ndarray, dst: np.ndarray, kept: np.ndarray, *,
+            n_max: int) -> np.ndarray:
+    """Out-of-place order-preserving compaction of one [nb][H][b][d] pool."""
+    lib = _load()
+    pool = np.ascontiguousarray(pool)
+    nb, H, b, d = pool.shape
+    out = np.empty_like(pool)
+    R = int(src.shape[0])
+    k_keep = int(kept.shape[-1])
+    lib.zpo_compact(int(pool.size), H, d, b, pool.itemsize, n_max, R, k_keep, _vp(pool), _vp(out),
+                    _i32(np.ascontiguousarray(src, dtype=np.int32)),
+                    _i32(np.ascontiguousarray(dst, dtype=np.int32)),
+                    _i32(np.ascontiguousarray(kept, dtype=np.int32)))
+    return out
+
+
+def append(kpool: np.ndarray, vpool: np.ndarray, k_new: np.ndarray, v_new: np.ndarray,
+           slot_mapping: np.ndarray) -> None:
+    """In-place append of one token per request into the pools (host copies)."""
+    lib = _load()
+    nb, H, b, d = kpool.shape
+    R = int(slot_mapping.shape[0])
+    lib.zpo_append(H, d, b, kpool.itemsize, R, _vp(kpool), _vp(vpool),
+                   _vp(np.ascontiguousarray(k_new)), _vp(np.ascontiguousarray(v_new)),
+                   _i32(np.ascontiguousarray(slot_mapping, dtype=np.int32)))
+
+
+def decode(kpool: np.ndarray, vpool: np.ndarray, q: np.ndarray, tables: np.ndarray,
+           seq_lens: np.ndarray, *, num_q_heads: int, scale: Optional[float] = None) -> np.ndarray:
+    """Dense paged decode attention in double: [R][Hq][d] float64."""
+    lib = _load()
+    nb, H, b, d = kpool.shape
+    is_bf16 = int(kpool.dtype == np.uint16)
+    tables = np.ascontiguousarray(tables, dtype=np.int32)
+    R, max_blocks = tables.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    out = np.zeros((R, num_q_heads, d))
+    lib.zpo_decode(H, num_q_heads, d, b, is_bf16, R, _vp(np.ascontiguousarray(kpool)),
+                   _vp(np.ascontiguousarray(vpool)), _vp(np.ascontiguousarray(q)), _i32(tables),
+                   max_blocks, _i32(np.ascontiguousarray(seq_lens, dtype=np.int32)), float(scale),
+                   _f64(out))
+    return out
+
+
+@dataclass
+class CompressResult:
+    plan: Plan
+    A: List[np.ndarray]       # per layer [R][H][T]
+    R: List[np.ndarray]
+    s: List[np.ndarray]
+    kept: List[np.ndarray]    # per layer [R][H][K_keep]
+    k_pool: List[np.ndarray]  # compacted pools (out of place)
+    v_pool: List[np.ndarray]
+
+
+def compress(case, layers: Optional[List[int]] = None) -> CompressResult:
+    """The whole compression call of a synthetic case, step by step."""
+    g = case.geom
+    n_max, w, b = case.n_max, case.window, g.block_size
+    k_keep = (n_max - 1) * b
+    k_sel = k_keep - w
+    p = plan(case.refcounts, case.tables, n_max)
+    if p.status != OK:
+        raise RuntimeError(f"oracle plan failed with status {p.status}")
+    layers = list(range(g.num_layers)) if layers is None else layers
+    out = CompressResult(p, [], [], [], [], [], [])
+    for layer in layers:
+        A, Rr, s = scores(case.k_pool[layer], case.window_q[layer], p.src,
+                          num_kv_heads=g.num_kv_heads, num_q_heads=g.num_q_heads,
+                          head_dim=g.head_dim, block_size=b, n_max=n_max, window=w)
+        kept = select(s, w, k_sel)
+        out.A.append(A)
+        out.R.append(Rr)
+        out.s.append(s)
+        out.kept.append(kept)
+        out.k_pool.append(compact(case.k_pool[layer], p.src, p.dst, kept, n_max=n_max))
+        out.v_pool.append(compact(case.v_pool[layer], p.src, p.dst, kept, n_max=n_max))
+    return out
