@@ -1,0 +1,298 @@
+"""ctypes binding of libzp.so (the C ABI declared in include/zp.h).
+
+Argument marshalling only: tensors are passed as device pointers
+(``Tensor.data_ptr()``), streams as their hipStream_t handle, host arrays as
+NumPy int32 buffers.  Every computation happens in the library's HIP kernels.
+There is deliberately no fallback: if the library is missing or fails to
+load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libzp.so")
+
+ZP_OK, ZP_ERR_INVALID, ZP_ERR_NO_BLOCKS, ZP_ERR_HIP, ZP_ERR_STATE = range(5)
+ZP_F32, ZP_BF16 = 0, 1
+ZP_POOL_MANUAL_FENCE = 1
+
+_STATUS_NAMES = {0: "ZP_OK", 1: "ZP_ERR_INVALID", 2: "ZP_ERR_NO_BLOCKS", 3: "ZP_ERR_HIP",
+                 4: "ZP_ERR_STATE"}
+
+
+class ZpError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class _KVCache(ctypes.Structure):
+    _fields_ = [("num_layers", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("num_q_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("k_cache", ctypes.POINTER(ctypes.c_void_p)),
+                ("v_cache", ctypes.POINTER(ctypes.c_void_p))]
+
+
+class _Debug(ctypes.Structure):
+    _fields_ = [("importance", ctypes.c_void_p), ("redundancy", ctypes.c_void_p),
+                ("score", ctypes.c_void_p), ("kept", ctypes.c_void_p)]
+
+
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_vp = ctypes.c_void_p
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libzp.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it first "
+                           "(python -c 'import __graft_entry__; __graft_entry__.build()')")
+    L = ctypes.CDLL(LIB_PATH)
+    S = ctypes.c_int  # zp_status
+    sig = {
+        "zp_last_error": (ctypes.c_char_p, []),
+        "zp_version": (ctypes.c_int32, []),
+        "zp_block_pool_create": (S, [ctypes.c_int32, ctypes.c_uint32, ctypes.POINTER(_vp)]),
+        "zp_block_pool_destroy": (None, [_vp]),
+        "zp_block_alloc": (S, [_vp, ctypes.c_int32, _i32p]),
+        "zp_block_share": (S, [_vp, _i32p, ctypes.c_int32]),
+        "zp_block_release": (S, [_vp, _i32p, ctypes.c_int32, _i32p, _i32p]),
+        "zp_block_refcount": (ctypes.c_int32, [_vp, ctypes.c_int32]),
+        "zp_block_num_free": (ctypes.c_int32, [_vp]),
+        "zp_block_num_pending": (ctypes.c_int32, [_vp]),
+        "zp_block_pool_fence": (S, [_vp]),
+        "zp_block_pool_sync": (S, [_vp]),
+        "zp_compress_plan": (S, [_vp, ctypes.c_int32, ctypes.c_int32, _i32p, _i32p, _i32p, _i32p,
+                                 _i32p]),
+        "zp_compress_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(_KVCache), ctypes.c_int32,
+                                                          ctypes.c_int32, ctypes.c_int32]),
+        "zp_compress": (S, [ctypes.POINTER(_KVCache), _vp, ctypes.c_int32, ctypes.c_int32,
+                            ctypes.c_int32, _i32p, ctypes.POINTER(_vp), _vp, ctypes.c_size_t,
+                            _i32p, _i32p, _vp, ctypes.POINTER(_Debug)]),
+        "zp_append_kv": (S, [ctypes.POINTER(_KVCache), ctypes.c_int32, ctypes.c_int32, _vp, _vp,
+                             _vp, _vp]),
+        "zp_paged_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(_KVCache),
+                                                              ctypes.c_int32, ctypes.c_int32]),
+        "zp_paged_decode": (S, [ctypes.POINTER(_KVCache), ctypes.c_int32, ctypes.c_int32, _vp, _vp,
+                                ctypes.c_int32, _vp, ctypes.c_float, _vp, _vp, ctypes.c_size_t,
+                                _vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def last_error() -> str:
+    return lib().zp_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != ZP_OK:
+        raise ZpError(status, last_error())
+
+
+def _i32(a: np.ndarray):
+    assert a.dtype == np.int32 and a.flags.c_contiguous
+    return a.ctypes.data_as(_i32p)
+
+
+def _stream_handle(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dptr(t) -> Optional[int]:
+    return None if t is None else int(t.data_ptr())
+
+
+# --------------------------------------------------------------------------- pool
+
+class BlockPool:
+    """Host block pool (reference counts, free set, deferred frees)."""
+
+    def __init__(self, num_blocks: int, manual_fence: bool = False):
+        h = _vp()
+        _check(lib().zp_block_pool_create(num_blocks, ZP_POOL_MANUAL_FENCE if manual_fence else 0,
+                                          ctypes.byref(h)))
+        self._h = h
+        self.num_blocks = num_blocks
+
+    @property
+    def handle(self):
+        if self._h is None:
+            raise RuntimeError("pool destroyed")
+        return self._h
+
+    def close(self):
+        if self._h is not None:
+            lib().zp_block_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def alloc(self, n: int) -> np.ndarray:
+        ids = np.zeros(max(n, 1), dtype=np.int32)
+        _check(lib().zp_block_alloc(self.handle, n, _i32(ids)))
+        return ids[:n]
+
+    def share(self, ids: Sequence[int]) -> None:
+        a = np.ascontiguousarray(ids, dtype=np.int32)
+        _check(lib().zp_block_share(self.handle, _i32(a), int(a.size)))
+
+    def release(self, ids: Sequence[int]) -> np.ndarray:
+        a = np.ascontiguousarray(ids, dtype=np.int32)
+        freed = np.zeros(max(a.size, 1), dtype=np.int32)
+        n = np.zeros(1, dtype=np.int32)
+        _check(lib().zp_block_release(self.handle, _i32(a), int(a.size), _i32(freed), _i32(n)))
+        return freed[: int(n[0])]
+
+    def refcount(self, i: int) -> int:
+        return int(lib().zp_block_refcount(self.handle, i))
+
+    def refcounts(self) -> np.ndarray:
+        return np.array([self.refcount(i) for i in range(self.num_blocks)], dtype=np.int32)
+
+    def num_free(self) -> int:
+        return int(lib().zp_block_num_free(self.handle))
+
+    def num_pending(self) -> int:
+        return int(lib().zp_block_num_pending(self.handle))
+
+    def fence(self) -> None:
+        _check(lib().zp_block_pool_fence(self.handle))
+
+    def sync(self) -> None:
+        _check(lib().zp_block_pool_sync(self.handle))
+
+    @classmethod
+    def from_refcounts(cls, refcounts: np.ndarray, manual_fence: bool = False) -> "BlockPool":
+        """A pool whose reference counts equal ``refcounts`` (allocate every
+        referenced block, then share it up to its count)."""
+        rc = np.asarray(refcounts, dtype=np.int32)
+        pool = cls(int(rc.size), manual_fence=manual_fence)
+        used = np.flatnonzero(rc > 0).astype(np.int32)
+        if used.size:
+            got = pool.alloc(int(rc.size))  # every id, smallest first
+            unused = got[rc[got] == 0]
+            if unused.size:
+                pool.release(unused)
+            extra = np.repeat(used, rc[used] - 1).astype(np.int32)
+            if extra.size:
+                pool.share(extra)
+        return pool
+
+
+def compress_plan(pool: BlockPool, n_max: int, tables: np.ndarray):
+    """Host planner (zp_compress_plan).  ``tables`` (int32 [R][n_max]) is
+    rewritten in place; returns (src, dst, freed)."""
+    assert tables.dtype == np.int32 and tables.flags.c_contiguous
+    R = int(tables.shape[0])
+    src = np.zeros((R, n_max), dtype=np.int32)
+    dst = np.zeros((R, max(n_max - 1, 1)), dtype=np.int32)
+    freed = np.zeros(max(R * n_max, 1), dtype=np.int32)
+    n = np.zeros(1, dtype=np.int32)
+    _check(lib().zp_compress_plan(pool.handle, n_max, R, _i32(tables), _i32(src), _i32(dst),
+                                  _i32(freed), _i32(n)))
+    return src, dst, freed[: int(n[0])]
+
+
+# --------------------------------------------------------------------------- cache
+
+class KVCache:
+    """Geometry plus per-layer K and V pools (caller-owned device tensors,
+    each [num_blocks][num_kv_heads][block_size][head_dim])."""
+
+    def __init__(self, k_pools: List, v_pools: List, num_q_heads: int):
+        assert len(k_pools) == len(v_pools) and k_pools
+        k0 = k_pools[0]
+        nb, H, b, d = (int(x) for x in k0.shape)
+        self.k_pools, self.v_pools = list(k_pools), list(v_pools)
+        self.num_layers = len(k_pools)
+        self.num_kv_heads, self.num_q_heads = H, int(num_q_heads)
+        self.head_dim, self.block_size, self.num_blocks = d, b, nb
+        name = str(k0.dtype)
+        if name.endswith("bfloat16"):
+            self.dtype = ZP_BF16
+        elif name.endswith("float32"):
+            self.dtype = ZP_F32
+        else:
+            raise ValueError(f"unsupported cache dtype {k0.dtype}")
+        for t in self.k_pools + self.v_pools:
+            if tuple(t.shape) != (nb, H, b, d) or t.dtype != k0.dtype or not t.is_contiguous():
+                raise ValueError("every pool must be a contiguous tensor of the same shape and dtype")
+        n = self.num_layers
+        self._k_arr = (_vp * n)(*[t.data_ptr() for t in self.k_pools])
+        self._v_arr = (_vp * n)(*[t.data_ptr() for t in self.v_pools])
+        self.c = _KVCache(n, H, self.num_q_heads, d, b, nb, self.dtype,
+                          ctypes.cast(self._k_arr, ctypes.POINTER(_vp)),
+                          ctypes.cast(self._v_arr, ctypes.POINTER(_vp)))
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+def compress_workspace_bytes(cache: KVCache, num_reqs: int, n_max: int, window: int) -> int:
+    n = int(lib().zp_compress_workspace_bytes(cache.ref, num_reqs, n_max, window))
+    if n == 0:
+        raise ZpError(ZP_ERR_INVALID, last_error())
+    return n
+
+
+def compress(cache: KVCache, pool: BlockPool, n_max: int, window: int, tables: np.ndarray,
+             window_q: List, workspace, stream=None, debug: Optional[dict] = None) -> np.ndarray:
+    """zp_compress.  ``tables`` (host int32 [R][n_max]) is rewritten on
+    success; returns the freed block ids."""
+    assert tables.dtype == np.int32 and tables.flags.c_contiguous
+    R = int(tables.shape[0])
+    wq = (_vp * cache.num_layers)(*[t.data_ptr() for t in window_q])
+    freed = np.zeros(max(R * n_max, 1), dtype=np.int32)
+    n = np.zeros(1, dtype=np.int32)
+    dbg = None
+    if debug:
+        dbg = _Debug(_dptr(debug.get("importance")), _dptr(debug.get("redundancy")),
+                     _dptr(debug.get("score")), _dptr(debug.get("kept")))
+    st = lib().zp_compress(cache.ref, pool.handle, n_max, window, R, _i32(tables),
+                           ctypes.cast(wq, ctypes.POINTER(_vp)), workspace.data_ptr(),
+                           workspace.numel() * workspace.element_size(), _i32(freed), _i32(n),
+                           _stream_handle(stream), ctypes.byref(dbg) if dbg else None)
+    _check(st)
+    return freed[: int(n[0])]
+
+
+def append_kv(cache: KVCache, layer: int, k_new, v_new, slot_mapping, stream=None) -> None:
+    _check(lib().zp_append_kv(cache.ref, layer, int(slot_mapping.shape[0]), k_new.data_ptr(),
+                              v_new.data_ptr(), slot_mapping.data_ptr(), _stream_handle(stream)))
+
+
+def paged_decode_workspace_bytes(cache: KVCache, num_reqs: int, max_blocks: int) -> int:
+    return int(lib().zp_paged_decode_workspace_bytes(cache.ref, num_reqs, max_blocks))
+
+
+def paged_decode(cache: KVCache, layer: int, q, tables, seq_lens, scale: float, out, workspace,
+                 stream=None) -> None:
+    R, max_blocks = (int(x) for x in tables.shape)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().zp_paged_decode(cache.ref, layer, R, q.data_ptr(), tables.data_ptr(), max_blocks,
+                                 seq_lens.data_ptr(), float(scale), out.data_ptr(), ws_ptr,
+                                 ws_bytes, _stream_handle(stream)))

@@ -1,0 +1,50 @@
+// Host-side block pool: reference counts, smallest-id-first free set, and
+// groups of freed blocks that wait for the GPU work still reading them.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <set>
+#include <vector>
+
+#include "zp.h"
+
+struct zp_block_pool {
+  struct Pending {
+    hipEvent_t event = nullptr;  // null: released by zp_block_pool_fence/sync
+    std::vector<int32_t> ids;
+  };
+  int32_t num_blocks = 0;
+  uint32_t flags = 0;
+  bool poisoned = false;
+  std::vector<int32_t> rc;
+  std::set<int32_t> free_ids;
+  std::vector<Pending> pending;
+
+  bool manual_fence() const { return (flags & ZP_POOL_MANUAL_FENCE) != 0; }
+  // Move every pending group whose GPU work is done into the free set.
+  void reap();
+  int32_t pending_count() const;
+};
+
+namespace zp {
+
+// Output of the planner for one compression call.
+struct PlanResult {
+  std::vector<int32_t> src;    // [R][n_max]
+  std::vector<int32_t> dst;    // [R][n_max-1]
+  std::vector<int32_t> freed;  // ids whose refcount reached 0
+};
+
+// Validate and plan one compression call; on success updates the pool and
+// the tables and returns the plan (freed ids are NOT yet pending: the caller
+// attaches them with add_pending).  On failure nothing changes.
+zp_status plan_compression(zp_block_pool* pool, int32_t n_max, int32_t num_reqs,
+                           int32_t* block_tables, PlanResult* out);
+
+// Attach freed ids to a pending group released by `event` (or by a fence
+// when event is null).  Takes ownership of the event.
+void add_pending(zp_block_pool* pool, std::vector<int32_t> ids, hipEvent_t event);
+
+}  // namespace zp

@@ -1,0 +1,122 @@
+// Order-preserving compaction of the compression pass (gfx950).
+//
+// For every (layer, request, KV head) and for K and V separately, logical
+// slot r < K_keep of the target blocks receives old logical slot kept[r]
+// (nl page Methodologie item 1: survivors move into the first N_max-1
+// blocks; ko page section 2.C: shared blocks are never written, their
+// survivors go to new target blocks).  The survivor list is not stored:
+// with the ascending evicted slots e_0 < e_1 < ... and f_i = e_i - i,
+//   kept[r] = r + #{ i : f_i <= r },
+// found by binary search in LDS.
+//
+// In-place safety.  A target block is either a fresh block (no one reads it)
+// or the source block of the same logical position (private block).  Then
+// writing slot r can only clobber old slot r, which is read by the row r'
+// with kept[r'] = r, and r' <= r.  One workgroup walks the rows in ascending
+// tiles; inside a tile every load has returned before the barrier and
+// every store comes after it, so no store of a tile reaches a slot that
+// the tile (or an earlier one) still has to read, and later tiles only read
+// slots >= their first row.  Rows whose source and target are the same
+// physical row (unmoved prefix of an in-place block) are skipped.
+//
+// Grid: x = (head, K|V), y = (layer, request).  256 threads; each row of
+// d * elem_bytes bytes is VPR 16-byte vectors, one per thread, U rows per
+// thread per tile.
+#include "zp_device.h"
+#include "zp_internal.h"
+
+namespace zp {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 8;
+constexpr int kMaxEvicted = 1024;  // E = block_size * (blocks beyond N_max - 1)
+constexpr int kMaxBlocks = 1024;   // n_max bound for the LDS block tables (host checks the same)
+
+template <int VPR>
+__global__ __launch_bounds__(kThreads) void k_compact(CompactParams p) {
+  constexpr int kRowsPerPass = kThreads / VPR;
+  constexpr int kRowsPerTile = kRowsPerPass * kUnroll;
+  const int h = blockIdx.x >> 1, kv = blockIdx.x & 1;
+  const int lr = blockIdx.y;
+  const int l = lr / p.R, r = lr - l * p.R;
+  const int tid = threadIdx.x;
+  const int vec = tid % VPR, rsub = tid / VPR;
+  const size_t unit = (size_t)lr * p.H + h;
+  const int b = p.K_keep / (p.n_max - 1);
+  const size_t row_bytes = (size_t)VPR * 16;
+
+  __shared__ int f[kMaxEvicted];
+  __shared__ int srcb[kMaxBlocks];
+  __shared__ int dstb[kMaxBlocks];
+  const int32_t* ev = p.evicted + unit * p.E;
+  for (int i = tid; i < p.E; i += kThreads) f[i] = ev[i] - i;
+  for (int n = tid; n < p.n_max; n += kThreads) srcb[n] = p.src[(size_t)r * p.n_max + n];
+  for (int n = tid; n < p.n_max - 1; n += kThreads) dstb[n] = p.dst[(size_t)r * (p.n_max - 1) + n];
+  __syncthreads();
+
+  char* base = static_cast<char*>(p.layer_ptrs[l * kPtrsPerLayer + kv]);
+  const size_t head_stride = (size_t)b * row_bytes;          // one (block, head) tile
+  const size_t block_stride = (size_t)p.H * head_stride;    // one physical block
+
+  for (int t0 = 0; t0 < p.K_keep; t0 += kRowsPerTile) {
+    uint4 buf[kUnroll];
+    char* dst_ptr[kUnroll];
+    const char* src_ptr[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; u++) {
+      dst_ptr[u] = nullptr;
+      src_ptr[u] = nullptr;
+      const int row = t0 + rsub + u * kRowsPerPass;
+      if (row < p.K_keep) {
+        // number of f_i <= row (f is non-decreasing)
+        int lo = 0, hi = p.E;
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (f[mid] <= row) lo = mid + 1; else hi = mid;
+        }
+        const int j = row + lo;
+        const char* from = base + (size_t)srcb[j / b] * block_stride + h * head_stride +
+                           (size_t)(j % b) * row_bytes + vec * 16;
+        char* to = base + (size_t)dstb[row / b] * block_stride + h * head_stride +
+                   (size_t)(row % b) * row_bytes + vec * 16;
+        if (from != to) {
+          src_ptr[u] = from;
+          dst_ptr[u] = to;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; u++)
+      buf[u] = src_ptr[u] ? ldg16(src_ptr[u]) : make_uint4(0, 0, 0, 0);
+    // Every load of the tile must have returned its data before any thread of
+    // the tile stores: the empty asm consumes the loaded registers, so the
+    // compiler waits for them here, ahead of the barrier.
+#pragma unroll
+    for (int u = 0; u < kUnroll; u++)
+      asm volatile("" ::"v"(buf[u].x), "v"(buf[u].y), "v"(buf[u].z), "v"(buf[u].w));
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kUnroll; u++)
+      if (dst_ptr[u]) stg16(dst_ptr[u], buf[u]);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_compact(const CompactParams& p, int num_layers, int row_bytes, int block_size,
+                          hipStream_t s) {
+  (void)block_size;
+  if (p.R <= 0) return hipSuccess;
+  if (p.E > kMaxEvicted || p.n_max > kMaxBlocks) return hipErrorInvalidValue;
+  dim3 grid(2 * p.H, num_layers * p.R), block(kThreads);
+  switch (row_bytes / 16) {
+    case 8: hipLaunchKernelGGL(k_compact<8>, grid, block, 0, s, p); break;
+    case 16: hipLaunchKernelGGL(k_compact<16>, grid, block, 0, s, p); break;
+    case 32: hipLaunchKernelGGL(k_compact<32>, grid, block, 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace zp

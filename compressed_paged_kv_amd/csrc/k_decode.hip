@@ -1,0 +1,316 @@
+// Paged decode attention, its split combine, and the KV append (gfx950).
+//
+// Decode reads each request's keys and values through its block table
+// (upskillscore.com guide, "How it works": logical blocks map to arbitrary
+// physical blocks).  It is a streaming, HBM-bound pass (4 flops per byte),
+// so it runs on the vector ALUs: bf16 q.k through v_dot2c_f32_bf16 with
+// float32 accumulation, p*v as float32 FMAs.
+//
+// Grid: x = split of the block list, y = KV head (and query-head subgroup),
+// z = request.  A workgroup
+// has 4 waves; wave w takes the split's blocks w, w+4, ...  Within a wave,
+// lane = 4*t + c handles token t (0..15) of a 16-token step and the c-th
+// quarter of the head dimension, as 16-byte vectors at byte offsets
+// 64*v + 16*c of the row, so one load instruction of the wave covers whole
+// 64-byte segments of 16 rows.  All G query heads of the KV head are done
+// together, so K and V are read once for the group.  The four lanes of a
+// token add their partial dot products; every lane then keeps its own
+// running softmax state (max m, sum l, accumulator) for the tokens it saw,
+// rescaled only when the max grows by more than 2^8 (exact up to rounding:
+// the final normalisation divides by the same stale max), and the states of
+// lanes, waves and splits are merged by log-sum-exp at the end.
+#include "zp_device.h"
+#include "zp_internal.h"
+
+namespace zp {
+namespace {
+
+constexpr float kInitMax = -1.0e30f;
+constexpr float kLazy = 8.0f;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+template <int DT>
+struct Elem;
+
+template <>
+struct Elem<ZP_BF16> {
+  static constexpr int kBytes = 2;
+  // dot of 8 bf16 pairs (one 16-byte vector of q and k) added to acc
+  __device__ static inline float dot(uint4 q, uint4 k, float acc) {
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.x), __builtin_bit_cast(bf16x2_t, k.x), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.y), __builtin_bit_cast(bf16x2_t, k.y), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.z), __builtin_bit_cast(bf16x2_t, k.z), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.w), __builtin_bit_cast(bf16x2_t, k.w), acc, false);
+    return acc;
+  }
+  static constexpr int kPerVec = 8;
+  __device__ static inline void unpack(uint4 v, float (&o)[8]) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      o[2 * k] = __uint_as_float(w[k] << 16);
+      o[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+    }
+  }
+};
+
+template <>
+struct Elem<ZP_F32> {
+  static constexpr int kBytes = 4;
+  __device__ static inline float dot(uint4 q, uint4 k, float acc) {
+    acc = fmaf(__uint_as_float(q.x), __uint_as_float(k.x), acc);
+    acc = fmaf(__uint_as_float(q.y), __uint_as_float(k.y), acc);
+    acc = fmaf(__uint_as_float(q.z), __uint_as_float(k.z), acc);
+    acc = fmaf(__uint_as_float(q.w), __uint_as_float(k.w), acc);
+    return acc;
+  }
+  static constexpr int kPerVec = 4;
+  __device__ static inline void unpack(uint4 v, float (&o)[4]) {
+    o[0] = __uint_as_float(v.x);
+    o[1] = __uint_as_float(v.y);
+    o[2] = __uint_as_float(v.z);
+    o[3] = __uint_as_float(v.w);
+  }
+};
+
+__device__ inline uint4 ld16(const char* p) { return ldg16(p); }
+
+// G here is the number of query heads one workgroup handles (at most 4, to
+// keep the accumulators in registers); larger groups are split over
+// blockIdx.y = kv_head * nsub + sub.
+template <int DT, int D, int B, int G>
+__global__ __launch_bounds__(256) void k_decode(DecodeParams p) {
+  constexpr int EB = Elem<DT>::kBytes;
+  constexpr int NV = D * EB / 64;          // 16-byte vectors per lane per row
+  constexpr int EPV = Elem<DT>::kPerVec;   // elements per vector
+  constexpr int NE = NV * EPV;             // = D / 4 elements per lane
+  constexpr int ROW = D * EB;
+  const int split = blockIdx.x, r = blockIdx.z;
+  const int group = p.Hq / p.H, nsub = group / G;
+  const int h = blockIdx.y / nsub, hq0 = h * group + (blockIdx.y - h * nsub) * G;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tok = lane >> 2, qd = lane & 3;
+  const int Hq = p.Hq;
+
+  // device-side lengths and ids are clamped / skipped so that a bad table
+  // can never send a load outside the pools
+  const int seq = min(max(p.seq_lens[r], 0), p.max_blocks * B);
+  const int nblk = (seq + B - 1) / B;
+  const int blk_begin = split * p.blocks_per_split;
+  const int blk_end = min(blk_begin + p.blocks_per_split, nblk);
+
+  uint4 q[G][NV];
+#pragma unroll
+  for (int g = 0; g < G; g++) {
+    const char* qp = static_cast<const char*>(p.q) + ((size_t)r * Hq + hq0 + g) * ROW + qd * 16;
+#pragma unroll
+    for (int v = 0; v < NV; v++) q[g][v] = ld16(qp + v * 64);
+  }
+  float m[G], l[G], acc[G][NE];
+#pragma unroll
+  for (int g = 0; g < G; g++) {
+    m[g] = kInitMax;
+    l[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < NE; e++) acc[g][e] = 0.f;
+  }
+
+  const char* kb = static_cast<const char*>(p.k);
+  const char* vb = static_cast<const char*>(p.v);
+  const size_t tile_bytes = (size_t)B * ROW;
+  for (int blk = blk_begin + wave; blk < blk_end; blk += 4) {
+    const int pblk = p.tables[(size_t)r * p.max_blocks + blk];
+    if ((unsigned)pblk >= (unsigned)p.num_blocks) continue;
+    const size_t off = ((size_t)pblk * p.H + h) * tile_bytes + qd * 16;
+#pragma unroll
+    for (int st = 0; st < B / 16; st++) {
+      const int t = blk * B + st * 16 + tok;
+      const char* krow = kb + off + (size_t)(st * 16 + tok) * ROW;
+      const char* vrow = vb + off + (size_t)(st * 16 + tok) * ROW;
+      uint4 kv[NV], vv[NV];
+#pragma unroll
+      for (int v = 0; v < NV; v++) kv[v] = ld16(krow + v * 64);
+#pragma unroll
+      for (int v = 0; v < NV; v++) vv[v] = ld16(vrow + v * 64);
+      float x[G];
+#pragma unroll
+      for (int g = 0; g < G; g++) {
+        float s = 0.f;
+#pragma unroll
+        for (int v = 0; v < NV; v++) s = Elem<DT>::dot(q[g][v], kv[v], s);
+        s += __shfl_xor(s, 1);
+        s += __shfl_xor(s, 2);
+        x[g] = s * p.scale_log2;
+      }
+      if (t < seq) {
+        float vf[NE];
+#pragma unroll
+        for (int v = 0; v < NV; v++) {
+          float tmp[EPV];
+          Elem<DT>::unpack(vv[v], tmp);
+#pragma unroll
+          for (int k = 0; k < EPV; k++) vf[v * EPV + k] = tmp[k];
+        }
+#pragma unroll
+        for (int g = 0; g < G; g++) {
+          if (x[g] > m[g] + kLazy) {
+            const float c = exp2f(m[g] - x[g]);
+            l[g] *= c;
+#pragma unroll
+            for (int e = 0; e < NE; e++) acc[g][e] *= c;
+            m[g] = x[g];
+          }
+          const float pr = exp2f(x[g] - m[g]);
+          l[g] += pr;
+#pragma unroll
+          for (int e = 0; e < NE; e++) acc[g][e] = fmaf(pr, vf[e], acc[g][e]);
+        }
+      }
+    }
+  }
+  // merge the 16 token lanes that share a head-dimension quarter
+#pragma unroll
+  for (int off = 4; off < 64; off <<= 1) {
+#pragma unroll
+    for (int g = 0; g < G; g++) {
+      const float m2 = __shfl_xor(m[g], off);
+      const float l2 = __shfl_xor(l[g], off);
+      const float M = fmaxf(m[g], m2);
+      const float c1 = exp2f(m[g] - M), c2 = exp2f(m2 - M);
+      l[g] = l[g] * c1 + l2 * c2;
+#pragma unroll
+      for (int e = 0; e < NE; e++) {
+        const float a2 = __shfl_xor(acc[g][e], off);
+        acc[g][e] = acc[g][e] * c1 + a2 * c2;
+      }
+      m[g] = M;
+    }
+  }
+  // merge the 4 waves through LDS
+  __shared__ float s_acc[4][G][D];
+  __shared__ float s_ml[4][G][2];
+  if (tok == 0) {
+#pragma unroll
+    for (int g = 0; g < G; g++) {
+#pragma unroll
+      for (int v = 0; v < NV; v++)
+#pragma unroll
+        for (int k = 0; k < EPV; k++) s_acc[wave][g][v * (64 / EB) + qd * EPV + k] = acc[g][v * EPV + k];
+      if (qd == 0) {
+        s_ml[wave][g][0] = m[g];
+        s_ml[wave][g][1] = l[g];
+      }
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+    const int g = idx / D, d = idx - g * D;
+    float M = s_ml[0][g][0];
+#pragma unroll
+    for (int w = 1; w < 4; w++) M = fmaxf(M, s_ml[w][g][0]);
+    float L = 0.f, o = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; w++) {
+      const float c = exp2f(s_ml[w][g][0] - M);
+      L = fmaf(s_ml[w][g][1], c, L);
+      o = fmaf(s_acc[w][g][d], c, o);
+    }
+    const int hq = hq0 + g;
+    if (p.nsplit == 1) {
+      p.out[((size_t)r * Hq + hq) * D + d] = L > 0.f ? o / L : 0.f;
+    } else {
+      float* part = p.partial + (((size_t)r * Hq + hq) * p.nsplit + split) * (D + 2);
+      part[2 + d] = o;
+      if (d == 0) {
+        part[0] = M;
+        part[1] = L;
+      }
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(D) void k_decode_combine(DecodeParams p) {
+  const int rh = blockIdx.x;  // r * Hq + hq
+  const int d = threadIdx.x;
+  const float* part = p.partial + (size_t)rh * p.nsplit * (D + 2);
+  float M = kInitMax;
+  for (int s = 0; s < p.nsplit; s++) M = fmaxf(M, part[(size_t)s * (D + 2)]);
+  float L = 0.f, o = 0.f;
+  for (int s = 0; s < p.nsplit; s++) {
+    const float* ps = part + (size_t)s * (D + 2);
+    const float c = exp2f(ps[0] - M);
+    L = fmaf(ps[1], c, L);
+    o = fmaf(ps[2 + d], c, o);
+  }
+  p.out[(size_t)rh * D + d] = L > 0.f ? o / L : 0.f;
+}
+
+__global__ __launch_bounds__(256) void k_append(AppendParams p) {
+  const int r = blockIdx.x;
+  const int slot = p.slot_mapping[r];
+  if (slot < 0) return;
+  const int blk = slot / p.block_size, off = slot - blk * p.block_size;
+  if (blk >= p.num_blocks) return;
+  const int vpr = p.row_bytes / 16;
+  const int per_pool = p.H * vpr;
+  for (int idx = threadIdx.x; idx < 2 * per_pool; idx += blockDim.x) {
+    const int kv = idx / per_pool, rem = idx - kv * per_pool;
+    const int h = rem / vpr, vec = rem - h * vpr;
+    const char* from = static_cast<const char*>(kv ? p.v_new : p.k_new) +
+                       ((size_t)r * p.H + h) * p.row_bytes + vec * 16;
+    char* to = static_cast<char*>(kv ? p.v : p.k) +
+               (((size_t)blk * p.H + h) * p.block_size + off) * p.row_bytes + vec * 16;
+    stg16(to, ldg16(from));
+  }
+}
+
+template <int DT, int D, int B>
+hipError_t launch_g(const DecodeParams& p, hipStream_t s) {
+  const int group = p.Hq / p.H;
+  const int per_wg = group < 4 ? group : 4;
+  dim3 grid(p.nsplit, p.H * (group / per_wg), p.R), block(256);
+  switch (per_wg) {
+    case 1: hipLaunchKernelGGL((k_decode<DT, D, B, 1>), grid, block, 0, s, p); break;
+    case 2: hipLaunchKernelGGL((k_decode<DT, D, B, 2>), grid, block, 0, s, p); break;
+    case 4: hipLaunchKernelGGL((k_decode<DT, D, B, 4>), grid, block, 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.nsplit == 1) return e;
+  hipLaunchKernelGGL((k_decode_combine<D>), dim3(p.R * p.Hq), dim3(D), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int DT, int D>
+hipError_t launch_d(const DecodeParams& p, int block_size, hipStream_t s) {
+  if (block_size == 16) return launch_g<DT, D, 16>(p, s);
+  if (block_size == 32) return launch_g<DT, D, 32>(p, s);
+  return hipErrorInvalidValue;
+}
+
+template <int DT>
+hipError_t launch_dt(const DecodeParams& p, int head_dim, int block_size, hipStream_t s) {
+  if (head_dim == 64) return launch_d<DT, 64>(p, block_size, s);
+  if (head_dim == 128) return launch_d<DT, 128>(p, block_size, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, int block_size,
+                         hipStream_t s) {
+  if (p.R <= 0) return hipSuccess;
+  if (dtype == ZP_BF16) return launch_dt<ZP_BF16>(p, head_dim, block_size, s);
+  if (dtype == ZP_F32) return launch_dt<ZP_F32>(p, head_dim, block_size, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_append(const AppendParams& p, hipStream_t s) {
+  if (p.R <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_append, dim3(p.R), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace zp

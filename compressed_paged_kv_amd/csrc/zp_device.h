@@ -1,0 +1,30 @@
+// Device helpers shared by the kernels: 16-byte global loads and stores.
+//
+// Pool and query pointers reach the kernels through parameter structs and a
+// device-side pointer table, so the compiler cannot prove they point to
+// global memory and would emit flat instructions (which also occupy the LDS
+// counter).  Casting to address space 1 selects global_load / global_store.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace zp {
+
+// HIP's uint4 is a struct, and loads of it through an address-space-1
+// pointer still become flat instructions; a native vector type does not.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const u32x4_t g_cu32x4;
+typedef __attribute__((address_space(1))) u32x4_t g_u32x4;
+
+__device__ inline uint4 ldg16(const void* p) {
+  const u32x4_t v = *(g_cu32x4*)(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ inline void stg16(void* p, uint4 v) {
+  const u32x4_t w = {v.x, v.y, v.z, v.w};
+  *(g_u32x4*)(p) = w;
+}
+
+}  // namespace zp

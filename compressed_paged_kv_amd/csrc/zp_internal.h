@@ -1,0 +1,95 @@
+// Internal declarations of the HIP library: launch parameters, launchers and
+// error helpers.  Not part of the public ABI (that is include/zp.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "zp.h"
+
+namespace zp {
+
+// Thread-local error message behind zp_last_error().
+void set_error(const char* fmt, ...) __attribute__((format(printf, 1, 2)));
+void clear_error();
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Per-layer device pointers uploaded for the compression kernels:
+// entry [l*3 + 0] = K pool, [l*3 + 1] = V pool, [l*3 + 2] = window queries.
+constexpr int kPtrsPerLayer = 3;
+
+// Token chunk handled by one workgroup of the scoring kernels.
+constexpr int kScoreChunkTokens = 512;
+// Largest number of (query head, window row) pairs per KV head.
+constexpr int kMaxScoreRows = 128;
+// Blocks per split of the paged decode kernel.
+constexpr int kDecodeBlocksPerSplit16 = 16;  // for block_size 16
+constexpr int kDecodeBlocksPerSplit32 = 8;   // for block_size 32
+
+struct ScoreParams {
+  void* const* layer_ptrs;  // device [L][3]
+  const int32_t* src;       // device [R][n_max]
+  float* stats;             // [L*R*H][nchunk][rows_pad][2]
+  float* score;             // [L*R*H][T]
+  float* dbg_importance;    // optional [L*R*H][T]
+  float* dbg_redundancy;    // optional [L*R*H][T]
+  float* dbg_score;         // optional [L*R*H][T]
+  int32_t R, H, Hq, G, w, n_max, T, C, rows, rows_pad, nchunk, chunk_blocks;
+  float scale_log2;  // log2(e) / sqrt(d)
+};
+
+struct SelectParams {
+  const float* score;  // [units][T]
+  int32_t* evicted;    // [units][E], ascending
+  int32_t* dbg_kept;   // optional [units][K_keep]
+  int32_t units, T, C, E, K_keep;
+};
+
+struct CompactParams {
+  void* const* layer_ptrs;  // device [L][3]
+  const int32_t* src;       // device [R][n_max]
+  const int32_t* dst;       // device [R][n_max-1]
+  const int32_t* evicted;   // [L*R*H][E]
+  int32_t R, H, n_max, E, K_keep;
+};
+
+struct DecodeParams {
+  const void* k;
+  const void* v;
+  const void* q;            // [R][Hq][d]
+  const int32_t* tables;    // [R][max_blocks]
+  const int32_t* seq_lens;  // [R]
+  float* out;               // [R][Hq][d]
+  float* partial;           // [R][Hq][nsplit][d + 2]
+  int32_t R, H, Hq, max_blocks, nsplit, blocks_per_split, num_blocks;
+  float scale_log2;
+};
+
+struct AppendParams {
+  void* k;
+  void* v;
+  const void* k_new;  // [R][H][d]
+  const void* v_new;
+  const int32_t* slot_mapping;
+  int32_t R, H, block_size, row_bytes, num_blocks;
+};
+
+// Launchers (defined in the .hip files); they only check the template
+// dispatch and enqueue.  Return hipSuccess or the launch error.
+hipError_t launch_score(const ScoreParams& p, int dtype, int head_dim, int block_size, int units,
+                        hipStream_t s);
+hipError_t launch_select(const SelectParams& p, hipStream_t s);
+hipError_t launch_compact(const CompactParams& p, int num_layers, int row_bytes, int block_size,
+                          hipStream_t s);
+hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, int block_size,
+                         hipStream_t s);
+hipError_t launch_append(const AppendParams& p, hipStream_t s);
+
+// Geometry helpers shared by the validation and the workspace layout.
+int score_row_tiles(int rows);  // 1, 2, 4 or 8 tiles of 16 rows; 0 if rows > kMaxScoreRows
+int select_per_thread(int T);   // slots per thread of the selection kernel; 0 if too many
+
+}  // namespace zp

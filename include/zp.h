@@ -1,0 +1,236 @@
+/*
+ * zp.h -- C ABI of the Compressed PagedAttention hot path for MI355X (gfx950).
+ *
+ * Compressed PagedAttention (Zipage) keeps every request's KV cache within a
+ * fixed number of paged blocks.  Once a request holds N_max full blocks, a
+ * compression pass scores every cached token per layer and per KV head,
+ * drops the lowest-scoring ones, and relocates the survivors, in order, into
+ * the first N_max-1 blocks; the last block is kept free for the tokens that
+ * follow, and surplus blocks are released (gist.science/nl/paper/2603.08743,
+ * "Technische samenvatting", Methodologie item 1; gist.science/ko/paper/
+ * 2603.08743, "기술 요약", section 2.A).  Decode attention then reads the
+ * compacted blocks through the usual block table (upskillscore.com guide
+ * "Paged KV cache and continuous batching", "How it works").
+ *
+ * All entry points are plain C.  Device buffers are CALLER-owned (for
+ * example PyTorch tensors); the library owns only the host-side block pool
+ * (reference counts, free set, deferred frees), a few HIP events and a small
+ * ring of pinned host staging buffers used to upload block tables.  Streams
+ * are passed as `void*` holding a hipStream_t (NULL = the null stream).
+ *
+ * Errors: every call returns a zp_status; on any error other than ZP_ERR_HIP
+ * the call has changed nothing (tables, reference counts, pool, device
+ * memory).  zp_last_error() gives a human-readable reason for the calling
+ * thread's last failure.  Work is enqueued asynchronously; a HIP failure
+ * after the pool was updated marks the pool unusable (ZP_ERR_STATE from then
+ * on).  The pool is not thread-safe: one scheduler thread owns it.
+ *
+ * Layouts (row-major, no padding):
+ *   KV pool of one layer .... [num_blocks][H][b][d] elements, one pool for K
+ *                             and one for V per layer; the (block, head) tile
+ *                             is a contiguous b*d run.
+ *   block table ............. int32 [R][n] physical block ids; logical slot j
+ *                             of a request lives in block table[j / b] at
+ *                             offset j % b.
+ *   window queries .......... [R][w][Hq][d] per layer, the queries of the
+ *                             last w cached slots (the "query slots").
+ *   decode query ............ [R][Hq][d]; output float32 [R][Hq][d].
+ * Query head hq belongs to KV head hq / G with G = Hq / H (grouped queries).
+ * Element type: float32 or bfloat16 for caches and queries alike.
+ */
+#ifndef ZP_H
+#define ZP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ZP_VERSION 1
+
+typedef enum {
+  ZP_OK = 0,
+  ZP_ERR_INVALID = 1,   /* bad argument; nothing changed */
+  ZP_ERR_NO_BLOCKS = 2, /* not enough free blocks; nothing changed */
+  ZP_ERR_HIP = 3,       /* HIP runtime failure */
+  ZP_ERR_STATE = 4      /* pool unusable after an earlier HIP failure */
+} zp_status;
+
+typedef enum { ZP_F32 = 0, ZP_BF16 = 1 } zp_dtype;
+
+/* Reason for the calling thread's last failure ("" if none). */
+const char* zp_last_error(void);
+int32_t zp_version(void);
+
+/* Geometry of a paged KV cache.  head_dim in {64, 128}, block_size in
+ * {16, 32}, num_q_heads a multiple of num_kv_heads with G in {1, 2, 4, 8}.
+ * k_cache / v_cache: host arrays of num_layers device pointers, each to a
+ * [num_blocks][num_kv_heads][block_size][head_dim] pool (caller-owned). */
+typedef struct zp_kv_cache {
+  int32_t num_layers;
+  int32_t num_kv_heads;
+  int32_t num_q_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t num_blocks;
+  int32_t dtype; /* zp_dtype */
+  void* const* k_cache;
+  void* const* v_cache;
+} zp_kv_cache;
+
+/* ------------------------------------------------------------------------
+ * Block pool (host object): reference counts per physical block, a free set
+ * handed out smallest id first, and blocks whose release waits for the GPU
+ * work that still reads them.  Sharing through reference counts and
+ * allocate-then-decrement follow the paged-cache guide ("How it works") and
+ * the shared-prefix handling of the Zipage summaries (ko page section 2.C,
+ * nl page Methodologie item 3).
+ * ---------------------------------------------------------------------- */
+typedef struct zp_block_pool zp_block_pool;
+
+#define ZP_POOL_MANUAL_FENCE 1u /* deferred frees wait for zp_block_pool_fence()
+                                   instead of HIP events (CPU-only use) */
+
+/* Create a pool of num_blocks ids, all free (refcount 0). */
+zp_status zp_block_pool_create(int32_t num_blocks, uint32_t flags, zp_block_pool** out);
+void zp_block_pool_destroy(zp_block_pool* pool);
+/* Allocate n blocks, smallest free ids first, refcount := 1; all or nothing
+ * (ZP_ERR_NO_BLOCKS leaves the pool unchanged).  Completed deferred frees are
+ * reclaimed first. */
+zp_status zp_block_alloc(zp_block_pool* pool, int32_t n, int32_t* ids_out);
+/* refcount += 1 for each id (prefix sharing); every id must be in use. */
+zp_status zp_block_share(zp_block_pool* pool, const int32_t* ids, int32_t n);
+/* refcount -= 1 for each id; ids reaching 0 are freed at once and listed in
+ * freed_out (capacity n, may be NULL) / *n_freed (may be NULL).  The caller
+ * guarantees no queued GPU work still reads them. */
+zp_status zp_block_release(zp_block_pool* pool, const int32_t* ids, int32_t n,
+                           int32_t* freed_out, int32_t* n_freed);
+int32_t zp_block_refcount(const zp_block_pool* pool, int32_t id); /* -1 if out of range */
+int32_t zp_block_num_free(const zp_block_pool* pool);    /* allocatable now */
+int32_t zp_block_num_pending(const zp_block_pool* pool); /* freed, waiting for GPU work */
+/* ZP_POOL_MANUAL_FENCE pools: mark every pending group complete. */
+zp_status zp_block_pool_fence(zp_block_pool* pool);
+/* Wait for the GPU work of every pending group and reclaim its blocks. */
+zp_status zp_block_pool_sync(zp_block_pool* pool);
+
+/* ------------------------------------------------------------------------
+ * Compression planning (host only; also called by zp_compress).
+ *
+ * Trigger (decided by the caller): each of the num_reqs requests holds
+ * exactly n_max full blocks (nl page Methodologie item 1: N_max blocks and
+ * the last block full).  Reference counts are read as they stand at the
+ * start of the call.  For each request, in order, and each logical block
+ * n < n_max-1: a block held only by this request is compacted in place; a
+ * shared block is replaced by a newly allocated target block (smallest free
+ * id) and this request drops its reference to it (ko page section 2.C: new
+ * target blocks keep the shared blocks intact).  The last logical block
+ * becomes the reserved block: kept if private, replaced by a fresh block if
+ * shared.  Blocks whose count reaches 0 are released once the GPU work of
+ * the call is done (pending until then).
+ *
+ * block_tables: HOST int32 [num_reqs][n_max], rewritten on success.
+ * src_out:      HOST int32 [num_reqs][n_max]   (the tables as they were).
+ * dst_out:      HOST int32 [num_reqs][n_max-1] (compaction targets).
+ * freed_ids:    HOST int32, capacity num_reqs*n_max; *num_freed entries.
+ * Rejected (ZP_ERR_INVALID, nothing changed): n_max < 2, num_reqs < 0, ids
+ * out of range, ids with refcount 0, an id twice in one table, an id listed
+ * more often than its refcount.  ZP_ERR_NO_BLOCKS if fewer free blocks than
+ * shared table entries.  The pending group of a plan made without
+ * zp_compress is released by zp_block_pool_fence() / zp_block_pool_sync().
+ * ---------------------------------------------------------------------- */
+zp_status zp_compress_plan(zp_block_pool* pool, int32_t n_max, int32_t num_reqs,
+                           int32_t* block_tables, int32_t* src_out, int32_t* dst_out,
+                           int32_t* freed_ids, int32_t* num_freed);
+
+/* Optional device outputs of zp_compress for checking (any may be NULL).
+ * T = n_max*block_size, K_keep = (n_max-1)*block_size. */
+typedef struct zp_compress_debug {
+  float* importance;  /* [L][R][H][T]: observation-window importance A */
+  float* redundancy;  /* [L][R][H][T]: Lightning Redundancy Score R */
+  float* score;       /* [L][R][H][T]: s = A*(1-R); slots >= T-w are not scored */
+  int32_t* kept;      /* [L][R][H][K_keep]: surviving old slots, ascending */
+} zp_compress_debug;
+
+/* Device workspace (caller-owned) needed by zp_compress. */
+size_t zp_compress_workspace_bytes(const zp_kv_cache* cache, int32_t num_reqs, int32_t n_max,
+                                   int32_t window);
+
+/* ------------------------------------------------------------------------
+ * zp_compress: one compression call over every layer for num_reqs requests
+ * that each hold n_max full blocks.
+ *
+ * Per layer l, request r and KV head h, with T = n_max*b cached slots, the
+ * window slots C..T-1 (C = T-w), and the G query heads of h:
+ *   importance  A[j] = mean over the G*w (query head, window row i) pairs of
+ *               the causal softmax, over slots 0..C+i, of q.k_j/sqrt(d), at
+ *               slot j (ko page section 2.A: scores from the queries of the
+ *               last w tokens of the last block);
+ *   redundancy  R[j] = mean cosine similarity of k_j with the other b-1 keys
+ *               of its block, 0 for a zero-norm key (Lightning Redundancy
+ *               Score: similarity only inside a block, nl page Methodologie
+ *               item 5, ko page section 2.E);
+ *   score       s[j] = A[j] * (1 - R[j]) for candidates j < C (the pages do
+ *               not say how the two combine; this is the fixed reading);
+ *   survivors   the window slots plus the K_sel = (n_max-1)*b - w candidates
+ *               with the largest s (equal s: lower slot kept), moved in
+ *               ascending slot order into logical slots 0..K_keep-1 of the
+ *               targets from zp_compress_plan, for K and V alike.
+ * Afterwards each request's table is [targets..., reserved block] and its
+ * length is K_keep; the next token goes to slot K_keep.
+ *
+ * window_q:  host array [num_layers] of device pointers to [R][w][Hq][d].
+ * workspace: device, >= zp_compress_workspace_bytes(), 256-byte aligned,
+ *            must stay untouched until the stream has passed this call.
+ * freed_ids / num_freed: as zp_compress_plan (blocks become allocatable
+ *            only after this call's GPU work has completed).
+ * stream:    hipStream_t; all device work is enqueued on it, with no
+ *            device-to-host synchronisation.
+ * Rejects (ZP_ERR_INVALID) everything zp_compress_plan rejects, plus bad
+ * geometry, window < 1 or window > block_size, NULL pointers, a short or
+ * misaligned workspace, and a pool created with ZP_POOL_MANUAL_FENCE.
+ * ---------------------------------------------------------------------- */
+zp_status zp_compress(const zp_kv_cache* cache, zp_block_pool* pool, int32_t n_max,
+                      int32_t window, int32_t num_reqs, int32_t* block_tables,
+                      const void* const* window_q, void* workspace, size_t workspace_bytes,
+                      int32_t* freed_ids, int32_t* num_freed, void* stream,
+                      const zp_compress_debug* debug);
+
+/* ------------------------------------------------------------------------
+ * zp_append_kv: write one new token per request into layer `layer`.
+ * k_new, v_new: device [R][H][d]; slot_mapping: device int32 [R], physical
+ * slot block*b + offset (negative = skip).  Tokens go into the last
+ * partially filled block, as in paged attention ("How it works": a new block
+ * only when the previous ones are full).
+ * ---------------------------------------------------------------------- */
+zp_status zp_append_kv(const zp_kv_cache* cache, int32_t layer, int32_t num_reqs,
+                       const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                       void* stream);
+
+/* Device workspace for zp_paged_decode with tables of max_blocks columns. */
+size_t zp_paged_decode_workspace_bytes(const zp_kv_cache* cache, int32_t num_reqs,
+                                       int32_t max_blocks);
+
+/* ------------------------------------------------------------------------
+ * zp_paged_decode: attention of one new query per request over its cached
+ * slots, read through the block table ("How it works": logical blocks map to
+ * non-contiguous physical blocks).  For request r and query head hq:
+ *   out[r][hq] = sum over j < seq_lens[r] of softmax_j(scale * q.k_j) v_j
+ * with k_j, v_j of KV head hq/G at block block_tables[r][j/b], offset j%b.
+ * q: device [R][Hq][d] (cache dtype); block_tables: device int32
+ * [R][max_blocks]; seq_lens: device int32 [R], 0 <= seq_len <= max_blocks*b
+ * (0 gives a zero output); out: device float32 [R][Hq][d]; workspace:
+ * device, >= zp_paged_decode_workspace_bytes().  Entries of a table beyond
+ * ceil(seq_len/b) are never read.
+ * ---------------------------------------------------------------------- */
+zp_status zp_paged_decode(const zp_kv_cache* cache, int32_t layer, int32_t num_reqs,
+                          const void* q, const int32_t* block_tables, int32_t max_blocks,
+                          const int32_t* seq_lens, float scale, float* out, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZP_H */

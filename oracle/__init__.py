@@ -187,8 +187,9 @@ class CompressResult:
     v_pool: List[np.ndarray]
 
 
-def compress(case, layers: Optional[List[int]] = None) -> CompressResult:
-    """The whole compression call of a synthetic case, step by step."""
+def compress(case, layers: Optional[List[int]] = None, with_pools: bool = True) -> CompressResult:
+    """The whole compression call of a synthetic case, step by step
+    (``with_pools=False`` skips the out-of-place compaction of the pools)."""
     g = case.geom
     n_max, w, b = case.n_max, case.window, g.block_size
     k_keep = (n_max - 1) * b
@@ -207,6 +208,7 @@ def compress(case, layers: Optional[List[int]] = None) -> CompressResult:
         out.R.append(Rr)
         out.s.append(s)
         out.kept.append(kept)
-        out.k_pool.append(compact(case.k_pool[layer], p.src, p.dst, kept, n_max=n_max))
-        out.v_pool.append(compact(case.v_pool[layer], p.src, p.dst, kept, n_max=n_max))
+        if with_pools:
+            out.k_pool.append(compact(case.k_pool[layer], p.src, p.dst, kept, n_max=n_max))
+            out.v_pool.append(compact(case.v_pool[layer], p.src, p.dst, kept, n_max=n_max))
     return out

@@ -1,0 +1,183 @@
+"""Helpers for the GPU parity tests: run a synthetic case through the HIP
+library and compare every output with the CPU oracle.
+
+Tolerances (fixed by the task's parity contract):
+  * importance A and combined score s: |gpu - cpu| <= 1e-3 |cpu| + 1e-30;
+  * redundancy R: |gpu - cpu| <= 1e-3 absolute (it crosses zero);
+  * survivor sets: the GPU decision must be exactly what the oracle's
+    selection rule gives on the GPU's own float32 scores, and may differ
+    from the oracle's fp64 decision only at slots whose oracle score is
+    within 1e-4 (relative) of the oracle's K_sel-th largest score;
+  * compacted K/V: bit-exact copies of the source rows the GPU kept;
+  * tables, refcounts, freed ids: exact;
+  * decode output: |gpu - cpu| <= 2e-3 absolute (float32 output, bf16 or
+    float32 inputs, float32 accumulation on the GPU, double in the oracle).
+"""
+from __future__ import annotations
+
+import sys
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+import compressed_paged_kv_amd as zp
+import oracle
+from synth.device import to_numpy, to_tensor
+
+A_RTOL, S_RTOL, FLOOR = 1e-3, 1e-3, 1e-30
+R_ATOL = 1e-3
+TIE_RTOL = 1e-4
+DECODE_ATOL = 2e-3
+
+
+def say(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@dataclass
+class GpuRun:
+    tables: np.ndarray
+    refcounts: np.ndarray
+    freed: np.ndarray
+    A: np.ndarray        # [L][R][H][T]
+    R: np.ndarray
+    s: np.ndarray
+    kept: np.ndarray     # [L][R][H][K_keep]
+    k_pool: list         # host copies after compression
+    v_pool: list
+    out: np.ndarray      # decode output [L][R][Hq][d]
+    appended_k: list     # host pools after the append (for the decode check)
+    appended_v: list
+
+
+def run_case(case, device="cuda", decode=True) -> GpuRun:
+    g = case.geom
+    L, H, b, n_max, w = g.num_layers, g.num_kv_heads, g.block_size, case.n_max, case.window
+    R = case.num_reqs
+    T, k_keep = n_max * b, (n_max - 1) * b
+    kp = [to_tensor(x, device) for x in case.k_pool]
+    vp = [to_tensor(x, device) for x in case.v_pool]
+    wq = [to_tensor(x, device) for x in case.window_q]
+    cache = zp.KVCache(kp, vp, g.num_q_heads)
+    pool = zp.BlockPool.from_refcounts(case.refcounts)
+    tables = case.tables.copy()
+    ws = torch.empty(zp.compress_workspace_bytes(cache, R, n_max, w), dtype=torch.uint8,
+                     device=device)
+    dbg = dict(importance=torch.full((L, R, H, T), float("nan"), device=device),
+               redundancy=torch.full((L, R, H, T), float("nan"), device=device),
+               score=torch.full((L, R, H, T), float("nan"), device=device),
+               kept=torch.full((L, R, H, k_keep), -1, dtype=torch.int32, device=device))
+    freed = zp.compress(cache, pool, n_max, w, tables, wq, ws, debug=dbg)
+    torch.cuda.synchronize()
+    run = GpuRun(tables=tables.copy(), refcounts=pool.refcounts(), freed=freed.copy(),
+                 A=dbg["importance"].cpu().numpy(), R=dbg["redundancy"].cpu().numpy(),
+                 s=dbg["score"].cpu().numpy(), kept=dbg["kept"].cpu().numpy(),
+                 k_pool=[to_numpy(t) for t in kp], v_pool=[to_numpy(t) for t in vp],
+                 out=None, appended_k=None, appended_v=None)
+    if decode:
+        slot = tables[:, k_keep // b] * b + k_keep % b
+        slot_t = torch.from_numpy(slot.astype(np.int32)).to(device)
+        tab_t = torch.from_numpy(tables).to(device)
+        seq = torch.full((R,), k_keep + 1, dtype=torch.int32, device=device)
+        dws_bytes = zp.paged_decode_workspace_bytes(cache, R, n_max)
+        dws = torch.empty(max(dws_bytes, 16), dtype=torch.uint8, device=device)
+        outs = []
+        for layer in range(L):
+            zp.append_kv(cache, layer, to_tensor(case.k_new[layer], device),
+                         to_tensor(case.v_new[layer], device), slot_t)
+            out = torch.empty((R, g.num_q_heads, g.head_dim), dtype=torch.float32, device=device)
+            zp.paged_decode(cache, layer, to_tensor(case.q_new[layer], device), tab_t, seq,
+                            1.0 / np.sqrt(g.head_dim), out, dws)
+            outs.append(out)
+        torch.cuda.synchronize()
+        run.out = np.stack([o.cpu().numpy() for o in outs])
+        run.appended_k = [to_numpy(t) for t in kp]
+        run.appended_v = [to_numpy(t) for t in vp]
+    pool.sync()
+    return run
+
+
+def words(pool: np.ndarray) -> np.ndarray:
+    """A [nb][H][b][d] pool viewed as 64-bit words per row (bit patterns)."""
+    nb, H, b, d = pool.shape
+    return np.ascontiguousarray(pool).view(np.uint64).reshape(nb, H, b, -1)
+
+
+def rel_ok(got, want, rtol, floor=FLOOR):
+    return np.abs(got - want) <= rtol * np.abs(want) + floor
+
+
+def check_case(case, run: GpuRun, *, check_decode=True, layers=None) -> dict:
+    """Compare one GPU run with the oracle; raises AssertionError on failure.
+    Returns a few statistics for the log."""
+    g = case.geom
+    b, n_max, w = g.block_size, case.n_max, case.window
+    T, k_keep = n_max * b, (n_max - 1) * b
+    C, k_sel = T - w, k_keep - w
+    layers = list(range(g.num_layers)) if layers is None else layers
+    ref = oracle.compress(case, layers=layers, with_pools=False)
+    # bookkeeping, exact
+    np.testing.assert_array_equal(run.tables, ref.plan.tables)
+    np.testing.assert_array_equal(run.refcounts, ref.plan.refcounts)
+    np.testing.assert_array_equal(np.sort(run.freed), np.sort(ref.plan.freed))
+    stats = dict(max_rel_A=0.0, max_abs_R=0.0, max_rel_s=0.0, near_tie_diffs=0, max_abs_out=0.0)
+    dst_blocks = set(ref.plan.dst.reshape(-1).tolist())
+    for li, layer in enumerate(layers):
+        A, Rr, s = run.A[layer], run.R[layer], run.s[layer]
+        Ao, Ro, so = ref.A[li], ref.R[li], ref.s[li]
+        assert np.isfinite(A).all() and np.isfinite(Rr).all()
+        okA = rel_ok(A, Ao, A_RTOL)
+        assert okA.all(), f"layer {layer}: importance off at {np.argwhere(~okA)[:5]}"
+        okR = np.abs(Rr - Ro) <= R_ATOL
+        assert okR.all(), f"layer {layer}: redundancy off at {np.argwhere(~okR)[:5]}"
+        okS = rel_ok(s[..., :C], so[..., :C], S_RTOL)
+        assert okS.all(), f"layer {layer}: score off at {np.argwhere(~okS)[:5]}"
+        stats["max_rel_A"] = max(stats["max_rel_A"], float(np.max(np.abs(A - Ao) / np.abs(Ao))))
+        stats["max_abs_R"] = max(stats["max_abs_R"], float(np.max(np.abs(Rr - Ro))))
+        stats["max_rel_s"] = max(stats["max_rel_s"],
+                                 float(np.max(np.abs(s[..., :C] - so[..., :C]) / np.abs(so[..., :C]))))
+        kept = run.kept[layer]
+        # the GPU decision is exactly the selection rule applied to its own scores
+        own = np.full(s.shape, np.nan)
+        own[..., :C] = s[..., :C].astype(np.float64)
+        np.testing.assert_array_equal(kept, oracle.select(own, w, k_sel))
+        # and differs from the oracle's decision only at near-ties
+        ko = ref.kept[li]
+        for r, h in zip(*np.nonzero(np.any(kept != ko, axis=-1))):
+            gs, os_ = set(kept[r, h].tolist()), set(ko[r, h].tolist())
+            tau = np.sort(so[r, h, :C])[::-1][k_sel - 1]
+            for j in gs ^ os_:
+                assert abs(so[r, h, j] - tau) <= TIE_RTOL * abs(tau), \
+                    f"layer {layer} req {r} head {h}: slot {j} differs, not a near tie"
+            stats["near_tie_diffs"] += len(gs ^ os_)
+        # compacted bytes: GPU rows == source rows at the GPU's own kept slots
+        ri = np.arange(kept.shape[0])[:, None, None]
+        hi = np.arange(kept.shape[1])[None, :, None]
+        kk = np.arange(k_keep)[None, None, :]
+        others = np.array(sorted(set(range(g.num_blocks)) - dst_blocks), dtype=np.int64)
+        for pool_before, pool_after in ((case.k_pool[layer], run.k_pool[layer]),
+                                        (case.v_pool[layer], run.v_pool[layer])):
+            pb, pa = words(pool_before), words(pool_after)
+            want = pb[ref.plan.src[ri, kept // b], hi, kept % b]        # [R][H][K_keep][W]
+            got = pa[run.tables[ri, kk // b], hi, kk % b]
+            bad = np.any(got != want, axis=-1)
+            assert not bad.any(), f"layer {layer}: compacted rows differ at {np.argwhere(bad)[:5]}"
+            # every block that is not a compaction target is untouched
+            assert np.array_equal(pa[others], pb[others]), f"layer {layer}: a non-target block changed"
+        if check_decode and run.out is not None:
+            # oracle decode on the GPU-compacted, GPU-appended cache
+            seq = np.full(run.tables.shape[0], k_keep + 1, dtype=np.int32)
+            kp, vp = run.k_pool[layer].copy(), run.v_pool[layer].copy()
+            slot = (run.tables[:, k_keep // b] * b + k_keep % b).astype(np.int32)
+            oracle.append(kp, vp, case.k_new[layer], case.v_new[layer], slot)
+            assert np.array_equal(words(run.appended_k[layer]), words(kp))
+            assert np.array_equal(words(run.appended_v[layer]), words(vp))
+            want = oracle.decode(kp, vp, case.q_new[layer], run.tables, seq,
+                                 num_q_heads=g.num_q_heads)
+            err = np.abs(run.out[layer] - want)
+            assert np.isfinite(run.out[layer]).all()
+            assert err.max() <= DECODE_ATOL, f"layer {layer}: decode error {err.max()}"
+            stats["max_abs_out"] = max(stats["max_abs_out"], float(err.max()))
+    return stats

@@ -1,0 +1,177 @@
+"""GPU parity: the HIP path against the CPU oracle, element by element.
+
+Every case prints its name and shape before it touches the GPU.  Shapes
+span several score chunks and compaction tiles with ragged tails (n_max not a
+multiple of the 512-token chunk, G*w not a multiple of 16, C not a multiple
+of 256), both block sizes, both head dims, both element types and group
+sizes 1..8; the Qwen3-8B-shaped layer runs at its full size (64 requests,
+budget 2048) in the launch configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_common import DECODE_ATOL, check_case, run_case, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import compressed_paged_kv_amd as zp
+    zp.lib()  # raises if the HIP library is missing
+
+
+def _case(name, seed, **kw):
+    base = dict(num_reqs=2, num_layers=1, num_kv_heads=2, num_q_heads=4, head_dim=128,
+                block_size=16, n_max=12, window=16, num_blocks=64, dtype="bf16")
+    base.update(kw)
+    return synth.make_case(name, seed, **base)
+
+
+CASES = {
+    # the tiny CPU-checkable workload: fp32, d=64, b=16, N_max=8, w=8, G=2
+    "tiny": lambda: synth.case_tiny(),
+    # ragged: 37 blocks -> two score chunks, the second partial; G*w = 64
+    "bf16_d128_b16_ragged": lambda: _case("r1", 201, num_reqs=3, n_max=37, num_blocks=160,
+                                          num_kv_heads=2, num_q_heads=8),
+    # b=32, w=32, G=4 -> 128 window rows (8 row tiles), d=64
+    "bf16_d64_b32_rows128": lambda: _case("r2", 202, head_dim=64, block_size=32, n_max=20,
+                                          window=32, num_q_heads=8, num_blocks=64),
+    # fp32, b=32, w=5, G=1 -> 5 rows padded to one tile, d=128
+    "f32_d128_b32_w5": lambda: _case("r3", 203, dtype="f32", block_size=32, n_max=9, window=5,
+                                     num_q_heads=2, num_blocks=40),
+    # G=8 (decode splits the group over two workgroups), 128 rows
+    "bf16_g8": lambda: _case("r4", 204, num_kv_heads=1, num_q_heads=8, n_max=16, num_blocks=40),
+    # f32, d=64, b=16, w=1 (a single window query), G=4
+    "f32_d64_w1": lambda: _case("r5", 205, dtype="f32", head_dim=64, window=1, n_max=10,
+                                num_q_heads=8, num_blocks=40),
+    # two layers, shared prefix of 3 blocks among 4 requests (new target blocks)
+    "shared_prefix_2layers": lambda: _case("r6", 206, num_reqs=4, num_layers=2, n_max=12,
+                                           num_blocks=80, shared_prefix_blocks=3),
+    # per-head key scales as in the Qwen3-8B-shaped workload, longer cache
+    "bf16_scaled_keys": lambda: _case("r7", 207, num_reqs=2, n_max=64, num_kv_heads=2,
+                                      num_q_heads=8, num_blocks=160, key_scale_range=(0.5, 2.0)),
+    # AR(1) keys with planted x8 keys (structured budget-4096 shape, reduced)
+    "ar1_planted_b32": lambda: _case("r8", 208, block_size=32, window=32, n_max=24,
+                                     num_q_heads=8, num_blocks=64, key_kind="ar1",
+                                     planted_frac=0.01),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_compress_and_decode_match_oracle(name):
+    case = CASES[name]()
+    g = case.geom
+    say(f"[gpu parity] {name}: R={case.num_reqs} L={g.num_layers} H={g.num_kv_heads} "
+        f"Hq={g.num_q_heads} d={g.head_dim} b={g.block_size} n_max={case.n_max} "
+        f"w={case.window} dtype={g.dtype}")
+    run = run_case(case)
+    stats = check_case(case, run)
+    say(f"[gpu parity] {name}: ok {stats}")
+
+
+def _exact_tie_case(dtype, d, b, n_max, w):
+    """Zero window queries and, inside every block, keys along distinct
+    coordinate axes: every logit is 0 and every in-block cosine is exactly 0,
+    so all candidates carry the same score and the tie rule alone decides."""
+    c = _case("tie", 209, dtype=dtype, head_dim=d, block_size=b, n_max=n_max, window=w,
+              num_blocks=4 * n_max)
+    R, H = c.num_reqs, c.geom.num_kv_heads
+    T = n_max * b
+    K = np.zeros((R, H, T, d))
+    for j in range(T):
+        K[:, :, j, j % b] = 1.0 + (j % 3)
+    c.k_pool[0] = synth.pool_from_logical(K, c.tables, c.geom.num_blocks, dtype)
+    c.window_q[0] = np.zeros_like(c.window_q[0])
+    return c
+
+
+@pytest.mark.parametrize("dtype,d,b,n_max,w", [("bf16", 128, 16, 20, 16), ("f32", 64, 16, 8, 8),
+                                               ("bf16", 64, 32, 9, 7)])
+def test_exact_ties_keep_the_lower_slots(dtype, d, b, n_max, w):
+    case = _exact_tie_case(dtype, d, b, n_max, w)
+    say(f"[gpu parity] exact tie {dtype} d={d} b={b} n_max={n_max} w={w}")
+    run = run_case(case)
+    T, k_keep = n_max * b, (n_max - 1) * b
+    C = T - w
+    E = C - (k_keep - w)
+    want = np.array(list(range(C - E)) + list(range(C, T)))
+    assert np.all(run.R[0] == 0.0)
+    cand = run.s[0][..., :C]
+    assert np.all(cand == cand[..., :1])          # bit-identical scores
+    for r in range(case.num_reqs):
+        for h in range(case.geom.num_kv_heads):
+            np.testing.assert_array_equal(run.kept[0, r, h], want)
+    check_case(case, run)
+
+
+def test_qwen3_8b_layer_full_size():
+    """64 requests at budget 2048 (N_max=128, b=16, w=16), 8 KV / 32 query
+    heads, d=128, bf16, pool of 16384 blocks: every output compared."""
+    case = synth.case_qwen3_8b_layer()
+    say("[gpu parity] qwen3-8b layer, 64 requests, budget 2048")
+    run = run_case(case)
+    stats = check_case(case, run)
+    say(f"[gpu parity] qwen3-8b layer: ok {stats}")
+
+
+# ---------------------------------------------------------------- decode alone
+
+@pytest.mark.parametrize("dtype,d,b,G", [("bf16", 128, 16, 4), ("f32", 64, 32, 2), ("bf16", 64, 16, 8),
+                                         ("f32", 128, 16, 1)])
+def test_paged_decode_ragged_lengths(dtype, d, b, G):
+    import compressed_paged_kv_amd as zp
+    from synth.device import to_tensor
+    H, max_blocks = 2, 40
+    seqs = np.array([0, 1, b - 1, b, b + 1, 7 * b + 3, 16 * b, 16 * b + 1, 33 * b - 5,
+                     max_blocks * b], dtype=np.int32)
+    R = seqs.size
+    c = _case("dec", 210, dtype=dtype, head_dim=d, block_size=b, num_reqs=R, num_kv_heads=H,
+              num_q_heads=H * G, n_max=max_blocks, window=1, num_blocks=R * max_blocks + 3)
+    say(f"[gpu parity] decode {dtype} d={d} b={b} G={G} seqs={seqs.tolist()}")
+    dev = "cuda"
+    kp, vp = to_tensor(c.k_pool[0], dev), to_tensor(c.v_pool[0], dev)
+    cache = zp.KVCache([kp], [vp], H * G)
+    tab = torch.from_numpy(c.tables).to(dev)
+    seq_t = torch.from_numpy(seqs).to(dev)
+    out = torch.full((R, H * G, d), float("nan"), device=dev)
+    ws = torch.empty(max(zp.paged_decode_workspace_bytes(cache, R, max_blocks), 16),
+                     dtype=torch.uint8, device=dev)
+    zp.paged_decode(cache, 0, to_tensor(c.q_new[0], dev), tab, seq_t, 1.0 / np.sqrt(d), out, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    want = oracle.decode(c.k_pool[0], c.v_pool[0], c.q_new[0], c.tables, seqs, num_q_heads=H * G)
+    assert np.isfinite(got).all()
+    np.testing.assert_array_equal(got[0], 0.0)      # empty sequence -> zeros
+    err = np.abs(got - want)
+    assert err.max() <= DECODE_ATOL, err.max()
+
+
+def test_append_then_decode_one_token():
+    """A request of length 1: the appended row is the only key, so the output
+    equals the appended value exactly (softmax over one slot)."""
+    import compressed_paged_kv_amd as zp
+    from synth.device import to_tensor
+    c = _case("app", 211, dtype="f32", num_reqs=3, n_max=4, num_blocks=16, head_dim=64)
+    dev = "cuda"
+    kp, vp = to_tensor(c.k_pool[0], dev), to_tensor(c.v_pool[0], dev)
+    cache = zp.KVCache([kp], [vp], 4)
+    slot = (c.tables[:, 0] * 16).astype(np.int32)
+    slot[1] = -1                                     # skipped
+    zp.append_kv(cache, 0, to_tensor(c.k_new[0], dev), to_tensor(c.v_new[0], dev),
+                 torch.from_numpy(slot).to(dev))
+    out = torch.empty((3, 4, 64), device=dev)
+    zp.paged_decode(cache, 0, to_tensor(c.q_new[0], dev), torch.from_numpy(c.tables).to(dev),
+                    torch.ones(3, dtype=torch.int32, device=dev), 0.125, out, None)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for r in (0, 2):
+        for hq in range(4):
+            np.testing.assert_array_equal(got[r, hq], c.v_new[0][r, hq // 2])
+    blk = int(c.tables[1, 0])
+    np.testing.assert_array_equal(kp[blk].cpu().numpy(), c.k_pool[0][blk])

@@ -1,0 +1,278 @@
+"""Host-side checks of the C ABI (no GPU work): symbols, block pool,
+planner parity with the oracle, and argument validation."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import compressed_paged_kv_amd as zp
+import oracle
+import synth
+from compressed_paged_kv_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if not fn.endswith(".h"):
+            continue
+        text = open(os.path.join(ROOT, "include", fn)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^\s*[\w\s\*]+?\b(zp_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared_functions()
+    assert "zp_compress" in names and "zp_paged_decode" in names and "zp_block_alloc" in names
+    lib = zp.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (zp_\w+)", out))
+    assert set(names) <= exported
+    assert zp.lib().zp_version() == 1
+
+
+def test_library_links_no_oracle():
+    out = subprocess.run(["nm", "-D", B.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    assert "zpo_" not in out
+    deps = subprocess.run(["ldd", B.LIB_PATH], capture_output=True, text=True).stdout
+    assert "oracle" not in deps
+
+
+# ------------------------------------------------------------------ block pool
+
+def test_pool_alloc_smallest_first_and_all_or_nothing():
+    p = zp.BlockPool(8, manual_fence=True)
+    assert p.alloc(3).tolist() == [0, 1, 2]
+    p.release([1])
+    assert p.alloc(2).tolist() == [1, 3]
+    assert p.num_free() == 4
+    with pytest.raises(zp.ZpError) as e:
+        p.alloc(5)
+    assert e.value.status == zp.ZP_ERR_NO_BLOCKS
+    assert p.num_free() == 4
+    assert [p.refcount(i) for i in range(8)] == [1, 1, 1, 1, 0, 0, 0, 0]
+
+
+def test_pool_share_release_and_errors():
+    p = zp.BlockPool(6, manual_fence=True)
+    ids = p.alloc(2)
+    p.share([ids[0], ids[0]])
+    assert p.refcount(ids[0]) == 3
+    assert p.release([ids[0]]).tolist() == []
+    assert p.release([ids[0], ids[0], ids[1]]).tolist() == [ids[0], ids[1]]
+    assert p.num_free() == 6
+    for bad in ([7], [-1]):
+        with pytest.raises(zp.ZpError) as e:
+            p.share(bad)
+        assert e.value.status == zp.ZP_ERR_INVALID
+    with pytest.raises(zp.ZpError):
+        p.share([2])                  # not allocated
+    x = p.alloc(1)
+    with pytest.raises(zp.ZpError):
+        p.release([x[0], x[0]])       # more releases than references
+    assert p.refcount(int(x[0])) == 1
+    assert p.refcount(99) == -1
+
+
+def test_pool_from_refcounts_roundtrip():
+    rc = np.array([0, 2, 1, 0, 5, 1], dtype=np.int32)
+    p = zp.BlockPool.from_refcounts(rc, manual_fence=True)
+    np.testing.assert_array_equal(p.refcounts(), rc)
+    assert p.num_free() == 2
+
+
+# ------------------------------------------------------------------ planner
+
+def _scenario(seed):
+    rng = np.random.default_rng(seed)
+    pool = int(rng.integers(40, 90))
+    n_max = int(rng.integers(2, 7))
+    R = int(rng.integers(1, 6))
+    ids = rng.permutation(pool)
+    tables = ids[: R * n_max].reshape(R, n_max).astype(np.int32)
+    # share some blocks between requests (prefix-like and random)
+    if R > 1 and rng.random() < 0.8:
+        P = int(rng.integers(1, n_max + 1))
+        tables[:, :P] = tables[0, :P]
+    for _ in range(int(rng.integers(0, 3))):
+        r1, r2 = rng.integers(0, R, size=2)
+        n1, n2 = rng.integers(0, n_max, size=2)
+        if r1 != r2 and tables[r2, n2] not in tables[r1]:
+            tables[r1, n1] = tables[r2, n2]
+    rc = np.zeros(pool, dtype=np.int32)
+    np.add.at(rc, tables.reshape(-1), 1)
+    # external holders (e.g. a prefix cache) on a few blocks
+    for x in rng.choice(np.flatnonzero(rc > 0), size=2):
+        rc[x] += int(rng.integers(0, 2))
+    return tables, rc, n_max
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_planner_matches_oracle(seed):
+    tables, rc, n_max = _scenario(seed)
+    want = oracle.plan(rc, tables, n_max)
+    pool = zp.BlockPool.from_refcounts(rc, manual_fence=True)
+    tab = tables.copy()
+    if want.status == oracle.NO_BLOCKS:
+        with pytest.raises(zp.ZpError) as e:
+            zp.compress_plan(pool, n_max, tab)
+        assert e.value.status == zp.ZP_ERR_NO_BLOCKS
+        np.testing.assert_array_equal(tab, tables)
+        np.testing.assert_array_equal(pool.refcounts(), rc)
+        return
+    assert want.status == oracle.OK
+    src, dst, freed = zp.compress_plan(pool, n_max, tab)
+    np.testing.assert_array_equal(tab, want.tables)
+    np.testing.assert_array_equal(src, want.src)
+    np.testing.assert_array_equal(dst, want.dst[:, : n_max - 1])
+    np.testing.assert_array_equal(freed, want.freed)
+    np.testing.assert_array_equal(pool.refcounts(), want.refcounts)
+    # freed blocks wait for the fence
+    assert pool.num_pending() == freed.size
+    before = pool.num_free()
+    pool.fence()
+    assert pool.num_pending() == 0
+    assert pool.num_free() == before + freed.size
+    # invariants: counts = table references + external holders; freed in no table
+    ext = rc.copy()
+    np.subtract.at(ext, tables.reshape(-1), 1)
+    want_rc = ext.copy()
+    np.add.at(want_rc, tab.reshape(-1), 1)
+    np.testing.assert_array_equal(pool.refcounts(), want_rc)
+    assert not set(freed.tolist()) & set(tab.reshape(-1).tolist())
+
+
+def test_planner_invalid_inputs_change_nothing():
+    tables = np.array([[3, 4, 5], [6, 7, 5]], dtype=np.int32)
+    rc = np.zeros(10, dtype=np.int32)
+    np.add.at(rc, tables.reshape(-1), 1)
+    pool = zp.BlockPool.from_refcounts(rc, manual_fence=True)
+    for bad in ([[3, 3, 5]], [[3, 4, 10]], [[3, 4, 0]], [[5, 4, 3], [5, 6, 7], [5, 1, 2]]):
+        t = np.array(bad, dtype=np.int32)
+        t0 = t.copy()
+        with pytest.raises(zp.ZpError) as e:
+            zp.compress_plan(pool, 3, t)
+        assert e.value.status == zp.ZP_ERR_INVALID
+        np.testing.assert_array_equal(t, t0)
+        np.testing.assert_array_equal(pool.refcounts(), rc)
+    with pytest.raises(zp.ZpError):
+        zp.compress_plan(pool, 1, np.array([[3]], dtype=np.int32))
+
+
+def test_planner_shared_prefix_case_conserves_refcounts():
+    c = synth.make_case("pfx", 31, num_reqs=6, num_layers=1, num_kv_heads=1, num_q_heads=1,
+                        head_dim=64, block_size=16, n_max=9, window=16, num_blocks=120,
+                        dtype="f32", shared_prefix_blocks=4)
+    pool = zp.BlockPool.from_refcounts(c.refcounts, manual_fence=True)
+    tab = c.tables.copy()
+    src, dst, freed = zp.compress_plan(pool, 9, tab)
+    prefix = c.tables[0, :4]
+    assert sorted(freed.tolist()) == sorted(prefix.tolist())
+    assert all(pool.refcount(int(x)) == 0 for x in prefix)
+    assert pool.num_pending() == 4
+    total = sum(pool.refcount(i) for i in range(120))
+    assert total == tab.size
+
+
+# ------------------------------------------------------------------ validation
+
+class _FakeTensor:
+    """Host buffer posing as a device tensor for calls that must fail in
+    validation before touching any device memory."""
+
+    def __init__(self, shape, dtype_name, nbytes=64):
+        self.shape = shape
+        self.dtype = dtype_name
+        self._buf = ctypes.create_string_buffer(max(nbytes, 64) + 256)
+        self._ptr = (ctypes.addressof(self._buf) + 255) // 256 * 256
+
+    def data_ptr(self):
+        return self._ptr
+
+    def is_contiguous(self):
+        return True
+
+    def numel(self):
+        return 64
+
+    def element_size(self):
+        return 1
+
+
+def _fake_cache(L=1, H=2, Hq=4, d=64, b=16, nb=16, dtype="torch.float32"):
+    ks = [_FakeTensor((nb, H, b, d), dtype) for _ in range(L)]
+    vs = [_FakeTensor((nb, H, b, d), dtype) for _ in range(L)]
+    return zp.KVCache(ks, vs, Hq)
+
+
+def test_compress_rejects_bad_arguments_before_any_work():
+    cache = _fake_cache()
+    n_max = 8
+    pool = zp.BlockPool(16)
+    tables = np.arange(8, dtype=np.int32)[None].copy()
+    pool.alloc(8)
+    wq = [_FakeTensor((1, 8, 4, 64), "torch.float32")]
+    ws = _FakeTensor((1,), "torch.uint8")
+    for kwargs in (dict(window=0), dict(window=17), dict(n_max=1)):
+        args = dict(n_max=n_max, window=8)
+        args.update(kwargs)
+        t = tables.copy()
+        with pytest.raises(zp.ZpError) as e:
+            zp.compress(cache, pool, args["n_max"], args["window"], t, wq, ws, stream=0)
+        assert e.value.status == zp.ZP_ERR_INVALID
+        np.testing.assert_array_equal(t, tables)
+    # workspace too small (the fake reports 64 bytes)
+    with pytest.raises(zp.ZpError) as e:
+        zp.compress(cache, pool, n_max, 8, tables.copy(), wq, ws, stream=0)
+    assert e.value.status == zp.ZP_ERR_INVALID and "workspace" in str(e.value)
+    assert [pool.refcount(i) for i in range(8)] == [1] * 8
+    # manual-fence pools are for host planning only
+    mpool = zp.BlockPool(16, manual_fence=True)
+    with pytest.raises(zp.ZpError):
+        zp.compress(cache, mpool, n_max, 8, tables.copy(), wq, ws, stream=0)
+
+
+@pytest.mark.parametrize("field,value", [("head_dim", 96), ("block_size", 8), ("num_q_heads", 6),
+                                         ("num_q_heads", 32)])
+def test_geometry_validation(field, value):
+    cache = _fake_cache()
+    setattr(cache.c, field, value)
+    assert zp.lib().zp_compress_workspace_bytes(cache.ref, 1, 8, 8) == 0
+    assert zp.last_error()
+
+
+def test_workspace_sizes_grow_with_the_batch():
+    cache = _fake_cache(L=2, H=8, Hq=32, d=128, b=16, nb=4096, dtype="torch.bfloat16")
+    a = zp.compress_workspace_bytes(cache, 1, 128, 16)
+    b = zp.compress_workspace_bytes(cache, 64, 128, 16)
+    assert 0 < a < b and b % 256 == 0
+    # the score buffer alone: L*R*H*T floats
+    assert b >= 2 * 64 * 8 * 2048 * 4
+    assert zp.paged_decode_workspace_bytes(cache, 64, 8) == 0        # one split
+    assert zp.paged_decode_workspace_bytes(cache, 64, 128) == 64 * 32 * 8 * 130 * 4
+
+
+def test_decode_and_append_reject_bad_arguments():
+    cache = _fake_cache()
+    t = _FakeTensor((1,), "torch.int32")
+    tab = _FakeTensor((1, 8), "torch.int32")
+    with pytest.raises(zp.ZpError):
+        zp.paged_decode(cache, 1, t, tab, t, 0.125, t, None, stream=0)      # layer out of range
+    with pytest.raises(zp.ZpError):
+        zp.paged_decode(cache, 0, t, tab, t, -1.0, t, None, stream=0)       # bad scale
+    tab_big = _FakeTensor((1, 64), "torch.int32")
+    with pytest.raises(zp.ZpError) as e:
+        zp.paged_decode(cache, 0, t, tab_big, t, 0.125, t, None, stream=0)  # needs a workspace
+    assert "workspace" in str(e.value)
+    lib = zp.lib()
+    assert lib.zp_append_kv(cache.ref, 3, 1, t.data_ptr(), t.data_ptr(), t.data_ptr(), None) == \
+        zp.ZP_ERR_INVALID
