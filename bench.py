@@ -1,0 +1,358 @@
+#!/usr/bin/env python
+"""Benchmark of the Compressed PagedAttention hot path on one MI355X.
+
+Workload (one "step"): the Qwen3-8B-shaped layer at budget 2048 -- 64
+requests, 8 KV / 32 query heads, head_dim 128, bf16 K/V, block 16,
+N_max = 128, window 16, 16384-block pool with the requests' blocks
+scattered at random.  Every request holds 128 full blocks; one step is the
+whole hot path over that batch: plan the targets on the host, compress all
+64 (request, layer) caches (window importance + Lightning Redundancy Score,
+per-head selection, in-place order-preserving compaction of K and V), append
+the pending token of every request at slot 2032, and run paged decode over
+the 2033 cached tokens.  After a step each request again holds 128 full
+blocks (127 compacted + the reserved block, which keeps the appended token
+and the block's older rows), so the next step repeats the same work.
+
+Printed (one JSON line on stdout): value = (request, layer) compressions per
+second of the whole step, decode tokens/s, per-kernel times from HIP events
+recorded live on the launch stream over the timed region, the roofline of
+the dominant kernel, and the CPU oracle timed on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KV compressions/sec + decode tok/s at budget 2048; % of HBM peak GB/s"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "hot_path_kernels_qwen3_8b_layer_budget2048.txt")
+KERNEL_SOURCES = {
+    "compact": "compressed_paged_kv_amd/csrc/k_compact.hip",
+    "score_stats": "compressed_paged_kv_amd/csrc/k_score.hip",
+    "score": "compressed_paged_kv_amd/csrc/k_score.hip",
+    "select": "compressed_paged_kv_amd/csrc/k_select.hip",
+    "decode": "compressed_paged_kv_amd/csrc/k_decode.hip",
+    "combine": "compressed_paged_kv_amd/csrc/k_decode.hip",
+    "append": "compressed_paged_kv_amd/csrc/k_decode.hip",
+}
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_sha(rel: str) -> str:
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_counters(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when absent or taken on a different kernel source."""
+    if not os.path.exists(PROFILE_COUNTERS):
+        return None
+    text = open(PROFILE_COUNTERS).read()
+    m = re.search(rf"^phase {kernel}: fetch_bytes=(\d+) write_bytes=(\d+) source_sha=(\w+)", text,
+                  re.M)
+    if not m or m.group(3) != source_sha(KERNEL_SOURCES[kernel]):
+        return None
+    return int(m.group(1)) + int(m.group(2))
+
+
+def cpu_baseline(case, min_seconds: float = 10.0) -> dict:
+    """The oracle, as it stands, on the same workload: repeated full steps
+    until at least ``min_seconds`` of CPU work, mean step time reported."""
+    import numpy as np
+    import oracle
+    g = case.geom
+    b, n_max, w = g.block_size, case.n_max, case.window
+    k_keep = (n_max - 1) * b
+    R = case.num_reqs
+    times = []
+    while sum(times) < min_seconds and len(times) < 10:
+        t0 = time.perf_counter()
+        res = oracle.compress(case)
+        kp, vp = res.k_pool[0], res.v_pool[0]
+        slot = (res.plan.tables[:, k_keep // b] * b + k_keep % b).astype(np.int32)
+        oracle.append(kp, vp, case.k_new[0], case.v_new[0], slot)
+        oracle.decode(kp, vp, case.q_new[0], res.plan.tables,
+                      np.full(R, k_keep + 1, dtype=np.int32), num_q_heads=g.num_q_heads)
+        times.append(time.perf_counter() - t0)
+        log(f"cpu oracle step {len(times)}: {times[-1]:.2f} s")
+    mean = sum(times) / len(times)
+    return {"value": R / mean, "unit": "compressions/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{len(times)} full step(s) of the same workload ({R} requests x 1 layer: "
+                      f"plan, fp64 scores, sort-based selection, out-of-place K/V compaction, "
+                      f"append, dense fp64 decode), mean {mean:.2f} s per step"}
+
+
+def calibrate_copy() -> int:
+    """A plain device copy of a known size (1 GiB read + 1 GiB written),
+    run under rocprofv3 --pmc to scale FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)  # an elementwise kernel, not a DMA copy
+    torch.cuda.synchronize()
+    log(f"copy calibration: 3 elementwise copies of {src.numel() * 4} bytes")
+    return 0
+
+
+def _read_csv(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize(kt_dir: str, fetch_dir: str, write_dir: str) -> int:
+    """Summary text of rocprofv3 outputs: kernel-trace statistics of the
+    bench run, and HBM bytes per dispatch of each hot-path kernel from the
+    FETCH_SIZE / WRITE_SIZE runs, scaled by what the same counters read for
+    the calibration copy (1 GiB each way)."""
+    import glob
+    stats = _read_csv(glob.glob(os.path.join(kt_dir, "*kernel_stats.csv"))[0])
+    print("# kernel-trace statistics (rocprofv3 --kernel-trace --stats)")
+    print(f"{'kernel':70s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s}")
+    for r in stats:
+        print(f"{r['Name'][:70]:70s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
+              f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f}")
+    phases = {"k_score_stats": "score_stats", "k_score_final": "score", "k_select": "select",
+              "k_compact": "compact", "k_append": "append", "k_decode<": "decode",
+              "k_decode_combine": "combine"}
+
+    def per_kernel(d, counter):
+        rows = _read_csv(glob.glob(os.path.join(d, "*counter_collection.csv"))[0])
+        acc = {}
+        for r in rows:
+            if r["Counter_Name"] != counter:
+                continue
+            acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in acc.items()}
+
+    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    gib_kib = (1 << 30) / 1024.0
+    def is_cal(name):
+        return "elementwise" in name.lower() and "mul" in name.lower()
+
+    cal_f = [v for k, v in fetch.items() if is_cal(k)]
+    cal_w = [v for k, v in write.items() if is_cal(k)]
+    f_scale = gib_kib / max(cal_f) if cal_f else None
+    w_scale = gib_kib / max(cal_w) if cal_w else None
+    print()
+    print("# HBM traffic per dispatch (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE; KiB per dispatch)")
+    print(f"copy calibration: FETCH_SIZE reads {max(cal_f) if cal_f else 'n/a'} KiB and WRITE_SIZE "
+          f"{max(cal_w) if cal_w else 'n/a'} KiB for 1 GiB each way -> scale "
+          f"fetch x{f_scale:.4f}, write x{w_scale:.4f}" if cal_f and cal_w else "copy calibration missing")
+    for key, phase in phases.items():
+        fk = [v for k, v in fetch.items() if key in k]
+        wk = [v for k, v in write.items() if key in k]
+        if not fk or not wk or f_scale is None:
+            continue
+        fb = int(fk[0] * 1024 * f_scale)
+        wb = int(wk[0] * 1024 * w_scale)
+        src = KERNEL_SOURCES[phase]
+        print(f"phase {phase}: fetch_bytes={fb} write_bytes={wb} source_sha={source_sha(src)} "
+              f"(raw FETCH_SIZE {fk[0]:.1f} KiB, WRITE_SIZE {wk[0]:.1f} KiB; {src})")
+    return 0
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a 1 GiB device copy (counter calibration under rocprofv3)")
+    ap.add_argument("--summarize", nargs=3, metavar=("KT_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="print the summary of rocprofv3 csv outputs and exit")
+    args = ap.parse_args()
+    if args.summarize:
+        return summarize(*args.summarize)
+    if args.calibrate_copy:
+        calibrate_copy()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this path runs without sharding or "
+              f"collectives, so --gpus {args.gpus} is not supported", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import compressed_paged_kv_amd as zp
+    import synth
+    from synth.device import to_tensor
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    log("generating the Qwen3-8B-shaped layer (64 requests, budget 2048)")
+    case = synth.case_qwen3_8b_layer()
+    g = case.geom
+    R, H, Hq, d, b = case.num_reqs, g.num_kv_heads, g.num_q_heads, g.head_dim, g.block_size
+    n_max, w = case.n_max, case.window
+    T, k_keep = n_max * b, (n_max - 1) * b
+    seq = k_keep + 1
+    eb = 2
+
+    kp = [to_tensor(case.k_pool[0], dev)]
+    vp = [to_tensor(case.v_pool[0], dev)]
+    cache = zp.KVCache(kp, vp, Hq)
+    rng = np.random.default_rng(1102)
+    # a few window-query sets, rotated per step, so eviction positions vary
+    wq_sets = [[to_tensor(case.window_q[0], dev)]] + [
+        [to_tensor(synth.f32_to_bf16_bits(rng.standard_normal(case.window_q[0].shape)
+                                          .astype(np.float32)), dev)] for _ in range(3)]
+    q_new = to_tensor(case.q_new[0], dev)
+    k_new = to_tensor(case.k_new[0], dev)
+    v_new = to_tensor(case.v_new[0], dev)
+    pool = zp.BlockPool.from_refcounts(case.refcounts)
+    tables = case.tables.copy()
+    tab_t = torch.from_numpy(tables).to(dev)
+    slot_t = torch.from_numpy((tables[:, k_keep // b] * b + k_keep % b).astype(np.int32)).to(dev)
+    seq_t = torch.full((R,), seq, dtype=torch.int32, device=dev)
+    ws = torch.empty(zp.compress_workspace_bytes(cache, R, n_max, w), dtype=torch.uint8, device=dev)
+    dws = torch.empty(max(zp.paged_decode_workspace_bytes(cache, R, n_max), 16), dtype=torch.uint8,
+                      device=dev)
+    out = torch.empty((R, Hq, d), dtype=torch.float32, device=dev)
+    scale = 1.0 / float(np.sqrt(d))
+    torch.cuda.synchronize()
+
+    def step(i: int, debug=None):
+        zp.compress(cache, pool, n_max, w, tables, wq_sets[i % len(wq_sets)], ws, debug=debug)
+        zp.append_kv(cache, 0, k_new, v_new, slot_t)
+        zp.paged_decode(cache, 0, q_new, tab_t, seq_t, scale, out, dws)
+
+    def moved_rows() -> int:
+        """Rows the compaction actually moves in one step (from the kept lists)."""
+        kept = torch.empty((1, R, H, k_keep), dtype=torch.int32, device=dev)
+        step(0, debug={"kept": kept})
+        torch.cuda.synchronize()
+        k = kept.cpu().numpy()[0]
+        return int(np.count_nonzero(k != np.arange(k_keep)[None, None, :]))
+
+    moved_before = moved_rows()
+    log(f"warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # 1) the timed region: K steps back to back, nothing else on the stream
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    # 2) the same K steps again with HIP events recorded around every kernel
+    #    on its launch stream, for per-kernel durations (the events add small
+    #    gaps between kernels, so this region's wall time is reported apart)
+    log(f"timing {args.steps} steps with per-kernel events")
+    zp.profile_enable(True)
+    zp.profile_read()
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t3 = time.perf_counter()
+    prof = zp.profile_read()
+    zp.profile_enable(False)
+    ms_per_step_events = (t3 - t2) * 1e3 / args.steps
+    moved_after = moved_rows()
+    assert tables.tolist() == case.tables.tolist(), "in-place compression changed the tables"
+    assert np.isfinite(out.cpu().numpy()).all()
+
+    # algorithmic bytes (and flops) per launch, per phase
+    moved = 0.5 * (moved_before + moved_after)
+    kv_row = d * eb
+    alg = {
+        "upload": R * n_max * 4 + R * (n_max - 1) * 4,
+        "score_stats": R * H * T * kv_row + R * w * Hq * kv_row,
+        "score": R * H * T * kv_row + R * w * Hq * kv_row + R * H * T * 4,
+        "select": R * H * (T - w) * 4 + R * H * b * 4,
+        "compact": moved * kv_row * 2 * 2,
+        "append": R * H * kv_row * 2 * 2,
+        "decode": R * H * seq * kv_row * 2 + R * Hq * kv_row,
+        "combine": R * Hq * (n_max // 16) * (d + 2) * 4 + R * Hq * d * 4,
+    }
+    flops = {"score_stats": 2 * Hq * w * T * d * R,
+             "score": 2 * Hq * w * T * d * R + 2 * H * n_max * b * b * d * R}
+    kernels = []
+    for name, (tot_ms, n) in prof.items():
+        if n == 0:
+            continue
+        avg_us = tot_ms * 1e3 / n
+        gbs = alg[name] / (avg_us * 1e-6) / 1e9
+        row = {"phase": name, "avg_us": round(avg_us, 2), "launches": n,
+               "alg_bytes": int(alg[name]), "alg_GBs": round(gbs, 1),
+               "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+        if name in flops:
+            tf = flops[name] / (avg_us * 1e-6) / 1e12
+            row["mfma_TFLOPs"] = round(tf, 1)
+            row["mfma_frac"] = round(tf / MFMA_BF16_PEAK_TFLOPS, 4)
+        kernels.append(row)
+    gpu_kernels = [k for k in kernels if k["phase"] != "upload"]
+    dom = max(gpu_kernels, key=lambda k: k["avg_us"] * k["launches"])
+    traffic = read_counters(dom["phase"])
+    roofline = {"bound": "hbm", "kernel": dom["phase"], "achieved": dom["alg_GBs"],
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dom["hbm_frac"],
+                "traffic": traffic}
+    per = {k["phase"]: k["avg_us"] for k in kernels}
+    comp_us = sum(per.get(p, 0.0) for p in ("score_stats", "score", "select", "compact"))
+    dec_us = sum(per.get(p, 0.0) for p in ("append", "decode", "combine"))
+    comp_bytes = sum(alg[p] for p in ("score_stats", "score", "select", "compact"))
+    dec_bytes = sum(alg[p] for p in ("append", "decode", "combine"))
+
+    result = {
+        "metric": METRIC,
+        "value": round(R / (ms_per_step * 1e-3), 1),
+        "unit": "compressions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_with_kernel_events": round(ms_per_step_events, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "qwen3_8b_layer_budget2048", "requests": R, "layers": 1,
+                   "kv_heads": H, "q_heads": Hq, "head_dim": d, "block_size": b, "n_max": n_max,
+                   "window": w, "pool_blocks": g.num_blocks, "decode_len": seq},
+        "compress_per_s": round(R / (comp_us * 1e-6), 1),
+        "compress_us": round(comp_us, 2),
+        "compress_hbm_frac": round(comp_bytes / (comp_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "decode_tok_s_per_layer": round(R / (dec_us * 1e-6), 1),
+        "decode_tok_s_36_layers": round(R / (36 * dec_us * 1e-6), 1),
+        "decode_us": round(dec_us, 2),
+        "decode_hbm_frac": round(dec_bytes / (dec_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "moved_rows_per_step": int(moved),
+        "kernels": kernels,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(case)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

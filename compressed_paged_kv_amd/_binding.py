@@ -83,6 +83,8 @@ def lib() -> ctypes.CDLL:
                              _vp, _vp]),
         "zp_paged_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(_KVCache),
                                                               ctypes.c_int32, ctypes.c_int32]),
+        "zp_profile_enable": (S, [ctypes.c_int32]),
+        "zp_profile_read": (S, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
         "zp_paged_decode": (S, [ctypes.POINTER(_KVCache), ctypes.c_int32, ctypes.c_int32, _vp, _vp,
                                 ctypes.c_int32, _vp, ctypes.c_float, _vp, _vp, ctypes.c_size_t,
                                 _vp]),
@@ -296,3 +298,20 @@ def paged_decode(cache: KVCache, layer: int, q, tables, seq_lens, scale: float, 
     _check(lib().zp_paged_decode(cache.ref, layer, R, q.data_ptr(), tables.data_ptr(), max_blocks,
                                  seq_lens.data_ptr(), float(scale), out.data_ptr(), ws_ptr,
                                  ws_bytes, _stream_handle(stream)))
+
+
+# --------------------------------------------------------------------------- timing
+
+PHASES = ("upload", "score_stats", "score", "select", "compact", "append", "decode", "combine")
+
+
+def profile_enable(on: bool = True) -> None:
+    _check(lib().zp_profile_enable(1 if on else 0))
+
+
+def profile_read() -> dict:
+    """{phase: (total_ms, launches)} accumulated since the last read."""
+    ms = (ctypes.c_double * len(PHASES))()
+    n = (ctypes.c_int64 * len(PHASES))()
+    _check(lib().zp_profile_read(ms, n))
+    return {p: (float(ms[i]), int(n[i])) for i, p in enumerate(PHASES)}

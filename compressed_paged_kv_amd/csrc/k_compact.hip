@@ -110,12 +110,15 @@ hipError_t launch_compact(const CompactParams& p, int num_layers, int row_bytes,
   if (p.R <= 0) return hipSuccess;
   if (p.E > kMaxEvicted || p.n_max > kMaxBlocks) return hipErrorInvalidValue;
   dim3 grid(2 * p.H, num_layers * p.R), block(kThreads);
-  switch (row_bytes / 16) {
+  const int vpr = row_bytes / 16;
+  if (vpr != 8 && vpr != 16 && vpr != 32) return hipErrorInvalidValue;
+  prof_begin(ZP_PHASE_COMPACT, s);
+  switch (vpr) {
     case 8: hipLaunchKernelGGL(k_compact<8>, grid, block, 0, s, p); break;
     case 16: hipLaunchKernelGGL(k_compact<16>, grid, block, 0, s, p); break;
     case 32: hipLaunchKernelGGL(k_compact<32>, grid, block, 0, s, p); break;
-    default: return hipErrorInvalidValue;
   }
+  prof_end(ZP_PHASE_COMPACT, s);
   return hipGetLastError();
 }
 

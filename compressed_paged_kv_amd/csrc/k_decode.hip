@@ -7,13 +7,13 @@
 // float32 accumulation, p*v as float32 FMAs.
 //
 // Grid: x = split of the block list, y = KV head (and query-head subgroup),
-// z = request.  A workgroup
-// has 4 waves; wave w takes the split's blocks w, w+4, ...  Within a wave,
-// lane = 4*t + c handles token t (0..15) of a 16-token step and the c-th
-// quarter of the head dimension, as 16-byte vectors at byte offsets
-// 64*v + 16*c of the row, so one load instruction of the wave covers whole
-// 64-byte segments of 16 rows.  All G query heads of the KV head are done
-// together, so K and V are read once for the group.  The four lanes of a
+// z = request.  A workgroup has 8 waves; wave w takes the split's blocks
+// w, w+8, ...  Within a wave, lane = 8*t + c handles token t (0..7) of an
+// 8-token step and the c-th eighth of the head dimension, as 16-byte vectors
+// at byte offsets 128*v + 16*c of the row, so one load instruction covers
+// 128 contiguous bytes of 8 rows.  All G query heads of the KV head are done
+// together, so K and V are read once for the group; the next step's K and V
+// are loaded before the current one is consumed.  The eight lanes of a
 // token add their partial dot products; every lane then keeps its own
 // running softmax state (max m, sum l, accumulator) for the tokens it saw,
 // rescaled only when the max grows by more than 2^8 (exact up to rounding:
@@ -27,6 +27,15 @@ namespace {
 
 constexpr float kInitMax = -1.0e30f;
 constexpr float kLazy = 8.0f;
+// Tuning knobs (defaults chosen by measurement on MI355X).
+#ifndef ZP_DECODE_LANES_PER_TOKEN
+#define ZP_DECODE_LANES_PER_TOKEN 16
+#endif
+#ifndef ZP_DECODE_PREFETCH
+#define ZP_DECODE_PREFETCH 1  // steps loaded ahead of the one being consumed
+#endif
+constexpr int kLanesPerToken = ZP_DECODE_LANES_PER_TOKEN;  // lanes sharing one token row
+constexpr int PD = ZP_DECODE_PREFETCH;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
@@ -76,22 +85,46 @@ struct Elem<ZP_F32> {
 
 __device__ inline uint4 ld16(const char* p) { return ldg16(p); }
 
+// Sum over groups of LPT consecutive lanes (LPT = 4, 8 or 16) with DPP
+// row permutations: xor 1 and xor 2 inside quads, then the half-row and
+// row mirrors pair the 4- and 8-lane halves.  Every lane of the group ends
+// with the same (commutatively added) value.
+template <int LPT>
+__device__ inline float group_sum(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, true));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, true));
+  if constexpr (LPT >= 8)
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x141, 0xF, 0xF, true));
+  if constexpr (LPT >= 16)
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x140, 0xF, 0xF, true));
+  return x;
+}
+
+// 2^x on the hardware unit (no denormal rescue: results below 2^-126 flush
+// to zero, which only drops probabilities far below the output tolerance).
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // G here is the number of query heads one workgroup handles (at most 4, to
 // keep the accumulators in registers); larger groups are split over
 // blockIdx.y = kv_head * nsub + sub.
 template <int DT, int D, int B, int G>
-__global__ __launch_bounds__(256) void k_decode(DecodeParams p) {
+__global__ __launch_bounds__(kDecodeThreads) void k_decode(DecodeParams p) {
   constexpr int EB = Elem<DT>::kBytes;
-  constexpr int NV = D * EB / 64;          // 16-byte vectors per lane per row
-  constexpr int EPV = Elem<DT>::kPerVec;   // elements per vector
-  constexpr int NE = NV * EPV;             // = D / 4 elements per lane
+  // lanes per token row: the knob, capped at one 16-byte vector per lane
+  constexpr int LPT = (D * EB / 16 < kLanesPerToken) ? D * EB / 16 : kLanesPerToken;
+  constexpr int TPS = 64 / LPT;                        // tokens per step
+  constexpr int NV = D * EB / (16 * LPT);              // 16-byte vectors per lane per row
+  constexpr int EPV = Elem<DT>::kPerVec;              // elements per vector
+  constexpr int NE = NV * EPV;                         // = D / LPT
   constexpr int ROW = D * EB;
+  constexpr int SPB = B / TPS;                         // steps per block
+  constexpr int NW = kDecodeThreads / 64;              // waves per workgroup
   const int split = blockIdx.x, r = blockIdx.z;
   const int group = p.Hq / p.H, nsub = group / G;
   const int h = blockIdx.y / nsub, hq0 = h * group + (blockIdx.y - h * nsub) * G;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int tok = lane >> 2, qd = lane & 3;
-  const int Hq = p.Hq;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tok = lane / LPT, c = lane % LPT;
 
   // device-side lengths and ids are clamped / skipped so that a bad table
   // can never send a load outside the pools
@@ -103,9 +136,9 @@ __global__ __launch_bounds__(256) void k_decode(DecodeParams p) {
   uint4 q[G][NV];
 #pragma unroll
   for (int g = 0; g < G; g++) {
-    const char* qp = static_cast<const char*>(p.q) + ((size_t)r * Hq + hq0 + g) * ROW + qd * 16;
+    const char* qp = static_cast<const char*>(p.q) + ((size_t)r * p.Hq + hq0 + g) * ROW + c * 16;
 #pragma unroll
-    for (int v = 0; v < NV; v++) q[g][v] = ld16(qp + v * 64);
+    for (int v = 0; v < NV; v++) q[g][v] = ld16(qp + v * 16 * LPT);
   }
   float m[G], l[G], acc[G][NE];
 #pragma unroll
@@ -119,49 +152,84 @@ __global__ __launch_bounds__(256) void k_decode(DecodeParams p) {
   const char* kb = static_cast<const char*>(p.k);
   const char* vb = static_cast<const char*>(p.v);
   const size_t tile_bytes = (size_t)B * ROW;
-  for (int blk = blk_begin + wave; blk < blk_end; blk += 4) {
-    const int pblk = p.tables[(size_t)r * p.max_blocks + blk];
-    if ((unsigned)pblk >= (unsigned)p.num_blocks) continue;
-    const size_t off = ((size_t)pblk * p.H + h) * tile_bytes + qd * 16;
+  const int lane_off = tok * ROW + c * 16;  // this lane's bytes inside a step
+  // This wave's blocks are blk_begin + wave + NW*i.  Lane i holds the
+  // physical id of the wave's i-th block of the current group of 64.
+  const int my_blocks = blk_end - blk_begin - wave > 0 ? (blk_end - blk_begin - wave + NW - 1) / NW : 0;
+  for (int g0 = 0; g0 < my_blocks; g0 += 64) {
+    const int nb_here = min(64, my_blocks - g0);
+    int id = -1;
+    if (lane < nb_here) {
+      id = p.tables[(size_t)r * p.max_blocks + blk_begin + wave + NW * (g0 + lane)];
+      if ((unsigned)id >= (unsigned)p.num_blocks) id = -1;
+    }
+    const int n_items = nb_here * SPB;
+    // item -> (block i = item / SPB, step st = item % SPB).  Items past the
+    // end re-read the last item and a skipped block reads row 0 of the pool:
+    // the loads stay unconditional (straight-line code lets the compiler
+    // count outstanding loads instead of draining them) and such items are
+    // masked out below.
+    auto item_base = [&](int item) -> long long {
+      const int it = min(item, n_items - 1);
+      const int i = it / SPB, st = it - i * SPB;
+      const int pid = __builtin_amdgcn_readlane(id, i);
+      if (pid < 0) return 0;
+      return (long long)(((size_t)pid * p.H + h) * tile_bytes) + (long long)st * TPS * ROW + lane_off;
+    };
+    auto item_live = [&](int item) -> bool {
+      if (item >= n_items) return false;
+      const int i = item / SPB, st = item - i * SPB;
+      const int pid = __builtin_amdgcn_readlane(id, i);
+      return pid >= 0 && (blk_begin + wave + NW * (g0 + i)) * B + st * TPS + tok < seq;
+    };
+    // ring of PD+1 register slots: item k lives in slot k % (PD+1) and is
+    // loaded PD items before it is consumed
+    uint4 kr[PD + 1][NV], vr[PD + 1][NV];
+    auto fetch = [&](int item, uint4 (&kd)[NV], uint4 (&vd)[NV]) {
+      const long long o = item_base(item);
 #pragma unroll
-    for (int st = 0; st < B / 16; st++) {
-      const int t = blk * B + st * 16 + tok;
-      const char* krow = kb + off + (size_t)(st * 16 + tok) * ROW;
-      const char* vrow = vb + off + (size_t)(st * 16 + tok) * ROW;
-      uint4 kv[NV], vv[NV];
-#pragma unroll
-      for (int v = 0; v < NV; v++) kv[v] = ld16(krow + v * 64);
-#pragma unroll
-      for (int v = 0; v < NV; v++) vv[v] = ld16(vrow + v * 64);
-      float x[G];
-#pragma unroll
-      for (int g = 0; g < G; g++) {
-        float s = 0.f;
-#pragma unroll
-        for (int v = 0; v < NV; v++) s = Elem<DT>::dot(q[g][v], kv[v], s);
-        s += __shfl_xor(s, 1);
-        s += __shfl_xor(s, 2);
-        x[g] = s * p.scale_log2;
+      for (int v = 0; v < NV; v++) {
+        kd[v] = ld16(kb + o + v * 16 * LPT);
+        vd[v] = ld16(vb + o + v * 16 * LPT);
       }
-      if (t < seq) {
+    };
+#pragma unroll
+    for (int k = 0; k < PD; k++) fetch(k, kr[k], vr[k]);
+    for (int base = 0; base < n_items; base += PD + 1) {
+#pragma unroll
+      for (int sl = 0; sl < PD + 1; sl++) {
+        const int item = base + sl;
+        fetch(item + PD, kr[(sl + PD) % (PD + 1)], vr[(sl + PD) % (PD + 1)]);
+        // a skipped block, a token past the end or an item past the end
+        // contributes nothing
+        const bool live = item_live(item);
+        float x[G];
+#pragma unroll
+        for (int g = 0; g < G; g++) {
+          float sdot = 0.f;
+#pragma unroll
+          for (int v = 0; v < NV; v++) sdot = Elem<DT>::dot(q[g][v], kr[sl][v], sdot);
+          sdot = group_sum<LPT>(sdot);
+          x[g] = live ? sdot * p.scale_log2 : kInitMax;
+        }
         float vf[NE];
 #pragma unroll
         for (int v = 0; v < NV; v++) {
           float tmp[EPV];
-          Elem<DT>::unpack(vv[v], tmp);
+          Elem<DT>::unpack(vr[sl][v], tmp);
 #pragma unroll
-          for (int k = 0; k < EPV; k++) vf[v * EPV + k] = tmp[k];
+          for (int k = 0; k < EPV; k++) vf[v * EPV + k] = live ? tmp[k] : 0.f;
         }
 #pragma unroll
         for (int g = 0; g < G; g++) {
           if (x[g] > m[g] + kLazy) {
-            const float c = exp2f(m[g] - x[g]);
-            l[g] *= c;
+            const float cr = fast_exp2(m[g] - x[g]);
+            l[g] *= cr;
 #pragma unroll
-            for (int e = 0; e < NE; e++) acc[g][e] *= c;
+            for (int e = 0; e < NE; e++) acc[g][e] *= cr;
             m[g] = x[g];
           }
-          const float pr = exp2f(x[g] - m[g]);
+          const float pr = fast_exp2(x[g] - m[g]);
           l[g] += pr;
 #pragma unroll
           for (int e = 0; e < NE; e++) acc[g][e] = fmaf(pr, vf[e], acc[g][e]);
@@ -169,9 +237,9 @@ __global__ __launch_bounds__(256) void k_decode(DecodeParams p) {
       }
     }
   }
-  // merge the 16 token lanes that share a head-dimension quarter
+  // merge the token lanes that share a head-dimension slice
 #pragma unroll
-  for (int off = 4; off < 64; off <<= 1) {
+  for (int off = LPT; off < 64; off <<= 1) {
 #pragma unroll
     for (int g = 0; g < G; g++) {
       const float m2 = __shfl_xor(m[g], off);
@@ -187,40 +255,41 @@ __global__ __launch_bounds__(256) void k_decode(DecodeParams p) {
       m[g] = M;
     }
   }
-  // merge the 4 waves through LDS
-  __shared__ float s_acc[4][G][D];
-  __shared__ float s_ml[4][G][2];
+  // merge the waves through LDS
+  __shared__ float s_acc[NW][G][D];
+  __shared__ float s_ml[NW][G][2];
   if (tok == 0) {
 #pragma unroll
     for (int g = 0; g < G; g++) {
 #pragma unroll
       for (int v = 0; v < NV; v++)
 #pragma unroll
-        for (int k = 0; k < EPV; k++) s_acc[wave][g][v * (64 / EB) + qd * EPV + k] = acc[g][v * EPV + k];
-      if (qd == 0) {
+        for (int k = 0; k < EPV; k++)
+          s_acc[wave][g][v * (16 * LPT / EB) + c * EPV + k] = acc[g][v * EPV + k];
+      if (c == 0) {
         s_ml[wave][g][0] = m[g];
         s_ml[wave][g][1] = l[g];
       }
     }
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+  for (int idx = threadIdx.x; idx < G * D; idx += kDecodeThreads) {
     const int g = idx / D, d = idx - g * D;
     float M = s_ml[0][g][0];
 #pragma unroll
-    for (int w = 1; w < 4; w++) M = fmaxf(M, s_ml[w][g][0]);
+    for (int w = 1; w < NW; w++) M = fmaxf(M, s_ml[w][g][0]);
     float L = 0.f, o = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; w++) {
-      const float c = exp2f(s_ml[w][g][0] - M);
-      L = fmaf(s_ml[w][g][1], c, L);
-      o = fmaf(s_acc[w][g][d], c, o);
+    for (int w = 0; w < NW; w++) {
+      const float cw = exp2f(s_ml[w][g][0] - M);
+      L = fmaf(s_ml[w][g][1], cw, L);
+      o = fmaf(s_acc[w][g][d], cw, o);
     }
     const int hq = hq0 + g;
     if (p.nsplit == 1) {
-      p.out[((size_t)r * Hq + hq) * D + d] = L > 0.f ? o / L : 0.f;
+      p.out[((size_t)r * p.Hq + hq) * D + d] = L > 0.f ? o / L : 0.f;
     } else {
-      float* part = p.partial + (((size_t)r * Hq + hq) * p.nsplit + split) * (D + 2);
+      float* part = p.partial + (((size_t)r * p.Hq + hq) * p.nsplit + split) * (D + 2);
       part[2 + d] = o;
       if (d == 0) {
         part[0] = M;
@@ -270,16 +339,20 @@ template <int DT, int D, int B>
 hipError_t launch_g(const DecodeParams& p, hipStream_t s) {
   const int group = p.Hq / p.H;
   const int per_wg = group < 4 ? group : 4;
-  dim3 grid(p.nsplit, p.H * (group / per_wg), p.R), block(256);
+  dim3 grid(p.nsplit, p.H * (group / per_wg), p.R), block(kDecodeThreads);
+  if (per_wg != 1 && per_wg != 2 && per_wg != 4) return hipErrorInvalidValue;
+  prof_begin(ZP_PHASE_DECODE, s);
   switch (per_wg) {
     case 1: hipLaunchKernelGGL((k_decode<DT, D, B, 1>), grid, block, 0, s, p); break;
     case 2: hipLaunchKernelGGL((k_decode<DT, D, B, 2>), grid, block, 0, s, p); break;
     case 4: hipLaunchKernelGGL((k_decode<DT, D, B, 4>), grid, block, 0, s, p); break;
-    default: return hipErrorInvalidValue;
   }
+  prof_end(ZP_PHASE_DECODE, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.nsplit == 1) return e;
+  prof_begin(ZP_PHASE_COMBINE, s);
   hipLaunchKernelGGL((k_decode_combine<D>), dim3(p.R * p.Hq), dim3(D), 0, s, p);
+  prof_end(ZP_PHASE_COMBINE, s);
   return hipGetLastError();
 }
 
@@ -309,7 +382,9 @@ hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, int blo
 
 hipError_t launch_append(const AppendParams& p, hipStream_t s) {
   if (p.R <= 0) return hipSuccess;
+  prof_begin(ZP_PHASE_APPEND, s);
   hipLaunchKernelGGL(k_append, dim3(p.R), dim3(256), 0, s, p);
+  prof_end(ZP_PHASE_APPEND, s);
   return hipGetLastError();
 }
 

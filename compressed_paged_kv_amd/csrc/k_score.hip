@@ -74,11 +74,22 @@ struct Mma<ZP_F32> {
 
 __device__ inline uint4 ld16(const char* p) { return ldg16(p); }
 
+// 2^x on the hardware unit (results below 2^-126 flush to zero).
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Merge two (max, sum) pairs that represent sum_k 2^(x_k - max).
 __device__ inline void merge_stat(float& m, float& z, float m2, float z2) {
   float M = fmaxf(m, m2);
-  z = z * exp2f(m - M) + z2 * exp2f(m2 - M);
+  z = z * fast_exp2(m - M) + z2 * fast_exp2(m2 - M);
   m = M;
+}
+
+// Physical id of block blk0 + wave + 4*i is held by lane i (i < 64); the
+// wave's block list is read once instead of once per block.
+__device__ inline int wave_block_ids(const ScoreParams& p, int r, int blk0, int blk1, int wave,
+                                     int lane) {
+  const int n = blk0 + wave + 4 * lane;
+  return n < blk1 ? p.src[(size_t)r * p.n_max + n] : 0;
 }
 
 // Query fragments of the unit's rows: row = i*G + g holds window position i
@@ -141,33 +152,48 @@ __global__ __launch_bounds__(256) void k_score_stats(ScoreParams p) {
 
   const int blk0 = chunk * p.chunk_blocks;
   const int blk1 = min(blk0 + p.chunk_blocks, p.n_max);
-  for (int n = blk0 + wave; n < blk1; n += 4) {
-    const int pblk = p.src[(size_t)r * p.n_max + n];
-    const char* tile = kbase + ((size_t)pblk * p.H + h) * B * D * EB;
+  const int n_items = blk1 - blk0 - wave > 0 ? (blk1 - blk0 - wave + 3) / 4 : 0;
+  const int ids = wave_block_ids(p, r, blk0, blk1, wave, lane);
+  const int row_off = col * D * EB + grp * 16;
+  // K fragments of the wave's next block are loaded (unconditionally, the
+  // last block again at the end) while the current one is consumed
+  auto fetch = [&](int i, uint4 (&kf)[NST][NV]) {
+    const int pblk = __builtin_amdgcn_readlane(ids, min(i, n_items - 1));
+    const char* tile = kbase + ((size_t)pblk * p.H + h) * B * D * EB + row_off;
+#pragma unroll
+    for (int st = 0; st < NST; st++)
+#pragma unroll
+      for (int v = 0; v < NV; v++) kf[st][v] = ld16(tile + st * 16 * D * EB + v * 64);
+  };
+  uint4 kcur[NST][NV], knext[NST][NV];
+  if (n_items > 0) fetch(0, kcur);
+  for (int it = 0; it < n_items; it++) {
+    fetch(it + 1, knext);
+    const int n = blk0 + wave + 4 * it;
 #pragma unroll
     for (int st = 0; st < NST; st++) {
-      uint4 kf[NV];
-      const char* rowp = tile + (size_t)(st * 16 + col) * D * EB + grp * 16;
-#pragma unroll
-      for (int v = 0; v < NV; v++) kf[v] = ld16(rowp + v * 64);
       const int j = n * B + st * 16 + col;
 #pragma unroll
       for (int rt = 0; rt < RT; rt++) {
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int v = 0; v < NV; v++) acc = Mma<DT>::step(qf[rt][v], kf[v], acc);
+        for (int v = 0; v < NV; v++) acc = Mma<DT>::step(qf[rt][v], kcur[st][v], acc);
 #pragma unroll
         for (int i = 0; i < 4; i++) {
           if (j <= lim[rt][i]) {
             const float x = acc[i] * p.scale_log2;
             const bool up = x > m[rt][i] + kLazy;
-            const float t = exp2f(up ? m[rt][i] - x : x - m[rt][i]);
+            const float t = fast_exp2(up ? m[rt][i] - x : x - m[rt][i]);
             z[rt][i] = up ? fmaf(z[rt][i], t, 1.f) : z[rt][i] + t;
             m[rt][i] = up ? x : m[rt][i];
           }
         }
       }
     }
+#pragma unroll
+    for (int st = 0; st < NST; st++)
+#pragma unroll
+      for (int v = 0; v < NV; v++) kcur[st][v] = knext[st][v];
   }
   // merge the 16 columns of every row
 #pragma unroll
@@ -208,7 +234,11 @@ __global__ __launch_bounds__(256) void k_score_final(ScoreParams p) {
   constexpr int NV = D * EB / 64;
   constexpr int NST = B / 16;
   constexpr int RP = RT * 16;
-  const int chunk = blockIdx.x, h = blockIdx.y, lr = blockIdx.z;
+  // Workgroups run in the reverse order of the statistics pass, so the keys
+  // read last by that pass (most likely still in the last-level cache) are
+  // read again first.
+  const int chunk = gridDim.x - 1 - blockIdx.x, h = gridDim.y - 1 - blockIdx.y;
+  const int lr = gridDim.z - 1 - blockIdx.z;
   const int l = lr / p.R, r = lr - l * p.R;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
@@ -245,16 +275,22 @@ __global__ __launch_bounds__(256) void k_score_final(ScoreParams p) {
 
   const int blk0 = chunk * p.chunk_blocks;
   const int blk1 = min(blk0 + p.chunk_blocks, p.n_max);
-  for (int n = blk0 + wave; n < blk1; n += 4) {
-    const int pblk = p.src[(size_t)r * p.n_max + n];
-    const char* tile = kbase + ((size_t)pblk * p.H + h) * B * D * EB;
-    uint4 kf[NST][NV];
+  const int n_items = blk1 - blk0 - wave > 0 ? (blk1 - blk0 - wave + 3) / 4 : 0;
+  const int ids = wave_block_ids(p, r, blk0, blk1, wave, lane);
+  const int row_off = col * D * EB + grp * 16;
+  auto fetch = [&](int i, uint4 (&kd)[NST][NV]) {
+    const int pblk = __builtin_amdgcn_readlane(ids, min(i, n_items - 1));
+    const char* tile = kbase + ((size_t)pblk * p.H + h) * B * D * EB + row_off;
 #pragma unroll
-    for (int st = 0; st < NST; st++) {
-      const char* rowp = tile + (size_t)(st * 16 + col) * D * EB + grp * 16;
+    for (int st = 0; st < NST; st++)
 #pragma unroll
-      for (int v = 0; v < NV; v++) kf[st][v] = ld16(rowp + v * 64);
-    }
+      for (int v = 0; v < NV; v++) kd[st][v] = ld16(tile + st * 16 * D * EB + v * 64);
+  };
+  uint4 kf[NST][NV], knext[NST][NV];
+  if (n_items > 0) fetch(0, kf);
+  for (int it = 0; it < n_items; it++) {
+    fetch(it + 1, knext);
+    const int n = blk0 + wave + 4 * it;
     float A[NST], Rd[NST], nrm[NST];
 #pragma unroll
     for (int st = 0; st < NST; st++) {
@@ -268,7 +304,7 @@ __global__ __launch_bounds__(256) void k_score_final(ScoreParams p) {
         for (int v = 0; v < NV; v++) acc = Mma<DT>::step(qf[rt][v], kf[st][v], acc);
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-          const float pr = exp2f(acc[i] * p.scale_log2 - rm[rt][i]) * rz[rt][i];
+          const float pr = fast_exp2(acc[i] * p.scale_log2 - rm[rt][i]) * rz[rt][i];
           cs += (j <= lim[rt][i]) ? pr : 0.f;
         }
       }
@@ -326,16 +362,24 @@ __global__ __launch_bounds__(256) void k_score_final(ScoreParams p) {
         if (p.dbg_score && j < p.C) p.dbg_score[o] = s;
       }
     }
+#pragma unroll
+    for (int st = 0; st < NST; st++)
+#pragma unroll
+      for (int v = 0; v < NV; v++) kf[st][v] = knext[st][v];
   }
 }
 
 template <int DT, int D, int B, int RT>
 hipError_t launch_rt(const ScoreParams& p, int units, hipStream_t s) {
   dim3 grid(p.nchunk, p.H, units / p.H);
+  prof_begin(ZP_PHASE_SCORE_STATS, s);
   hipLaunchKernelGGL((k_score_stats<DT, D, B, RT>), grid, dim3(256), 0, s, p);
+  prof_end(ZP_PHASE_SCORE_STATS, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  prof_begin(ZP_PHASE_SCORE, s);
   hipLaunchKernelGGL((k_score_final<DT, D, B, RT>), grid, dim3(256), 0, s, p);
+  prof_end(ZP_PHASE_SCORE, s);
   return hipGetLastError();
 }
 

@@ -152,15 +152,18 @@ int select_per_thread(int T) {
 hipError_t launch_select(const SelectParams& p, hipStream_t s) {
   if (p.units <= 0) return hipSuccess;
   dim3 grid(p.units), block(kThreads);
-  switch (select_per_thread(p.T)) {
+  const int per = select_per_thread(p.T);
+  if (per == 0) return hipErrorInvalidValue;
+  prof_begin(ZP_PHASE_SELECT, s);
+  switch (per) {
     case 1: hipLaunchKernelGGL(k_select<1>, grid, block, 0, s, p); break;
     case 2: hipLaunchKernelGGL(k_select<2>, grid, block, 0, s, p); break;
     case 4: hipLaunchKernelGGL(k_select<4>, grid, block, 0, s, p); break;
     case 8: hipLaunchKernelGGL(k_select<8>, grid, block, 0, s, p); break;
     case 16: hipLaunchKernelGGL(k_select<16>, grid, block, 0, s, p); break;
     case 32: hipLaunchKernelGGL(k_select<32>, grid, block, 0, s, p); break;
-    default: return hipErrorInvalidValue;
   }
+  prof_end(ZP_PHASE_SELECT, s);
   return hipGetLastError();
 }
 

@@ -25,9 +25,16 @@ constexpr int kPtrsPerLayer = 3;
 constexpr int kScoreChunkTokens = 512;
 // Largest number of (query head, window row) pairs per KV head.
 constexpr int kMaxScoreRows = 128;
-// Blocks per split of the paged decode kernel.
-constexpr int kDecodeBlocksPerSplit16 = 16;  // for block_size 16
-constexpr int kDecodeBlocksPerSplit32 = 8;   // for block_size 32
+// Paged decode: threads per workgroup, and the workgroup count below which
+// a request's block list is split over several workgroups.
+#ifndef ZP_DECODE_THREADS
+#define ZP_DECODE_THREADS 512
+#endif
+constexpr int kDecodeThreads = ZP_DECODE_THREADS;
+#ifndef ZP_DECODE_TARGET_WORKGROUPS
+#define ZP_DECODE_TARGET_WORKGROUPS 512
+#endif
+constexpr int kDecodeTargetWorkgroups = ZP_DECODE_TARGET_WORKGROUPS;
 
 struct ScoreParams {
   void* const* layer_ptrs;  // device [L][3]
@@ -87,6 +94,11 @@ hipError_t launch_compact(const CompactParams& p, int num_layers, int row_bytes,
 hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, int block_size,
                          hipStream_t s);
 hipError_t launch_append(const AppendParams& p, hipStream_t s);
+
+// Kernel timing (no-ops unless enabled by zp_profile_enable): bracket one
+// phase on stream s.
+void prof_begin(int phase, hipStream_t s);
+void prof_end(int phase, hipStream_t s);
 
 // Geometry helpers shared by the validation and the workspace layout.
 int score_row_tiles(int rows);  // 1, 2, 4 or 8 tiles of 16 rows; 0 if rows > kMaxScoreRows

@@ -229,6 +229,30 @@ zp_status zp_paged_decode(const zp_kv_cache* cache, int32_t layer, int32_t num_r
                           const int32_t* seq_lens, float scale, float* out, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Kernel timing.  While enabled, every kernel launch of the calls above is
+ * bracketed by HIP events recorded on the caller's stream (a few events per
+ * call, no synchronisation).  zp_profile_read() waits for the recorded
+ * events, adds up the elapsed time per phase since the last read, and
+ * forgets them.  Not thread-safe against concurrent calls of the entry
+ * points on other threads.
+ * ---------------------------------------------------------------------- */
+typedef enum {
+  ZP_PHASE_UPLOAD = 0,      /* table / pointer upload of zp_compress */
+  ZP_PHASE_SCORE_STATS = 1, /* per-chunk softmax statistics */
+  ZP_PHASE_SCORE = 2,       /* importance, redundancy, combined score */
+  ZP_PHASE_SELECT = 3,      /* per-head survivor selection */
+  ZP_PHASE_COMPACT = 4,     /* order-preserving gather of K and V */
+  ZP_PHASE_APPEND = 5,      /* zp_append_kv */
+  ZP_PHASE_DECODE = 6,      /* paged decode attention */
+  ZP_PHASE_COMBINE = 7,     /* merge of the decode splits */
+  ZP_NUM_PHASES = 8
+} zp_phase;
+
+zp_status zp_profile_enable(int32_t on);
+/* total_ms[ZP_NUM_PHASES], launches[ZP_NUM_PHASES] (either may be NULL). */
+zp_status zp_profile_read(double* total_ms, int64_t* launches);
+
 #ifdef __cplusplus
 }
 #endif

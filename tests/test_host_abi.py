@@ -257,8 +257,12 @@ def test_workspace_sizes_grow_with_the_batch():
     assert 0 < a < b and b % 256 == 0
     # the score buffer alone: L*R*H*T floats
     assert b >= 2 * 64 * 8 * 2048 * 4
-    assert zp.paged_decode_workspace_bytes(cache, 64, 8) == 0        # one split
-    assert zp.paged_decode_workspace_bytes(cache, 64, 128) == 64 * 32 * 8 * 130 * 4
+    # 64 requests x 8 KV heads fill the GPU: one workgroup per (request, head),
+    # no split and no workspace; a single request is split in chunks of whole
+    # multiples of 8 blocks, with one partial (m, l, o[d]) per split
+    assert zp.paged_decode_workspace_bytes(cache, 64, 128) == 0
+    assert zp.paged_decode_workspace_bytes(cache, 64, 8) == 0
+    assert zp.paged_decode_workspace_bytes(cache, 1, 128) == 1 * 32 * 16 * 130 * 4
 
 
 def test_decode_and_append_reject_bad_arguments():
