@@ -1,24 +1,36 @@
-// Scoring kernels of the compression pass (gfx950).
+// Scoring and survivor selection of the compression pass (gfx950).
 //
-// For one (layer, request, KV head) "unit" the observation window supplies
-// rows = G*w query rows (G query heads of the group times the w window
-// positions; ko page section 2.A).  Every cached slot j gets
+// One workgroup (8 waves) per (layer, request, KV head) "unit".  The
+// observation window supplies rows = G*w query rows (the G query heads of
+// the group times the w window positions; ko page section 2.A).  Every
+// cached slot j gets
 //   A[j] = mean over rows of the causal softmax of q.k_j / sqrt(d),
 //   R[j] = mean cosine of k_j with the other keys of its block (Lightning
 //          Redundancy Score, nl page Methodologie item 5 / ko page 2.E),
-//   s[j] = A[j] * (1 - R[j]) for the candidates j < T - w.
-// The softmax needs each row's max and normaliser over all T slots before
-// any probability can be summed over rows, so the pass runs twice over K:
-//   k_score_stats: per token chunk, running (max, sum) of every row;
-//   k_score_final: merges the chunk statistics, recomputes the logits and
-//                  accumulates A, computes the in-block Gram for R, writes s.
-// Both contractions (rows x b logits, b x b Gram) are 16x16 MFMA tiles:
+//   s[j] = A[j] * (1 - R[j]) for the candidates j < C = T - w,
+// and the E = T - K_keep candidates with the smallest (s, then highest
+// slot) are evicted; the window slots always stay.
+//
+// Phases, all inside the workgroup:
+//   1. softmax statistics: each wave runs over its share of the unit's
+//      blocks keeping, per window row, a running (max, sum of 2^(x - max))
+//      that is rescaled only when the max grows by more than 2^8; lanes and
+//      waves are then merged in LDS into one exponent offset per row,
+//      M + log2(Z), so a probability is a single 2^(x - offset);
+//   2. the same blocks again (now in cache): probabilities summed over the
+//      rows in a fixed order (so equal inputs give bit-equal importances),
+//      the in-block Gram matrix for the cosines, and s into LDS;
+//   3. a radix select (4 passes of 8 bits over order-preserving 32-bit keys)
+//      finds the E-th smallest score and how many equal scores go; prefix
+//      counts in slot order give the ascending evicted list.
+// The rows x b logit tiles and the b x b Gram tiles are 16x16 MFMA tiles:
 // v_mfma_f32_16x16x32_bf16 for bfloat16 caches, v_mfma_f32_16x16x4f32 for
 // float32 ones.  A lane holds operand row (lane % 16) and a 16-byte slice of
-// the head dimension chosen by lane / 16; the output tile gives lane
-// rows 4*(lane/16)+i, column lane % 16.  Q and K use the same slicing, so the
+// the head dimension chosen by lane / 16; the output tile gives lane rows
+// 4*(lane/16)+i, column lane % 16.  Q and K use the same slicing, so the
 // contraction over the head dimension is exact whatever order the hardware
-// sums the slices in.
+// sums the slices in.  With more than 64 rows the waves split into two row
+// groups whose partial importances are added once both are done.
 #include "zp_device.h"
 #include "zp_internal.h"
 
@@ -28,8 +40,11 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr float kInitMax = -1.0e30f;  // finite "minus infinity" so merges never form inf - inf
-constexpr float kLazy = 8.0f;         // rescale the running sum only when the max grows by > 2^8
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr float kInitMax = -1.0e30f;  // finite "minus infinity": merges never form inf - inf
+constexpr float kLazy = 8.0f;         // rescale a running sum only when its max grows by > 2^8
+constexpr int kLdsFloats = 3 * 4096;  // scores (T <= 8192), or three T <= 4096 arrays
 
 template <int DT>
 struct Mma;
@@ -46,8 +61,8 @@ struct Mma<ZP_BF16> {
     float s = 0.f;
 #pragma unroll
     for (int k = 0; k < 4; k++) {
-      float lo = __uint_as_float(w[k] << 16);
-      float hi = __uint_as_float(w[k] & 0xFFFF0000u);
+      const float lo = __uint_as_float(w[k] << 16);
+      const float hi = __uint_as_float(w[k] & 0xFFFF0000u);
       s = fmaf(lo, lo, s);
       s = fmaf(hi, hi, s);
     }
@@ -66,45 +81,124 @@ struct Mma<ZP_F32> {
     return c;
   }
   __device__ static inline float sumsq(uint4 a) {
-    float x = __uint_as_float(a.x), y = __uint_as_float(a.y);
-    float z = __uint_as_float(a.z), w = __uint_as_float(a.w);
+    const float x = __uint_as_float(a.x), y = __uint_as_float(a.y);
+    const float z = __uint_as_float(a.z), w = __uint_as_float(a.w);
     return fmaf(w, w, fmaf(z, z, fmaf(y, y, x * x)));
   }
 };
 
 __device__ inline uint4 ld16(const char* p) { return ldg16(p); }
 
-// 2^x on the hardware unit (results below 2^-126 flush to zero).
+// 2^x and log2(x) on the hardware unit (2^x below 2^-126 flushes to zero).
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ inline float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+template <int CTRL>
+__device__ inline float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over the four 16-lane rows: every lane gets ((row0 + row1) + (row2 +
+// row3)) for its column, in the same order for every column.
+__device__ inline float sum_rows(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
 // Merge two (max, sum) pairs that represent sum_k 2^(x_k - max).
 __device__ inline void merge_stat(float& m, float& z, float m2, float z2) {
-  float M = fmaxf(m, m2);
+  const float M = fmaxf(m, m2);
   z = z * fast_exp2(m - M) + z2 * fast_exp2(m2 - M);
   m = M;
 }
 
-// Physical id of block blk0 + wave + 4*i is held by lane i (i < 64); the
-// wave's block list is read once instead of once per block.
-__device__ inline int wave_block_ids(const ScoreParams& p, int r, int blk0, int blk1, int wave,
-                                     int lane) {
-  const int n = blk0 + wave + 4 * lane;
-  return n < blk1 ? p.src[(size_t)r * p.n_max + n] : 0;
+template <int CTRL>
+__device__ inline void merge_dpp(float& m, float& z) {
+  const float m2 = dpp<CTRL>(m), z2 = dpp<CTRL>(z);
+  merge_stat(m, z, m2, z2);
 }
 
-// Query fragments of the unit's rows: row = i*G + g holds window position i
-// of query head h*G + g.  Rows beyond `rows` are zero.
-template <int DT, int D, int RT>
-__device__ inline void load_q(const ScoreParams& p, const char* qbase, int r, int h, int col,
-                              int grp, uint4 (&qf)[RT][D * Mma<DT>::kElemBytes / 64]) {
-  constexpr int EB = Mma<DT>::kElemBytes;
-  constexpr int NV = D * EB / 64;
+// Running statistics update for one logit x (log2 units).
+__device__ inline void lazy_update(float& m, float& z, float x) {
+  const bool up = x > m + kLazy;
+  const float t = fast_exp2(up ? m - x : x - m);
+  z = up ? fmaf(z, t, 1.f) : z + t;
+  m = up ? x : m;
+}
+
+__device__ inline uint32_t order_key(float s) {
+  const uint32_t u = __float_as_uint(s + 0.0f);  // -0 + 0 = +0 under round-to-nearest
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Inclusive workgroup-wide sum; `scratch` holds >= kWaves ints.  Ends with
+// a barrier so scratch may be reused.
+__device__ inline int block_incl_sum(int v, int* scratch) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int rt = 0; rt < RT; rt++) {
-    const int row = rt * 16 + col;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(v, off);
+    if (lane >= off) v += t;
+  }
+  if (lane == 63) scratch[wave] = v;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; w++) before += scratch[w];
+  __syncthreads();
+  return v + before;
+}
+
+__device__ inline int block_broadcast_last(int v, int* scratch) {
+  if (threadIdx.x == kThreads - 1) scratch[kWaves] = v;
+  __syncthreads();
+  const int t = scratch[kWaves];
+  __syncthreads();
+  return t;
+}
+
+template <int DT, int D, int B, int RT>
+__global__ __launch_bounds__(kThreads) void k_score_select(ScoreParams p) {
+  constexpr int EB = Mma<DT>::kElemBytes;
+  constexpr int NV = D * EB / 64;       // 16-byte fragments per lane per 16-token tile
+  constexpr int NST = B / 16;           // 16-token sub-tiles per block
+  constexpr int RG = RT > 4 ? 2 : 1;    // row groups
+  constexpr int RTW = RT / RG;          // row tiles per wave
+  constexpr int WPG = kWaves / RG;      // waves per row group
+  constexpr int RPW = RTW * 16;         // rows per wave
+  constexpr int ROWB = D * EB;          // bytes per key row
+
+  const size_t unit = blockIdx.x;
+  const int h = (int)(unit % p.H);
+  const int lr = (int)(unit / p.H);
+  const int l = lr / p.R, r = lr - l * p.R;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, grp = lane >> 4;
+  const int rg = wave / WPG, wl = wave - rg * WPG;
+  const char* kbase = static_cast<const char*>(p.layer_ptrs[l * kPtrsPerLayer + 0]);
+  const char* qbase = static_cast<const char*>(p.layer_ptrs[l * kPtrsPerLayer + 2]);
+
+  __shared__ float s_buf[kLdsFloats];
+  __shared__ float s_wst[kWaves][RPW][2];
+  __shared__ float s_off[RT * 16];
+  __shared__ float s_nrm[kWaves][B];
+  __shared__ int s_hist[256];
+  __shared__ int s_scr[kWaves + 1];
+  __shared__ int s_sel[2];
+  float* s_sc = s_buf;          // scores (with two row groups: group 0's partial importance)
+  float* s_aux = s_buf + 4096;  // group 1's partial importance (two row groups only)
+  float* s_rr = s_buf + 8192;   // redundancy (two row groups only)
+
+  // query fragments: row = i*G + g is window position i of query head h*G+g
+  uint4 qf[RTW][NV];
+#pragma unroll
+  for (int rt = 0; rt < RTW; rt++) {
+    const int row = rg * RPW + rt * 16 + col;
     if (row < p.rows) {
       const int i = row / p.G, g = row - i * p.G;
-      const char* ptr = qbase + ((size_t)(r * p.w + i) * p.Hq + (size_t)h * p.G + g) * D * EB + grp * 16;
+      const char* ptr = qbase + ((size_t)(r * p.w + i) * p.Hq + (size_t)h * p.G + g) * ROWB + grp * 16;
 #pragma unroll
       for (int v = 0; v < NV; v++) qf[rt][v] = ld16(ptr + v * 64);
     } else {
@@ -112,280 +206,308 @@ __device__ inline void load_q(const ScoreParams& p, const char* qbase, int r, in
       for (int v = 0; v < NV; v++) qf[rt][v] = make_uint4(0, 0, 0, 0);
     }
   }
-}
-
-// Last slot each of the lane's output rows may attend to (causal window),
-// -1 for padding rows.
-template <int RT>
-__device__ inline void row_limits(const ScoreParams& p, int grp, int (&lim)[RT][4]) {
+  // last slot each output row may attend to (causal window); -1 for padding
+  int lim[RTW][4];
 #pragma unroll
-  for (int rt = 0; rt < RT; rt++)
+  for (int rt = 0; rt < RTW; rt++)
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      const int row = rt * 16 + 4 * grp + i;
+      const int row = rg * RPW + rt * 16 + 4 * grp + i;
       lim[rt][i] = row < p.rows ? p.T - p.w + row / p.G : -1;
     }
-}
 
-template <int DT, int D, int B, int RT>
-__global__ __launch_bounds__(256) void k_score_stats(ScoreParams p) {
-  constexpr int EB = Mma<DT>::kElemBytes;
-  constexpr int NV = D * EB / 64;
-  constexpr int NST = B / 16;
-  constexpr int RP = RT * 16;
-  const int chunk = blockIdx.x, h = blockIdx.y, lr = blockIdx.z;
-  const int l = lr / p.R, r = lr - l * p.R;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int col = lane & 15, grp = lane >> 4;
-  const char* kbase = static_cast<const char*>(p.layer_ptrs[l * kPtrsPerLayer + 0]);
-  const char* qbase = static_cast<const char*>(p.layer_ptrs[l * kPtrsPerLayer + 2]);
-
-  uint4 qf[RT][NV];
-  load_q<DT, D, RT>(p, qbase, r, h, col, grp, qf);
-  int lim[RT][4];
-  row_limits<RT>(p, grp, lim);
-  float m[RT][4], z[RT][4];
-#pragma unroll
-  for (int rt = 0; rt < RT; rt++)
-#pragma unroll
-    for (int i = 0; i < 4; i++) { m[rt][i] = kInitMax; z[rt][i] = 0.f; }
-
-  const int blk0 = chunk * p.chunk_blocks;
-  const int blk1 = min(blk0 + p.chunk_blocks, p.n_max);
-  const int n_items = blk1 - blk0 - wave > 0 ? (blk1 - blk0 - wave + 3) / 4 : 0;
-  const int ids = wave_block_ids(p, r, blk0, blk1, wave, lane);
-  const int row_off = col * D * EB + grp * 16;
-  // K fragments of the wave's next block are loaded (unconditionally, the
-  // last block again at the end) while the current one is consumed
-  auto fetch = [&](int i, uint4 (&kf)[NST][NV]) {
-    const int pblk = __builtin_amdgcn_readlane(ids, min(i, n_items - 1));
-    const char* tile = kbase + ((size_t)pblk * p.H + h) * B * D * EB + row_off;
+  // this wave's blocks are wl + WPG*k; lane k holds the physical id of the k-th
+  const int nbw = p.n_max > wl ? (p.n_max - wl + WPG - 1) / WPG : 0;
+  const int ids = lane < nbw ? p.src[(size_t)r * p.n_max + wl + WPG * lane] : 0;
+  const int row_off = col * ROWB + grp * 16;
+  // K fragments of the wave's it-th block (the last block again past the
+  // end: loads stay unconditional so the compiler can count them)
+  auto fetch = [&](int it, uint4 (&kd)[NST][NV]) {
+    const int pblk = __builtin_amdgcn_readlane(ids, min(it, nbw - 1));
+    const char* tile = kbase + ((size_t)pblk * p.H + h) * B * ROWB + row_off;
 #pragma unroll
     for (int st = 0; st < NST; st++)
 #pragma unroll
-      for (int v = 0; v < NV; v++) kf[st][v] = ld16(tile + st * 16 * D * EB + v * 64);
+      for (int v = 0; v < NV; v++) kd[st][v] = ld16(tile + st * 16 * ROWB + v * 64);
   };
-  uint4 kcur[NST][NV], knext[NST][NV];
-  if (n_items > 0) fetch(0, kcur);
-  for (int it = 0; it < n_items; it++) {
-    fetch(it + 1, knext);
-    const int n = blk0 + wave + 4 * it;
-#pragma unroll
-    for (int st = 0; st < NST; st++) {
-      const int j = n * B + st * 16 + col;
-#pragma unroll
-      for (int rt = 0; rt < RT; rt++) {
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int v = 0; v < NV; v++) acc = Mma<DT>::step(qf[rt][v], kcur[st][v], acc);
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-          if (j <= lim[rt][i]) {
-            const float x = acc[i] * p.scale_log2;
-            const bool up = x > m[rt][i] + kLazy;
-            const float t = fast_exp2(up ? m[rt][i] - x : x - m[rt][i]);
-            z[rt][i] = up ? fmaf(z[rt][i], t, 1.f) : z[rt][i] + t;
-            m[rt][i] = up ? x : m[rt][i];
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int st = 0; st < NST; st++)
-#pragma unroll
-      for (int v = 0; v < NV; v++) kcur[st][v] = knext[st][v];
-  }
-  // merge the 16 columns of every row
-#pragma unroll
-  for (int rt = 0; rt < RT; rt++)
-#pragma unroll
-    for (int i = 0; i < 4; i++)
-#pragma unroll
-      for (int off = 1; off < 16; off <<= 1) {
-        const float m2 = __shfl_xor(m[rt][i], off);
-        const float z2 = __shfl_xor(z[rt][i], off);
-        merge_stat(m[rt][i], z[rt][i], m2, z2);
-      }
-  __shared__ float sm[4][RP][2];
-  if (col == 0) {
-#pragma unroll
-    for (int rt = 0; rt < RT; rt++)
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        sm[wave][rt * 16 + 4 * grp + i][0] = m[rt][i];
-        sm[wave][rt * 16 + 4 * grp + i][1] = z[rt][i];
-      }
-  }
-  __syncthreads();
-  if (threadIdx.x < RP) {
-    const int row = threadIdx.x;
-    float M = sm[0][row][0], Z = sm[0][row][1];
-    for (int wv = 1; wv < 4; wv++) merge_stat(M, Z, sm[wv][row][0], sm[wv][row][1]);
-    const size_t unit = (size_t)lr * p.H + h;
-    float* out = p.stats + ((unit * p.nchunk + chunk) * p.rows_pad + row) * 2;
-    out[0] = M;
-    out[1] = Z;
-  }
-}
 
-template <int DT, int D, int B, int RT>
-__global__ __launch_bounds__(256) void k_score_final(ScoreParams p) {
-  constexpr int EB = Mma<DT>::kElemBytes;
-  constexpr int NV = D * EB / 64;
-  constexpr int NST = B / 16;
-  constexpr int RP = RT * 16;
-  // Workgroups run in the reverse order of the statistics pass, so the keys
-  // read last by that pass (most likely still in the last-level cache) are
-  // read again first.
-  const int chunk = gridDim.x - 1 - blockIdx.x, h = gridDim.y - 1 - blockIdx.y;
-  const int lr = gridDim.z - 1 - blockIdx.z;
-  const int l = lr / p.R, r = lr - l * p.R;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int col = lane & 15, grp = lane >> 4;
-  const size_t unit = (size_t)lr * p.H + h;
-  const char* kbase = static_cast<const char*>(p.layer_ptrs[l * kPtrsPerLayer + 0]);
-  const char* qbase = static_cast<const char*>(p.layer_ptrs[l * kPtrsPerLayer + 2]);
-
-  // final (max, 1/sum) of every row from the chunk statistics
-  __shared__ float smz[RP][2];
-  if (threadIdx.x < RP) {
-    const int row = threadIdx.x;
-    const float* st = p.stats + (unit * p.nchunk * p.rows_pad + row) * 2;
-    float M = kInitMax, Z = 0.f;
-    for (int c = 0; c < p.nchunk; c++)
-      merge_stat(M, Z, st[(size_t)c * p.rows_pad * 2], st[(size_t)c * p.rows_pad * 2 + 1]);
-    smz[row][0] = M;
-    smz[row][1] = Z > 0.f ? 1.0f / Z : 0.f;
-  }
-  __syncthreads();
-  float rm[RT][4], rz[RT][4];
+  // ---------------------------------------------------------------- pass 1
+  float m[RTW][4], z[RTW][4];
 #pragma unroll
-  for (int rt = 0; rt < RT; rt++)
+  for (int rt = 0; rt < RTW; rt++)
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      rm[rt][i] = smz[rt * 16 + 4 * grp + i][0];
-      rz[rt][i] = smz[rt * 16 + 4 * grp + i][1];
+      m[rt][i] = kInitMax;
+      z[rt][i] = 0.f;
     }
-  uint4 qf[RT][NV];
-  load_q<DT, D, RT>(p, qbase, r, h, col, grp, qf);
-  int lim[RT][4];
-  row_limits<RT>(p, grp, lim);
-  const float inv_rows = 1.0f / (float)p.rows;
-  const float inv_bm1 = 1.0f / (float)(B - 1);
-
-  const int blk0 = chunk * p.chunk_blocks;
-  const int blk1 = min(blk0 + p.chunk_blocks, p.n_max);
-  const int n_items = blk1 - blk0 - wave > 0 ? (blk1 - blk0 - wave + 3) / 4 : 0;
-  const int ids = wave_block_ids(p, r, blk0, blk1, wave, lane);
-  const int row_off = col * D * EB + grp * 16;
-  auto fetch = [&](int i, uint4 (&kd)[NST][NV]) {
-    const int pblk = __builtin_amdgcn_readlane(ids, min(i, n_items - 1));
-    const char* tile = kbase + ((size_t)pblk * p.H + h) * B * D * EB + row_off;
-#pragma unroll
-    for (int st = 0; st < NST; st++)
-#pragma unroll
-      for (int v = 0; v < NV; v++) kd[st][v] = ld16(tile + st * 16 * D * EB + v * 64);
-  };
-  uint4 kf[NST][NV], knext[NST][NV];
-  if (n_items > 0) fetch(0, kf);
-  for (int it = 0; it < n_items; it++) {
-    fetch(it + 1, knext);
-    const int n = blk0 + wave + 4 * it;
-    float A[NST], Rd[NST], nrm[NST];
-#pragma unroll
-    for (int st = 0; st < NST; st++) {
-      // importance: column sums of the row probabilities, fixed order
-      const int j = n * B + st * 16 + col;
-      float cs = 0.f;
-#pragma unroll
-      for (int rt = 0; rt < RT; rt++) {
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int v = 0; v < NV; v++) acc = Mma<DT>::step(qf[rt][v], kf[st][v], acc);
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-          const float pr = fast_exp2(acc[i] * p.scale_log2 - rm[rt][i]) * rz[rt][i];
-          cs += (j <= lim[rt][i]) ? pr : 0.f;
-        }
-      }
-      cs += __shfl_xor(cs, 16);
-      cs += __shfl_xor(cs, 32);
-      A[st] = cs * inv_rows;
-      // squared norm of key (st*16 + col)
-      float ss = 0.f;
-#pragma unroll
-      for (int v = 0; v < NV; v++) ss += Mma<DT>::sumsq(kf[st][v]);
-      ss += __shfl_xor(ss, 16);
-      ss += __shfl_xor(ss, 32);
-      nrm[st] = ss;
-    }
-    // redundancy: column sums of the in-block cosine matrix, diagonal excluded.
-    // Inverse norms of the lane's output rows (key 4*grp+i of sub-tile s1)
-    // come from the lane that holds that key as its column.
-    float ra[NST][4];
-#pragma unroll
-    for (int s1 = 0; s1 < NST; s1++)
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const float na = __shfl(nrm[s1], 4 * grp + i);
-        ra[s1][i] = na > 0.f ? rsqrtf(na) : 0.f;
-      }
-#pragma unroll
-    for (int s2 = 0; s2 < NST; s2++) {
-      float cs = 0.f;
-      const float nc = nrm[s2];
-      const float rc = nc > 0.f ? rsqrtf(nc) : 0.f;
-#pragma unroll
-      for (int s1 = 0; s1 < NST; s1++) {
-        f32x4_t g = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int v = 0; v < NV; v++) g = Mma<DT>::step(kf[s1][v], kf[s2][v], g);
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-          const bool diag = (s1 == s2) && (4 * grp + i == col);
-          cs += diag ? 0.f : g[i] * ra[s1][i] * rc;
-        }
-      }
-      cs += __shfl_xor(cs, 16);
-      cs += __shfl_xor(cs, 32);
-      Rd[s2] = cs * inv_bm1;
-    }
-    if (grp == 0) {
+  {
+    uint4 kc[NST][NV], kn[NST][NV];
+    if (nbw > 0) fetch(0, kc);
+    for (int it = 0; it < nbw; it++) {
+      fetch(it + 1, kn);
+      const int n = wl + WPG * it;
+      const bool last = n == p.n_max - 1;  // only the last block meets the causal limit
 #pragma unroll
       for (int st = 0; st < NST; st++) {
         const int j = n * B + st * 16 + col;
-        const float s = A[st] * (1.0f - Rd[st]);
-        const size_t o = unit * p.T + j;
-        p.score[o] = s;
-        if (p.dbg_importance) p.dbg_importance[o] = A[st];
-        if (p.dbg_redundancy) p.dbg_redundancy[o] = Rd[st];
-        if (p.dbg_score && j < p.C) p.dbg_score[o] = s;
+        f32x4_t acc[RTW];
+#pragma unroll
+        for (int rt = 0; rt < RTW; rt++) {
+          acc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int v = 0; v < NV; v++) acc[rt] = Mma<DT>::step(qf[rt][v], kc[st][v], acc[rt]);
+        }
+        bool slow = last;
+#pragma unroll
+        for (int rt = 0; rt < RTW; rt++)
+#pragma unroll
+          for (int i = 0; i < 4; i++) slow |= acc[rt][i] * p.scale_log2 > m[rt][i] + kLazy;
+        if (slow) {
+#pragma unroll
+          for (int rt = 0; rt < RTW; rt++)
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+              if (j <= lim[rt][i]) lazy_update(m[rt][i], z[rt][i], acc[rt][i] * p.scale_log2);
+        } else {
+#pragma unroll
+          for (int rt = 0; rt < RTW; rt++)
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+              z[rt][i] += fast_exp2(fmaf(acc[rt][i], p.scale_log2, -m[rt][i]));
+        }
+      }
+#pragma unroll
+      for (int st = 0; st < NST; st++)
+#pragma unroll
+        for (int v = 0; v < NV; v++) kc[st][v] = kn[st][v];
+    }
+  }
+  // merge the 16 columns of every row (DPP inside 16-lane rows)
+#pragma unroll
+  for (int rt = 0; rt < RTW; rt++)
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      merge_dpp<0xB1>(m[rt][i], z[rt][i]);   // quad_perm [1,0,3,2]
+      merge_dpp<0x4E>(m[rt][i], z[rt][i]);   // quad_perm [2,3,0,1]
+      merge_dpp<0x141>(m[rt][i], z[rt][i]);  // row_half_mirror
+      merge_dpp<0x140>(m[rt][i], z[rt][i]);  // row_mirror
+    }
+  if (col == 0) {
+#pragma unroll
+    for (int rt = 0; rt < RTW; rt++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        s_wst[wave][rt * 16 + 4 * grp + i][0] = m[rt][i];
+        s_wst[wave][rt * 16 + 4 * grp + i][1] = z[rt][i];
+      }
+  }
+  __syncthreads();
+  if (tid < RT * 16) {
+    const int g = tid / RPW, row = tid - g * RPW;
+    float M = kInitMax, Z = 0.f;
+    for (int w = g * WPG; w < (g + 1) * WPG; w++) merge_stat(M, Z, s_wst[w][row][0], s_wst[w][row][1]);
+    // probability of a logit x (log2 units) in this row: 2^(x - offset)
+    s_off[tid] = Z > 0.f ? M + fast_log2(Z) : 1.0e30f;
+  }
+  __syncthreads();
+  float off[RTW][4];
+#pragma unroll
+  for (int rt = 0; rt < RTW; rt++)
+#pragma unroll
+    for (int i = 0; i < 4; i++) off[rt][i] = s_off[rg * RPW + rt * 16 + 4 * grp + i];
+
+  // ---------------------------------------------------------------- pass 2
+  const float inv_rows = 1.0f / (float)p.rows;
+  const float inv_bm1 = 1.0f / (float)(B - 1);
+  {
+    uint4 kc[NST][NV], kn[NST][NV];
+    if (nbw > 0) fetch(0, kc);
+    for (int it = 0; it < nbw; it++) {
+      fetch(it + 1, kn);
+      const int n = wl + WPG * it;
+      const bool last = n == p.n_max - 1;
+      float A[NST], nrm[NST];
+#pragma unroll
+      for (int st = 0; st < NST; st++) {
+        const int j = n * B + st * 16 + col;
+        float cs = 0.f;
+#pragma unroll
+        for (int rt = 0; rt < RTW; rt++) {
+          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int v = 0; v < NV; v++) acc = Mma<DT>::step(qf[rt][v], kc[st][v], acc);
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            const float pr = fast_exp2(fmaf(acc[i], p.scale_log2, -off[rt][i]));
+            cs += (!last || j <= lim[rt][i]) ? pr : 0.f;
+          }
+        }
+        A[st] = sum_rows(cs);
+        float ss = 0.f;
+#pragma unroll
+        for (int v = 0; v < NV; v++) ss += Mma<DT>::sumsq(kc[st][v]);
+        nrm[st] = sum_rows(ss);
+      }
+      if (RG == 1 || rg == 0) {
+        // redundancy: column sums of the in-block cosine matrix, diagonal
+        // excluded; the inverse norms of a lane's output rows (keys 4*grp+i)
+        // come through a per-wave LDS slot
+        if (grp == 0) {
+#pragma unroll
+          for (int st = 0; st < NST; st++) s_nrm[wave][st * 16 + col] = nrm[st];
+        }
+        __builtin_amdgcn_wave_barrier();
+        float ra[NST][4];
+#pragma unroll
+        for (int s1 = 0; s1 < NST; s1++)
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            const float na = s_nrm[wave][s1 * 16 + 4 * grp + i];
+            ra[s1][i] = na > 0.f ? rsqrtf(na) : 0.f;
+          }
+        __builtin_amdgcn_wave_barrier();
+        float Rd[NST];
+#pragma unroll
+        for (int s2 = 0; s2 < NST; s2++) {
+          float cs = 0.f;
+          const float rc = nrm[s2] > 0.f ? rsqrtf(nrm[s2]) : 0.f;
+#pragma unroll
+          for (int s1 = 0; s1 < NST; s1++) {
+            f32x4_t gm = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int v = 0; v < NV; v++) gm = Mma<DT>::step(kc[s1][v], kc[s2][v], gm);
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+              const bool diag = (s1 == s2) && (4 * grp + i == col);
+              cs += diag ? 0.f : gm[i] * ra[s1][i] * rc;
+            }
+          }
+          Rd[s2] = sum_rows(cs) * inv_bm1;
+        }
+        if (grp == 0) {
+#pragma unroll
+          for (int st = 0; st < NST; st++) {
+            const int j = n * B + st * 16 + col;
+            if (RG == 1) {
+              const float a = A[st] * inv_rows;
+              const float s = a * (1.0f - Rd[st]);
+              s_sc[j] = s;
+              const size_t o = unit * p.T + j;
+              if (p.dbg_importance) p.dbg_importance[o] = a;
+              if (p.dbg_redundancy) p.dbg_redundancy[o] = Rd[st];
+              if (p.dbg_score && j < p.C) p.dbg_score[o] = s;
+            } else {
+              s_sc[j] = A[st];
+              s_rr[j] = Rd[st];
+            }
+          }
+        }
+      } else if (grp == 0) {
+#pragma unroll
+        for (int st = 0; st < NST; st++) s_aux[n * B + st * 16 + col] = A[st];
+      }
+#pragma unroll
+      for (int st = 0; st < NST; st++)
+#pragma unroll
+        for (int v = 0; v < NV; v++) kc[st][v] = kn[st][v];
+    }
+  }
+  __syncthreads();
+  if (RG == 2) {
+    for (int j = tid; j < p.T; j += kThreads) {
+      const float a = (s_sc[j] + s_aux[j]) * inv_rows;
+      const float s = a * (1.0f - s_rr[j]);
+      const size_t o = unit * p.T + j;
+      if (p.dbg_importance) p.dbg_importance[o] = a;
+      if (p.dbg_redundancy) p.dbg_redundancy[o] = s_rr[j];
+      if (p.dbg_score && j < p.C) p.dbg_score[o] = s;
+      s_sc[j] = s;
+    }
+    __syncthreads();
+  }
+
+  // ---------------------------------------------------------------- select
+  // thread t owns the contiguous slots [t*per, (t+1)*per)
+  const int per = (p.T + kThreads - 1) / kThreads;
+  const int j0 = tid * per, j1 = min(j0 + per, p.C);
+  uint32_t prefix = 0, pmask = 0;
+  int rank = p.E;  // the E-th smallest candidate key, counted from 1
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    if (tid < 256) s_hist[tid] = 0;
+    __syncthreads();
+    for (int j = j0; j < j1; j++) {
+      const uint32_t key = order_key(s_sc[j]);
+      if ((key & pmask) == prefix) atomicAdd(&s_hist[(key >> shift) & 0xFFu], 1);
+    }
+    __syncthreads();
+    const int cnt = tid < 256 ? s_hist[tid] : 0;
+    const int incl = block_incl_sum(cnt, s_scr);
+    if (tid < 256 && incl - cnt < rank && incl >= rank) {
+      s_sel[0] = tid;
+      s_sel[1] = incl - cnt;
+    }
+    __syncthreads();
+    prefix |= (uint32_t)s_sel[0] << shift;
+    pmask |= 0xFFu << shift;
+    rank -= s_sel[1];
+    __syncthreads();
+  }
+  const uint32_t tau = prefix;  // the E-th smallest key
+  const int evict_ties = rank;  // how many keys equal to tau are evicted
+  int my_ties = 0;
+  for (int j = j0; j < j1; j++) my_ties += order_key(s_sc[j]) == tau ? 1 : 0;
+  const int ties_incl = block_incl_sum(my_ties, s_scr);
+  const int ties_total = block_broadcast_last(ties_incl, s_scr);
+  // evicted: keys below tau, and the evict_ties highest slots equal to tau
+  int tie_rank = ties_incl - my_ties;
+  int my_ev = 0;
+  for (int j = j0; j < j1; j++) {
+    const uint32_t key = order_key(s_sc[j]);
+    if (key < tau) {
+      my_ev++;
+    } else if (key == tau) {
+      my_ev += tie_rank >= ties_total - evict_ties ? 1 : 0;
+      tie_rank++;
+    }
+  }
+  const int ev_incl = block_incl_sum(my_ev, s_scr);
+  int pos = ev_incl - my_ev;
+  int32_t* out = p.evicted + unit * p.E;
+  tie_rank = ties_incl - my_ties;
+  int kept_pos = j0 - pos;  // survivors below j0
+  const int jend = min(j0 + per, p.T);
+  for (int j = j0; j < jend; j++) {
+    bool ev = false;
+    if (j < p.C) {
+      const uint32_t key = order_key(s_sc[j]);
+      if (key < tau) {
+        ev = true;
+      } else if (key == tau) {
+        ev = tie_rank >= ties_total - evict_ties;
+        tie_rank++;
       }
     }
-#pragma unroll
-    for (int st = 0; st < NST; st++)
-#pragma unroll
-      for (int v = 0; v < NV; v++) kf[st][v] = knext[st][v];
+    if (ev) {
+      if (pos < p.E) out[pos] = j;
+      pos++;
+    } else {
+      if (p.dbg_kept && kept_pos >= 0 && kept_pos < p.K_keep) p.dbg_kept[unit * p.K_keep + kept_pos] = j;
+      kept_pos++;
+    }
   }
 }
 
 template <int DT, int D, int B, int RT>
 hipError_t launch_rt(const ScoreParams& p, int units, hipStream_t s) {
-  dim3 grid(p.nchunk, p.H, units / p.H);
-  prof_begin(ZP_PHASE_SCORE_STATS, s);
-  hipLaunchKernelGGL((k_score_stats<DT, D, B, RT>), grid, dim3(256), 0, s, p);
-  prof_end(ZP_PHASE_SCORE_STATS, s);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   prof_begin(ZP_PHASE_SCORE, s);
-  hipLaunchKernelGGL((k_score_final<DT, D, B, RT>), grid, dim3(256), 0, s, p);
+  hipLaunchKernelGGL((k_score_select<DT, D, B, RT>), dim3(units), dim3(kThreads), 0, s, p);
   prof_end(ZP_PHASE_SCORE, s);
   return hipGetLastError();
 }
 
 template <int DT, int D, int B>
-hipError_t launch_b(const ScoreParams& p, int units, hipStream_t s) {
-  switch (p.rows_pad / 16) {
+hipError_t launch_b(const ScoreParams& p, int row_tiles, int units, hipStream_t s) {
+  switch (row_tiles) {
     case 1: return launch_rt<DT, D, B, 1>(p, units, s);
     case 2: return launch_rt<DT, D, B, 2>(p, units, s);
     case 4: return launch_rt<DT, D, B, 4>(p, units, s);
@@ -395,16 +517,17 @@ hipError_t launch_b(const ScoreParams& p, int units, hipStream_t s) {
 }
 
 template <int DT, int D>
-hipError_t launch_d(const ScoreParams& p, int block_size, int units, hipStream_t s) {
-  if (block_size == 16) return launch_b<DT, D, 16>(p, units, s);
-  if (block_size == 32) return launch_b<DT, D, 32>(p, units, s);
+hipError_t launch_d(const ScoreParams& p, int block_size, int row_tiles, int units, hipStream_t s) {
+  if (block_size == 16) return launch_b<DT, D, 16>(p, row_tiles, units, s);
+  if (block_size == 32) return launch_b<DT, D, 32>(p, row_tiles, units, s);
   return hipErrorInvalidValue;
 }
 
 template <int DT>
-hipError_t launch_dt(const ScoreParams& p, int head_dim, int block_size, int units, hipStream_t s) {
-  if (head_dim == 64) return launch_d<DT, 64>(p, block_size, units, s);
-  if (head_dim == 128) return launch_d<DT, 128>(p, block_size, units, s);
+hipError_t launch_dt(const ScoreParams& p, int head_dim, int block_size, int row_tiles, int units,
+                     hipStream_t s) {
+  if (head_dim == 64) return launch_d<DT, 64>(p, block_size, row_tiles, units, s);
+  if (head_dim == 128) return launch_d<DT, 128>(p, block_size, row_tiles, units, s);
   return hipErrorInvalidValue;
 }
 
@@ -412,17 +535,25 @@ hipError_t launch_dt(const ScoreParams& p, int head_dim, int block_size, int uni
 
 int score_row_tiles(int rows) {
   if (rows <= 0 || rows > kMaxScoreRows) return 0;
-  int t = (rows + 15) / 16;
+  const int t = (rows + 15) / 16;
   int p2 = 1;
   while (p2 < t) p2 <<= 1;
   return p2;
 }
 
+bool score_fits(int rows, int T) {
+  const int rt = score_row_tiles(rows);
+  if (rt == 0 || T > kMaxScoreSlots) return false;
+  return rt <= 4 || T <= 4096;  // two row groups keep three T-long arrays in LDS
+}
+
 hipError_t launch_score(const ScoreParams& p, int dtype, int head_dim, int block_size, int units,
                         hipStream_t s) {
   if (units <= 0) return hipSuccess;
-  if (dtype == ZP_BF16) return launch_dt<ZP_BF16>(p, head_dim, block_size, units, s);
-  if (dtype == ZP_F32) return launch_dt<ZP_F32>(p, head_dim, block_size, units, s);
+  if (!score_fits(p.rows, p.T)) return hipErrorInvalidValue;
+  const int rt = score_row_tiles(p.rows);
+  if (dtype == ZP_BF16) return launch_dt<ZP_BF16>(p, head_dim, block_size, rt, units, s);
+  if (dtype == ZP_F32) return launch_dt<ZP_F32>(p, head_dim, block_size, rt, units, s);
   return hipErrorInvalidValue;
 }
 

@@ -27,4 +27,15 @@ __device__ inline void stg16(void* p, uint4 v) {
   *(g_u32x4*)(p) = w;
 }
 
+// Streaming variants: the data is touched once, so ask the memory system not
+// to keep it (non-temporal hint on the global load / store).
+__device__ inline uint4 ldg16_stream(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load((g_cu32x4*)(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ inline void stg16_stream(void* p, uint4 v) {
+  const u32x4_t w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, (g_u32x4*)(p));
+}
+
 }  // namespace zp

@@ -21,10 +21,10 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // entry [l*3 + 0] = K pool, [l*3 + 1] = V pool, [l*3 + 2] = window queries.
 constexpr int kPtrsPerLayer = 3;
 
-// Token chunk handled by one workgroup of the scoring kernels.
-constexpr int kScoreChunkTokens = 512;
-// Largest number of (query head, window row) pairs per KV head.
+// Largest number of (query head, window row) pairs per KV head, and the
+// largest cached length the in-LDS scoring and selection handle.
 constexpr int kMaxScoreRows = 128;
+constexpr int kMaxScoreSlots = 8192;
 // Paged decode: threads per workgroup, and the workgroup count below which
 // a request's block list is split over several workgroups.
 #ifndef ZP_DECODE_THREADS
@@ -39,20 +39,13 @@ constexpr int kDecodeTargetWorkgroups = ZP_DECODE_TARGET_WORKGROUPS;
 struct ScoreParams {
   void* const* layer_ptrs;  // device [L][3]
   const int32_t* src;       // device [R][n_max]
-  float* stats;             // [L*R*H][nchunk][rows_pad][2]
-  float* score;             // [L*R*H][T]
+  int32_t* evicted;         // [L*R*H][E], ascending
   float* dbg_importance;    // optional [L*R*H][T]
   float* dbg_redundancy;    // optional [L*R*H][T]
   float* dbg_score;         // optional [L*R*H][T]
-  int32_t R, H, Hq, G, w, n_max, T, C, rows, rows_pad, nchunk, chunk_blocks;
+  int32_t* dbg_kept;        // optional [L*R*H][K_keep]
+  int32_t R, H, Hq, G, w, n_max, T, C, E, K_keep, rows;
   float scale_log2;  // log2(e) / sqrt(d)
-};
-
-struct SelectParams {
-  const float* score;  // [units][T]
-  int32_t* evicted;    // [units][E], ascending
-  int32_t* dbg_kept;   // optional [units][K_keep]
-  int32_t units, T, C, E, K_keep;
 };
 
 struct CompactParams {
@@ -88,7 +81,6 @@ struct AppendParams {
 // dispatch and enqueue.  Return hipSuccess or the launch error.
 hipError_t launch_score(const ScoreParams& p, int dtype, int head_dim, int block_size, int units,
                         hipStream_t s);
-hipError_t launch_select(const SelectParams& p, hipStream_t s);
 hipError_t launch_compact(const CompactParams& p, int num_layers, int row_bytes, int block_size,
                           hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, int block_size,
@@ -101,7 +93,7 @@ void prof_begin(int phase, hipStream_t s);
 void prof_end(int phase, hipStream_t s);
 
 // Geometry helpers shared by the validation and the workspace layout.
-int score_row_tiles(int rows);  // 1, 2, 4 or 8 tiles of 16 rows; 0 if rows > kMaxScoreRows
-int select_per_thread(int T);   // slots per thread of the selection kernel; 0 if too many
+int score_row_tiles(int rows);     // 1, 2, 4 or 8 tiles of 16 rows; 0 if rows > kMaxScoreRows
+bool score_fits(int rows, int T);  // the fused scoring + selection kernel handles this shape
 
 }  // namespace zp

@@ -255,8 +255,8 @@ def test_workspace_sizes_grow_with_the_batch():
     a = zp.compress_workspace_bytes(cache, 1, 128, 16)
     b = zp.compress_workspace_bytes(cache, 64, 128, 16)
     assert 0 < a < b and b % 256 == 0
-    # the score buffer alone: L*R*H*T floats
-    assert b >= 2 * 64 * 8 * 2048 * 4
+    # tables and pointers, plus the evicted slots: L*R*H*E int32
+    assert b >= 2 * 64 * 8 * 16 * 4 + 64 * 128 * 4 + 64 * 127 * 4
     # 64 requests x 8 KV heads fill the GPU: one workgroup per (request, head),
     # no split and no workspace; a single request is split in chunks of whole
     # multiples of 8 blocks, with one partial (m, l, o[d]) per split
