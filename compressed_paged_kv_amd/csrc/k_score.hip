@@ -14,7 +14,7 @@
 // Phases, all inside the workgroup:
 //   1. softmax statistics: each wave runs over its share of the unit's
 //      blocks keeping, per window row, a running (max, sum of 2^(x - max))
-//      that is rescaled only when the max grows by more than 2^8; lanes and
+//      that is rescaled only when the max grows by more than 64 (log2 units); lanes and
 //      waves are then merged in LDS into one exponent offset per row,
 //      M + log2(Z), so a probability is a single 2^(x - offset);
 //   2. the same blocks again (now in cache): probabilities summed over the
@@ -43,8 +43,26 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kInitMax = -1.0e30f;  // finite "minus infinity": merges never form inf - inf
-constexpr float kLazy = 8.0f;         // rescale a running sum only when its max grows by > 2^8
+// A running sum is rescaled only when a term would exceed 2^kLazy: terms stay
+// below 2^64 and a sum of at most 8192 of them below 2^77, far from the float
+// range, while a lane that saw one low logit first (it holds one key per
+// block) rarely has to leave the fast path.
+constexpr float kLazy = 64.0f;
+constexpr float kLazyTerm = 18446744073709551616.0f;  // 2^kLazy
+constexpr float kMasked = -3.0e38f;   // logit of a causally masked slot: adds 2^(-huge) = 0
 constexpr int kLdsFloats = 3 * 4096;  // scores (T <= 8192), or three T <= 4096 arrays
+#ifndef ZP_SCORE_RING_VGPRS
+#define ZP_SCORE_RING_VGPRS 32
+#endif
+#ifndef ZP_SCORE_REVERSE
+#define ZP_SCORE_REVERSE 1
+#endif
+constexpr bool kReversePass2 = ZP_SCORE_REVERSE != 0;
+
+template <bool V>
+struct BoolC {
+  static constexpr bool value = V;
+};
 
 template <int DT>
 struct Mma;
@@ -158,16 +176,29 @@ __device__ inline int block_broadcast_last(int v, int* scratch) {
   return t;
 }
 
-template <int DT, int D, int B, int RT>
-__global__ __launch_bounds__(kThreads) void k_score_select(ScoreParams p) {
+// Two workgroups fit a CU when a wave's Q fragments and K ring stay small
+// (at most 128 registers a lane); otherwise one.
+template <int DT, int D, int RTW, int B>
+constexpr int score_min_blocks() {
+  return (RTW * D * Mma<DT>::kElemBytes / 64 <= 8 && (B / 16) * D * Mma<DT>::kElemBytes / 64 <= 4) ? 2 : 1;
+}
+
+// RG row groups: with two, waves 0-3 take the first half of the row tiles and
+// waves 4-7 the second, both over all blocks, which halves the Q fragments a
+// wave holds.
+template <int DT, int D, int B, int RT, int RG>
+__global__ __launch_bounds__(kThreads, (score_min_blocks<DT, D, RT / RG, B>())) void k_score_select(ScoreParams p) {
   constexpr int EB = Mma<DT>::kElemBytes;
   constexpr int NV = D * EB / 64;       // 16-byte fragments per lane per 16-token tile
   constexpr int NST = B / 16;           // 16-token sub-tiles per block
-  constexpr int RG = RT > 4 ? 2 : 1;    // row groups
   constexpr int RTW = RT / RG;          // row tiles per wave
   constexpr int WPG = kWaves / RG;      // waves per row group
   constexpr int RPW = RTW * 16;         // rows per wave
   constexpr int ROWB = D * EB;          // bytes per key row
+  // K ring slots: as many block tiles as fit the register budget, 2 to 4
+  constexpr int kPrefetch = ZP_SCORE_RING_VGPRS / (NST * NV * 4) < 2   ? 2
+                            : ZP_SCORE_RING_VGPRS / (NST * NV * 4) > 4 ? 4
+                                                                       : ZP_SCORE_RING_VGPRS / (NST * NV * 4);
 
   const size_t unit = blockIdx.x;
   const int h = (int)(unit % p.H);
@@ -206,32 +237,56 @@ __global__ __launch_bounds__(kThreads) void k_score_select(ScoreParams p) {
       for (int v = 0; v < NV; v++) qf[rt][v] = make_uint4(0, 0, 0, 0);
     }
   }
-  // last slot each output row may attend to (causal window); -1 for padding
-  int lim[RTW][4];
-#pragma unroll
-  for (int rt = 0; rt < RTW; rt++)
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int row = rg * RPW + rt * 16 + 4 * grp + i;
-      lim[rt][i] = row < p.rows ? p.T - p.w + row / p.G : -1;
-    }
+  // last slot output row (rt, i) of this lane may attend to (causal window);
+  // -1 for padding rows.  Only the last block needs it, so it is not kept.
+  auto lim = [&](int rt, int i) {
+    const int row = rg * RPW + rt * 16 + 4 * grp + i;
+    return row < p.rows ? p.T - p.w + row / p.G : -1;
+  };
 
   // this wave's blocks are wl + WPG*k; lane k holds the physical id of the k-th
   const int nbw = p.n_max > wl ? (p.n_max - wl + WPG - 1) / WPG : 0;
   const int ids = lane < nbw ? p.src[(size_t)r * p.n_max + wl + WPG * lane] : 0;
   const int row_off = col * ROWB + grp * 16;
-  // K fragments of the wave's it-th block (the last block again past the
-  // end: loads stay unconditional so the compiler can count them)
-  auto fetch = [&](int it, uint4 (&kd)[NST][NV]) {
-    const int pblk = __builtin_amdgcn_readlane(ids, min(it, nbw - 1));
+  // K fragments of the wave's k-th block (k is clamped, so the loads stay
+  // unconditional and the compiler can wait for each ring slot on its own)
+  auto fetch = [&](int k, uint4 (&kd)[NST][NV]) {
+    const int pblk = __builtin_amdgcn_readlane(ids, max(min(k, nbw - 1), 0));
     const char* tile = kbase + ((size_t)pblk * p.H + h) * B * ROWB + row_off;
 #pragma unroll
     for (int st = 0; st < NST; st++)
 #pragma unroll
       for (int v = 0; v < NV; v++) kd[st][v] = ld16(tile + st * 16 * ROWB + v * 64);
   };
+  // Runs body(k, fragments) over the wave's blocks through a ring of PD
+  // register buffers: slot s is refilled right after it is consumed, so
+  // PD - 1 blocks stay in flight.  Pass 2 walks the blocks in reverse, so it
+  // starts on those pass 1 read last (still in L2 / the memory-side cache).
+  auto ring = [&](auto reverse, auto body) {
+    constexpr bool REV = decltype(reverse)::value;
+    auto kof = [&](int it) { return REV ? nbw - 1 - it : it; };
+    if (nbw == 0) return;
+    uint4 kb[kPrefetch][NST][NV];
+    // the prologue keeps slot order (the scheduler may not interleave the
+    // fetches), so the wait before slot s counts the same loads on entry as
+    // in the steady state
+#pragma unroll
+    for (int s = 0; s < kPrefetch; s++) {
+      fetch(kof(s), kb[s]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int it0 = 0; it0 < nbw; it0 += kPrefetch) {
+#pragma unroll
+      for (int s = 0; s < kPrefetch; s++) {
+        const int it = it0 + s;
+        if (it < nbw) body(kof(it), kb[s]);
+        fetch(kof(it + kPrefetch), kb[s]);
+      }
+    }
+  };
 
   // ---------------------------------------------------------------- pass 1
+  const float sl2 = p.scale_log2;
   float m[RTW][4], z[RTW][4];
 #pragma unroll
   for (int rt = 0; rt < RTW; rt++)
@@ -240,48 +295,44 @@ __global__ __launch_bounds__(kThreads) void k_score_select(ScoreParams p) {
       m[rt][i] = kInitMax;
       z[rt][i] = 0.f;
     }
-  {
-    uint4 kc[NST][NV], kn[NST][NV];
-    if (nbw > 0) fetch(0, kc);
-    for (int it = 0; it < nbw; it++) {
-      fetch(it + 1, kn);
-      const int n = wl + WPG * it;
-      const bool last = n == p.n_max - 1;  // only the last block meets the causal limit
+  ring(BoolC<false>{}, [&](int k, const uint4 (&kt)[NST][NV]) {
+    const int n = wl + WPG * k;
+    const bool last = n == p.n_max - 1;  // only the last block meets the causal limit
 #pragma unroll
-      for (int st = 0; st < NST; st++) {
-        const int j = n * B + st * 16 + col;
-        f32x4_t acc[RTW];
+    for (int st = 0; st < NST; st++) {
+      const int j = n * B + st * 16 + col;
+      f32x4_t acc[RTW];
 #pragma unroll
-        for (int rt = 0; rt < RTW; rt++) {
-          acc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int rt = 0; rt < RTW; rt++) {
+        acc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int v = 0; v < NV; v++) acc[rt] = Mma<DT>::step(qf[rt][v], kc[st][v], acc[rt]);
+        for (int v = 0; v < NV; v++) acc[rt] = Mma<DT>::step(qf[rt][v], kt[st][v], acc[rt]);
+      }
+      // 2^(x - m) for every logit; a term above 2^kLazy (or the causal
+      // block) sends the lane through the rescaling update instead
+      float e[RTW][4];
+      bool slow = last;
+#pragma unroll
+      for (int rt = 0; rt < RTW; rt++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          e[rt][i] = fast_exp2(fmaf(acc[rt][i], sl2, -m[rt][i]));
+          slow |= e[rt][i] > kLazyTerm;
         }
-        bool slow = last;
+      if (slow) {
 #pragma unroll
         for (int rt = 0; rt < RTW; rt++)
 #pragma unroll
-          for (int i = 0; i < 4; i++) slow |= acc[rt][i] * p.scale_log2 > m[rt][i] + kLazy;
-        if (slow) {
+          for (int i = 0; i < 4; i++)
+            lazy_update(m[rt][i], z[rt][i], j <= lim(rt, i) ? acc[rt][i] * sl2 : kMasked);
+      } else {
 #pragma unroll
-          for (int rt = 0; rt < RTW; rt++)
+        for (int rt = 0; rt < RTW; rt++)
 #pragma unroll
-            for (int i = 0; i < 4; i++)
-              if (j <= lim[rt][i]) lazy_update(m[rt][i], z[rt][i], acc[rt][i] * p.scale_log2);
-        } else {
-#pragma unroll
-          for (int rt = 0; rt < RTW; rt++)
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-              z[rt][i] += fast_exp2(fmaf(acc[rt][i], p.scale_log2, -m[rt][i]));
-        }
+          for (int i = 0; i < 4; i++) z[rt][i] += e[rt][i];
       }
-#pragma unroll
-      for (int st = 0; st < NST; st++)
-#pragma unroll
-        for (int v = 0; v < NV; v++) kc[st][v] = kn[st][v];
     }
-  }
+  });
   // merge the 16 columns of every row (DPP inside 16-lane rows)
 #pragma unroll
   for (int rt = 0; rt < RTW; rt++)
@@ -319,99 +370,108 @@ __global__ __launch_bounds__(kThreads) void k_score_select(ScoreParams p) {
   // ---------------------------------------------------------------- pass 2
   const float inv_rows = 1.0f / (float)p.rows;
   const float inv_bm1 = 1.0f / (float)(B - 1);
-  {
-    uint4 kc[NST][NV], kn[NST][NV];
-    if (nbw > 0) fetch(0, kc);
-    for (int it = 0; it < nbw; it++) {
-      fetch(it + 1, kn);
-      const int n = wl + WPG * it;
-      const bool last = n == p.n_max - 1;
-      float A[NST], nrm[NST];
+  // column sums of the probabilities of sub-tile st (causal mask: last block only)
+  auto prob_sum = [&](auto lastc, int j, const uint4 (&kf)[NV]) {
+    constexpr bool LAST = decltype(lastc)::value;
+    float cs = 0.f;
+#pragma unroll
+    for (int rt = 0; rt < RTW; rt++) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int v = 0; v < NV; v++) acc = Mma<DT>::step(qf[rt][v], kf[v], acc);
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const float pr = fast_exp2(fmaf(acc[i], sl2, -off[rt][i]));
+        cs += (!LAST || j <= lim(rt, i)) ? pr : 0.f;
+      }
+    }
+    return sum_rows(cs);
+  };
+  ring(BoolC<kReversePass2>{}, [&](int k, const uint4 (&kt)[NST][NV]) {
+    const int n = wl + WPG * k;
+    const bool last = n == p.n_max - 1;
+    float A[NST];
+#pragma unroll
+    for (int st = 0; st < NST; st++) {
+      const int j = n * B + st * 16 + col;
+      A[st] = last ? prob_sum(BoolC<true>{}, j, kt[st]) : prob_sum(BoolC<false>{}, j, kt[st]);
+    }
+    if (RG == 2 && grp == 0) {
+      float* dst = rg == 0 ? s_sc : s_aux;
+#pragma unroll
+      for (int st = 0; st < NST; st++) dst[n * B + st * 16 + col] = A[st];
+    }
+    // the two row groups see the same blocks: they take turns on the Gram work
+    if (RG == 1 || (k & 1) == rg) {
+      // redundancy: column sums of the in-block cosine matrix, diagonal
+      // excluded.  gm[s1][s2] holds the dot products of keys 16*s1 + 4*grp + i
+      // (rows) with keys 16*s2 + col; the diagonal tiles give the squared
+      // norms, and the inverse norms of a lane's rows come through LDS.
+      f32x4_t gm[NST][NST];
+#pragma unroll
+      for (int s1 = 0; s1 < NST; s1++)
+#pragma unroll
+        for (int s2 = 0; s2 < NST; s2++) {
+          gm[s1][s2] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int v = 0; v < NV; v++) gm[s1][s2] = Mma<DT>::step(kt[s1][v], kt[s2][v], gm[s1][s2]);
+        }
+      float nrm[NST];
 #pragma unroll
       for (int st = 0; st < NST; st++) {
-        const int j = n * B + st * 16 + col;
-        float cs = 0.f;
-#pragma unroll
-        for (int rt = 0; rt < RTW; rt++) {
-          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int v = 0; v < NV; v++) acc = Mma<DT>::step(qf[rt][v], kc[st][v], acc);
-#pragma unroll
-          for (int i = 0; i < 4; i++) {
-            const float pr = fast_exp2(fmaf(acc[i], p.scale_log2, -off[rt][i]));
-            cs += (!last || j <= lim[rt][i]) ? pr : 0.f;
-          }
-        }
-        A[st] = sum_rows(cs);
-        float ss = 0.f;
-#pragma unroll
-        for (int v = 0; v < NV; v++) ss += Mma<DT>::sumsq(kc[st][v]);
-        nrm[st] = sum_rows(ss);
+        const f32x4_t g = gm[st][st];
+        const int e = col & 3;
+        float dg = e == 0 ? g[0] : e == 1 ? g[1] : e == 2 ? g[2] : g[3];
+        dg = (col >> 2) == grp ? dg : 0.f;  // lane (col/4, col) holds key col's diagonal entry
+        nrm[st] = sum_rows(dg);
       }
-      if (RG == 1 || rg == 0) {
-        // redundancy: column sums of the in-block cosine matrix, diagonal
-        // excluded; the inverse norms of a lane's output rows (keys 4*grp+i)
-        // come through a per-wave LDS slot
-        if (grp == 0) {
+      if (grp == 0) {
 #pragma unroll
-          for (int st = 0; st < NST; st++) s_nrm[wave][st * 16 + col] = nrm[st];
+        for (int st = 0; st < NST; st++) s_nrm[wave][st * 16 + col] = nrm[st];
+      }
+      __builtin_amdgcn_wave_barrier();
+      float ra[NST][4];
+#pragma unroll
+      for (int s1 = 0; s1 < NST; s1++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const float na = s_nrm[wave][s1 * 16 + 4 * grp + i];
+          ra[s1][i] = na > 0.f ? rsqrtf(na) : 0.f;
         }
-        __builtin_amdgcn_wave_barrier();
-        float ra[NST][4];
+      __builtin_amdgcn_wave_barrier();
+      float Rd[NST];
+#pragma unroll
+      for (int s2 = 0; s2 < NST; s2++) {
+        float cs = 0.f;
+        const float rc = nrm[s2] > 0.f ? rsqrtf(nrm[s2]) : 0.f;
 #pragma unroll
         for (int s1 = 0; s1 < NST; s1++)
 #pragma unroll
           for (int i = 0; i < 4; i++) {
-            const float na = s_nrm[wave][s1 * 16 + 4 * grp + i];
-            ra[s1][i] = na > 0.f ? rsqrtf(na) : 0.f;
+            const bool diag = (s1 == s2) && (4 * grp + i == col);
+            cs += diag ? 0.f : gm[s1][s2][i] * ra[s1][i] * rc;
           }
-        __builtin_amdgcn_wave_barrier();
-        float Rd[NST];
-#pragma unroll
-        for (int s2 = 0; s2 < NST; s2++) {
-          float cs = 0.f;
-          const float rc = nrm[s2] > 0.f ? rsqrtf(nrm[s2]) : 0.f;
-#pragma unroll
-          for (int s1 = 0; s1 < NST; s1++) {
-            f32x4_t gm = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int v = 0; v < NV; v++) gm = Mma<DT>::step(kc[s1][v], kc[s2][v], gm);
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-              const bool diag = (s1 == s2) && (4 * grp + i == col);
-              cs += diag ? 0.f : gm[i] * ra[s1][i] * rc;
-            }
-          }
-          Rd[s2] = sum_rows(cs) * inv_bm1;
-        }
-        if (grp == 0) {
-#pragma unroll
-          for (int st = 0; st < NST; st++) {
-            const int j = n * B + st * 16 + col;
-            if (RG == 1) {
-              const float a = A[st] * inv_rows;
-              const float s = a * (1.0f - Rd[st]);
-              s_sc[j] = s;
-              const size_t o = unit * p.T + j;
-              if (p.dbg_importance) p.dbg_importance[o] = a;
-              if (p.dbg_redundancy) p.dbg_redundancy[o] = Rd[st];
-              if (p.dbg_score && j < p.C) p.dbg_score[o] = s;
-            } else {
-              s_sc[j] = A[st];
-              s_rr[j] = Rd[st];
-            }
-          }
-        }
-      } else if (grp == 0) {
-#pragma unroll
-        for (int st = 0; st < NST; st++) s_aux[n * B + st * 16 + col] = A[st];
+        Rd[s2] = sum_rows(cs) * inv_bm1;
       }
+      if (grp == 0) {
 #pragma unroll
-      for (int st = 0; st < NST; st++)
-#pragma unroll
-        for (int v = 0; v < NV; v++) kc[st][v] = kn[st][v];
+        for (int st = 0; st < NST; st++) {
+          const int j = n * B + st * 16 + col;
+          if (RG == 1) {
+            const float a = A[st] * inv_rows;
+            const float s = a * (1.0f - Rd[st]);
+            s_sc[j] = s;
+            const size_t o = unit * p.T + j;
+            if (p.dbg_importance) p.dbg_importance[o] = a;
+            if (p.dbg_redundancy) p.dbg_redundancy[o] = Rd[st];
+            if (p.dbg_score && j < p.C) p.dbg_score[o] = s;
+          } else {
+            s_rr[j] = Rd[st];
+          }
+        }
+      }
     }
-  }
+  });
   __syncthreads();
   if (RG == 2) {
     for (int j = tid; j < p.T; j += kThreads) {
@@ -497,21 +557,28 @@ __global__ __launch_bounds__(kThreads) void k_score_select(ScoreParams p) {
   }
 }
 
-template <int DT, int D, int B, int RT>
+// More than 64 rows take two row groups, which keep three T-long arrays in
+// LDS (T <= 4096, which also keeps a wave's block count within one id per
+// lane).  At 64 rows or fewer one group is faster: with two, each block is
+// read by two waves and the second read often misses L2.
+bool score_two_groups(int row_tiles, int T) { return row_tiles > 4 && T <= 4096; }
+
+template <int DT, int D, int B, int RT, int RG>
 hipError_t launch_rt(const ScoreParams& p, int units, hipStream_t s) {
   prof_begin(ZP_PHASE_SCORE, s);
-  hipLaunchKernelGGL((k_score_select<DT, D, B, RT>), dim3(units), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL((k_score_select<DT, D, B, RT, RG>), dim3(units), dim3(kThreads), 0, s, p);
   prof_end(ZP_PHASE_SCORE, s);
   return hipGetLastError();
 }
 
 template <int DT, int D, int B>
 hipError_t launch_b(const ScoreParams& p, int row_tiles, int units, hipStream_t s) {
+  const bool two_groups = score_two_groups(row_tiles, p.T);
   switch (row_tiles) {
-    case 1: return launch_rt<DT, D, B, 1>(p, units, s);
-    case 2: return launch_rt<DT, D, B, 2>(p, units, s);
-    case 4: return launch_rt<DT, D, B, 4>(p, units, s);
-    case 8: return launch_rt<DT, D, B, 8>(p, units, s);
+    case 1: return launch_rt<DT, D, B, 1, 1>(p, units, s);
+    case 2: return launch_rt<DT, D, B, 2, 1>(p, units, s);
+    case 4: return launch_rt<DT, D, B, 4, 1>(p, units, s);
+    case 8: return two_groups ? launch_rt<DT, D, B, 8, 2>(p, units, s) : hipErrorInvalidValue;
   }
   return hipErrorInvalidValue;
 }
@@ -544,7 +611,7 @@ int score_row_tiles(int rows) {
 bool score_fits(int rows, int T) {
   const int rt = score_row_tiles(rows);
   if (rt == 0 || T > kMaxScoreSlots) return false;
-  return rt <= 4 || T <= 4096;  // two row groups keep three T-long arrays in LDS
+  return rt <= 4 || score_two_groups(rt, T);
 }
 
 hipError_t launch_score(const ScoreParams& p, int dtype, int head_dim, int block_size, int units,
