@@ -86,6 +86,9 @@ hipError_t launch_compact(const CompactParams& p, int num_layers, int row_bytes,
 hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, int block_size,
                          hipStream_t s);
 hipError_t launch_append(const AppendParams& p, hipStream_t s);
+// Copies bytes (a multiple of 16, 16-byte aligned ends) from device-visible
+// pinned host memory to device memory with a kernel on stream s.
+hipError_t launch_upload(const void* host_src, void* dst, size_t bytes, hipStream_t s);
 
 // Kernel timing (no-ops unless enabled by zp_profile_enable): bracket one
 // phase on stream s.
