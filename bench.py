@@ -36,10 +36,9 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "hot_path_kernels_qwen3_8b_layer_budget2048.txt")
 KERNEL_SOURCES = {
-    "compact": "compressed_paged_kv_amd/csrc/k_compact.hip",
-    "score_stats": "compressed_paged_kv_amd/csrc/k_score.hip",
+    "upload": "compressed_paged_kv_amd/csrc/k_upload.hip",
     "score": "compressed_paged_kv_amd/csrc/k_score.hip",
-    "select": "compressed_paged_kv_amd/csrc/k_select.hip",
+    "compact": "compressed_paged_kv_amd/csrc/k_compact.hip",
     "decode": "compressed_paged_kv_amd/csrc/k_decode.hip",
     "combine": "compressed_paged_kv_amd/csrc/k_decode.hip",
     "append": "compressed_paged_kv_amd/csrc/k_decode.hip",
@@ -127,9 +126,8 @@ def summarize(kt_dir: str, fetch_dir: str, write_dir: str) -> int:
     for r in stats:
         print(f"{r['Name'][:70]:70s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
               f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f}")
-    phases = {"k_score_stats": "score_stats", "k_score_final": "score", "k_select": "select",
-              "k_compact": "compact", "k_append": "append", "k_decode<": "decode",
-              "k_decode_combine": "combine"}
+    phases = {"k_upload": "upload", "k_score_select": "score", "k_compact": "compact",
+              "k_append": "append", "k_decode<": "decode", "k_decode_combine": "combine"}
 
     def per_kernel(d, counter):
         rows = _read_csv(glob.glob(os.path.join(d, "*counter_collection.csv"))[0])
@@ -167,59 +165,61 @@ def summarize(kt_dir: str, fetch_dir: str, write_dir: str) -> int:
     return 0
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--calibrate-copy", action="store_true",
-                    help="first run a 1 GiB device copy (counter calibration under rocprofv3)")
-    ap.add_argument("--summarize", nargs=3, metavar=("KT_DIR", "FETCH_DIR", "WRITE_DIR"),
-                    help="print the summary of rocprofv3 csv outputs and exit")
-    args = ap.parse_args()
-    if args.summarize:
-        return summarize(*args.summarize)
-    if args.calibrate_copy:
-        calibrate_copy()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this path runs without sharding or "
-              f"collectives, so --gpus {args.gpus} is not supported", file=sys.stderr)
-        return 2
+WORKLOADS = ("qwen3_8b_layer_budget2048", "structured_b32_budget4096", "mix_qwen3_8b_36layers",
+             "shared_prefix_32req_32layers")
 
+
+def _kernel_rows(prof: dict, alg: dict, flops: dict) -> list:
+    rows = []
+    for name, (tot_ms, n) in prof.items():
+        if n == 0:
+            continue
+        avg_us = tot_ms * 1e3 / n
+        gbs = alg.get(name, 0) / (avg_us * 1e-6) / 1e9
+        row = {"phase": name, "avg_us": round(avg_us, 2), "launches": n,
+               "alg_bytes": int(alg.get(name, 0)), "alg_GBs": round(gbs, 1),
+               "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+        if name in flops:
+            tf = flops[name] / (avg_us * 1e-6) / 1e12
+            row["mfma_TFLOPs"] = round(tf, 1)
+            row["mfma_frac"] = round(tf / MFMA_BF16_PEAK_TFLOPS, 4)
+        rows.append(row)
+    return rows
+
+
+def _alg_bytes(R_c, R_d, L, H, Hq, d, b, n_max, w, moved_rows, dec_tokens, eb=2, nsplit=0):
+    """Algorithmic bytes (and MFMA flops) per launch of each phase: what the
+    method must move or compute, not the kernels' own traffic."""
+    T, kv_row = n_max * b, d * eb
+    alg = {
+        "upload": 2 * (R_c * n_max * 4 + R_c * (n_max - 1) * 4),
+        # K read once, the window queries, the evicted lists (the kernel reads
+        # K twice -- the softmax needs each row's statistics before any
+        # probability -- which is traffic, not algorithmic bytes)
+        "score": L * (R_c * H * T * kv_row + R_c * w * Hq * kv_row + R_c * H * b * 4),
+        "compact": moved_rows * kv_row * 2 * 2,
+        "append": R_d * H * kv_row * 2 * 2,
+        "decode": dec_tokens * H * kv_row * 2 + R_d * Hq * kv_row,
+        "combine": R_d * Hq * nsplit * (d + 2) * 4 + R_d * Hq * d * 4,
+    }
+    flops = {"score": L * (2 * Hq * w * T * d * R_c + 2 * H * n_max * b * b * d * R_c)}
+    return alg, flops
+
+
+def run_single_stream(args, workload, cache, pool, tables, wq_sets, q_new, k_new, v_new, geom,
+                      n_max, w, cpu_case=None):
+    """One step = host plan + compression of every request's single layer +
+    append of the pending token + paged decode over the compacted cache, all
+    on one stream; the compression is in place, so every step repeats it."""
     import numpy as np
     import torch
-
     import compressed_paged_kv_amd as zp
-    import synth
-    from synth.device import to_tensor
-
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        return 1
     dev = torch.device("cuda:0")
-    log("generating the Qwen3-8B-shaped layer (64 requests, budget 2048)")
-    case = synth.case_qwen3_8b_layer()
-    g = case.geom
-    R, H, Hq, d, b = case.num_reqs, g.num_kv_heads, g.num_q_heads, g.head_dim, g.block_size
-    n_max, w = case.n_max, case.window
+    R = tables.shape[0]
+    H, Hq, d, b = geom.num_kv_heads, geom.num_q_heads, geom.head_dim, geom.block_size
     T, k_keep = n_max * b, (n_max - 1) * b
     seq = k_keep + 1
-    eb = 2
-
-    kp = [to_tensor(case.k_pool[0], dev)]
-    vp = [to_tensor(case.v_pool[0], dev)]
-    cache = zp.KVCache(kp, vp, Hq)
-    rng = np.random.default_rng(1102)
-    # a few window-query sets, rotated per step, so eviction positions vary
-    wq_sets = [[to_tensor(case.window_q[0], dev)]] + [
-        [to_tensor(synth.f32_to_bf16_bits(rng.standard_normal(case.window_q[0].shape)
-                                          .astype(np.float32)), dev)] for _ in range(3)]
-    q_new = to_tensor(case.q_new[0], dev)
-    k_new = to_tensor(case.k_new[0], dev)
-    v_new = to_tensor(case.v_new[0], dev)
-    pool = zp.BlockPool.from_refcounts(case.refcounts)
-    tables = case.tables.copy()
+    tables0 = tables.copy()
     tab_t = torch.from_numpy(tables).to(dev)
     slot_t = torch.from_numpy((tables[:, k_keep // b] * b + k_keep % b).astype(np.int32)).to(dev)
     seq_t = torch.full((R,), seq, dtype=torch.int32, device=dev)
@@ -273,50 +273,25 @@ def main() -> int:
     zp.profile_enable(False)
     ms_per_step_events = (t3 - t2) * 1e3 / args.steps
     moved_after = moved_rows()
-    assert tables.tolist() == case.tables.tolist(), "in-place compression changed the tables"
+    assert tables.tolist() == tables0.tolist(), "in-place compression changed the tables"
     assert np.isfinite(out.cpu().numpy()).all()
 
-    # algorithmic bytes (and flops) per launch, per phase
     moved = 0.5 * (moved_before + moved_after)
-    kv_row = d * eb
-    alg = {
-        "upload": R * n_max * 4 + R * (n_max - 1) * 4,
-        "score_stats": R * H * T * kv_row + R * w * Hq * kv_row,
-        "score": R * H * T * kv_row + R * w * Hq * kv_row + R * H * T * 4,
-        "select": R * H * (T - w) * 4 + R * H * b * 4,
-        "compact": moved * kv_row * 2 * 2,
-        "append": R * H * kv_row * 2 * 2,
-        "decode": R * H * seq * kv_row * 2 + R * Hq * kv_row,
-        "combine": R * Hq * (n_max // 16) * (d + 2) * 4 + R * Hq * d * 4,
-    }
-    flops = {"score_stats": 2 * Hq * w * T * d * R,
-             "score": 2 * Hq * w * T * d * R + 2 * H * n_max * b * b * d * R}
-    kernels = []
-    for name, (tot_ms, n) in prof.items():
-        if n == 0:
-            continue
-        avg_us = tot_ms * 1e3 / n
-        gbs = alg[name] / (avg_us * 1e-6) / 1e9
-        row = {"phase": name, "avg_us": round(avg_us, 2), "launches": n,
-               "alg_bytes": int(alg[name]), "alg_GBs": round(gbs, 1),
-               "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
-        if name in flops:
-            tf = flops[name] / (avg_us * 1e-6) / 1e12
-            row["mfma_TFLOPs"] = round(tf, 1)
-            row["mfma_frac"] = round(tf / MFMA_BF16_PEAK_TFLOPS, 4)
-        kernels.append(row)
+    nsplit = zp.paged_decode_workspace_bytes(cache, R, n_max) // (R * Hq * (d + 2) * 4)
+    alg, flops = _alg_bytes(R, R, 1, H, Hq, d, b, n_max, w, moved, R * seq, nsplit=nsplit)
+    kernels = _kernel_rows(prof, alg, flops)
     gpu_kernels = [k for k in kernels if k["phase"] != "upload"]
     dom = max(gpu_kernels, key=lambda k: k["avg_us"] * k["launches"])
-    traffic = read_counters(dom["phase"])
+    traffic = read_counters(dom["phase"]) if workload == WORKLOADS[0] else None
     roofline = {"bound": "hbm", "kernel": dom["phase"], "achieved": dom["alg_GBs"],
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dom["hbm_frac"],
                 "traffic": traffic}
     per = {k["phase"]: k["avg_us"] for k in kernels}
-    comp_us = sum(per.get(p, 0.0) for p in ("score_stats", "score", "select", "compact"))
+    comp_us = sum(per.get(p, 0.0) for p in ("upload", "score", "compact"))
     dec_us = sum(per.get(p, 0.0) for p in ("append", "decode", "combine"))
-    comp_bytes = sum(alg[p] for p in ("score_stats", "score", "select", "compact"))
+    comp_bytes = sum(alg[p] for p in ("upload", "score", "compact"))
     dec_bytes = sum(alg[p] for p in ("append", "decode", "combine"))
-
+    layers_model = 36 if b == 16 else 32
     result = {
         "metric": METRIC,
         "value": round(R / (ms_per_step * 1e-3), 1),
@@ -331,25 +306,275 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "qwen3_8b_layer_budget2048", "requests": R, "layers": 1,
+        "config": {"workload": workload, "requests": R, "layers": 1,
                    "kv_heads": H, "q_heads": Hq, "head_dim": d, "block_size": b, "n_max": n_max,
-                   "window": w, "pool_blocks": g.num_blocks, "decode_len": seq},
+                   "window": w, "pool_blocks": geom.num_blocks, "decode_len": seq},
         "compress_per_s": round(R / (comp_us * 1e-6), 1),
         "compress_us": round(comp_us, 2),
         "compress_hbm_frac": round(comp_bytes / (comp_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         "decode_tok_s_per_layer": round(R / (dec_us * 1e-6), 1),
-        "decode_tok_s_36_layers": round(R / (36 * dec_us * 1e-6), 1),
+        f"decode_tok_s_{layers_model}_layers": round(R / (layers_model * dec_us * 1e-6), 1),
         "decode_us": round(dec_us, 2),
         "decode_hbm_frac": round(dec_bytes / (dec_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         "moved_rows_per_step": int(moved),
         "kernels": kernels,
         "roofline": roofline,
     }
-    if not args.no_cpu_baseline:
+    if cpu_case is not None and not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        result["cpu_baseline"] = cpu_baseline(case)
+        result["cpu_baseline"] = cpu_baseline(cpu_case)
     else:
         result["cpu_baseline"] = None
+    return result
+
+
+def run_mix(args):
+    """Continuous-batching mix (36 layers, 256 requests): the 10% of requests
+    at the cap compress on one stream while the others append + decode on
+    another; the decode of step t waits for the compression of step t-1 (the
+    compressed requests would join decoding there)."""
+    import numpy as np
+    import torch
+    import compressed_paged_kv_amd as zp
+    from synth.device_gen import case_mix_device
+    dev = torch.device("cuda:0")
+    log("generating the 36-layer mix on the device")
+    case = case_mix_device(dev)
+    g = case.geom
+    L, H, Hq, d, b = g.num_layers, g.num_kv_heads, g.num_q_heads, g.head_dim, g.block_size
+    n_max, w = case.n_max, case.window
+    k_keep = (n_max - 1) * b
+    lens = case.seq_lens
+    comp = np.nonzero(lens == n_max * b)[0]
+    dec = np.nonzero(lens < n_max * b)[0]
+    Rc, Rd = len(comp), len(dec)
+    cache = zp.KVCache(case.k_pool, case.v_pool, Hq)
+    pool = zp.BlockPool.from_refcounts(case.refcounts)
+    tables_c = np.ascontiguousarray(case.tables[comp])
+    comp_t = torch.from_numpy(comp.astype(np.int64)).to(dev)
+    dec_t = torch.from_numpy(dec.astype(np.int64)).to(dev)
+    wq = [q.index_select(0, comp_t).contiguous() for q in case.window_q]
+    qn = [q.index_select(0, dec_t).contiguous() for q in case.q_new]
+    kn = [k.index_select(0, dec_t).contiguous() for k in case.k_new]
+    vn = [v.index_select(0, dec_t).contiguous() for v in case.v_new]
+    tables_d = np.ascontiguousarray(case.tables[dec])
+    ld = lens[dec]
+    tab_d = torch.from_numpy(tables_d).to(dev)
+    slot_d = torch.from_numpy((tables_d[np.arange(Rd), ld // b] * b + ld % b).astype(np.int32)).to(dev)
+    seq_d = torch.from_numpy((ld + 1).astype(np.int32)).to(dev)
+    ws = torch.empty(zp.compress_workspace_bytes(cache, Rc, n_max, w), dtype=torch.uint8, device=dev)
+    dws = torch.empty(max(zp.paged_decode_workspace_bytes(cache, Rd, n_max), 16), dtype=torch.uint8,
+                      device=dev)
+    out = torch.empty((Rd, Hq, d), dtype=torch.float32, device=dev)
+    scale = 1.0 / float(np.sqrt(d))
+    s_c, s_d = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+
+    def compress():
+        zp.compress(cache, pool, n_max, w, tables_c, wq, ws, stream=s_c)
+
+    def decode():
+        for l in range(L):
+            zp.append_kv(cache, l, kn[l], vn[l], slot_d, stream=s_d)
+            zp.paged_decode(cache, l, qn[l], tab_d, seq_d, scale, out, dws, stream=s_d)
+
+    def timed(fn, n):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(n):
+            fn(i)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / n
+
+    ev = [torch.cuda.Event() for _ in range(2)]
+
+    def overlapped(i):
+        # decode(t) waits for compress(t-1), then compress(t) runs beside it
+        if i > 0:
+            s_d.wait_event(ev[(i - 1) % 2])
+        compress()
+        ev[i % 2].record(s_c)
+        decode()
+
+    kept = torch.empty((L, Rc, H, k_keep), dtype=torch.int32, device=dev)
+    zp.compress(cache, pool, n_max, w, tables_c, wq, ws, stream=s_c, debug={"kept": kept})
+    torch.cuda.synchronize()
+    moved = int(np.count_nonzero(kept.cpu().numpy() != np.arange(k_keep)[None, None, None, :]))
+    del kept
+    for i in range(args.warmup):
+        overlapped(i)
+    log(f"timing {args.steps} steps: compression alone, decode alone, overlapped")
+    t_c = timed(lambda i: compress(), args.steps)
+    t_d = timed(lambda i: decode(), args.steps)
+    t_o = timed(overlapped, args.steps)
+    zp.profile_enable(True)
+    zp.profile_read()
+    timed(overlapped, args.steps)
+    prof = zp.profile_read()
+    zp.profile_enable(False)
+    assert np.isfinite(out.cpu().numpy()).all()
+    dec_tokens = int((ld + 1).sum())
+    nsplit = zp.paged_decode_workspace_bytes(cache, Rd, n_max) // (Rd * Hq * (d + 2) * 4)
+    alg, flops = _alg_bytes(Rc, Rd, L, H, Hq, d, b, n_max, w, moved, dec_tokens, nsplit=nsplit)
+    kernels = _kernel_rows(prof, alg, flops)
+    eff = (t_c + t_d - t_o) / min(t_c, t_d)
+    return {
+        "metric": METRIC, "value": round(Rc * L / (t_o * 1e-3), 1), "unit": "compressions/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(t_o, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "mix_qwen3_8b_36layers", "requests": int(len(lens)),
+                   "compressing_requests": Rc, "decoding_requests": Rd, "layers": L, "kv_heads": H,
+                   "q_heads": Hq, "head_dim": d, "block_size": b, "n_max": n_max, "window": w,
+                   "pool_blocks": g.num_blocks, "decode_tokens_per_layer": dec_tokens},
+        "compress_ms": round(t_c, 4), "decode_ms": round(t_d, 4), "overlapped_ms": round(t_o, 4),
+        "serial_ms": round(t_c + t_d, 4), "overlap_efficiency": round(eff, 4),
+        "compress_per_s": round(Rc * L / (t_c * 1e-3), 1),
+        "decode_tok_s": round(Rd / (t_d * 1e-3), 1),
+        "step_decode_tok_s": round(Rd / (t_o * 1e-3), 1),
+        "moved_rows_per_step": moved,
+        "kernels_overlapped": kernels,
+    }
+
+
+def run_shared_prefix(args):
+    """32 requests x 32 layers sharing a 32-block prefix: every compression
+    re-targets the shared positions into new blocks (1024 allocations) and
+    frees the prefix once the last reference drops.  Each step starts from
+    the original tables and refcounts (a fresh pool object, host side), so
+    the same targets are planned every time; compression time is the GPU
+    time between events around the call (the host plan included)."""
+    import numpy as np
+    import torch
+    import compressed_paged_kv_amd as zp
+    from synth.device_gen import case_shared_prefix_device
+    dev = torch.device("cuda:0")
+    log("generating the shared-prefix workload on the device")
+    case = case_shared_prefix_device(dev)
+    g = case.geom
+    L, H, Hq, d, b = g.num_layers, g.num_kv_heads, g.num_q_heads, g.head_dim, g.block_size
+    n_max, w = case.n_max, case.window
+    R = case.num_reqs
+    k_keep = (n_max - 1) * b
+    cache = zp.KVCache(case.k_pool, case.v_pool, Hq)
+    ws = torch.empty(zp.compress_workspace_bytes(cache, R, n_max, w), dtype=torch.uint8, device=dev)
+    dws = torch.empty(max(zp.paged_decode_workspace_bytes(cache, R, n_max), 16), dtype=torch.uint8,
+                      device=dev)
+    out = torch.empty((R, Hq, d), dtype=torch.float32, device=dev)
+    scale = 1.0 / float(np.sqrt(d))
+    seq_t = torch.full((R,), k_keep + 1, dtype=torch.int32, device=dev)
+    e0, e1, e2 = torch.cuda.Event(True), torch.cuda.Event(True), torch.cuda.Event(True)
+    comp_ms, dec_ms, freed_counts = [], [], []
+    for i in range(args.warmup + args.steps):
+        pool = zp.BlockPool.from_refcounts(case.refcounts)
+        tables = case.tables.copy()
+        torch.cuda.synchronize()
+        e0.record()
+        freed = zp.compress(cache, pool, n_max, w, tables, case.window_q, ws)
+        e1.record()
+        tab_t = torch.from_numpy(tables).to(dev, non_blocking=False)
+        slot_t = torch.from_numpy((tables[:, k_keep // b] * b + k_keep % b).astype(np.int32)).to(dev)
+        torch.cuda.synchronize()
+        e1b = torch.cuda.Event(True)
+        e1b.record()
+        for l in range(L):
+            zp.append_kv(cache, l, case.k_new[l], case.v_new[l], slot_t)
+            zp.paged_decode(cache, l, case.q_new[l], tab_t, seq_t, scale, out, dws)
+        e2.record()
+        torch.cuda.synchronize()
+        if i >= args.warmup:
+            comp_ms.append(e0.elapsed_time(e1))
+            dec_ms.append(e1b.elapsed_time(e2))
+            freed_counts.append(len(freed))
+        pool.sync()
+        assert pool.refcounts()[case.tables[0, :32]].tolist() == [0] * 32
+        pool.close()
+    t_c = float(np.median(comp_ms))
+    t_d = float(np.median(dec_ms))
+    assert np.isfinite(out.cpu().numpy()).all()
+    return {
+        "metric": METRIC, "value": round(R * L / (t_c * 1e-3), 1), "unit": "compressions/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(t_c + t_d, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "shared_prefix_32req_32layers", "requests": R, "layers": L,
+                   "shared_prefix_blocks": 32, "kv_heads": H, "q_heads": Hq, "head_dim": d,
+                   "block_size": b, "n_max": n_max, "window": w, "pool_blocks": g.num_blocks},
+        "compress_ms": round(t_c, 4), "decode_ms_all_layers": round(t_d, 4),
+        "compress_per_s": round(R * L / (t_c * 1e-3), 1),
+        "decode_tok_s": round(R / (t_d * 1e-3), 1),
+        "freed_per_step": int(np.median(freed_counts)),
+        "new_targets_per_step": R * 32,
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", choices=WORKLOADS, default=WORKLOADS[0],
+                    help="the Qwen3-8B layer at budget 2048 (default, the headline line) or one of "
+                         "the wider workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a 1 GiB device copy (counter calibration under rocprofv3)")
+    ap.add_argument("--summarize", nargs=3, metavar=("KT_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="print the summary of rocprofv3 csv outputs and exit")
+    args = ap.parse_args()
+    if args.summarize:
+        return summarize(*args.summarize)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this path runs without sharding or "
+              f"collectives, so --gpus {args.gpus} is not supported", file=sys.stderr)
+        return 2
+    if args.calibrate_copy:
+        calibrate_copy()
+
+    import numpy as np
+    import torch
+
+    import compressed_paged_kv_amd as zp
+    import synth
+    from synth.device import to_tensor
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    if args.workload == "mix_qwen3_8b_36layers":
+        result = run_mix(args)
+    elif args.workload == "shared_prefix_32req_32layers":
+        result = run_shared_prefix(args)
+    elif args.workload == "structured_b32_budget4096":
+        from synth.device_gen import case_structured_device
+        log("generating the structured b=32 workload on the device (512 requests, budget 4096)")
+        case = case_structured_device(dev)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(1105)
+        wq_sets = [[case.window_q[0]]] + [
+            [torch.randn(case.window_q[0].shape, generator=gen, device=dev).to(torch.bfloat16)]
+            for _ in range(3)]
+        cache = zp.KVCache(case.k_pool, case.v_pool, case.geom.num_q_heads)
+        pool = zp.BlockPool.from_refcounts(case.refcounts)
+        result = run_single_stream(args, args.workload, cache, pool, case.tables.copy(), wq_sets,
+                                   case.q_new[0], case.k_new[0], case.v_new[0], case.geom,
+                                   case.n_max, case.window)
+    else:
+        log("generating the Qwen3-8B-shaped layer (64 requests, budget 2048)")
+        case = synth.case_qwen3_8b_layer()
+        rng = np.random.default_rng(1102)
+        # a few window-query sets, rotated per step, so eviction positions vary
+        wq_sets = [[to_tensor(case.window_q[0], dev)]] + [
+            [to_tensor(synth.f32_to_bf16_bits(rng.standard_normal(case.window_q[0].shape)
+                                              .astype(np.float32)), dev)] for _ in range(3)]
+        cache = zp.KVCache([to_tensor(case.k_pool[0], dev)], [to_tensor(case.v_pool[0], dev)],
+                           case.geom.num_q_heads)
+        pool = zp.BlockPool.from_refcounts(case.refcounts)
+        result = run_single_stream(args, args.workload, cache, pool, case.tables.copy(), wq_sets,
+                                   to_tensor(case.q_new[0], dev), to_tensor(case.k_new[0], dev),
+                                   to_tensor(case.v_new[0], dev), case.geom, case.n_max,
+                                   case.window, cpu_case=case)
     print(json.dumps(result), flush=True)
     return 0
 
