@@ -195,10 +195,21 @@ __global__ __launch_bounds__(kThreads, (score_min_blocks<DT, D, RT / RG, B>())) 
   constexpr int WPG = kWaves / RG;      // waves per row group
   constexpr int RPW = RTW * 16;         // rows per wave
   constexpr int ROWB = D * EB;          // bytes per key row
-  // K ring slots: as many block tiles as fit the register budget, 2 to 4
-  constexpr int kPrefetch = ZP_SCORE_RING_VGPRS / (NST * NV * 4) < 2   ? 2
-                            : ZP_SCORE_RING_VGPRS / (NST * NV * 4) > 4 ? 4
-                                                                       : ZP_SCORE_RING_VGPRS / (NST * NV * 4);
+  constexpr int F = NST * NV;           // 16-byte fragments per lane per block
+  // Shared tiles: with two row groups, the two waves of a pair (same blocks,
+  // different rows) each load half of a block's fragments and swap the other
+  // half through LDS, so every K byte is read from memory once per pass.
+  // (Not for 16 fragments a lane, whose exchange buffers would not fit.)
+  constexpr bool SH = RG == 2 && F <= 8;
+  constexpr int FL = SH ? F / 2 : F;    // fragments a wave loads per block
+  // K ring slots: as many block loads as fit the register budget, 2 to 4
+  constexpr int kPrefetch = ZP_SCORE_RING_VGPRS / (FL * 4) < 2   ? 2
+                            : ZP_SCORE_RING_VGPRS / (FL * 4) > 4 ? 4
+                                                                 : ZP_SCORE_RING_VGPRS / (FL * 4);
+  // Gram split: with shared tiles and two sub-tiles, each wave of a pair
+  // takes the diagonal tiles (norms) and the off-diagonal tile of its own
+  // column sub-tile; otherwise the pair alternates whole blocks.
+  constexpr bool GSPLIT = SH && NST == 2;
 
   const size_t unit = blockIdx.x;
   const int h = (int)(unit % p.H);
@@ -218,6 +229,7 @@ __global__ __launch_bounds__(kThreads, (score_min_blocks<DT, D, RT / RG, B>())) 
   __shared__ int s_hist[256];
   __shared__ int s_scr[kWaves + 1];
   __shared__ int s_sel[2];
+  __shared__ uint4 s_x[SH ? 2 : 1][SH ? WPG : 1][SH ? F : 1][64];  // [parity][pair][fragment][lane]
   float* s_sc = s_buf;          // scores (with two row groups: group 0's partial importance)
   float* s_aux = s_buf + 4096;  // group 1's partial importance (two row groups only)
   float* s_rr = s_buf + 8192;   // redundancy (two row groups only)
@@ -249,24 +261,31 @@ __global__ __launch_bounds__(kThreads, (score_min_blocks<DT, D, RT / RG, B>())) 
   const int ids = lane < nbw ? p.src[(size_t)r * p.n_max + wl + WPG * lane] : 0;
   const int row_off = col * ROWB + grp * 16;
   // K fragments of the wave's k-th block (k is clamped, so the loads stay
-  // unconditional and the compiler can wait for each ring slot on its own)
-  auto fetch = [&](int k, uint4 (&kd)[NST][NV]) {
+  // unconditional and the compiler can wait for each ring slot on its own).
+  // Fragment f is sub-tile f / NV, 16-byte slice f % NV; with shared tiles a
+  // wave loads fragments [rg*FL, rg*FL + FL).
+  auto fetch = [&](int k, uint4 (&kd)[FL]) {
     const int pblk = __builtin_amdgcn_readlane(ids, max(min(k, nbw - 1), 0));
     const char* tile = kbase + ((size_t)pblk * p.H + h) * B * ROWB + row_off;
 #pragma unroll
-    for (int st = 0; st < NST; st++)
-#pragma unroll
-      for (int v = 0; v < NV; v++) kd[st][v] = ld16(tile + st * 16 * ROWB + v * 64);
+    for (int q = 0; q < FL; q++) {
+      const int f = (SH ? rg * FL : 0) + q;
+      kd[q] = ld16(tile + (f / NV) * 16 * ROWB + (f % NV) * 64);
+    }
   };
   // Runs body(k, fragments) over the wave's blocks through a ring of PD
   // register buffers: slot s is refilled right after it is consumed, so
   // PD - 1 blocks stay in flight.  Pass 2 walks the blocks in reverse, so it
   // starts on those pass 1 read last (still in L2 / the memory-side cache).
+  // With shared tiles every wave runs the same number of iterations (the
+  // largest block count of any wave), each with one workgroup barrier
+  // between the LDS writes of the own half and the reads of the partner's.
   auto ring = [&](auto reverse, auto body) {
     constexpr bool REV = decltype(reverse)::value;
     auto kof = [&](int it) { return REV ? nbw - 1 - it : it; };
-    if (nbw == 0) return;
-    uint4 kb[kPrefetch][NST][NV];
+    const int iters = SH ? (p.n_max + WPG - 1) / WPG : nbw;
+    if (iters == 0) return;
+    uint4 kb[kPrefetch][FL];
     // the prologue keeps slot order (the scheduler may not interleave the
     // fetches), so the wait before slot s counts the same loads on entry as
     // in the steady state
@@ -275,11 +294,39 @@ __global__ __launch_bounds__(kThreads, (score_min_blocks<DT, D, RT / RG, B>())) 
       fetch(kof(s), kb[s]);
       __builtin_amdgcn_sched_barrier(0);
     }
-    for (int it0 = 0; it0 < nbw; it0 += kPrefetch) {
+    for (int it0 = 0; it0 < iters; it0 += kPrefetch) {
 #pragma unroll
       for (int s = 0; s < kPrefetch; s++) {
         const int it = it0 + s;
-        if (it < nbw) body(kof(it), kb[s]);
+        if constexpr (SH) {
+          if (it < iters) {
+            const bool live = it < nbw;
+            uint4* xb = &s_x[it & 1][wl][0][0];
+            if (live) {
+#pragma unroll
+              for (int q = 0; q < FL; q++) xb[(rg * FL + q) * 64 + lane] = kb[s][q];
+            }
+            __syncthreads();
+            if (live) {
+              uint4 kt[NST][NV];
+#pragma unroll
+              for (int f = 0; f < F; f++) {
+                if (f / FL == rg)
+                  kt[f / NV][f % NV] = kb[s][f % FL];
+                else
+                  kt[f / NV][f % NV] = xb[f * 64 + lane];
+              }
+              body(kof(it), kt);
+            }
+          }
+        } else {
+          if (it < nbw) {
+            uint4 kt[NST][NV];
+#pragma unroll
+            for (int f = 0; f < F; f++) kt[f / NV][f % NV] = kb[s][f];
+            body(kof(it), kt);
+          }
+        }
         fetch(kof(it + kPrefetch), kb[s]);
       }
     }
@@ -401,20 +448,24 @@ __global__ __launch_bounds__(kThreads, (score_min_blocks<DT, D, RT / RG, B>())) 
 #pragma unroll
       for (int st = 0; st < NST; st++) dst[n * B + st * 16 + col] = A[st];
     }
-    // the two row groups see the same blocks: they take turns on the Gram work
-    if (RG == 1 || (k & 1) == rg) {
+    // the two row groups see the same blocks: they share or take turns on
+    // the Gram work
+    if (GSPLIT || RG == 1 || (k & 1) == rg) {
       // redundancy: column sums of the in-block cosine matrix, diagonal
       // excluded.  gm[s1][s2] holds the dot products of keys 16*s1 + 4*grp + i
       // (rows) with keys 16*s2 + col; the diagonal tiles give the squared
       // norms, and the inverse norms of a lane's rows come through LDS.
+      auto mine = [&](int s2) { return !GSPLIT || s2 == rg; };  // column sub-tiles this wave sums
       f32x4_t gm[NST][NST];
 #pragma unroll
       for (int s1 = 0; s1 < NST; s1++)
 #pragma unroll
         for (int s2 = 0; s2 < NST; s2++) {
           gm[s1][s2] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          if (s1 == s2 || mine(s2)) {
 #pragma unroll
-          for (int v = 0; v < NV; v++) gm[s1][s2] = Mma<DT>::step(kt[s1][v], kt[s2][v], gm[s1][s2]);
+            for (int v = 0; v < NV; v++) gm[s1][s2] = Mma<DT>::step(kt[s1][v], kt[s2][v], gm[s1][s2]);
+          }
         }
       float nrm[NST];
 #pragma unroll
@@ -465,7 +516,7 @@ __global__ __launch_bounds__(kThreads, (score_min_blocks<DT, D, RT / RG, B>())) 
             if (p.dbg_importance) p.dbg_importance[o] = a;
             if (p.dbg_redundancy) p.dbg_redundancy[o] = Rd[st];
             if (p.dbg_score && j < p.C) p.dbg_score[o] = s;
-          } else {
+          } else if (mine(st)) {
             s_rr[j] = Rd[st];
           }
         }
