@@ -17,7 +17,9 @@
 // the tile (or an earlier one) still has to read, and later tiles only read
 // slots >= their first row -- which is also why the next tile's loads may be
 // issued before this tile's stores.  Rows whose source and target are the
-// same physical row (unmoved prefix of an in-place block) are not written.
+// same physical row (unmoved prefix of an in-place block) are not written,
+// and the walk starts at the first row that moves: before the first evicted
+// slot and the first re-targeted block nothing changes.
 //
 // Grid: x = (head, K|V), y = (layer, request).  256 threads; each row of
 // d * elem_bytes bytes is VPR 16-byte vectors, one per thread, U rows per
@@ -29,7 +31,10 @@ namespace zp {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 8;
+#ifndef ZP_COMPACT_UNROLL
+#define ZP_COMPACT_UNROLL 6  // rows per thread per tile
+#endif
+constexpr int kUnroll = ZP_COMPACT_UNROLL;
 constexpr int kMaxEvicted = 1024;  // E = block_size * (blocks beyond N_max - 1)
 constexpr int kMaxSlots = 8192;    // T = n_max * block_size (the host checks the same)
 constexpr int kMaxBlocks = 512;    // n_max bound for the LDS block tables (T <= 8192, b >= 16)
@@ -37,8 +42,8 @@ constexpr int kMaxBlocks = 512;    // n_max bound for the LDS block tables (T <=
 #define ZP_COMPACT_STREAM 2  // 1: non-temporal stores, 2: non-temporal loads and stores
 #endif
 
-template <int VPR>
-__global__ __launch_bounds__(kThreads) void k_compact(CompactParams p) {
+template <int VPR, int B>
+__global__ __launch_bounds__(kThreads, 4) void k_compact(CompactParams p) {
   constexpr int kRowsPerPass = kThreads / VPR;
   constexpr int kRowsPerTile = kRowsPerPass * kUnroll;
   const int h = blockIdx.x >> 1, kv = blockIdx.x & 1;
@@ -47,18 +52,25 @@ __global__ __launch_bounds__(kThreads) void k_compact(CompactParams p) {
   const int tid = threadIdx.x;
   const int vec = tid % VPR, rsub = tid / VPR;
   const size_t unit = (size_t)lr * p.H + h;
-  const int b = p.K_keep / (p.n_max - 1);
-  const size_t row_bytes = (size_t)VPR * 16;
+  constexpr int b = B;
+  constexpr size_t row_bytes = (size_t)VPR * 16;
 
   __shared__ int f[kMaxEvicted];
   __shared__ int srcb[kMaxBlocks];
   __shared__ int dstb[kMaxBlocks];
   __shared__ unsigned short kept[kMaxSlots];
+  __shared__ int s_first;
   const int32_t* ev = p.evicted + unit * p.E;
   for (int i = tid; i < p.E; i += kThreads) f[i] = ev[i] - i;
   for (int n = tid; n < p.n_max; n += kThreads) srcb[n] = p.src[(size_t)r * p.n_max + n];
   for (int n = tid; n < p.n_max - 1; n += kThreads) dstb[n] = p.dst[(size_t)r * (p.n_max - 1) + n];
+  if (tid == 0) s_first = p.E > 0 ? ev[0] : p.K_keep;  // rows below the first eviction stay put
   __syncthreads();
+  // ... unless their block is re-targeted (a new block for a shared source)
+  for (int n = tid; n < p.n_max - 1; n += kThreads)
+    if (dstb[n] != srcb[n]) atomicMin(&s_first, n * b);
+  __syncthreads();
+  const int first = min(s_first, p.K_keep);
   // survivor list, once per workgroup: kept[r] = r + #{i : f_i <= r}
   for (int row = tid; row < p.K_keep; row += kThreads) {
     int lo = 0, hi = p.E;
@@ -70,31 +82,31 @@ __global__ __launch_bounds__(kThreads) void k_compact(CompactParams p) {
   }
   __syncthreads();
 
-  char* base = static_cast<char*>(p.layer_ptrs[l * kPtrsPerLayer + kv]);
-  const size_t head_stride = (size_t)b * row_bytes;          // one (block, head) tile
-  const size_t block_stride = (size_t)p.H * head_stride;    // one physical block
-  auto row_addr = [&](int blk, int off) -> char* {
-    return base + (size_t)blk * block_stride + h * head_stride + (size_t)off * row_bytes + vec * 16;
-  };
+  // a row of the pool as one index (block, head, offset), below 2^31 for
+  // any pool the host accepts; the byte address is formed at the access
+  char* const base = static_cast<char*>(p.layer_ptrs[l * kPtrsPerLayer + kv]) + vec * 16;
+  auto row_of = [&](int blk, int off) -> int { return (blk * p.H + h) * b + off; };
+  auto addr = [&](int row) -> char* { return base + (size_t)(unsigned)row * row_bytes; };
   // Rows past the end are clamped to the last row; an unmoved row is read
-  // but not written.  Loads stay unconditional, so the compiler can keep
-  // the next tile's loads in flight while this tile is stored.
-  auto load_tile = [&](int t0, uint4 (&buf)[kUnroll], char* (&to)[kUnroll]) {
+  // but not written (target -1).  Loads stay unconditional, so the compiler
+  // can keep the next tile's loads in flight while this tile is stored.
+  auto load_tile = [&](int t0, uint4 (&buf)[kUnroll], int (&to)[kUnroll]) {
 #pragma unroll
     for (int u = 0; u < kUnroll; u++) {
       const int row = min(t0 + rsub + u * kRowsPerPass, p.K_keep - 1);
       const int j = kept[row];
-      const char* from = row_addr(srcb[j / b], j % b);
-      char* dst = row_addr(dstb[row / b], row % b);
-      buf[u] = ZP_COMPACT_STREAM >= 2 ? ldg16_stream(from) : ldg16(from);
-      to[u] = (dst != from && t0 + rsub + u * kRowsPerPass < p.K_keep) ? dst : nullptr;
+      const int from = row_of(srcb[j / b], j % b);
+      const int dst = row_of(dstb[row / b], row % b);
+      buf[u] = ZP_COMPACT_STREAM >= 2 ? ldg16_stream(addr(from)) : ldg16(addr(from));
+      to[u] = (dst != from && t0 + rsub + u * kRowsPerPass < p.K_keep) ? dst : -1;
     }
   };
+  if (first >= p.K_keep) return;  // nothing moves (uniform across the workgroup)
   uint4 cur[kUnroll], nxt[kUnroll];
-  char* cur_to[kUnroll];
-  char* nxt_to[kUnroll];
-  load_tile(0, cur, cur_to);
-  for (int t0 = 0; t0 < p.K_keep; t0 += kRowsPerTile) {
+  int cur_to[kUnroll];
+  int nxt_to[kUnroll];
+  load_tile(first, cur, cur_to);
+  for (int t0 = first; t0 < p.K_keep; t0 += kRowsPerTile) {
     load_tile(min(t0 + kRowsPerTile, p.K_keep - 1), nxt, nxt_to);
     // Every load of this tile must have returned its data before any thread
     // of the tile stores: the empty asm consumes the loaded registers, so the
@@ -105,8 +117,8 @@ __global__ __launch_bounds__(kThreads) void k_compact(CompactParams p) {
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < kUnroll; u++)
-      if (cur_to[u]) {
-        if (ZP_COMPACT_STREAM >= 1) stg16_stream(cur_to[u], cur[u]); else stg16(cur_to[u], cur[u]);
+      if (cur_to[u] >= 0) {
+        if (ZP_COMPACT_STREAM >= 1) stg16_stream(addr(cur_to[u]), cur[u]); else stg16(addr(cur_to[u]), cur[u]);
       }
 #pragma unroll
     for (int u = 0; u < kUnroll; u++) {
@@ -118,19 +130,28 @@ __global__ __launch_bounds__(kThreads) void k_compact(CompactParams p) {
 
 }  // namespace
 
+template <int VPR>
+void launch_vpr(const CompactParams& p, dim3 grid, int block_size, hipStream_t s) {
+  if (block_size == 16)
+    hipLaunchKernelGGL((k_compact<VPR, 16>), grid, dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL((k_compact<VPR, 32>), grid, dim3(kThreads), 0, s, p);
+}
+
 hipError_t launch_compact(const CompactParams& p, int num_layers, int row_bytes, int block_size,
                           hipStream_t s) {
-  (void)block_size;
   if (p.R <= 0) return hipSuccess;
   if (p.E > kMaxEvicted || p.n_max > kMaxBlocks || p.K_keep > kMaxSlots) return hipErrorInvalidValue;
-  dim3 grid(2 * p.H, num_layers * p.R), block(kThreads);
+  if (block_size != 16 && block_size != 32) return hipErrorInvalidValue;
+  if (p.K_keep != (p.n_max - 1) * block_size) return hipErrorInvalidValue;
+  dim3 grid(2 * p.H, num_layers * p.R);
   const int vpr = row_bytes / 16;
   if (vpr != 8 && vpr != 16 && vpr != 32) return hipErrorInvalidValue;
   prof_begin(ZP_PHASE_COMPACT, s);
   switch (vpr) {
-    case 8: hipLaunchKernelGGL(k_compact<8>, grid, block, 0, s, p); break;
-    case 16: hipLaunchKernelGGL(k_compact<16>, grid, block, 0, s, p); break;
-    case 32: hipLaunchKernelGGL(k_compact<32>, grid, block, 0, s, p); break;
+    case 8: launch_vpr<8>(p, grid, block_size, s); break;
+    case 16: launch_vpr<16>(p, grid, block_size, s); break;
+    case 32: launch_vpr<32>(p, grid, block_size, s); break;
   }
   prof_end(ZP_PHASE_COMPACT, s);
   return hipGetLastError();
