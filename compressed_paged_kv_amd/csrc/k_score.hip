@@ -1,6 +1,7 @@
 // Scoring and survivor selection of the compression pass (gfx950).
 //
-// One workgroup (8 waves) per (layer, request, KV head) "unit".  The
+// One workgroup (four waves, or eight with two row groups) per (layer,
+// request, KV head) "unit".  The
 // observation window supplies rows = G*w query rows (the G query heads of
 // the group times the w window positions; ko page section 2.A).  Every
 // cached slot j gets
@@ -40,8 +41,12 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
+// Waves per workgroup: four with one row group (two workgroups share a CU,
+// so one selects while the other streams K); eight with two row groups,
+// whose paired waves exchange K tiles through LDS.
+template <int RG>
+constexpr int score_waves() { return RG == 2 ? 8 : 4; }
+constexpr int kMaxWaves = 8;
 constexpr float kInitMax = -1.0e30f;  // finite "minus infinity": merges never form inf - inf
 // A running sum is rescaled only when a term would exceed 2^kLazy: terms stay
 // below 2^64 and a sum of at most 8192 of them below 2^77, far from the float
@@ -50,7 +55,9 @@ constexpr float kInitMax = -1.0e30f;  // finite "minus infinity": merges never f
 constexpr float kLazy = 64.0f;
 constexpr float kLazyTerm = 18446744073709551616.0f;  // 2^kLazy
 constexpr float kMasked = -3.0e38f;   // logit of a causally masked slot: adds 2^(-huge) = 0
-constexpr int kLdsFloats = 3 * 4096;  // scores (T <= 8192), or three T <= 4096 arrays
+// scores (T <= 8192) with one row group; three T <= 4096 arrays with two
+template <int RG>
+constexpr int lds_floats() { return RG == 2 ? 3 * 4096 : 8192; }
 #ifndef ZP_SCORE_RING_VGPRS
 #define ZP_SCORE_RING_VGPRS 32
 #endif
@@ -151,7 +158,7 @@ __device__ inline uint32_t order_key(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Inclusive workgroup-wide sum; `scratch` holds >= kWaves ints.  Ends with
+// Inclusive workgroup-wide sum; `scratch` holds >= NW ints.  Ends with
 // a barrier so scratch may be reused.
 __device__ inline int block_incl_sum(int v, int* scratch) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -168,16 +175,17 @@ __device__ inline int block_incl_sum(int v, int* scratch) {
   return v + before;
 }
 
+template <int NW>
 __device__ inline int block_broadcast_last(int v, int* scratch) {
-  if (threadIdx.x == kThreads - 1) scratch[kWaves] = v;
+  if (threadIdx.x == 64 * NW - 1) scratch[NW] = v;
   __syncthreads();
-  const int t = scratch[kWaves];
+  const int t = scratch[NW];
   __syncthreads();
   return t;
 }
 
-// Two workgroups fit a CU when a wave's Q fragments and K ring stay small
-// (at most 128 registers a lane); otherwise one.
+// Sixteen waves fit a CU when a wave's Q fragments and K ring stay small
+// (at most 128 registers a lane); otherwise eight.
 template <int DT, int D, int RTW, int B>
 constexpr int score_min_blocks() {
   return (RTW * D * Mma<DT>::kElemBytes / 64 <= 8 && (B / 16) * D * Mma<DT>::kElemBytes / 64 <= 4) ? 2 : 1;
@@ -187,7 +195,9 @@ constexpr int score_min_blocks() {
 // waves 4-7 the second, both over all blocks, which halves the Q fragments a
 // wave holds.
 template <int DT, int D, int B, int RT, int RG>
-__global__ __launch_bounds__(kThreads, (score_min_blocks<DT, D, RT / RG, B>())) void k_score_select(ScoreParams p) {
+__global__ __launch_bounds__(64 * score_waves<RG>(), (kMaxWaves / score_waves<RG>()) * (score_min_blocks<DT, D, RT / RG, B>())) void k_score_select(ScoreParams p) {
+  constexpr int kWaves = score_waves<RG>();
+  constexpr int kThreads = 64 * kWaves;
   constexpr int EB = Mma<DT>::kElemBytes;
   constexpr int NV = D * EB / 64;       // 16-byte fragments per lane per 16-token tile
   constexpr int NST = B / 16;           // 16-token sub-tiles per block
@@ -222,7 +232,7 @@ __global__ __launch_bounds__(kThreads, (score_min_blocks<DT, D, RT / RG, B>())) 
   const char* kbase = static_cast<const char*>(p.layer_ptrs[l * kPtrsPerLayer + 0]);
   const char* qbase = static_cast<const char*>(p.layer_ptrs[l * kPtrsPerLayer + 2]);
 
-  __shared__ float s_buf[kLdsFloats];
+  __shared__ float s_buf[lds_floats<RG>()];
   __shared__ float s_wst[kWaves][RPW][2];
   __shared__ float s_off[RT * 16];
   __shared__ float s_nrm[kWaves][B];
@@ -258,14 +268,18 @@ __global__ __launch_bounds__(kThreads, (score_min_blocks<DT, D, RT / RG, B>())) 
 
   // this wave's blocks are wl + WPG*k; lane k holds the physical id of the k-th
   const int nbw = p.n_max > wl ? (p.n_max - wl + WPG - 1) / WPG : 0;
-  const int ids = lane < nbw ? p.src[(size_t)r * p.n_max + wl + WPG * lane] : 0;
+  // (a wave has at most 128 blocks: n_max <= 512 at four waves per row group)
+  const int32_t* tab = p.src + (size_t)r * p.n_max + wl;
+  const int ids0 = lane < nbw ? tab[WPG * lane] : 0;
+  const int ids1 = lane + 64 < nbw ? tab[WPG * (lane + 64)] : 0;
   const int row_off = col * ROWB + grp * 16;
   // K fragments of the wave's k-th block (k is clamped, so the loads stay
   // unconditional and the compiler can wait for each ring slot on its own).
   // Fragment f is sub-tile f / NV, 16-byte slice f % NV; with shared tiles a
   // wave loads fragments [rg*FL, rg*FL + FL).
   auto fetch = [&](int k, uint4 (&kd)[FL]) {
-    const int pblk = __builtin_amdgcn_readlane(ids, max(min(k, nbw - 1), 0));
+    const int kc = max(min(k, nbw - 1), 0);
+    const int pblk = kc < 64 ? __builtin_amdgcn_readlane(ids0, kc) : __builtin_amdgcn_readlane(ids1, kc - 64);
     const char* tile = kbase + ((size_t)pblk * p.H + h) * B * ROWB + row_off;
 #pragma unroll
     for (int q = 0; q < FL; q++) {
@@ -568,7 +582,7 @@ __global__ __launch_bounds__(kThreads, (score_min_blocks<DT, D, RT / RG, B>())) 
   int my_ties = 0;
   for (int j = j0; j < j1; j++) my_ties += order_key(s_sc[j]) == tau ? 1 : 0;
   const int ties_incl = block_incl_sum(my_ties, s_scr);
-  const int ties_total = block_broadcast_last(ties_incl, s_scr);
+  const int ties_total = block_broadcast_last<kWaves>(ties_incl, s_scr);
   // evicted: keys below tau, and the evict_ties highest slots equal to tau
   int tie_rank = ties_incl - my_ties;
   int my_ev = 0;
@@ -617,7 +631,7 @@ bool score_two_groups(int row_tiles, int T) { return row_tiles > 4 && T <= 4096;
 template <int DT, int D, int B, int RT, int RG>
 hipError_t launch_rt(const ScoreParams& p, int units, hipStream_t s) {
   prof_begin(ZP_PHASE_SCORE, s);
-  hipLaunchKernelGGL((k_score_select<DT, D, B, RT, RG>), dim3(units), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL((k_score_select<DT, D, B, RT, RG>), dim3(units), dim3(64 * score_waves<RG>()), 0, s, p);
   prof_end(ZP_PHASE_SCORE, s);
   return hipGetLastError();
 }

@@ -60,6 +60,12 @@ CASES = {
     "ar1_planted_b32": lambda: _case("r8", 208, block_size=32, window=32, n_max=24,
                                      num_q_heads=8, num_blocks=64, key_kind="ar1",
                                      planted_frac=0.01),
+    # long caches: more than 64 blocks per wave in the scoring kernel, one row
+    # group (G*w = 64, 300 blocks) and two row groups (G*w = 128, 200 blocks)
+    "bf16_long_300_blocks": lambda: _case("r9", 212, num_reqs=1, num_kv_heads=1, num_q_heads=4,
+                                          n_max=300, num_blocks=310),
+    "bf16_long_200_blocks_rows128": lambda: _case("r10", 213, num_reqs=1, num_kv_heads=1,
+                                                  num_q_heads=8, n_max=200, num_blocks=210),
 }
 
 
