@@ -79,6 +79,10 @@ def lib() -> ctypes.CDLL:
         "zp_compress": (S, [ctypes.POINTER(_KVCache), _vp, ctypes.c_int32, ctypes.c_int32,
                             ctypes.c_int32, _i32p, ctypes.POINTER(_vp), _vp, ctypes.c_size_t,
                             _i32p, _i32p, _vp, ctypes.POINTER(_Debug)]),
+        "zp_compress_lse": (S, [ctypes.POINTER(_KVCache), _vp, ctypes.c_int32, ctypes.c_int32,
+                                ctypes.c_int32, _i32p, ctypes.POINTER(_vp), ctypes.POINTER(_vp),
+                                _vp, ctypes.c_size_t, _i32p, _i32p, _vp,
+                                ctypes.POINTER(_Debug)]),
         "zp_append_kv": (S, [ctypes.POINTER(_KVCache), ctypes.c_int32, ctypes.c_int32, _vp, _vp,
                              _vp, _vp]),
         "zp_paged_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(_KVCache),
@@ -88,6 +92,9 @@ def lib() -> ctypes.CDLL:
         "zp_paged_decode": (S, [ctypes.POINTER(_KVCache), ctypes.c_int32, ctypes.c_int32, _vp, _vp,
                                 ctypes.c_int32, _vp, ctypes.c_float, _vp, _vp, ctypes.c_size_t,
                                 _vp]),
+        "zp_paged_decode_lse": (S, [ctypes.POINTER(_KVCache), ctypes.c_int32, ctypes.c_int32, _vp,
+                                    _vp, ctypes.c_int32, _vp, ctypes.c_float, _vp, _vp, _vp,
+                                    ctypes.c_int32, _vp, ctypes.c_size_t, _vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -261,22 +268,36 @@ def compress_workspace_bytes(cache: KVCache, num_reqs: int, n_max: int, window: 
 
 
 def compress(cache: KVCache, pool: BlockPool, n_max: int, window: int, tables: np.ndarray,
-             window_q: List, workspace, stream=None, debug: Optional[dict] = None) -> np.ndarray:
-    """zp_compress.  ``tables`` (host int32 [R][n_max]) is rewritten on
-    success; returns the freed block ids."""
+             window_q: List, workspace, stream=None, debug: Optional[dict] = None,
+             window_lse: Optional[List] = None) -> np.ndarray:
+    """zp_compress (zp_compress_lse when ``window_lse``, per-layer float
+    tensors [R][w][Hq] of the window rows' normalisers, is given).
+    ``tables`` (host int32 [R][n_max]) is rewritten on success; returns the
+    freed block ids."""
     assert tables.dtype == np.int32 and tables.flags.c_contiguous
     R = int(tables.shape[0])
     wq = (_vp * cache.num_layers)(*[t.data_ptr() for t in window_q])
+    wl = None
+    if window_lse is not None:
+        wl = (_vp * cache.num_layers)(*[t.data_ptr() for t in window_lse])
     freed = np.zeros(max(R * n_max, 1), dtype=np.int32)
     n = np.zeros(1, dtype=np.int32)
     dbg = None
     if debug:
         dbg = _Debug(_dptr(debug.get("importance")), _dptr(debug.get("redundancy")),
                      _dptr(debug.get("score")), _dptr(debug.get("kept")))
-    st = lib().zp_compress(cache.ref, pool.handle, n_max, window, R, _i32(tables),
-                           ctypes.cast(wq, ctypes.POINTER(_vp)), workspace.data_ptr(),
-                           workspace.numel() * workspace.element_size(), _i32(freed), _i32(n),
-                           _stream_handle(stream), ctypes.byref(dbg) if dbg else None)
+    if wl is None:
+        st = lib().zp_compress(cache.ref, pool.handle, n_max, window, R, _i32(tables),
+                               ctypes.cast(wq, ctypes.POINTER(_vp)), workspace.data_ptr(),
+                               workspace.numel() * workspace.element_size(), _i32(freed), _i32(n),
+                               _stream_handle(stream), ctypes.byref(dbg) if dbg else None)
+    else:
+        st = lib().zp_compress_lse(cache.ref, pool.handle, n_max, window, R, _i32(tables),
+                                   ctypes.cast(wq, ctypes.POINTER(_vp)),
+                                   ctypes.cast(wl, ctypes.POINTER(_vp)), workspace.data_ptr(),
+                                   workspace.numel() * workspace.element_size(), _i32(freed),
+                                   _i32(n), _stream_handle(stream),
+                                   ctypes.byref(dbg) if dbg else None)
     _check(st)
     return freed[: int(n[0])]
 
@@ -291,13 +312,21 @@ def paged_decode_workspace_bytes(cache: KVCache, num_reqs: int, max_blocks: int)
 
 
 def paged_decode(cache: KVCache, layer: int, q, tables, seq_lens, scale: float, out, workspace,
-                 stream=None) -> None:
+                 stream=None, lse_out=None, lse_rows=None) -> None:
+    """zp_paged_decode, or zp_paged_decode_lse when ``lse_out`` (float
+    [rows][Hq]) is given; ``lse_rows`` (int32 [R]) maps requests to rows."""
     R, max_blocks = (int(x) for x in tables.shape)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(lib().zp_paged_decode(cache.ref, layer, R, q.data_ptr(), tables.data_ptr(), max_blocks,
-                                 seq_lens.data_ptr(), float(scale), out.data_ptr(), ws_ptr,
-                                 ws_bytes, _stream_handle(stream)))
+    if lse_out is None:
+        _check(lib().zp_paged_decode(cache.ref, layer, R, q.data_ptr(), tables.data_ptr(),
+                                     max_blocks, seq_lens.data_ptr(), float(scale), out.data_ptr(),
+                                     ws_ptr, ws_bytes, _stream_handle(stream)))
+        return
+    _check(lib().zp_paged_decode_lse(cache.ref, layer, R, q.data_ptr(), tables.data_ptr(),
+                                     max_blocks, seq_lens.data_ptr(), float(scale), out.data_ptr(),
+                                     lse_out.data_ptr(), _dptr(lse_rows), int(lse_out.shape[0]),
+                                     ws_ptr, ws_bytes, _stream_handle(stream)))
 
 
 # --------------------------------------------------------------------------- timing

@@ -105,6 +105,15 @@ __device__ inline float group_sum(float x) {
 // to zero, which only drops probabilities far below the output tolerance).
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Optional output: the log-sum-exp of the scaled logits of query head hq,
+// ln sum_j exp(scale * q.k_j), from the merged (max M, sum L) in log2 units.
+__device__ inline void store_lse(const DecodeParams& p, int r, int hq, float M, float L) {
+  if (!p.lse) return;
+  const int row = p.lse_rows ? p.lse_rows[r] : r;
+  if (row < 0 || row >= p.lse_cap) return;
+  p.lse[(size_t)row * p.Hq + hq] = L > 0.f ? (M + log2f(L)) * 0.6931471805599453f : -__builtin_inff();
+}
+
 // G here is the number of query heads one workgroup handles (at most 4, to
 // keep the accumulators in registers); larger groups are split over
 // blockIdx.y = kv_head * nsub + sub.
@@ -289,6 +298,7 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode(DecodeParams p) {
     const int hq = hq0 + g;
     if (p.nsplit == 1) {
       p.out[((size_t)r * p.Hq + hq) * D + d] = L > 0.f ? o / L : 0.f;
+      if (d == 0) store_lse(p, r, hq, M, L);
     } else {
       float* part = p.partial + (((size_t)r * p.Hq + hq) * p.nsplit + split) * (D + 2);
       part[2 + d] = o;
@@ -315,6 +325,7 @@ __global__ __launch_bounds__(D) void k_decode_combine(DecodeParams p) {
     o = fmaf(ps[2 + d], c, o);
   }
   p.out[(size_t)rh * D + d] = L > 0.f ? o / L : 0.f;
+  if (d == 0) store_lse(p, rh / p.Hq, rh % p.Hq, M, L);
 }
 
 __global__ __launch_bounds__(256) void k_append(AppendParams p) {

@@ -347,79 +347,95 @@ __global__ __launch_bounds__(64 * score_waves<RG>(), (kMaxWaves / score_waves<RG
   };
 
   // ---------------------------------------------------------------- pass 1
+  // Skipped when the caller supplies the normalisers of the window rows
+  // (the log-sum-exp the decode steps of those rows computed over the same
+  // slots): then K is read once.
   const float sl2 = p.scale_log2;
-  float m[RTW][4], z[RTW][4];
-#pragma unroll
-  for (int rt = 0; rt < RTW; rt++)
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      m[rt][i] = kInitMax;
-      z[rt][i] = 0.f;
-    }
-  ring(BoolC<false>{}, [&](int k, const uint4 (&kt)[NST][NV]) {
-    const int n = wl + WPG * k;
-    const bool last = n == p.n_max - 1;  // only the last block meets the causal limit
-#pragma unroll
-    for (int st = 0; st < NST; st++) {
-      const int j = n * B + st * 16 + col;
-      f32x4_t acc[RTW];
-#pragma unroll
-      for (int rt = 0; rt < RTW; rt++) {
-        acc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int v = 0; v < NV; v++) acc[rt] = Mma<DT>::step(qf[rt][v], kt[st][v], acc[rt]);
+  const float* lse = static_cast<const float*>(p.layer_ptrs[l * kPtrsPerLayer + 3]);
+  if (lse != nullptr) {
+    if (tid < RT * 16) {
+      float o = 1.0e30f;  // padding rows: probability 0
+      if (tid < p.rows) {
+        const int i = tid / p.G, g = tid - i * p.G;
+        const float v = lse[((size_t)r * p.w + i) * p.Hq + (size_t)h * p.G + g];
+        o = isfinite(v) ? v * 1.4426950408889634f : 1.0e30f;
       }
-      // 2^(x - m) for every logit; a term above 2^kLazy (or the causal
-      // block) sends the lane through the rescaling update instead
-      float e[RTW][4];
-      bool slow = last;
-#pragma unroll
-      for (int rt = 0; rt < RTW; rt++)
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-          e[rt][i] = fast_exp2(fmaf(acc[rt][i], sl2, -m[rt][i]));
-          slow |= e[rt][i] > kLazyTerm;
-        }
-      if (slow) {
-#pragma unroll
-        for (int rt = 0; rt < RTW; rt++)
-#pragma unroll
-          for (int i = 0; i < 4; i++)
-            lazy_update(m[rt][i], z[rt][i], j <= lim(rt, i) ? acc[rt][i] * sl2 : kMasked);
-      } else {
-#pragma unroll
-        for (int rt = 0; rt < RTW; rt++)
-#pragma unroll
-          for (int i = 0; i < 4; i++) z[rt][i] += e[rt][i];
-      }
+      s_off[tid] = o;
     }
-  });
-  // merge the 16 columns of every row (DPP inside 16-lane rows)
-#pragma unroll
-  for (int rt = 0; rt < RTW; rt++)
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      merge_dpp<0xB1>(m[rt][i], z[rt][i]);   // quad_perm [1,0,3,2]
-      merge_dpp<0x4E>(m[rt][i], z[rt][i]);   // quad_perm [2,3,0,1]
-      merge_dpp<0x141>(m[rt][i], z[rt][i]);  // row_half_mirror
-      merge_dpp<0x140>(m[rt][i], z[rt][i]);  // row_mirror
-    }
-  if (col == 0) {
+  } else {
+    float m[RTW][4], z[RTW][4];
 #pragma unroll
     for (int rt = 0; rt < RTW; rt++)
 #pragma unroll
       for (int i = 0; i < 4; i++) {
-        s_wst[wave][rt * 16 + 4 * grp + i][0] = m[rt][i];
-        s_wst[wave][rt * 16 + 4 * grp + i][1] = z[rt][i];
+        m[rt][i] = kInitMax;
+        z[rt][i] = 0.f;
       }
-  }
-  __syncthreads();
-  if (tid < RT * 16) {
-    const int g = tid / RPW, row = tid - g * RPW;
-    float M = kInitMax, Z = 0.f;
-    for (int w = g * WPG; w < (g + 1) * WPG; w++) merge_stat(M, Z, s_wst[w][row][0], s_wst[w][row][1]);
-    // probability of a logit x (log2 units) in this row: 2^(x - offset)
-    s_off[tid] = Z > 0.f ? M + fast_log2(Z) : 1.0e30f;
+    ring(BoolC<false>{}, [&](int k, const uint4 (&kt)[NST][NV]) {
+      const int n = wl + WPG * k;
+      const bool last = n == p.n_max - 1;  // only the last block meets the causal limit
+#pragma unroll
+      for (int st = 0; st < NST; st++) {
+        const int j = n * B + st * 16 + col;
+        f32x4_t acc[RTW];
+#pragma unroll
+        for (int rt = 0; rt < RTW; rt++) {
+          acc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int v = 0; v < NV; v++) acc[rt] = Mma<DT>::step(qf[rt][v], kt[st][v], acc[rt]);
+        }
+        // 2^(x - m) for every logit; a term above 2^kLazy (or the causal
+        // block) sends the lane through the rescaling update instead
+        float e[RTW][4];
+        bool slow = last;
+#pragma unroll
+        for (int rt = 0; rt < RTW; rt++)
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            e[rt][i] = fast_exp2(fmaf(acc[rt][i], sl2, -m[rt][i]));
+            slow |= e[rt][i] > kLazyTerm;
+          }
+        if (slow) {
+#pragma unroll
+          for (int rt = 0; rt < RTW; rt++)
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+              lazy_update(m[rt][i], z[rt][i], j <= lim(rt, i) ? acc[rt][i] * sl2 : kMasked);
+        } else {
+#pragma unroll
+          for (int rt = 0; rt < RTW; rt++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) z[rt][i] += e[rt][i];
+        }
+      }
+    });
+    // merge the 16 columns of every row (DPP inside 16-lane rows)
+#pragma unroll
+    for (int rt = 0; rt < RTW; rt++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        merge_dpp<0xB1>(m[rt][i], z[rt][i]);   // quad_perm [1,0,3,2]
+        merge_dpp<0x4E>(m[rt][i], z[rt][i]);   // quad_perm [2,3,0,1]
+        merge_dpp<0x141>(m[rt][i], z[rt][i]);  // row_half_mirror
+        merge_dpp<0x140>(m[rt][i], z[rt][i]);  // row_mirror
+      }
+    if (col == 0) {
+#pragma unroll
+      for (int rt = 0; rt < RTW; rt++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          s_wst[wave][rt * 16 + 4 * grp + i][0] = m[rt][i];
+          s_wst[wave][rt * 16 + 4 * grp + i][1] = z[rt][i];
+        }
+    }
+    __syncthreads();
+    if (tid < RT * 16) {
+      const int g = tid / RPW, row = tid - g * RPW;
+      float M = kInitMax, Z = 0.f;
+      for (int w = g * WPG; w < (g + 1) * WPG; w++) merge_stat(M, Z, s_wst[w][row][0], s_wst[w][row][1]);
+      // probability of a logit x (log2 units) in this row: 2^(x - offset)
+      s_off[tid] = Z > 0.f ? M + fast_log2(Z) : 1.0e30f;
+    }
   }
   __syncthreads();
   float off[RTW][4];

@@ -18,8 +18,9 @@ void clear_error();
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Per-layer device pointers uploaded for the compression kernels:
-// entry [l*3 + 0] = K pool, [l*3 + 1] = V pool, [l*3 + 2] = window queries.
-constexpr int kPtrsPerLayer = 3;
+// entry [l*4 + 0] = K pool, [l*4 + 1] = V pool, [l*4 + 2] = window queries,
+// [l*4 + 3] = recorded window normalisers (or null).
+constexpr int kPtrsPerLayer = 4;
 
 // Largest number of (query head, window row) pairs per KV head, and the
 // largest cached length the in-LDS scoring and selection handle.
@@ -37,7 +38,7 @@ constexpr int kDecodeThreads = ZP_DECODE_THREADS;
 constexpr int kDecodeTargetWorkgroups = ZP_DECODE_TARGET_WORKGROUPS;
 
 struct ScoreParams {
-  void* const* layer_ptrs;  // device [L][3]
+  void* const* layer_ptrs;  // device [L][kPtrsPerLayer]
   const int32_t* src;       // device [R][n_max]
   int32_t* evicted;         // [L*R*H][E], ascending
   float* dbg_importance;    // optional [L*R*H][T]
@@ -49,7 +50,7 @@ struct ScoreParams {
 };
 
 struct CompactParams {
-  void* const* layer_ptrs;  // device [L][3]
+  void* const* layer_ptrs;  // device [L][kPtrsPerLayer]
   const int32_t* src;       // device [R][n_max]
   const int32_t* dst;       // device [R][n_max-1]
   const int32_t* evicted;   // [L*R*H][E]
@@ -64,7 +65,9 @@ struct DecodeParams {
   const int32_t* seq_lens;  // [R]
   float* out;               // [R][Hq][d]
   float* partial;           // [R][Hq][nsplit][d + 2]
-  int32_t R, H, Hq, max_blocks, nsplit, blocks_per_split, num_blocks;
+  float* lse;               // optional [lse_cap][Hq]: natural-log normaliser per query head
+  const int32_t* lse_rows;  // optional [R]: row of lse for request r (default r; < 0 skips)
+  int32_t R, H, Hq, max_blocks, nsplit, blocks_per_split, num_blocks, lse_cap;
   float scale_log2;
 };
 

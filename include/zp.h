@@ -198,6 +198,31 @@ zp_status zp_compress(const zp_kv_cache* cache, zp_block_pool* pool, int32_t n_m
                       const zp_compress_debug* debug);
 
 /* ------------------------------------------------------------------------
+ * zp_compress_lse: zp_compress with the softmax normalisers of the window
+ * rows supplied by the caller, so the scoring reads K once instead of twice.
+ *
+ * The window queries are the queries of the last w decode steps of each
+ * request (the "query slots" of the hybrid scheduling, nl page Methodologie
+ * item 2, ko page section 2.B).  The decode step of window position i
+ * already attended over exactly the slots 0..C+i that the importance
+ * softmax of row i spans (causal window, no compression in between), so its
+ * log-sum-exp is that row's normaliser; zp_paged_decode_lse returns it.
+ *
+ * window_lse: NULL (then exactly zp_compress), or a host array [num_layers]
+ *   of device pointers to float [R][w][Hq]: for request r, window position i
+ *   and query head hq, ln sum over j <= C+i of exp(q.k_j / sqrt(head_dim)),
+ *   taken over the cache as it stands at this call.  Non-finite entries give
+ *   that row probability 0.  Values that do not match the cache are not
+ *   detected: the importances are then off by the per-row factor.
+ * Everything else, including the results up to rounding, as zp_compress.
+ * ---------------------------------------------------------------------- */
+zp_status zp_compress_lse(const zp_kv_cache* cache, zp_block_pool* pool, int32_t n_max,
+                          int32_t window, int32_t num_reqs, int32_t* block_tables,
+                          const void* const* window_q, const void* const* window_lse,
+                          void* workspace, size_t workspace_bytes, int32_t* freed_ids,
+                          int32_t* num_freed, void* stream, const zp_compress_debug* debug);
+
+/* ------------------------------------------------------------------------
  * zp_append_kv: write one new token per request into layer `layer`.
  * k_new, v_new: device [R][H][d]; slot_mapping: device int32 [R], physical
  * slot block*b + offset (negative = skip).  Tokens go into the last
@@ -228,6 +253,25 @@ zp_status zp_paged_decode(const zp_kv_cache* cache, int32_t layer, int32_t num_r
                           const void* q, const int32_t* block_tables, int32_t max_blocks,
                           const int32_t* seq_lens, float scale, float* out, void* workspace,
                           size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * zp_paged_decode_lse: zp_paged_decode that also returns, per request and
+ * query head, the log-sum-exp of the scaled logits,
+ *   lse[r][hq] = ln sum over j < seq_lens[r] of exp(scale * q.k_j)
+ * (-inf for an empty request).  With scale = 1/sqrt(head_dim) this is the
+ * normaliser zp_compress_lse takes for a window row.
+ * lse_out:      device float [lse_capacity][Hq].
+ * lse_rows:     NULL (request r writes row r; then lse_capacity >= num_reqs),
+ *               or device int32 [num_reqs]: the row request r writes; rows
+ *               outside [0, lse_capacity) are skipped (e.g. -1 for requests
+ *               that are not in their window).
+ * Other arguments, layouts and errors as zp_paged_decode.
+ * ---------------------------------------------------------------------- */
+zp_status zp_paged_decode_lse(const zp_kv_cache* cache, int32_t layer, int32_t num_reqs,
+                              const void* q, const int32_t* block_tables, int32_t max_blocks,
+                              const int32_t* seq_lens, float scale, float* out, float* lse_out,
+                              const int32_t* lse_rows, int32_t lse_capacity, void* workspace,
+                              size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Kernel timing.  While enabled, every kernel launch of the calls above is

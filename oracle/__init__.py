@@ -53,6 +53,9 @@ def _load():
     lib.zpo_decode.restype = None
     lib.zpo_decode.argtypes = [ctypes.c_int32] * 6 + [ctypes.c_void_p] * 3 + [
         _i32p, ctypes.c_int32, _i32p, ctypes.c_double, _f64p]
+    lib.zpo_decode_lse.restype = None
+    lib.zpo_decode_lse.argtypes = [ctypes.c_int32] * 6 + [ctypes.c_void_p] * 2 + [
+        _i32p, ctypes.c_int32, _i32p, ctypes.c_double, _f64p]
     _lib = lib
     return lib
 
@@ -173,6 +176,39 @@ def decode(kpool: np.ndarray, vpool: np.ndarray, q: np.ndarray, tables: np.ndarr
                    _vp(np.ascontiguousarray(vpool)), _vp(np.ascontiguousarray(q)), _i32(tables),
                    max_blocks, _i32(np.ascontiguousarray(seq_lens, dtype=np.int32)), float(scale),
                    _f64(out))
+    return out
+
+
+def decode_lse(kpool: np.ndarray, q: np.ndarray, tables: np.ndarray, seq_lens: np.ndarray, *,
+               num_q_heads: int, scale: Optional[float] = None) -> np.ndarray:
+    """log sum_j exp(scale q.k_j) over each request's slots, in double: [R][Hq]."""
+    lib = _load()
+    nb, H, b, d = kpool.shape
+    is_bf16 = int(kpool.dtype == np.uint16)
+    tables = np.ascontiguousarray(tables, dtype=np.int32)
+    R, max_blocks = tables.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    out = np.zeros((R, num_q_heads))
+    lib.zpo_decode_lse(H, num_q_heads, d, b, is_bf16, R, _vp(np.ascontiguousarray(kpool)),
+                       _vp(np.ascontiguousarray(q)), _i32(tables), max_blocks,
+                       _i32(np.ascontiguousarray(seq_lens, dtype=np.int32)), float(scale),
+                       _f64(out))
+    return out
+
+
+def window_lse(kpool: np.ndarray, window_q: np.ndarray, tables: np.ndarray, *, n_max: int,
+               window: int, num_q_heads: int) -> np.ndarray:
+    """Normalisers of the window rows: for window position i, the log-sum-exp
+    of q_i.k_j/sqrt(d) over slots j <= T-w+i (causal window): [R][w][Hq]."""
+    b = kpool.shape[2]
+    T = n_max * b
+    R = tables.shape[0]
+    out = np.zeros((R, window, num_q_heads))
+    for i in range(window):
+        lens = np.full(R, T - window + i + 1, dtype=np.int32)
+        out[:, i, :] = decode_lse(kpool, np.ascontiguousarray(window_q[:, i]), tables, lens,
+                                  num_q_heads=num_q_heads)
     return out
 
 

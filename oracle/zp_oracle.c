@@ -345,3 +345,37 @@ void zpo_decode(int32_t H, int32_t Hq, int32_t d, int32_t b, int32_t is_bf16, in
     free(qv);
   }
 }
+
+/* ---------------------------------------------------------------------
+ * Log-sum-exp of the decode logits: for request r and query head hq (KV
+ * head hq/G), lse = log sum over j < seq_len of exp(scale * q . k_j), with
+ * slot j at block tables[r][j/b], offset j%b; -inf for an empty request.
+ * This is the normaliser of the softmax in zpo_decode; the same quantity
+ * for a window query over slots 0..C+i is the normaliser of that window
+ * row's importance softmax.  lse: [R][Hq] doubles.
+ * --------------------------------------------------------------------- */
+void zpo_decode_lse(int32_t H, int32_t Hq, int32_t d, int32_t b, int32_t is_bf16, int32_t R,
+                    const void* kpool, const void* q, const int32_t* tables, int32_t max_blocks,
+                    const int32_t* seq_lens, double scale, double* lse) {
+  const int32_t G = Hq / H;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t unit = 0; unit < (int64_t)R * Hq; unit++) {
+    const int32_t r = (int32_t)(unit / Hq), hq = (int32_t)(unit % Hq), h = hq / G;
+    const int32_t n = seq_lens[r];
+    double* x = (double*)malloc((size_t)(n > 0 ? n : 1) * sizeof(double));
+    double m = -INFINITY;
+    for (int32_t j = 0; j < n; j++) {
+      int32_t blk = tables[(size_t)r * max_blocks + j / b];
+      size_t base = row_index(blk, h, j % b, H, b, d);
+      double dot = 0.0;
+      for (int32_t e = 0; e < d; e++)
+        dot += widen(q, ((size_t)r * Hq + hq) * d + e, is_bf16) * widen(kpool, base + e, is_bf16);
+      x[j] = scale * dot;
+      if (x[j] > m) m = x[j];
+    }
+    double Z = 0.0;
+    for (int32_t j = 0; j < n; j++) Z += exp(x[j] - m);
+    lse[(size_t)r * Hq + hq] = n > 0 ? m + log(Z) : -INFINITY;
+    free(x);
+  }
+}

@@ -52,7 +52,36 @@ class GpuRun:
     appended_v: list
 
 
-def run_case(case, device="cuda", decode=True) -> GpuRun:
+def window_lse_on_gpu(cache, case, kp_tensors, wq_tensors, device="cuda"):
+    """Normalisers of the window rows as the decode steps that produced the
+    window queries record them: for window position i, zp_paged_decode_lse
+    of query i over slots 0..T-w+i, written to row r*w + i of a [R*w][Hq]
+    buffer per layer (returned as [R][w][Hq] views)."""
+    g = case.geom
+    R, w, n_max, b = case.num_reqs, case.window, case.n_max, g.block_size
+    T = n_max * b
+    tab_t = torch.from_numpy(np.ascontiguousarray(case.tables)).to(device)
+    dws = torch.empty(max(zp.paged_decode_workspace_bytes(cache, R, n_max), 16),
+                      dtype=torch.uint8, device=device)
+    out = torch.empty((R, g.num_q_heads, g.head_dim), dtype=torch.float32, device=device)
+    res = []
+    for layer in range(g.num_layers):
+        buf = torch.full((R * w, g.num_q_heads), float("nan"), dtype=torch.float32, device=device)
+        for i in range(w):
+            seq = torch.full((R,), T - w + i + 1, dtype=torch.int32, device=device)
+            rows = (torch.arange(R, dtype=torch.int32, device=device) * w + i).contiguous()
+            q_i = wq_tensors[layer][:, i].contiguous()
+            zp.paged_decode(cache, layer, q_i, tab_t, seq, 1.0 / np.sqrt(g.head_dim), out, dws,
+                            lse_out=buf, lse_rows=rows)
+        res.append(buf.view(R, w, g.num_q_heads))
+    torch.cuda.synchronize()
+    return res
+
+
+def run_case(case, device="cuda", decode=True, recorded_lse=False) -> GpuRun:
+    """``recorded_lse``: compress with the window rows' normalisers taken
+    from zp_paged_decode_lse (the single-read scoring) instead of the
+    self-contained two-pass scoring."""
     g = case.geom
     L, H, b, n_max, w = g.num_layers, g.num_kv_heads, g.block_size, case.n_max, case.window
     R = case.num_reqs
@@ -69,7 +98,8 @@ def run_case(case, device="cuda", decode=True) -> GpuRun:
                redundancy=torch.full((L, R, H, T), float("nan"), device=device),
                score=torch.full((L, R, H, T), float("nan"), device=device),
                kept=torch.full((L, R, H, k_keep), -1, dtype=torch.int32, device=device))
-    freed = zp.compress(cache, pool, n_max, w, tables, wq, ws, debug=dbg)
+    wl = window_lse_on_gpu(cache, case, kp, wq, device) if recorded_lse else None
+    freed = zp.compress(cache, pool, n_max, w, tables, wq, ws, debug=dbg, window_lse=wl)
     torch.cuda.synchronize()
     run = GpuRun(tables=tables.copy(), refcounts=pool.refcounts(), freed=freed.copy(),
                  A=dbg["importance"].cpu().numpy(), R=dbg["redundancy"].cpu().numpy(),

@@ -415,6 +415,62 @@ def test_decode_dominant_logit_selects_one_value_row():
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_lse_matches_scipy_logsumexp(dtype):
+    from scipy.special import logsumexp
+    c = synth.make_case("lse", 26, num_reqs=3, num_layers=1, num_kv_heads=2, num_q_heads=6,
+                        head_dim=16, block_size=4, n_max=5, window=2, num_blocks=20, dtype=dtype)
+    seq = np.array([20, 13, 0], dtype=np.int32)
+    lse = oracle.decode_lse(c.k_pool[0], c.q_new[0], c.tables, seq, num_q_heads=6)
+    qf = c.q_new[0] if dtype == "f32" else synth.bf16_bits_to_f32(c.q_new[0])
+    for r in range(2):
+        for hq in range(6):
+            Kl = bf.logical_rows(c.k_pool[0], c.tables[r], hq // 3, int(seq[r]))
+            want = logsumexp(Kl @ qf[r, hq].astype(np.float64) / 4.0)
+            assert abs(lse[r, hq] - want) <= 1e-12 * max(1.0, abs(want))
+    assert np.all(np.isneginf(lse[2]))  # empty request
+
+
+def test_decode_lse_equal_keys_closed_form():
+    rng = np.random.default_rng(27)
+    H, Hq, d, n = 1, 2, 8, 11
+    k = rng.standard_normal(d)
+    K = np.broadcast_to(k, (1, H, 12, d)).copy()
+    tables = np.array([[2, 0, 1]], dtype=np.int32)
+    kp = synth.pool_from_logical(K, tables, 3, "f32")
+    q = rng.standard_normal((1, Hq, d)).astype(np.float32)
+    lse = oracle.decode_lse(kp, q, tables, np.array([n], dtype=np.int32), num_q_heads=Hq,
+                            scale=0.5)
+    kf = k.astype(np.float32).astype(np.float64)
+    for hq in range(Hq):
+        want = np.log(n) + 0.5 * float(q[0, hq].astype(np.float64) @ kf)
+        assert abs(lse[0, hq] - want) <= 1e-12 * max(1.0, abs(want))
+
+
+@pytest.mark.parametrize("G,w", [(1, 2), (4, 3)])
+def test_window_lse_normalises_the_importance_rows(G, w):
+    """The decode log-sum-exp of window query i over slots 0..T-w+i is the
+    normaliser of importance row i: recomputing A from it (dense logits in
+    NumPy) gives the oracle's A."""
+    rng = np.random.default_rng(31 + G)
+    H, d, b, n_max = 2, 8, 4, 6
+    T = n_max * b
+    tables, kpool, q, K, Q = _tiny_case(rng, H=H, Hq=H * G, d=d, b=b, n_max=n_max, w=w)
+    A, _, _ = oracle.scores(kpool, q, tables, num_kv_heads=H, num_q_heads=H * G, head_dim=d,
+                            block_size=b, n_max=n_max, window=w)
+    lse = oracle.window_lse(kpool, q, tables, n_max=n_max, window=w, num_q_heads=H * G)
+    Qf = q.astype(np.float64)
+    for r in range(2):
+        for h in range(H):
+            Kl = bf.logical_rows(kpool, tables[r], h, T)
+            acc = np.zeros(T)
+            for i in range(w):
+                for g in range(G):
+                    x = Kl[: T - w + i + 1] @ Qf[r, i, h * G + g] / np.sqrt(d)
+                    acc[: T - w + i + 1] += np.exp(x - lse[r, i, h * G + g])
+            np.testing.assert_allclose(A[r, h], acc / (G * w), rtol=1e-12)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_decode_matches_torch_sdpa(dtype):
     c = synth.make_case("dec", 25, num_reqs=3, num_layers=1, num_kv_heads=2, num_q_heads=6,
                         head_dim=16, block_size=4, n_max=5, window=2, num_blocks=20, dtype=dtype)
