@@ -187,7 +187,8 @@ def _kernel_rows(prof: dict, alg: dict, flops: dict) -> list:
     return rows
 
 
-def _alg_bytes(R_c, R_d, L, H, Hq, d, b, n_max, w, moved_rows, dec_tokens, eb=2, nsplit=0):
+def _alg_bytes(R_c, R_d, L, H, Hq, d, b, n_max, w, moved_rows, dec_tokens, eb=2, nsplit=0,
+               append_rows=None):
     """Algorithmic bytes (and MFMA flops) per launch of each phase: what the
     method must move or compute, not the kernels' own traffic."""
     T, kv_row = n_max * b, d * eb
@@ -198,7 +199,7 @@ def _alg_bytes(R_c, R_d, L, H, Hq, d, b, n_max, w, moved_rows, dec_tokens, eb=2,
         # probability -- which is traffic, not algorithmic bytes)
         "score": L * (R_c * H * T * kv_row + R_c * w * Hq * kv_row + R_c * H * b * 4),
         "compact": moved_rows * kv_row * 2 * 2,
-        "append": R_d * H * kv_row * 2 * 2,
+        "append": (R_d if append_rows is None else append_rows) * H * kv_row * 2 * 2,
         "decode": dec_tokens * H * kv_row * 2 + R_d * Hq * kv_row,
         "combine": R_d * Hq * nsplit * (d + 2) * 4 + R_d * Hq * d * 4,
     }
@@ -206,11 +207,93 @@ def _alg_bytes(R_c, R_d, L, H, Hq, d, b, n_max, w, moved_rows, dec_tokens, eb=2,
     return alg, flops
 
 
+def window_query_sets(first, n: int, seed: int, dev) -> list:
+    """Window queries for successive steps: the workload's own set, then
+    seeded N(0,1) sets (bf16) drawn on the device.  Every step compresses the
+    cache the previous step compacted, so fresh queries are what keeps the
+    steps alike: with a few sets reused, the survivors of earlier steps are
+    the keys those same queries favour, evictions drift to the newest slots
+    and the compaction moves ever fewer rows."""
+    import torch
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    return [[first]] + [[torch.randn(first.shape, generator=gen, device=dev).to(first.dtype)]
+                        for _ in range(n - 1)]
+
+
+def reserved_block_fills(cache, tables, k_new, v_new, n_max, n_sets, dev) -> list:
+    """Rows for the reserved block of every request, n_sets of them: fresh
+    N(0,1) keys (times each head's key scale, read off the cache) and N(0,1)
+    values, seeded, in the cache dtype: [R*b][H][d] each.  Row (r, 0) is the
+    pending token; it too changes from step to step (a token appended at
+    every step with the same key would pile up identical keys that the
+    redundancy score then evicts first)."""
+    import torch
+    R, b = tables.shape[0], cache.block_size
+    kp = cache.k_pools[0]
+    H, d = kp.shape[1], kp.shape[3]
+    used = torch.from_numpy(tables[: min(R, 8)].reshape(-1).astype("int64")).to(dev)
+    sig = kp.index_select(0, used).float().transpose(0, 1).reshape(H, -1).std(dim=1)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4242)
+    sets = []
+    for _ in range(n_sets):
+        kf = torch.randn((R, b, H, d), generator=gen, device=dev) * sig[None, None, :, None]
+        vf = torch.randn((R, b, H, d), generator=gen, device=dev)
+        sets.append((kf.to(kp.dtype).reshape(R * b, H, d).contiguous(),
+                     vf.to(kp.dtype).reshape(R * b, H, d).contiguous()))
+    return sets
+
+
+def recorded_lse_compress(steps, cache, pool, tables, next_wq, n_max, w, R, Hq, d, dev, ws, dws,
+                          step):
+    """Per step: the window normalisers on the current cache (decode calls,
+    untimed), then one full step whose compression takes them; returns the
+    per-phase event totals of the compressions."""
+    import numpy as np
+    import torch
+    import compressed_paged_kv_amd as zp
+    b = cache.block_size
+    T = n_max * b
+    tab_t = torch.from_numpy(np.ascontiguousarray(tables)).to(dev)
+    out = torch.empty((R, Hq, d), dtype=torch.float32, device=dev)
+    lse = [torch.empty((R * w, Hq), dtype=torch.float32, device=dev)]
+    rows = [(torch.arange(R, dtype=torch.int32, device=dev) * w + i).contiguous() for i in range(w)]
+    seqs = [torch.full((R,), T - w + i + 1, dtype=torch.int32, device=dev) for i in range(w)]
+    zp.profile_enable(False)
+    totals = {}
+    for it in range(steps):
+        wq = next_wq()
+        for i in range(w):
+            zp.paged_decode(cache, 0, wq[0][:, i].contiguous(), tab_t, seqs[i], 1.0 / np.sqrt(d),
+                            out, dws, lse_out=lse[0], lse_rows=rows[i])
+        zp.profile_enable(True)
+        zp.compress(cache, pool, n_max, w, tables, wq, ws,
+                    window_lse=[lse[0].view(R, w, Hq)])
+        zp.profile_enable(False)
+        step(it, compress=False)
+        torch.cuda.synchronize()
+        for k, (ms, n) in zp.profile_read().items():
+            t = totals.get(k, (0.0, 0))
+            totals[k] = (t[0] + ms, t[1] + n)
+    return totals
+
+
 def run_single_stream(args, workload, cache, pool, tables, wq_sets, q_new, k_new, v_new, geom,
                       n_max, w, cpu_case=None):
     """One step = host plan + compression of every request's single layer +
-    append of the pending token + paged decode over the compacted cache, all
-    on one stream; the compression is in place, so every step repeats it."""
+    append into the reserved block + paged decode over the compacted cache
+    and the pending token, all on one stream.
+
+    The compression is in place, so every step compresses the cache the
+    previous one left.  To keep the steps alike, the append writes the whole
+    reserved block: the pending token plus the b-1 tokens the following
+    decode steps would add before the next trigger, fresh rows from a
+    rotating set, so each step meets a full cache whose newest block (the
+    observation window) is new.  (Appending one token and compressing again
+    would leave the same b-1 stale rows in the window at every step; their
+    copies pile up among the candidates, are evicted as redundant, and the
+    compaction moves ever fewer rows.)"""
     import numpy as np
     import torch
     import compressed_paged_kv_amd as zp
@@ -220,8 +303,18 @@ def run_single_stream(args, workload, cache, pool, tables, wq_sets, q_new, k_new
     T, k_keep = n_max * b, (n_max - 1) * b
     seq = k_keep + 1
     tables0 = tables.copy()
+    rot = [0]
+
+    def next_wq():
+        rot[0] += 1
+        return wq_sets[(rot[0] - 1) % len(wq_sets)]
+
     tab_t = torch.from_numpy(tables).to(dev)
-    slot_t = torch.from_numpy((tables[:, k_keep // b] * b + k_keep % b).astype(np.int32)).to(dev)
+    # the reserved block of every request, all b slots (slot k_keep first)
+    slot_t = torch.from_numpy((tables[:, k_keep // b, None] * b
+                               + np.arange(b)[None, :]).reshape(-1).astype(np.int32)).to(dev)
+    fills = reserved_block_fills(cache, tables, k_new, v_new, n_max, 96 if R * b <= 1024 else 24,
+                                 dev)
     seq_t = torch.full((R,), seq, dtype=torch.int32, device=dev)
     ws = torch.empty(zp.compress_workspace_bytes(cache, R, n_max, w), dtype=torch.uint8, device=dev)
     dws = torch.empty(max(zp.paged_decode_workspace_bytes(cache, R, n_max), 16), dtype=torch.uint8,
@@ -230,18 +323,24 @@ def run_single_stream(args, workload, cache, pool, tables, wq_sets, q_new, k_new
     scale = 1.0 / float(np.sqrt(d))
     torch.cuda.synchronize()
 
-    def step(i: int, debug=None):
-        zp.compress(cache, pool, n_max, w, tables, wq_sets[i % len(wq_sets)], ws, debug=debug)
-        zp.append_kv(cache, 0, k_new, v_new, slot_t)
+    def step(i: int, debug=None, compress=True):
+        # i is ignored: the window-query sets rotate over the whole run
+        if compress:
+            zp.compress(cache, pool, n_max, w, tables, next_wq(), ws, debug=debug)
+        kf, vf = fills[rot[0] % len(fills)]
+        zp.append_kv(cache, 0, kf, vf, slot_t)
         zp.paged_decode(cache, 0, q_new, tab_t, seq_t, scale, out, dws)
 
-    def moved_rows() -> int:
-        """Rows the compaction actually moves in one step (from the kept lists)."""
+    def moved_rows() -> float:
+        """Rows the compaction moves per step (from the kept lists), averaged
+        over a few steps."""
         kept = torch.empty((1, R, H, k_keep), dtype=torch.int32, device=dev)
-        step(0, debug={"kept": kept})
-        torch.cuda.synchronize()
-        k = kept.cpu().numpy()[0]
-        return int(np.count_nonzero(k != np.arange(k_keep)[None, None, :]))
+        ar = torch.arange(k_keep, dtype=torch.int32, device=dev)
+        counts = []
+        for i in range(4):
+            step(i, debug={"kept": kept})
+            counts.append(int((kept[0] != ar).sum().item()))
+        return float(np.mean(counts))
 
     moved_before = moved_rows()
     log(f"warmup {args.warmup} steps")
@@ -254,9 +353,11 @@ def run_single_stream(args, workload, cache, pool, tables, wq_sets, q_new, k_new
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i)
+    t_enq = time.perf_counter()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+    host_ms_per_step = (t_enq - t0) * 1e3 / args.steps
     # 2) the same K steps again with HIP events recorded around every kernel
     #    on its launch stream, for per-kernel durations (the events add small
     #    gaps between kernels, so this region's wall time is reported apart)
@@ -272,13 +373,22 @@ def run_single_stream(args, workload, cache, pool, tables, wq_sets, q_new, k_new
     prof = zp.profile_read()
     zp.profile_enable(False)
     ms_per_step_events = (t3 - t2) * 1e3 / args.steps
+    # 3) the compression fed with recorded window normalisers (the scoring
+    #    reads K once): before each step the normalisers of the step's window
+    #    rows are computed on the current cache by zp_paged_decode_lse, as the
+    #    decode steps that produced those queries would have recorded them
+    #    (outside the events: that work belongs to the earlier decode steps)
+    log(f"timing {args.steps} compressions with recorded window normalisers")
+    rec = recorded_lse_compress(args.steps, cache, pool, tables, next_wq, n_max, w, R, Hq, d,
+                                dev, ws, dws, step)
     moved_after = moved_rows()
     assert tables.tolist() == tables0.tolist(), "in-place compression changed the tables"
     assert np.isfinite(out.cpu().numpy()).all()
 
     moved = 0.5 * (moved_before + moved_after)
     nsplit = zp.paged_decode_workspace_bytes(cache, R, n_max) // (R * Hq * (d + 2) * 4)
-    alg, flops = _alg_bytes(R, R, 1, H, Hq, d, b, n_max, w, moved, R * seq, nsplit=nsplit)
+    alg, flops = _alg_bytes(R, R, 1, H, Hq, d, b, n_max, w, moved, R * seq, nsplit=nsplit,
+                            append_rows=R * b)
     kernels = _kernel_rows(prof, alg, flops)
     gpu_kernels = [k for k in kernels if k["phase"] != "upload"]
     dom = max(gpu_kernels, key=lambda k: k["avg_us"] * k["launches"])
@@ -301,6 +411,7 @@ def run_single_stream(args, workload, cache, pool, tables, wq_sets, q_new, k_new
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
         "ms_per_step_with_kernel_events": round(ms_per_step_events, 4),
+        "host_enqueue_ms_per_step": round(host_ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -317,8 +428,21 @@ def run_single_stream(args, workload, cache, pool, tables, wq_sets, q_new, k_new
         "decode_us": round(dec_us, 2),
         "decode_hbm_frac": round(dec_bytes / (dec_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         "moved_rows_per_step": int(moved),
+        "moved_rows_before_after": [moved_before, moved_after],
         "kernels": kernels,
         "roofline": roofline,
+    }
+    rec_us = {k["phase"]: k["avg_us"] for k in _kernel_rows(rec, alg, flops)}
+    rec_comp = sum(rec_us.get(p, 0.0) for p in ("upload", "score", "compact"))
+    result["recorded_lse"] = {
+        "what": "compression with the window rows' softmax normalisers recorded by the decode "
+                "steps that produced the window queries (zp_compress_lse): the scoring reads K "
+                "once; per-phase HIP-event averages",
+        "score_us": rec_us.get("score"), "compact_us": rec_us.get("compact"),
+        "compress_us": round(rec_comp, 2),
+        "compress_per_s": round(R / (rec_comp * 1e-6), 1),
+        "score_hbm_frac": round(alg["score"] / (rec_us["score"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "compress_hbm_frac": round(comp_bytes / (rec_comp * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
     }
     if cpu_case is not None and not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
@@ -550,11 +674,7 @@ def main() -> int:
         from synth.device_gen import case_structured_device
         log("generating the structured b=32 workload on the device (512 requests, budget 4096)")
         case = case_structured_device(dev)
-        gen = torch.Generator(device=dev)
-        gen.manual_seed(1105)
-        wq_sets = [[case.window_q[0]]] + [
-            [torch.randn(case.window_q[0].shape, generator=gen, device=dev).to(torch.bfloat16)]
-            for _ in range(3)]
+        wq_sets = window_query_sets(case.window_q[0], 16, 1105, dev)
         cache = zp.KVCache(case.k_pool, case.v_pool, case.geom.num_q_heads)
         pool = zp.BlockPool.from_refcounts(case.refcounts)
         result = run_single_stream(args, args.workload, cache, pool, case.tables.copy(), wq_sets,
@@ -563,11 +683,7 @@ def main() -> int:
     else:
         log("generating the Qwen3-8B-shaped layer (64 requests, budget 2048)")
         case = synth.case_qwen3_8b_layer()
-        rng = np.random.default_rng(1102)
-        # a few window-query sets, rotated per step, so eviction positions vary
-        wq_sets = [[to_tensor(case.window_q[0], dev)]] + [
-            [to_tensor(synth.f32_to_bf16_bits(rng.standard_normal(case.window_q[0].shape)
-                                              .astype(np.float32)), dev)] for _ in range(3)]
+        wq_sets = window_query_sets(to_tensor(case.window_q[0], dev), 64, 1102, dev)
         cache = zp.KVCache([to_tensor(case.k_pool[0], dev)], [to_tensor(case.v_pool[0], dev)],
                            case.geom.num_q_heads)
         pool = zp.BlockPool.from_refcounts(case.refcounts)
