@@ -37,8 +37,8 @@ def _load():
     lib = ctypes.CDLL(_build.LIB)
     lib.zpo_num_threads.restype = ctypes.c_int
     lib.zpo_plan.restype = ctypes.c_int
-    lib.zpo_plan.argtypes = [ctypes.c_int32, _i32p, ctypes.c_int32, ctypes.c_int32, _i32p,
-                             _i32p, _i32p, _i32p, _i32p]
+    lib.zpo_plan.argtypes = [ctypes.c_int32, _i32p, ctypes.c_int32, ctypes.c_int32,
+                             ctypes.c_int32, _i32p, _i32p, _i32p, _i32p, _i32p]
     lib.zpo_scores.restype = None
     lib.zpo_scores.argtypes = [ctypes.c_int32] * 8 + [ctypes.c_void_p, ctypes.c_void_p, _i32p,
                                                       _f64p, _f64p, _f64p]
@@ -46,7 +46,7 @@ def _load():
     lib.zpo_select.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                _f64p, _i32p]
     lib.zpo_compact.restype = None
-    lib.zpo_compact.argtypes = [ctypes.c_int64] + [ctypes.c_int32] * 7 + [
+    lib.zpo_compact.argtypes = [ctypes.c_int64] + [ctypes.c_int32] * 8 + [
         ctypes.c_void_p, ctypes.c_void_p, _i32p, _i32p, _i32p]
     lib.zpo_append.restype = None
     lib.zpo_append.argtypes = [ctypes.c_int32] * 5 + [ctypes.c_void_p] * 4 + [_i32p]
@@ -85,39 +85,44 @@ OK, INVALID, NO_BLOCKS = 0, 1, 2
 @dataclass
 class Plan:
     status: int
-    tables: np.ndarray      # new tables [R][n_max]
+    tables: np.ndarray      # new tables [R][n_src]: n_max ids, then -1 for the surplus
     refcounts: np.ndarray   # new refcounts
-    src: np.ndarray         # [R][n_max]
+    src: np.ndarray         # [R][n_src] (the old tables)
     dst: np.ndarray         # [R][n_max-1]
     freed: np.ndarray       # freed ids in order
 
 
 def plan(refcounts: np.ndarray, tables: np.ndarray, n_max: int) -> Plan:
-    """Target-block plan of one compression call (inputs are not modified)."""
+    """Target-block plan of one compression call (inputs are not modified).
+    ``tables`` is [R][n_src] with n_src >= n_max."""
     lib = _load()
     rc = np.ascontiguousarray(refcounts, dtype=np.int32).copy()
     tab = np.ascontiguousarray(tables, dtype=np.int32).copy()
-    R = int(tab.shape[0])
-    src = np.zeros((R, n_max), dtype=np.int32)
+    R, n_src = (int(x) for x in tab.shape)
+    src = np.zeros((R, n_src), dtype=np.int32)
     dst = np.zeros((R, max(n_max - 1, 1)), dtype=np.int32)
-    freed = np.zeros(max(R * n_max, 1), dtype=np.int32)
+    freed = np.zeros(max(R * n_src, 1), dtype=np.int32)
     nfreed = np.zeros(1, dtype=np.int32)
-    st = lib.zpo_plan(int(rc.shape[0]), _i32(rc), R, n_max, _i32(tab), _i32(src), _i32(dst),
-                      _i32(freed), _i32(nfreed))
+    st = lib.zpo_plan(int(rc.shape[0]), _i32(rc), R, n_src, n_max, _i32(tab), _i32(src),
+                      _i32(dst), _i32(freed), _i32(nfreed))
     return Plan(int(st), tab, rc, src, dst, freed[: int(nfreed[0])].copy())
 
 
 def scores(kpool: np.ndarray, window_q: np.ndarray, src: np.ndarray, *, num_kv_heads: int,
-           num_q_heads: int, head_dim: int, block_size: int, n_max: int, window: int):
-    """Importance A, redundancy R and combined score s, each [R][H][T] float64."""
+           num_q_heads: int, head_dim: int, block_size: int, window: int,
+           n_max: Optional[int] = None):
+    """Importance A, redundancy R and combined score s, each [R][H][T] float64,
+    over the T = n_src*b slots of the tables ``src`` [R][n_src] (``n_max``,
+    if given, must be that block count)."""
     lib = _load()
     is_bf16 = int(kpool.dtype == np.uint16)
-    R = int(src.shape[0])
-    T = n_max * block_size
+    R, n_src = (int(x) for x in src.shape)
+    assert n_max is None or n_max == n_src
+    T = n_src * block_size
     A = np.zeros((R, num_kv_heads, T))
     Rr = np.zeros((R, num_kv_heads, T))
     s = np.zeros((R, num_kv_heads, T))
-    lib.zpo_scores(num_kv_heads, num_q_heads, head_dim, block_size, is_bf16, n_max, window, R,
+    lib.zpo_scores(num_kv_heads, num_q_heads, head_dim, block_size, is_bf16, n_src, window, R,
                    _vp(np.ascontiguousarray(kpool)), _vp(np.ascontiguousarray(window_q)),
                    _i32(np.ascontiguousarray(src, dtype=np.int32)), _f64(A), _f64(Rr), _f64(s))
     return A, Rr, s
@@ -136,14 +141,16 @@ def select(s: np.ndarray, window: int, k_sel: int) -> np.ndarray:
 
 def compact(pool: np.ndarray, src: np.ndarray, dst: np.ndarray, kept: np.ndarray, *,
             n_max: int) -> np.ndarray:
-    """Out-of-place order-preserving compaction of one [nb][H][b][d] pool."""
+    """Out-of-place order-preserving compaction of one [nb][H][b][d] pool
+    (src [R][n_src] old tables, dst [R][n_max-1] targets)."""
     lib = _load()
     pool = np.ascontiguousarray(pool)
     nb, H, b, d = pool.shape
     out = np.empty_like(pool)
-    R = int(src.shape[0])
+    R, n_src = (int(x) for x in src.shape)
     k_keep = int(kept.shape[-1])
-    lib.zpo_compact(int(pool.size), H, d, b, pool.itemsize, n_max, R, k_keep, _vp(pool), _vp(out),
+    lib.zpo_compact(int(pool.size), H, d, b, pool.itemsize, n_src, n_max, R, k_keep, _vp(pool),
+                    _vp(out),
                     _i32(np.ascontiguousarray(src, dtype=np.int32)),
                     _i32(np.ascontiguousarray(dst, dtype=np.int32)),
                     _i32(np.ascontiguousarray(kept, dtype=np.int32)))
@@ -238,7 +245,7 @@ def compress(case, layers: Optional[List[int]] = None, with_pools: bool = True) 
     for layer in layers:
         A, Rr, s = scores(case.k_pool[layer], case.window_q[layer], p.src,
                           num_kv_heads=g.num_kv_heads, num_q_heads=g.num_q_heads,
-                          head_dim=g.head_dim, block_size=b, n_max=n_max, window=w)
+                          head_dim=g.head_dim, block_size=b, window=w)
         kept = select(s, w, k_sel)
         out.A.append(A)
         out.R.append(Rr)

@@ -80,34 +80,38 @@ int zpo_num_threads(void) {
 
 /* ---------------------------------------------------------------------
  * Planning (trigger already decided by the caller: every listed request
- * holds n_max full blocks).
+ * holds n_src >= n_max full blocks; n_src > n_max is a cache that grew past
+ * the cap, e.g. a long prompt, whose surplus blocks are released).
  *
  * Reference counts are read at the start of the call.  For each request,
  * in order, and each logical block n < n_max-1: a block referenced only by
  * this request is compacted in place; a shared one gets a new target block
  * (the smallest free id) and this request drops its reference to the
- * shared source.  The last logical block is kept as the reserved block if
- * private, otherwise replaced by a fresh block.  Blocks whose count reaches
- * zero are reported as freed.  Nothing is changed when the inputs are
- * invalid or when too few blocks are free.
+ * shared source.  Logical block n_max-1 is kept as the reserved block if
+ * private, otherwise replaced by a fresh block.  Blocks n_max..n_src-1 are
+ * surplus: the request drops its reference to each.  Blocks whose count
+ * reaches zero are reported as freed.  Nothing is changed when the inputs
+ * are invalid or when too few blocks are free.
  *
- * tables: [R][n_max] in/out.  src_out: [R][n_max] (the old table).
- * dst_out: [R][n_max-1] (compaction targets).  freed_out: capacity R*n_max.
+ * tables: [R][n_src] in; out: the n_max new ids, then -1 for the surplus.
+ * src_out: [R][n_src] (the old table).  dst_out: [R][n_max-1] (compaction
+ * targets).  freed_out: capacity R*n_src.
  * --------------------------------------------------------------------- */
-int zpo_plan(int32_t pool_size, int32_t* rc, int32_t R, int32_t n_max, int32_t* tables,
-             int32_t* src_out, int32_t* dst_out, int32_t* freed_out, int32_t* n_freed_out) {
-  if (pool_size <= 0 || R < 0 || n_max < 2) return ZPO_INVALID;
+int zpo_plan(int32_t pool_size, int32_t* rc, int32_t R, int32_t n_src, int32_t n_max,
+             int32_t* tables, int32_t* src_out, int32_t* dst_out, int32_t* freed_out,
+             int32_t* n_freed_out) {
+  if (pool_size <= 0 || R < 0 || n_max < 2 || n_src < n_max) return ZPO_INVALID;
   int32_t* seen = (int32_t*)calloc((size_t)pool_size, sizeof(int32_t));
   int32_t* rc0 = (int32_t*)malloc((size_t)pool_size * sizeof(int32_t));
   if (!seen || !rc0) { free(seen); free(rc0); return ZPO_INVALID; }
   memcpy(rc0, rc, (size_t)pool_size * sizeof(int32_t));
   int bad = 0;
   for (int32_t r = 0; r < R && !bad; r++) {
-    for (int32_t n = 0; n < n_max && !bad; n++) {
-      int32_t id = tables[(size_t)r * n_max + n];
+    for (int32_t n = 0; n < n_src && !bad; n++) {
+      int32_t id = tables[(size_t)r * n_src + n];
       if (id < 0 || id >= pool_size || rc0[id] < 1) { bad = 1; break; }
       for (int32_t m = 0; m < n; m++)
-        if (tables[(size_t)r * n_max + m] == id) { bad = 1; break; }
+        if (tables[(size_t)r * n_src + m] == id) { bad = 1; break; }
       seen[id] += 1;
       if (seen[id] > rc0[id]) bad = 1;
     }
@@ -116,7 +120,7 @@ int zpo_plan(int32_t pool_size, int32_t* rc, int32_t R, int32_t n_max, int32_t* 
   int64_t need = 0, nfree = 0;
   for (int32_t r = 0; r < R; r++)
     for (int32_t n = 0; n < n_max; n++)
-      if (rc0[tables[(size_t)r * n_max + n]] > 1) need++;
+      if (rc0[tables[(size_t)r * n_src + n]] > 1) need++;
   for (int32_t i = 0; i < pool_size; i++)
     if (rc0[i] == 0) nfree++;
   if (need > nfree) { free(seen); free(rc0); return ZPO_NO_BLOCKS; }
@@ -124,10 +128,16 @@ int zpo_plan(int32_t pool_size, int32_t* rc, int32_t R, int32_t n_max, int32_t* 
   int32_t next_free = 0; /* scan pointer over ids that were free at the start */
   int32_t nfreed = 0;
   for (int32_t r = 0; r < R; r++) {
-    int32_t* row = tables + (size_t)r * n_max;
-    for (int32_t n = 0; n < n_max; n++) src_out[(size_t)r * n_max + n] = row[n];
-    for (int32_t n = 0; n < n_max; n++) {
+    int32_t* row = tables + (size_t)r * n_src;
+    for (int32_t n = 0; n < n_src; n++) src_out[(size_t)r * n_src + n] = row[n];
+    for (int32_t n = 0; n < n_src; n++) {
       int32_t s = row[n];
+      if (n >= n_max) { /* surplus: released */
+        rc[s] -= 1;
+        if (rc[s] == 0) freed_out[nfreed++] = s;
+        row[n] = -1;
+        continue;
+      }
       int32_t target = s;
       if (rc0[s] > 1) {
         while (rc0[next_free] != 0) next_free++;
@@ -148,7 +158,7 @@ int zpo_plan(int32_t pool_size, int32_t* rc, int32_t R, int32_t n_max, int32_t* 
 
 /* ---------------------------------------------------------------------
  * Scores for one layer.  Per request r and KV head h (G = Hq/H query heads
- * per KV head), with T = n_max*b cached slots read through the block table:
+ * per KV head), with T = n_src*b cached slots read through the block table:
  *   importance A[j] = 1/(G w) * sum over g < G, i < w with p_i >= j of
  *       softmax over slots 0..p_i of x_{g,i}, where p_i = T-w+i and
  *       x_{g,i}[j] = q_{i, hG+g} . k_j / sqrt(d)   (causal window queries);
@@ -157,11 +167,11 @@ int zpo_plan(int32_t pool_size, int32_t* rc, int32_t R, int32_t n_max, int32_t* 
  *   s[j] = A[j] * (1 - R[j]) for the candidates j < T-w; NaN elsewhere.
  * Outputs are [R][H][T] doubles.
  * --------------------------------------------------------------------- */
-void zpo_scores(int32_t H, int32_t Hq, int32_t d, int32_t b, int32_t is_bf16, int32_t n_max,
+void zpo_scores(int32_t H, int32_t Hq, int32_t d, int32_t b, int32_t is_bf16, int32_t n_src,
                 int32_t w, int32_t R, const void* kpool, const void* window_q,
                 const int32_t* src, double* A_out, double* R_out, double* s_out) {
   const int32_t G = Hq / H;
-  const int32_t T = n_max * b;
+  const int32_t T = n_src * b;
   const int32_t C = T - w;
   const double inv_sqrt_d = 1.0 / sqrt((double)d);
 #pragma omp parallel for schedule(dynamic, 1)
@@ -174,7 +184,7 @@ void zpo_scores(int32_t H, int32_t Hq, int32_t d, int32_t b, int32_t is_bf16, in
     double* q = (double*)malloc((size_t)d * sizeof(double));
     double* nrm = (double*)malloc((size_t)T * sizeof(double));
     for (int32_t j = 0; j < T; j++) {
-      int32_t blk = src[(size_t)r * n_max + j / b];
+      int32_t blk = src[(size_t)r * n_src + j / b];
       size_t base = row_index(blk, h, j % b, H, b, d);
       for (int32_t e = 0; e < d; e++) K[(size_t)j * d + e] = widen(kpool, base + e, is_bf16);
     }
@@ -206,7 +216,7 @@ void zpo_scores(int32_t H, int32_t Hq, int32_t d, int32_t b, int32_t is_bf16, in
       for (int32_t e = 0; e < d; e++) ss += K[(size_t)j * d + e] * K[(size_t)j * d + e];
       nrm[j] = sqrt(ss);
     }
-    for (int32_t n = 0; n < n_max; n++) {
+    for (int32_t n = 0; n < n_src; n++) {
       for (int32_t a = 0; a < b; a++) {
         const int32_t ja = n * b + a;
         double acc = 0.0;
@@ -266,11 +276,11 @@ void zpo_select(int64_t units, int32_t T, int32_t w, int32_t k_sel, const double
  * place: pool_out starts as a copy of pool_in, then for every request and
  * head, new logical slot r (in the dst blocks) receives old logical slot
  * kept[r] (read through the src table from pool_in).
- * kept: [R][H][k_keep].
+ * src: [R][n_src], dst: [R][n_max-1], kept: [R][H][k_keep].
  * --------------------------------------------------------------------- */
 void zpo_compact(int64_t pool_elems, int32_t H, int32_t d, int32_t b, int32_t elem_bytes,
-                 int32_t n_max, int32_t R, int32_t k_keep, const void* pool_in, void* pool_out,
-                 const int32_t* src, const int32_t* dst, const int32_t* kept) {
+                 int32_t n_src, int32_t n_max, int32_t R, int32_t k_keep, const void* pool_in,
+                 void* pool_out, const int32_t* src, const int32_t* dst, const int32_t* kept) {
   memcpy(pool_out, pool_in, (size_t)pool_elems * (size_t)elem_bytes);
   const size_t row_bytes = (size_t)d * (size_t)elem_bytes;
   for (int32_t r = 0; r < R; r++) {
@@ -278,7 +288,7 @@ void zpo_compact(int64_t pool_elems, int32_t H, int32_t d, int32_t b, int32_t el
       const int32_t* kp = kept + ((size_t)r * H + h) * k_keep;
       for (int32_t slot = 0; slot < k_keep; slot++) {
         int32_t j = kp[slot];
-        int32_t sblk = src[(size_t)r * n_max + j / b];
+        int32_t sblk = src[(size_t)r * n_src + j / b];
         int32_t dblk = dst[(size_t)r * (n_max - 1) + slot / b];
         const char* from = (const char*)pool_in + row_index(sblk, h, j % b, H, b, d) * elem_bytes;
         char* to = (char*)pool_out + row_index(dblk, h, slot % b, H, b, d) * elem_bytes;

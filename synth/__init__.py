@@ -81,7 +81,7 @@ class CompressCase:
     geom: Geometry
     n_max: int
     window: int
-    tables: np.ndarray          # int32 [R][n_max]
+    tables: np.ndarray          # int32 [R][n_src] (n_src >= n_max; n_src > n_max: over the cap)
     refcounts: np.ndarray       # int32 [num_blocks]
     k_pool: List[np.ndarray]
     v_pool: List[np.ndarray]
@@ -95,6 +95,10 @@ class CompressCase:
     @property
     def num_reqs(self) -> int:
         return int(self.tables.shape[0])
+
+    @property
+    def n_src(self) -> int:
+        return int(self.tables.shape[1])
 
 
 def _to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
@@ -113,7 +117,8 @@ def make_case(name: str, seed: int, *, num_reqs: int, num_layers: int, num_kv_he
               num_q_heads: int, head_dim: int, block_size: int, n_max: int, window: int,
               num_blocks: int, dtype: str, key_scale_range: Optional[tuple] = None,
               shared_prefix_blocks: int = 0, key_kind: str = "iid", ar_rho: float = 0.9,
-              planted_frac: float = 0.0, planted_scale: float = 8.0) -> CompressCase:
+              planted_frac: float = 0.0, planted_scale: float = 8.0,
+              n_src: Optional[int] = None) -> CompressCase:
     """Build a seeded case.
 
     key_kind "iid": K ~ N(0,1) (optionally times a per (layer, head) scale
@@ -123,22 +128,27 @@ def make_case(name: str, seed: int, *, num_reqs: int, num_layers: int, num_kv_he
     without replacement, is multiplied by ``planted_scale``.
     ``shared_prefix_blocks`` > 0: every request's first blocks are the same
     physical ids with the same contents (refcount = num_reqs).
+    ``n_src`` (default n_max): blocks each request holds, all full; more than
+    n_max is a cache past the cap (e.g. a long prompt).
     """
     geom = Geometry(num_layers, num_kv_heads, num_q_heads, head_dim, block_size, num_blocks, dtype)
     rng = np.random.default_rng(seed)
     R, H, Hq, d, b = num_reqs, num_kv_heads, num_q_heads, head_dim, block_size
     P = shared_prefix_blocks
-    need = P + R * (n_max - P)
+    nb_req = n_max if n_src is None else int(n_src)
+    if nb_req < n_max:
+        raise ValueError("n_src must be >= n_max")
+    need = P + R * (nb_req - P)
     if need > num_blocks:
         raise ValueError(f"pool of {num_blocks} blocks cannot hold {need}")
     perm = rng.permutation(num_blocks).astype(np.int32)
-    tables = np.empty((R, n_max), dtype=np.int32)
+    tables = np.empty((R, nb_req), dtype=np.int32)
     tables[:, :P] = perm[:P]
-    tables[:, P:] = perm[P:need].reshape(R, n_max - P)
+    tables[:, P:] = perm[P:need].reshape(R, nb_req - P)
     refcounts = np.zeros(num_blocks, dtype=np.int32)
     np.add.at(refcounts, tables.reshape(-1), 1)
 
-    T = n_max * b
+    T = nb_req * b
     k_pool, v_pool, wq, qn, kn, vn = [], [], [], [], [], []
     for layer in range(num_layers):
         sigma = np.ones(H)
@@ -149,7 +159,7 @@ def make_case(name: str, seed: int, *, num_reqs: int, num_layers: int, num_kv_he
         shared_k = shared_v = None
         for r in range(R):
             if key_kind == "iid":
-                k = rng.standard_normal((n_max, H, b, d))
+                k = rng.standard_normal((nb_req, H, b, d))
             elif key_kind == "ar1":
                 eps = rng.standard_normal((H, T, d))
                 k_lin = np.empty_like(eps)
@@ -161,11 +171,11 @@ def make_case(name: str, seed: int, *, num_reqs: int, num_layers: int, num_kv_he
                     n_pl = int(round(planted_frac * H * T))
                     idx = rng.choice(H * T, size=n_pl, replace=False)
                     k_lin.reshape(H * T, d)[idx] *= planted_scale
-                k = k_lin.reshape(H, n_max, b, d).transpose(1, 0, 2, 3)
+                k = k_lin.reshape(H, nb_req, b, d).transpose(1, 0, 2, 3)
             else:
                 raise ValueError(key_kind)
             k = k * sigma[None, :, None, None]
-            v = rng.standard_normal((n_max, H, b, d))
+            v = rng.standard_normal((nb_req, H, b, d))
             if P:
                 if shared_k is None:
                     shared_k, shared_v = k[:P].copy(), v[:P].copy()

@@ -358,6 +358,60 @@ def test_plan_shared_reserved_block_is_replaced():
     assert p.freed.tolist() == [5]
 
 
+def test_plan_over_cap_releases_the_surplus():
+    """A request holding n_src > n_max blocks keeps its first n_max-1 blocks
+    as targets and block n_max-1 as the reserved one; blocks n_max.. are
+    released (freed when this was their last reference)."""
+    # request 0: private blocks; request 1 shares a surplus block with request 2
+    tables = np.array([[3, 4, 5, 6, 7], [8, 9, 10, 11, 12], [13, 14, 15, 16, 12]], dtype=np.int32)
+    rc = np.zeros(20, dtype=np.int32)
+    np.add.at(rc, tables.reshape(-1), 1)
+    p = oracle.plan(rc, tables, 3)
+    assert p.status == oracle.OK
+    assert p.tables.tolist() == [[3, 4, 5, -1, -1], [8, 9, 10, -1, -1], [13, 14, 15, -1, -1]]
+    assert p.dst.tolist() == [[3, 4], [8, 9], [13, 14]]
+    np.testing.assert_array_equal(p.src, tables)
+    # 6, 7, 11, 16 were private: freed; 12 was held twice: freed by request 2
+    assert sorted(p.freed.tolist()) == [6, 7, 11, 12, 16]
+    want = np.zeros(20, dtype=np.int32)
+    np.add.at(want, p.tables[p.tables >= 0], 1)
+    np.testing.assert_array_equal(p.refcounts, want)
+    # a surplus block also held by a request outside the call stays allocated
+    rc_ext = rc.copy()
+    rc_ext[7] += 1
+    p2 = oracle.plan(rc_ext, tables, 3)
+    assert 7 not in p2.freed.tolist() and p2.refcounts[7] == 1
+
+
+def test_over_cap_case_end_to_end_invariants():
+    """n_src = n_max + 2: E = 3b evictions per head, the window kept, the
+    survivors in order in the first n_max-1 blocks, the surplus freed."""
+    c = synth.make_case("over", 28, num_reqs=2, num_layers=1, num_kv_heads=2, num_q_heads=4,
+                        head_dim=16, block_size=4, n_max=5, window=3, num_blocks=24, dtype="f32",
+                        n_src=7)
+    b, n_max, n_src, w = 4, 5, 7, 3
+    T, k_keep = n_src * b, (n_max - 1) * b
+    res = oracle.compress(c)
+    kept = res.kept[0]
+    assert kept.shape == (2, 2, k_keep)
+    for r in range(2):
+        assert sorted(res.plan.freed.tolist()) == sorted(c.tables[:, n_max:].reshape(-1).tolist())
+        for h in range(2):
+            k = kept[r, h]
+            assert np.all(np.diff(k) > 0) and k[-w:].tolist() == list(range(T - w, T))
+            # the evicted candidates never beat a kept one
+            ev = sorted(set(range(T - w)) - set(k.tolist()))
+            assert len(ev) == T - k_keep
+            s = res.s[0][r, h]
+            assert max(s[e] for e in ev) <= min(s[j] for j in k[:-w])
+            # compacted rows are the kept source rows, read through the old table
+            for slot in range(k_keep):
+                j = k[slot]
+                want = c.k_pool[0][c.tables[r, j // b], h, j % b]
+                got = res.k_pool[0][res.plan.tables[r, slot // b], h, slot % b]
+                np.testing.assert_array_equal(got, want)
+
+
 def test_plan_all_or_nothing_errors():
     tables = np.array([[3, 4, 5], [6, 7, 5]], dtype=np.int32)
     rc = np.zeros(8, dtype=np.int32)
