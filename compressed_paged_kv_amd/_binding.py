@@ -83,6 +83,15 @@ def lib() -> ctypes.CDLL:
                                 ctypes.c_int32, _i32p, ctypes.POINTER(_vp), ctypes.POINTER(_vp),
                                 _vp, ctypes.c_size_t, _i32p, _i32p, _vp,
                                 ctypes.POINTER(_Debug)]),
+        "zp_compress_n": (S, [ctypes.POINTER(_KVCache), _vp, ctypes.c_int32, ctypes.c_int32,
+                              ctypes.c_int32, ctypes.c_int32, _i32p, ctypes.POINTER(_vp),
+                              ctypes.POINTER(_vp), _vp, ctypes.c_size_t, _i32p, _i32p, _vp,
+                              ctypes.POINTER(_Debug)]),
+        "zp_compress_plan_n": (S, [_vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _i32p,
+                                   _i32p, _i32p, _i32p, _i32p]),
+        "zp_compress_workspace_bytes_n": (ctypes.c_size_t, [ctypes.POINTER(_KVCache),
+                                                            ctypes.c_int32, ctypes.c_int32,
+                                                            ctypes.c_int32, ctypes.c_int32]),
         "zp_append_kv": (S, [ctypes.POINTER(_KVCache), ctypes.c_int32, ctypes.c_int32, _vp, _vp,
                              _vp, _vp]),
         "zp_paged_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(_KVCache),
@@ -211,16 +220,21 @@ class BlockPool:
 
 
 def compress_plan(pool: BlockPool, n_max: int, tables: np.ndarray):
-    """Host planner (zp_compress_plan).  ``tables`` (int32 [R][n_max]) is
-    rewritten in place; returns (src, dst, freed)."""
+    """Host planner (zp_compress_plan, or zp_compress_plan_n when ``tables``,
+    int32 [R][n_src], has more than n_max columns).  ``tables`` is rewritten
+    in place; returns (src, dst, freed)."""
     assert tables.dtype == np.int32 and tables.flags.c_contiguous
-    R = int(tables.shape[0])
-    src = np.zeros((R, n_max), dtype=np.int32)
+    R, n_src = (int(x) for x in tables.shape)
+    src = np.zeros((R, n_src), dtype=np.int32)
     dst = np.zeros((R, max(n_max - 1, 1)), dtype=np.int32)
-    freed = np.zeros(max(R * n_max, 1), dtype=np.int32)
+    freed = np.zeros(max(R * n_src, 1), dtype=np.int32)
     n = np.zeros(1, dtype=np.int32)
-    _check(lib().zp_compress_plan(pool.handle, n_max, R, _i32(tables), _i32(src), _i32(dst),
-                                  _i32(freed), _i32(n)))
+    if n_src == n_max:
+        _check(lib().zp_compress_plan(pool.handle, n_max, R, _i32(tables), _i32(src), _i32(dst),
+                                      _i32(freed), _i32(n)))
+    else:
+        _check(lib().zp_compress_plan_n(pool.handle, n_src, n_max, R, _i32(tables), _i32(src),
+                                        _i32(dst), _i32(freed), _i32(n)))
     return src, dst, freed[: int(n[0])]
 
 
@@ -260,8 +274,12 @@ class KVCache:
         return ctypes.byref(self.c)
 
 
-def compress_workspace_bytes(cache: KVCache, num_reqs: int, n_max: int, window: int) -> int:
-    n = int(lib().zp_compress_workspace_bytes(cache.ref, num_reqs, n_max, window))
+def compress_workspace_bytes(cache: KVCache, num_reqs: int, n_max: int, window: int,
+                             n_src: Optional[int] = None) -> int:
+    if n_src is None or n_src == n_max:
+        n = int(lib().zp_compress_workspace_bytes(cache.ref, num_reqs, n_max, window))
+    else:
+        n = int(lib().zp_compress_workspace_bytes_n(cache.ref, num_reqs, n_src, n_max, window))
     if n == 0:
         raise ZpError(ZP_ERR_INVALID, last_error())
     return n
@@ -271,22 +289,30 @@ def compress(cache: KVCache, pool: BlockPool, n_max: int, window: int, tables: n
              window_q: List, workspace, stream=None, debug: Optional[dict] = None,
              window_lse: Optional[List] = None) -> np.ndarray:
     """zp_compress (zp_compress_lse when ``window_lse``, per-layer float
-    tensors [R][w][Hq] of the window rows' normalisers, is given).
-    ``tables`` (host int32 [R][n_max]) is rewritten on success; returns the
-    freed block ids."""
+    tensors [R][w][Hq] of the window rows' normalisers, is given;
+    zp_compress_n when ``tables`` has n_src > n_max columns).  ``tables``
+    (host int32 [R][n_src]) is rewritten on success; returns the freed block
+    ids."""
     assert tables.dtype == np.int32 and tables.flags.c_contiguous
-    R = int(tables.shape[0])
+    R, n_src = (int(x) for x in tables.shape)
     wq = (_vp * cache.num_layers)(*[t.data_ptr() for t in window_q])
     wl = None
     if window_lse is not None:
         wl = (_vp * cache.num_layers)(*[t.data_ptr() for t in window_lse])
-    freed = np.zeros(max(R * n_max, 1), dtype=np.int32)
+    freed = np.zeros(max(R * n_src, 1), dtype=np.int32)
     n = np.zeros(1, dtype=np.int32)
     dbg = None
     if debug:
         dbg = _Debug(_dptr(debug.get("importance")), _dptr(debug.get("redundancy")),
                      _dptr(debug.get("score")), _dptr(debug.get("kept")))
-    if wl is None:
+    if n_src != n_max:
+        st = lib().zp_compress_n(cache.ref, pool.handle, n_src, n_max, window, R, _i32(tables),
+                                 ctypes.cast(wq, ctypes.POINTER(_vp)),
+                                 ctypes.cast(wl, ctypes.POINTER(_vp)) if wl is not None else None,
+                                 workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                 _i32(freed), _i32(n), _stream_handle(stream),
+                                 ctypes.byref(dbg) if dbg else None)
+    elif wl is None:
         st = lib().zp_compress(cache.ref, pool.handle, n_max, window, R, _i32(tables),
                                ctypes.cast(wq, ctypes.POINTER(_vp)), workspace.data_ptr(),
                                workspace.numel() * workspace.element_size(), _i32(freed), _i32(n),

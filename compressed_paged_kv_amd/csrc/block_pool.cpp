@@ -56,11 +56,12 @@ void add_pending(zp_block_pool* pool, std::vector<int32_t> ids, hipEvent_t event
   pool->pending.push_back(std::move(p));
 }
 
-zp_status plan_compression(zp_block_pool* pool, int32_t n_max, int32_t num_reqs,
+zp_status plan_compression(zp_block_pool* pool, int32_t n_src, int32_t n_max, int32_t num_reqs,
                            int32_t* block_tables, PlanResult* out) {
   if (!pool) { set_error("pool is NULL"); return ZP_ERR_INVALID; }
   if (pool->poisoned) { set_error("pool unusable after an earlier HIP failure"); return ZP_ERR_STATE; }
   if (n_max < 2) { set_error("n_max must be >= 2 (got %d)", n_max); return ZP_ERR_INVALID; }
+  if (n_src < n_max) { set_error("n_src (%d) must be >= n_max (%d)", n_src, n_max); return ZP_ERR_INVALID; }
   if (num_reqs < 0) { set_error("num_reqs < 0"); return ZP_ERR_INVALID; }
   if (num_reqs > 0 && !block_tables) { set_error("block_tables is NULL"); return ZP_ERR_INVALID; }
   const int32_t nb = pool->num_blocks;
@@ -68,8 +69,8 @@ zp_status plan_compression(zp_block_pool* pool, int32_t n_max, int32_t num_reqs,
   std::vector<int32_t> seen(nb, 0);
   int64_t need = 0;
   for (int32_t r = 0; r < num_reqs; r++) {
-    const int32_t* row = block_tables + (size_t)r * n_max;
-    for (int32_t n = 0; n < n_max; n++) {
+    const int32_t* row = block_tables + (size_t)r * n_src;
+    for (int32_t n = 0; n < n_src; n++) {
       const int32_t id = row[n];
       if (id < 0 || id >= nb) {
         set_error("request %d block %d: id %d out of range [0, %d)", r, n, id, nb);
@@ -88,7 +89,7 @@ zp_status plan_compression(zp_block_pool* pool, int32_t n_max, int32_t num_reqs,
         set_error("id %d listed %d times but its refcount is %d", id, seen[id], rc0[id]);
         return ZP_ERR_INVALID;
       }
-      if (rc0[id] > 1) need++;
+      if (n < n_max && rc0[id] > 1) need++;
     }
   }
   pool->reap();
@@ -99,14 +100,20 @@ zp_status plan_compression(zp_block_pool* pool, int32_t n_max, int32_t num_reqs,
 
   // Commit.  Decisions use the counts from the start of the call, so two
   // requests sharing a block both re-target it and the last one frees it.
+  // Blocks n_max.. are surplus (nl page Methodologie item 1: released).
   const std::vector<int32_t> start_rc = rc0;
-  out->src.assign(block_tables, block_tables + (size_t)num_reqs * n_max);
+  out->src.assign(block_tables, block_tables + (size_t)num_reqs * n_src);
   out->dst.assign((size_t)num_reqs * (n_max - 1), 0);
   out->freed.clear();
   for (int32_t r = 0; r < num_reqs; r++) {
-    int32_t* row = block_tables + (size_t)r * n_max;
-    for (int32_t n = 0; n < n_max; n++) {
+    int32_t* row = block_tables + (size_t)r * n_src;
+    for (int32_t n = 0; n < n_src; n++) {
       const int32_t s = row[n];
+      if (n >= n_max) {
+        if (--pool->rc[s] == 0) out->freed.push_back(s);
+        row[n] = -1;
+        continue;
+      }
       int32_t target = s;
       if (start_rc[s] > 1) {
         target = *pool->free_ids.begin();
@@ -278,13 +285,20 @@ zp_status zp_block_pool_sync(zp_block_pool* pool) {
 zp_status zp_compress_plan(zp_block_pool* pool, int32_t n_max, int32_t num_reqs,
                            int32_t* block_tables, int32_t* src_out, int32_t* dst_out,
                            int32_t* freed_ids, int32_t* num_freed) {
+  return zp_compress_plan_n(pool, n_max, n_max, num_reqs, block_tables, src_out, dst_out,
+                            freed_ids, num_freed);
+}
+
+zp_status zp_compress_plan_n(zp_block_pool* pool, int32_t n_src, int32_t n_max, int32_t num_reqs,
+                             int32_t* block_tables, int32_t* src_out, int32_t* dst_out,
+                             int32_t* freed_ids, int32_t* num_freed) {
   zp::clear_error();
   if (num_reqs > 0 && (!src_out || !dst_out || !freed_ids || !num_freed)) {
     zp::set_error("output pointers must not be NULL");
     return ZP_ERR_INVALID;
   }
   zp::PlanResult plan;
-  zp_status st = zp::plan_compression(pool, n_max, num_reqs, block_tables, &plan);
+  zp_status st = zp::plan_compression(pool, n_src, n_max, num_reqs, block_tables, &plan);
   if (st != ZP_OK) return st;
   if (num_reqs > 0) {
     std::memcpy(src_out, plan.src.data(), plan.src.size() * sizeof(int32_t));

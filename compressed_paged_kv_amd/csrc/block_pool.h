@@ -32,15 +32,17 @@ namespace zp {
 
 // Output of the planner for one compression call.
 struct PlanResult {
-  std::vector<int32_t> src;    // [R][n_max]
+  std::vector<int32_t> src;    // [R][n_src]
   std::vector<int32_t> dst;    // [R][n_max-1]
   std::vector<int32_t> freed;  // ids whose refcount reached 0
 };
 
-// Validate and plan one compression call; on success updates the pool and
-// the tables and returns the plan (freed ids are NOT yet pending: the caller
-// attaches them with add_pending).  On failure nothing changes.
-zp_status plan_compression(zp_block_pool* pool, int32_t n_max, int32_t num_reqs,
+// Validate and plan one compression call of requests holding n_src >= n_max
+// blocks (tables [R][n_src]); on success updates the pool and the tables
+// (n_max new ids, then -1 for the released surplus) and returns the plan
+// (freed ids are NOT yet pending: the caller attaches them with
+// add_pending).  On failure nothing changes.
+zp_status plan_compression(zp_block_pool* pool, int32_t n_src, int32_t n_max, int32_t num_reqs,
                            int32_t* block_tables, PlanResult* out);
 
 // Attach freed ids to a pending group released by `event` (or by a fence

@@ -35,9 +35,8 @@ constexpr int kThreads = 256;
 #define ZP_COMPACT_UNROLL 6  // rows per thread per tile
 #endif
 constexpr int kUnroll = ZP_COMPACT_UNROLL;
-constexpr int kMaxEvicted = 1024;  // E = block_size * (blocks beyond N_max - 1)
-constexpr int kMaxSlots = 8192;    // T = n_max * block_size (the host checks the same)
-constexpr int kMaxBlocks = 512;    // n_max bound for the LDS block tables (T <= 8192, b >= 16)
+constexpr int kMaxSlots = 8192;    // K_keep bound (T = n_src * block_size <= 8192, checked on the host)
+constexpr int kMaxBlocks = 512;    // n_src bound for the LDS block tables (T <= 8192, b >= 16)
 #ifndef ZP_COMPACT_STREAM
 #define ZP_COMPACT_STREAM 2  // 1: non-temporal stores, 2: non-temporal loads and stores
 #endif
@@ -62,7 +61,7 @@ __global__ __launch_bounds__(kThreads, 4) void k_compact(CompactParams p) {
   __shared__ int s_first;
   const int32_t* ev = p.evicted + unit * p.E;
   for (int i = tid; i < p.E; i += kThreads) f[i] = ev[i] - i;
-  for (int n = tid; n < p.n_max; n += kThreads) srcb[n] = p.src[(size_t)r * p.n_max + n];
+  for (int n = tid; n < p.n_src; n += kThreads) srcb[n] = p.src[(size_t)r * p.n_src + n];
   for (int n = tid; n < p.n_max - 1; n += kThreads) dstb[n] = p.dst[(size_t)r * (p.n_max - 1) + n];
   if (tid == 0) s_first = p.E > 0 ? ev[0] : p.K_keep;  // rows below the first eviction stay put
   __syncthreads();
@@ -141,7 +140,8 @@ void launch_vpr(const CompactParams& p, dim3 grid, int block_size, hipStream_t s
 hipError_t launch_compact(const CompactParams& p, int num_layers, int row_bytes, int block_size,
                           hipStream_t s) {
   if (p.R <= 0) return hipSuccess;
-  if (p.E > kMaxEvicted || p.n_max > kMaxBlocks || p.K_keep > kMaxSlots) return hipErrorInvalidValue;
+  if (p.E > kMaxEvicted || p.n_src > kMaxBlocks || p.n_max > p.n_src || p.K_keep > kMaxSlots)
+    return hipErrorInvalidValue;
   if (block_size != 16 && block_size != 32) return hipErrorInvalidValue;
   if (p.K_keep != (p.n_max - 1) * block_size) return hipErrorInvalidValue;
   dim3 grid(2 * p.H, num_layers * p.R);

@@ -267,9 +267,9 @@ __global__ __launch_bounds__(64 * score_waves<RG>(), (kMaxWaves / score_waves<RG
   };
 
   // this wave's blocks are wl + WPG*k; lane k holds the physical id of the k-th
-  const int nbw = p.n_max > wl ? (p.n_max - wl + WPG - 1) / WPG : 0;
-  // (a wave has at most 128 blocks: n_max <= 512 at four waves per row group)
-  const int32_t* tab = p.src + (size_t)r * p.n_max + wl;
+  const int nbw = p.n_src > wl ? (p.n_src - wl + WPG - 1) / WPG : 0;
+  // (a wave has at most 128 blocks: n_src <= 512 at four waves per row group)
+  const int32_t* tab = p.src + (size_t)r * p.n_src + wl;
   const int ids0 = lane < nbw ? tab[WPG * lane] : 0;
   const int ids1 = lane + 64 < nbw ? tab[WPG * (lane + 64)] : 0;
   const int row_off = col * ROWB + grp * 16;
@@ -297,7 +297,7 @@ __global__ __launch_bounds__(64 * score_waves<RG>(), (kMaxWaves / score_waves<RG
   auto ring = [&](auto reverse, auto body) {
     constexpr bool REV = decltype(reverse)::value;
     auto kof = [&](int it) { return REV ? nbw - 1 - it : it; };
-    const int iters = SH ? (p.n_max + WPG - 1) / WPG : nbw;
+    const int iters = SH ? (p.n_src + WPG - 1) / WPG : nbw;
     if (iters == 0) return;
     uint4 kb[kPrefetch][FL];
     // the prologue keeps slot order (the scheduler may not interleave the
@@ -373,7 +373,7 @@ __global__ __launch_bounds__(64 * score_waves<RG>(), (kMaxWaves / score_waves<RG
       }
     ring(BoolC<false>{}, [&](int k, const uint4 (&kt)[NST][NV]) {
       const int n = wl + WPG * k;
-      const bool last = n == p.n_max - 1;  // only the last block meets the causal limit
+      const bool last = n == p.n_src - 1;  // only the last block meets the causal limit
 #pragma unroll
       for (int st = 0; st < NST; st++) {
         const int j = n * B + st * 16 + col;
@@ -466,7 +466,7 @@ __global__ __launch_bounds__(64 * score_waves<RG>(), (kMaxWaves / score_waves<RG
   };
   ring(BoolC<kReversePass2>{}, [&](int k, const uint4 (&kt)[NST][NV]) {
     const int n = wl + WPG * k;
-    const bool last = n == p.n_max - 1;
+    const bool last = n == p.n_src - 1;
     float A[NST];
 #pragma unroll
     for (int st = 0; st < NST; st++) {

@@ -26,6 +26,9 @@ constexpr int kPtrsPerLayer = 4;
 // largest cached length the in-LDS scoring and selection handle.
 constexpr int kMaxScoreRows = 128;
 constexpr int kMaxScoreSlots = 8192;
+// Largest eviction count per (layer, request, head) the compaction's LDS list
+// holds: E = block_size * (n_src - n_max + 1).
+constexpr int kMaxEvicted = 1024;
 // Paged decode: threads per workgroup, and the workgroup count below which
 // a request's block list is split over several workgroups.
 #ifndef ZP_DECODE_THREADS
@@ -39,22 +42,22 @@ constexpr int kDecodeTargetWorkgroups = ZP_DECODE_TARGET_WORKGROUPS;
 
 struct ScoreParams {
   void* const* layer_ptrs;  // device [L][kPtrsPerLayer]
-  const int32_t* src;       // device [R][n_max]
+  const int32_t* src;       // device [R][n_src]: the request's blocks, n_src >= n_max
   int32_t* evicted;         // [L*R*H][E], ascending
   float* dbg_importance;    // optional [L*R*H][T]
   float* dbg_redundancy;    // optional [L*R*H][T]
   float* dbg_score;         // optional [L*R*H][T]
   int32_t* dbg_kept;        // optional [L*R*H][K_keep]
-  int32_t R, H, Hq, G, w, n_max, T, C, E, K_keep, rows;
+  int32_t R, H, Hq, G, w, n_src, T, C, E, K_keep, rows;  // T = n_src * b
   float scale_log2;  // log2(e) / sqrt(d)
 };
 
 struct CompactParams {
   void* const* layer_ptrs;  // device [L][kPtrsPerLayer]
-  const int32_t* src;       // device [R][n_max]
+  const int32_t* src;       // device [R][n_src]
   const int32_t* dst;       // device [R][n_max-1]
   const int32_t* evicted;   // [L*R*H][E]
-  int32_t R, H, n_max, E, K_keep;
+  int32_t R, H, n_src, n_max, E, K_keep;
 };
 
 struct DecodeParams {

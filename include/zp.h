@@ -144,8 +144,26 @@ zp_status zp_compress_plan(zp_block_pool* pool, int32_t n_max, int32_t num_reqs,
                            int32_t* block_tables, int32_t* src_out, int32_t* dst_out,
                            int32_t* freed_ids, int32_t* num_freed);
 
+/* zp_compress_plan for requests that hold n_src >= n_max full blocks: a
+ * cache past the cap (a prompt longer than the budget, or a chunk of one)
+ * is compressed to the same n_max-block shape, and its surplus blocks are
+ * released (nl page Methodologie item 1: the surplus blocks are freed).
+ * Blocks 0..n_max-2 become targets and block n_max-1 the reserved block as
+ * in zp_compress_plan; for blocks n_max..n_src-1 the request drops its
+ * reference (freed when it was the last).
+ * block_tables: HOST int32 [num_reqs][n_src]; on success each row holds
+ *               the n_max new ids followed by n_src-n_max entries of -1.
+ * src_out:      HOST int32 [num_reqs][n_src].
+ * dst_out:      HOST int32 [num_reqs][n_max-1].
+ * freed_ids:    HOST int32, capacity num_reqs*n_src.
+ * Rejected as zp_compress_plan, and n_src < n_max. */
+zp_status zp_compress_plan_n(zp_block_pool* pool, int32_t n_src, int32_t n_max, int32_t num_reqs,
+                             int32_t* block_tables, int32_t* src_out, int32_t* dst_out,
+                             int32_t* freed_ids, int32_t* num_freed);
+
 /* Optional device outputs of zp_compress for checking (any may be NULL).
- * T = n_max*block_size, K_keep = (n_max-1)*block_size. */
+ * T = n_src*block_size (n_src = n_max for zp_compress and zp_compress_lse),
+ * K_keep = (n_max-1)*block_size. */
 typedef struct zp_compress_debug {
   float* importance;  /* [L][R][H][T]: observation-window importance A */
   float* redundancy;  /* [L][R][H][T]: Lightning Redundancy Score R */
@@ -153,9 +171,12 @@ typedef struct zp_compress_debug {
   int32_t* kept;      /* [L][R][H][K_keep]: surviving old slots, ascending */
 } zp_compress_debug;
 
-/* Device workspace (caller-owned) needed by zp_compress. */
+/* Device workspace (caller-owned) needed by zp_compress / zp_compress_lse,
+ * and by zp_compress_n with n_src source blocks (0 on invalid arguments). */
 size_t zp_compress_workspace_bytes(const zp_kv_cache* cache, int32_t num_reqs, int32_t n_max,
                                    int32_t window);
+size_t zp_compress_workspace_bytes_n(const zp_kv_cache* cache, int32_t num_reqs, int32_t n_src,
+                                     int32_t n_max, int32_t window);
 
 /* ------------------------------------------------------------------------
  * zp_compress: one compression call over every layer for num_reqs requests
@@ -221,6 +242,27 @@ zp_status zp_compress_lse(const zp_kv_cache* cache, zp_block_pool* pool, int32_t
                           const void* const* window_q, const void* const* window_lse,
                           void* workspace, size_t workspace_bytes, int32_t* freed_ids,
                           int32_t* num_freed, void* stream, const zp_compress_debug* debug);
+
+/* ------------------------------------------------------------------------
+ * zp_compress_n: zp_compress_lse for requests that each hold n_src >= n_max
+ * full blocks (a cache past the cap: a long prompt, or a prefill chunk).
+ * T = n_src*b slots are scored as in zp_compress (window = the last w
+ * slots), E = (n_src - n_max + 1)*b candidates per (layer, head) are
+ * evicted, and the K_keep = (n_max-1)*b survivors move in order into the
+ * first n_max-1 blocks; the plan is zp_compress_plan_n's (surplus blocks
+ * released once the GPU work is done).
+ * block_tables: HOST int32 [num_reqs][n_src], rewritten as by
+ *               zp_compress_plan_n.
+ * window_lse:   as zp_compress_lse (may be NULL).
+ * freed_ids:    HOST int32, capacity num_reqs*n_src.
+ * Rejects everything zp_compress rejects, plus n_src < n_max, n_src > 512,
+ * n_src*b > 8192 and more than 1024 evictions per head.
+ * ---------------------------------------------------------------------- */
+zp_status zp_compress_n(const zp_kv_cache* cache, zp_block_pool* pool, int32_t n_src,
+                        int32_t n_max, int32_t window, int32_t num_reqs, int32_t* block_tables,
+                        const void* const* window_q, const void* const* window_lse,
+                        void* workspace, size_t workspace_bytes, int32_t* freed_ids,
+                        int32_t* num_freed, void* stream, const zp_compress_debug* debug);
 
 /* ------------------------------------------------------------------------
  * zp_append_kv: write one new token per request into layer `layer`.

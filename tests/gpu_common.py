@@ -58,10 +58,10 @@ def window_lse_on_gpu(cache, case, kp_tensors, wq_tensors, device="cuda"):
     of query i over slots 0..T-w+i, written to row r*w + i of a [R*w][Hq]
     buffer per layer (returned as [R][w][Hq] views)."""
     g = case.geom
-    R, w, n_max, b = case.num_reqs, case.window, case.n_max, g.block_size
-    T = n_max * b
+    R, w, n_src, b = case.num_reqs, case.window, case.n_src, g.block_size
+    T = n_src * b
     tab_t = torch.from_numpy(np.ascontiguousarray(case.tables)).to(device)
-    dws = torch.empty(max(zp.paged_decode_workspace_bytes(cache, R, n_max), 16),
+    dws = torch.empty(max(zp.paged_decode_workspace_bytes(cache, R, n_src), 16),
                       dtype=torch.uint8, device=device)
     out = torch.empty((R, g.num_q_heads, g.head_dim), dtype=torch.float32, device=device)
     res = []
@@ -84,16 +84,16 @@ def run_case(case, device="cuda", decode=True, recorded_lse=False) -> GpuRun:
     self-contained two-pass scoring."""
     g = case.geom
     L, H, b, n_max, w = g.num_layers, g.num_kv_heads, g.block_size, case.n_max, case.window
-    R = case.num_reqs
-    T, k_keep = n_max * b, (n_max - 1) * b
+    R, n_src = case.num_reqs, case.n_src
+    T, k_keep = n_src * b, (n_max - 1) * b
     kp = [to_tensor(x, device) for x in case.k_pool]
     vp = [to_tensor(x, device) for x in case.v_pool]
     wq = [to_tensor(x, device) for x in case.window_q]
     cache = zp.KVCache(kp, vp, g.num_q_heads)
     pool = zp.BlockPool.from_refcounts(case.refcounts)
     tables = case.tables.copy()
-    ws = torch.empty(zp.compress_workspace_bytes(cache, R, n_max, w), dtype=torch.uint8,
-                     device=device)
+    ws = torch.empty(zp.compress_workspace_bytes(cache, R, n_max, w, n_src=n_src),
+                     dtype=torch.uint8, device=device)
     dbg = dict(importance=torch.full((L, R, H, T), float("nan"), device=device),
                redundancy=torch.full((L, R, H, T), float("nan"), device=device),
                score=torch.full((L, R, H, T), float("nan"), device=device),
@@ -109,7 +109,7 @@ def run_case(case, device="cuda", decode=True, recorded_lse=False) -> GpuRun:
     if decode:
         slot = tables[:, k_keep // b] * b + k_keep % b
         slot_t = torch.from_numpy(slot.astype(np.int32)).to(device)
-        tab_t = torch.from_numpy(tables).to(device)
+        tab_t = torch.from_numpy(np.ascontiguousarray(tables[:, :n_max])).to(device)
         seq = torch.full((R,), k_keep + 1, dtype=torch.int32, device=device)
         dws_bytes = zp.paged_decode_workspace_bytes(cache, R, n_max)
         dws = torch.empty(max(dws_bytes, 16), dtype=torch.uint8, device=device)
@@ -144,7 +144,7 @@ def check_case(case, run: GpuRun, *, check_decode=True, layers=None) -> dict:
     Returns a few statistics for the log."""
     g = case.geom
     b, n_max, w = g.block_size, case.n_max, case.window
-    T, k_keep = n_max * b, (n_max - 1) * b
+    T, k_keep = case.n_src * b, (n_max - 1) * b
     C, k_sel = T - w, k_keep - w
     layers = list(range(g.num_layers)) if layers is None else layers
     ref = oracle.compress(case, layers=layers, with_pools=False)
@@ -204,7 +204,8 @@ def check_case(case, run: GpuRun, *, check_decode=True, layers=None) -> dict:
             oracle.append(kp, vp, case.k_new[layer], case.v_new[layer], slot)
             assert np.array_equal(words(run.appended_k[layer]), words(kp))
             assert np.array_equal(words(run.appended_v[layer]), words(vp))
-            want = oracle.decode(kp, vp, case.q_new[layer], run.tables, seq,
+            want = oracle.decode(kp, vp, case.q_new[layer],
+                                 np.ascontiguousarray(run.tables[:, :n_max]), seq,
                                  num_q_heads=g.num_q_heads)
             err = np.abs(run.out[layer] - want)
             assert np.isfinite(run.out[layer]).all()

@@ -66,6 +66,17 @@ CASES = {
                                           n_max=300, num_blocks=310),
     "bf16_long_200_blocks_rows128": lambda: _case("r10", 213, num_reqs=1, num_kv_heads=1,
                                                   num_q_heads=8, n_max=200, num_blocks=210),
+    # caches past the cap (n_src > n_max): E = (n_src - n_max + 1) b evictions per
+    # head (above the small-E sizes), surplus blocks released; one with a
+    # shared prefix and two layers, one at b=32 with two row groups
+    "over_cap_bf16_3_extra": lambda: _case("o1", 214, num_reqs=3, n_max=12, n_src=15,
+                                           num_blocks=64),
+    "over_cap_prefix_2layers": lambda: _case("o2", 215, num_reqs=3, num_layers=2, n_max=10,
+                                             n_src=16, num_blocks=80, shared_prefix_blocks=2),
+    "over_cap_b32_rows128": lambda: _case("o3", 216, head_dim=64, block_size=32, window=32,
+                                          num_q_heads=8, n_max=8, n_src=20, num_blocks=48),
+    "over_cap_f32_d64_many": lambda: _case("o4", 217, dtype="f32", head_dim=64, n_max=6,
+                                           n_src=60, num_blocks=130),
 }
 
 
