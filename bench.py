@@ -166,7 +166,7 @@ def summarize(kt_dir: str, fetch_dir: str, write_dir: str) -> int:
 
 
 WORKLOADS = ("qwen3_8b_layer_budget2048", "structured_b32_budget4096", "mix_qwen3_8b_36layers",
-             "shared_prefix_32req_32layers")
+             "shared_prefix_32req_32layers", "over_cap_qwen3_8b_prompt2560")
 
 
 def _kernel_rows(prof: dict, alg: dict, flops: dict) -> list:
@@ -188,16 +188,19 @@ def _kernel_rows(prof: dict, alg: dict, flops: dict) -> list:
 
 
 def _alg_bytes(R_c, R_d, L, H, Hq, d, b, n_max, w, moved_rows, dec_tokens, eb=2, nsplit=0,
-               append_rows=None):
+               append_rows=None, n_max_keep=None):
     """Algorithmic bytes (and MFMA flops) per launch of each phase: what the
-    method must move or compute, not the kernels' own traffic."""
+    method must move or compute, not the kernels' own traffic.  ``n_max`` is
+    the number of source blocks; ``n_max_keep`` the cap when it is lower."""
     T, kv_row = n_max * b, d * eb
+    n_keep = n_max if n_max_keep is None else n_max_keep
+    E = T - (n_keep - 1) * b
     alg = {
-        "upload": 2 * (R_c * n_max * 4 + R_c * (n_max - 1) * 4),
+        "upload": 2 * (R_c * n_max * 4 + R_c * (n_keep - 1) * 4),
         # K read once, the window queries, the evicted lists (the kernel reads
         # K twice -- the softmax needs each row's statistics before any
         # probability -- which is traffic, not algorithmic bytes)
-        "score": L * (R_c * H * T * kv_row + R_c * w * Hq * kv_row + R_c * H * b * 4),
+        "score": L * (R_c * H * T * kv_row + R_c * w * Hq * kv_row + R_c * H * E * 4),
         "compact": moved_rows * kv_row * 2 * 2,
         "append": (R_d if append_rows is None else append_rows) * H * kv_row * 2 * 2,
         "decode": dec_tokens * H * kv_row * 2 + R_d * Hq * kv_row,
@@ -561,6 +564,86 @@ def run_mix(args):
     }
 
 
+def run_over_cap(args):
+    """64 requests, each a 2560-token prompt (160 full blocks) past the
+    2048-token budget, compressed to 127 blocks + the reserved one
+    (zp_compress_n): E = 528 evictions per (request, head), 32 surplus blocks
+    released per request.  Before every step the blocks are restored from a
+    pristine copy, the tables and a fresh pool object from the originals
+    (all outside the events), so each step compresses the same fresh prompt;
+    the step time is between events recorded around the call on an idle
+    stream, so it includes the host plan and the launches (reported apart
+    from the kernels' own time)."""
+    import numpy as np
+    import torch
+    import compressed_paged_kv_amd as zp
+    from synth.device_gen import case_over_cap_device
+    dev = torch.device("cuda:0")
+    log("generating 64 prompts of 2560 tokens (Qwen3-8B layer shape) on the device")
+    case = case_over_cap_device(dev)
+    g = case.geom
+    H, Hq, d, b = g.num_kv_heads, g.num_q_heads, g.head_dim, g.block_size
+    n_max, n_src, w, R = case.n_max, case.n_src, case.window, case.num_reqs
+    k_keep, T = (n_max - 1) * b, n_src * b
+    cache = zp.KVCache(case.k_pool, case.v_pool, Hq)
+    ids = torch.from_numpy(case.tables.reshape(-1).astype(np.int64)).to(dev)
+    k0, v0 = case.k_pool[0].index_select(0, ids), case.v_pool[0].index_select(0, ids)
+    ws = torch.empty(zp.compress_workspace_bytes(cache, R, n_max, w, n_src=n_src),
+                     dtype=torch.uint8, device=dev)
+    e0, e1 = torch.cuda.Event(True), torch.cuda.Event(True)
+
+    def restore():
+        case.k_pool[0].index_copy_(0, ids, k0)
+        case.v_pool[0].index_copy_(0, ids, v0)
+
+    kept = torch.empty((1, R, H, k_keep), dtype=torch.int32, device=dev)
+    restore()
+    pool = zp.BlockPool.from_refcounts(case.refcounts)
+    tables = case.tables.copy()
+    freed = zp.compress(cache, pool, n_max, w, tables, case.window_q, ws, debug={"kept": kept})
+    torch.cuda.synchronize()
+    moved = int((kept[0] != torch.arange(k_keep, dtype=torch.int32, device=dev)).sum().item())
+    n_freed = int(freed.size)
+    times = []
+    zp.profile_enable(True)
+    zp.profile_read()
+    for i in range(args.warmup + args.steps):
+        restore()
+        pool = zp.BlockPool.from_refcounts(case.refcounts)
+        tables = case.tables.copy()
+        torch.cuda.synchronize()
+        if i == args.warmup:
+            zp.profile_read()
+        e0.record()
+        zp.compress(cache, pool, n_max, w, tables, case.window_q, ws)
+        e1.record()
+        torch.cuda.synchronize()
+        if i >= args.warmup:
+            times.append(e0.elapsed_time(e1))
+    prof = zp.profile_read()
+    zp.profile_enable(False)
+    t_c = float(np.median(times))
+    gpu_us = sum(k["avg_us"] for k in _kernel_rows(prof, {}, {})
+                 if k["phase"] in ("upload", "score", "compact"))
+    alg, flops = _alg_bytes(R, 0, 1, H, Hq, d, b, n_src, w, moved, 0, n_max_keep=n_max)
+    kernels = [k for k in _kernel_rows(prof, alg, flops) if k["phase"] in ("upload", "score", "compact")]
+    comp_bytes = alg["upload"] + alg["score"] + alg["compact"]
+    return {
+        "metric": METRIC, "value": round(R / (t_c * 1e-3), 1), "unit": "compressions/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(t_c, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "over_cap_qwen3_8b_prompt2560", "requests": R, "layers": 1,
+                   "kv_heads": H, "q_heads": Hq, "head_dim": d, "block_size": b, "n_src": n_src,
+                   "n_max": n_max, "window": w, "pool_blocks": g.num_blocks},
+        "evicted_per_head": T - k_keep, "moved_rows": moved, "freed_blocks": n_freed,
+        "gpu_us": round(gpu_us, 2),
+        "host_plan_and_launch_us": round(t_c * 1e3 - gpu_us, 2),
+        "compress_hbm_frac": round(comp_bytes / (t_c * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "kernels": kernels,
+    }
+
+
 def run_shared_prefix(args):
     """32 requests x 32 layers sharing a 32-block prefix: every compression
     re-targets the shared positions into new blocks (1024 allocations) and
@@ -670,6 +753,8 @@ def main() -> int:
         result = run_mix(args)
     elif args.workload == "shared_prefix_32req_32layers":
         result = run_shared_prefix(args)
+    elif args.workload == "over_cap_qwen3_8b_prompt2560":
+        result = run_over_cap(args)
     elif args.workload == "structured_b32_budget4096":
         from synth.device_gen import case_structured_device
         log("generating the structured b=32 workload on the device (512 requests, budget 4096)")

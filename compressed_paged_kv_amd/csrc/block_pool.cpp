@@ -67,6 +67,7 @@ zp_status plan_compression(zp_block_pool* pool, int32_t n_src, int32_t n_max, in
   const int32_t nb = pool->num_blocks;
   const std::vector<int32_t>& rc0 = pool->rc;  // counts at the start of the call
   std::vector<int32_t> seen(nb, 0);
+  std::vector<int32_t> last_row(nb, -1);  // last request whose table held the id
   int64_t need = 0;
   for (int32_t r = 0; r < num_reqs; r++) {
     const int32_t* row = block_tables + (size_t)r * n_src;
@@ -80,11 +81,11 @@ zp_status plan_compression(zp_block_pool* pool, int32_t n_src, int32_t n_max, in
         set_error("request %d block %d: id %d is not allocated", r, n, id);
         return ZP_ERR_INVALID;
       }
-      for (int32_t m = 0; m < n; m++)
-        if (row[m] == id) {
-          set_error("request %d: id %d appears twice in its table", r, id);
-          return ZP_ERR_INVALID;
-        }
+      if (last_row[id] == r) {
+        set_error("request %d: id %d appears twice in its table", r, id);
+        return ZP_ERR_INVALID;
+      }
+      last_row[id] = r;
       if (++seen[id] > rc0[id]) {
         set_error("id %d listed %d times but its refcount is %d", id, seen[id], rc0[id]);
         return ZP_ERR_INVALID;

@@ -30,7 +30,7 @@ class DeviceCase:
     geom: Geometry
     n_max: int
     window: int
-    tables: np.ndarray        # int32 [R][n_max] physical block ids (host)
+    tables: np.ndarray        # int32 [R][n_src] physical block ids (host), n_src >= n_max
     refcounts: np.ndarray     # int32 [num_blocks] (host)
     seq_lens: np.ndarray      # int32 [R] cached tokens before the pending one
     k_pool: List[torch.Tensor] = field(default_factory=list)  # per layer [nb][H][b][d]
@@ -44,6 +44,10 @@ class DeviceCase:
     @property
     def num_reqs(self) -> int:
         return int(self.tables.shape[0])
+
+    @property
+    def n_src(self) -> int:
+        return int(self.tables.shape[1])
 
 
 def _tdtype(dtype: str):
@@ -74,25 +78,28 @@ def make_device_case(name: str, seed: int, device, *, num_reqs: int, num_layers:
                      key_scale_range: Optional[tuple] = (0.5, 2.0), shared_prefix_blocks: int = 0,
                      key_kind: str = "iid", ar_rho: float = 0.9, planted_frac: float = 0.0,
                      planted_scale: float = 8.0, seq_lens: Optional[np.ndarray] = None,
-                     chunk_reqs: int = 32) -> DeviceCase:
-    """Every request holds n_max blocks (the first ``shared_prefix_blocks`` of
-    them shared by all requests); ``seq_lens`` (default n_max * block_size)
-    says how many of its slots are cached."""
+                     chunk_reqs: int = 32, n_src: Optional[int] = None) -> DeviceCase:
+    """Every request holds n_src (default n_max) blocks, the first
+    ``shared_prefix_blocks`` of them shared by all requests; ``seq_lens``
+    (default n_src * block_size) says how many of its slots are cached."""
     geom = Geometry(num_layers, num_kv_heads, num_q_heads, head_dim, block_size, num_blocks, dtype)
     R, H, Hq, d, b = num_reqs, num_kv_heads, num_q_heads, head_dim, block_size
     P = shared_prefix_blocks
-    need = P + R * (n_max - P)
+    nb_req = n_max if n_src is None else int(n_src)
+    if nb_req < n_max:
+        raise ValueError("n_src must be >= n_max")
+    need = P + R * (nb_req - P)
     if need > num_blocks:
         raise ValueError(f"pool of {num_blocks} blocks cannot hold {need}")
     rng = np.random.default_rng(seed)
     perm = rng.permutation(num_blocks).astype(np.int32)
-    tables = np.empty((R, n_max), dtype=np.int32)
+    tables = np.empty((R, nb_req), dtype=np.int32)
     tables[:, :P] = perm[:P]
-    tables[:, P:] = perm[P:need].reshape(R, n_max - P)
+    tables[:, P:] = perm[P:need].reshape(R, nb_req - P)
     refcounts = np.zeros(num_blocks, dtype=np.int32)
     np.add.at(refcounts, tables.reshape(-1), 1)
     if seq_lens is None:
-        seq_lens = np.full(R, n_max * b, dtype=np.int32)
+        seq_lens = np.full(R, nb_req * b, dtype=np.int32)
     seq_lens = np.asarray(seq_lens, dtype=np.int32)
 
     gen = torch.Generator(device=device)
@@ -101,7 +108,7 @@ def make_device_case(name: str, seed: int, device, *, num_reqs: int, num_layers:
     used = torch.zeros(num_blocks, dtype=torch.bool, device=device)
     used[torch.from_numpy(tables.reshape(-1).astype(np.int64)).to(device)] = True
     unused = ~used
-    T = n_max * b
+    T = nb_req * b
     case = DeviceCase(name, seed, geom, n_max, window, tables, refcounts, seq_lens)
     for _ in range(num_layers):
         sigma = torch.ones(H, device=device)
@@ -129,7 +136,7 @@ def make_device_case(name: str, seed: int, device, *, num_reqs: int, num_layers:
                         idx = torch.randperm(H * T, generator=gen, device=device)[:n_pl]
                         flat[i, idx] *= planted_scale
                 x = x * sigma[None, :, None, None]
-                blocks = x.view(r1 - r0, H, n_max, b, d).permute(0, 2, 1, 3, 4).to(tdt)
+                blocks = x.view(r1 - r0, H, nb_req, b, d).permute(0, 2, 1, 3, 4).to(tdt)
                 ids = torch.from_numpy(tables[r0:r1].astype(np.int64)).to(device)
                 kp.index_copy_(0, ids.reshape(-1), blocks.reshape(-1, H, b, d))
                 del x, blocks
@@ -177,6 +184,16 @@ def case_shared_prefix_device(device, seed: int = 104, num_reqs: int = 32,
                             num_kv_heads=8, num_q_heads=32, head_dim=128, block_size=16, n_max=128,
                             window=16, num_blocks=8192, key_scale_range=None,
                             shared_prefix_blocks=32)
+
+
+def case_over_cap_device(device, seed: int = 106, num_reqs: int = 64,
+                         n_src: int = 160) -> DeviceCase:
+    """Qwen3-8B shape past the cap: 64 requests each holding a 2560-token
+    prompt (160 full blocks) compressed to budget 2048 (N_max = 128, w = 16);
+    per-head key scale U(0.5, 2); pool 16384."""
+    return make_device_case("over_cap_qwen3_8b", seed, device, num_reqs=num_reqs, num_layers=1,
+                            num_kv_heads=8, num_q_heads=32, head_dim=128, block_size=16, n_max=128,
+                            window=16, num_blocks=16384, n_src=n_src)
 
 
 def case_structured_device(device, seed: int = 105, num_reqs: int = 512) -> DeviceCase:
