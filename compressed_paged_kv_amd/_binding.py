@@ -39,6 +39,28 @@ class _KVCache(ctypes.Structure):
                 ("v_cache", ctypes.POINTER(ctypes.c_void_p))]
 
 
+class _SchedConfig(ctypes.Structure):
+    _fields_ = [("n_max", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("num_query_slots", ctypes.c_int32),
+                ("max_running", ctypes.c_int32)]
+
+
+_i64p_t = ctypes.POINTER(ctypes.c_int64)
+_i32p_t = ctypes.POINTER(ctypes.c_int32)
+
+
+class _SchedStep(ctypes.Structure):
+    _fields_ = [("num_admitted", ctypes.c_int32), ("admitted", _i64p_t),
+                ("num_decode", ctypes.c_int32), ("decode_ids", _i64p_t),
+                ("decode_slot", _i32p_t), ("decode_seq_len", _i32p_t),
+                ("decode_record_row", _i32p_t),
+                ("num_compress", ctypes.c_int32), ("compress_ids", _i64p_t),
+                ("compress_qslot", _i32p_t),
+                ("num_preempted", ctypes.c_int32), ("preempted", _i64p_t),
+                ("num_finished", ctypes.c_int32), ("finished", _i64p_t),
+                ("num_released", ctypes.c_int32)]
+
+
 class _Debug(ctypes.Structure):
     _fields_ = [("importance", ctypes.c_void_p), ("redundancy", ctypes.c_void_p),
                 ("score", ctypes.c_void_p), ("kept", ctypes.c_void_p)]
@@ -104,6 +126,13 @@ def lib() -> ctypes.CDLL:
         "zp_paged_decode_lse": (S, [ctypes.POINTER(_KVCache), ctypes.c_int32, ctypes.c_int32, _vp,
                                     _vp, ctypes.c_int32, _vp, ctypes.c_float, _vp, _vp, _vp,
                                     ctypes.c_int32, _vp, ctypes.c_size_t, _vp]),
+        "zp_sched_create": (S, [_vp, ctypes.POINTER(_SchedConfig), ctypes.POINTER(_vp)]),
+        "zp_sched_destroy": (None, [_vp]),
+        "zp_sched_add": (S, [_vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]),
+        "zp_sched_plan": (S, [_vp, ctypes.POINTER(_SchedStep)]),
+        "zp_sched_tables": (S, [_vp, _i64p_t, ctypes.c_int32, ctypes.c_int32, _i32p, _i32p]),
+        "zp_sched_compress_commit": (S, [_vp, _i32p]),
+        "zp_sched_stats": (S, [_vp, _i32p, _i32p, _i32p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -353,6 +382,67 @@ def paged_decode(cache: KVCache, layer: int, q, tables, seq_lens, scale: float, 
                                      max_blocks, seq_lens.data_ptr(), float(scale), out.data_ptr(),
                                      lse_out.data_ptr(), _dptr(lse_rows), int(lse_out.shape[0]),
                                      ws_ptr, ws_bytes, _stream_handle(stream)))
+
+
+# --------------------------------------------------------------------------- scheduler
+
+class Scheduler:
+    """Hybrid scheduler (zp_sched_*): query slots only for requests in their
+    observation window, preemption of slot-less requests first."""
+
+    def __init__(self, pool: BlockPool, n_max: int, block_size: int, window: int,
+                 num_query_slots: int, max_running: int):
+        self.pool = pool  # keeps the pool alive
+        self.n_max, self.block_size, self.window = n_max, block_size, window
+        cfg = _SchedConfig(n_max, block_size, window, num_query_slots, max_running)
+        h = _vp()
+        _check(lib().zp_sched_create(pool.handle, ctypes.byref(cfg), ctypes.byref(h)))
+        self.handle = h
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _lib is not None:
+            _lib.zp_sched_destroy(self.handle)
+            self.handle = None
+
+    def add(self, req_id: int, prompt_len: int, max_new_tokens: int) -> None:
+        _check(lib().zp_sched_add(self.handle, int(req_id), int(prompt_len), int(max_new_tokens)))
+
+    def plan(self) -> dict:
+        st = _SchedStep()
+        _check(lib().zp_sched_plan(self.handle, ctypes.byref(st)))
+
+        def arr(ptr, n, dt):
+            return np.ctypeslib.as_array(ptr, shape=(n,)).astype(dt).copy() if n else np.zeros(0, dt)
+        return {
+            "admitted": arr(st.admitted, st.num_admitted, np.int64),
+            "decode_ids": arr(st.decode_ids, st.num_decode, np.int64),
+            "decode_slot": arr(st.decode_slot, st.num_decode, np.int32),
+            "decode_seq_len": arr(st.decode_seq_len, st.num_decode, np.int32),
+            "decode_record_row": arr(st.decode_record_row, st.num_decode, np.int32),
+            "compress_ids": arr(st.compress_ids, st.num_compress, np.int64),
+            "compress_qslot": arr(st.compress_qslot, st.num_compress, np.int32),
+            "preempted": arr(st.preempted, st.num_preempted, np.int64),
+            "finished": arr(st.finished, st.num_finished, np.int64),
+            "num_released": int(st.num_released),
+        }
+
+    def tables(self, ids, width: Optional[int] = None):
+        ids = np.ascontiguousarray(ids, dtype=np.int64)
+        width = self.n_max if width is None else int(width)
+        tab = np.zeros((ids.size, width), dtype=np.int32)
+        lens = np.zeros(max(ids.size, 1), dtype=np.int32)
+        _check(lib().zp_sched_tables(self.handle, ids.ctypes.data_as(_i64p_t), int(ids.size), width,
+                                     _i32(tab) if ids.size else None, _i32(lens)))
+        return tab, lens[: ids.size]
+
+    def compress_commit(self, new_tables: np.ndarray) -> None:
+        t = np.ascontiguousarray(new_tables, dtype=np.int32)
+        _check(lib().zp_sched_compress_commit(self.handle, _i32(t) if t.size else None))
+
+    def stats(self) -> dict:
+        w, r, f = (np.zeros(1, dtype=np.int32) for _ in range(3))
+        _check(lib().zp_sched_stats(self.handle, _i32(w), _i32(r), _i32(f)))
+        return {"waiting": int(w[0]), "running": int(r[0]), "free_query_slots": int(f[0])}
 
 
 # --------------------------------------------------------------------------- timing

@@ -316,6 +316,84 @@ zp_status zp_paged_decode_lse(const zp_kv_cache* cache, int32_t layer, int32_t n
                               size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Hybrid scheduler (host object, not thread-safe).
+ *
+ * Requests below the block cap decode without any extra resource; a request
+ * whose next token falls in the observation window [N_max*b - w, N_max*b)
+ * needs a query slot (the storage for the queries -- and, with
+ * zp_paged_decode_lse, the normalisers -- of its last w tokens) and waits
+ * for one when none is free (slots go to the longest-waiting requests
+ * first, then the earliest admitted); at the cap it compresses and rejoins decoding
+ * in the next step; when blocks run out, running requests are preempted,
+ * those without a query slot first (nl page "Technische samenvatting",
+ * Methodologie item 2; ko page "기술 요약", section 2.B), the most recently
+ * admitted first within each class, never one compressing in the step.  A
+ * request that finds no free block waits for the step (blocks given back
+ * become allocatable only after the fence below) and preempts one victim,
+ * possibly itself, unless blocks given back earlier in the step already
+ * cover it.  A preempted request returns its blocks and slot and goes back
+ * to the front of the queue to start over (recompute).  Waiting requests
+ * are admitted in arrival order while their prompt blocks and max_running
+ * allow.
+ *
+ * Blocks a step gives back (finished or preempted requests) reach reference
+ * count 0 but stay pending in the pool until zp_block_pool_fence(), which
+ * the caller calls once the GPU work that last read them has completed.
+ * ---------------------------------------------------------------------- */
+typedef struct zp_sched zp_sched;
+
+typedef struct zp_sched_config {
+  int32_t n_max;           /* block cap per request (N_max) */
+  int32_t block_size;      /* b, 16 or 32 */
+  int32_t window;          /* w, 1..b */
+  int32_t num_query_slots; /* query slots (each holds w rows), >= 1 */
+  int32_t max_running;     /* concurrency cap, >= 1 */
+} zp_sched_config;
+
+/* One step's plan; arrays are owned by the scheduler and valid until the
+ * next zp_sched_plan. */
+typedef struct zp_sched_step {
+  int32_t num_admitted;  /* prefilled this step: prompt in the request's blocks */
+  const int64_t* admitted;
+  int32_t num_decode;    /* decode one token each */
+  const int64_t* decode_ids;
+  const int32_t* decode_slot;        /* physical slot (block*b + offset) of the new token */
+  const int32_t* decode_seq_len;     /* length including the new token */
+  const int32_t* decode_record_row;  /* query-slot row slot*w + i for window position i, or -1 */
+  int32_t num_compress;  /* at the cap: compress this step (zp_sched_tables, then commit) */
+  const int64_t* compress_ids;
+  const int32_t* compress_qslot;     /* their query slots, rows slot*w .. slot*w + w-1 */
+  int32_t num_preempted;
+  const int64_t* preempted;
+  int32_t num_finished;
+  const int64_t* finished;
+  int32_t num_released;  /* blocks now pending in the pool (fence after the GPU work) */
+} zp_sched_step;
+
+/* Rejects n_max < 2, block_size not in {16,32}, window outside [1, b],
+ * num_query_slots < 1, max_running < 1.  The pool is borrowed. */
+zp_status zp_sched_create(zp_block_pool* pool, const zp_sched_config* cfg, zp_sched** out);
+void zp_sched_destroy(zp_sched* sched);
+/* Queue a request; prompt_len in [1, N_max*b - w] (longer prompts are
+ * compressed after prefill with zp_compress_n), max_new_tokens >= 1. */
+zp_status zp_sched_add(zp_sched* sched, int64_t id, int32_t prompt_len, int32_t max_new_tokens);
+/* Plan the next step (see above).  ZP_ERR_STATE if the previous plan's
+ * compressions were not committed; ZP_ERR_NO_BLOCKS if a request needs a
+ * block and no other request can be preempted. */
+zp_status zp_sched_plan(zp_sched* sched, zp_sched_step* out);
+/* Block tables (HOST int32 [n][width], width >= n_max, -1 past a request's
+ * blocks) and lengths (may be NULL) of the given requests. */
+zp_status zp_sched_tables(const zp_sched* sched, const int64_t* ids, int32_t n, int32_t width,
+                          int32_t* tables_out, int32_t* seq_lens_out);
+/* After the step's compression call (zp_compress or zp_compress_lse on
+ * zp_sched_tables(compress_ids, width = n_max), which rewrote those tables):
+ * new_tables HOST int32 [num_compress][n_max]; each request's length
+ * becomes (N_max-1)*b and its query slot is free again. */
+zp_status zp_sched_compress_commit(zp_sched* sched, const int32_t* new_tables);
+zp_status zp_sched_stats(const zp_sched* sched, int32_t* num_waiting, int32_t* num_running,
+                         int32_t* free_query_slots);
+
+/* ------------------------------------------------------------------------
  * Kernel timing.  While enabled, every kernel launch of the calls above is
  * bracketed by HIP events recorded on the caller's stream (a few events per
  * call, no synchronisation).  zp_profile_read() waits for the recorded

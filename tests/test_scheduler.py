@@ -1,0 +1,200 @@
+"""Host tests of the hybrid scheduler (zp_sched_*), no GPU.
+
+The scheduler follows the hybrid scheduling of the Zipage summaries (nl
+page, Methodologie item 2; ko page, section 2.B): query slots only for
+requests that will need compression, preemption of requests without a
+slot first.  Compression calls are replaced by the host planner
+(zp_compress_plan), which rewrites the tables exactly as zp_compress does.
+"""
+import numpy as np
+import pytest
+
+import compressed_paged_kv_amd as zp
+
+
+def _run_compress(pool, sched, plan, n_max):
+    if plan["compress_ids"].size:
+        tab, lens = sched.tables(plan["compress_ids"])
+        assert np.all(lens == n_max * sched.block_size)
+        zp.compress_plan(pool, n_max, tab)
+        sched.compress_commit(tab)
+
+
+def test_config_and_request_validation():
+    pool = zp.BlockPool(16, manual_fence=True)
+    for bad in (dict(n_max=1), dict(block_size=8), dict(window=0), dict(window=17),
+                dict(num_query_slots=0), dict(max_running=0)):
+        kw = dict(n_max=4, block_size=16, window=4, num_query_slots=1, max_running=4)
+        kw.update(bad)
+        with pytest.raises(zp.ZpError):
+            zp.Scheduler(pool, **kw)
+    s = zp.Scheduler(pool, n_max=4, block_size=16, window=4, num_query_slots=1, max_running=4)
+    s.add(1, 60, 5)                       # 60 = 4*16 - 4, the longest prompt
+    with pytest.raises(zp.ZpError):
+        s.add(1, 10, 5)                   # duplicate id
+    with pytest.raises(zp.ZpError):
+        s.add(2, 61, 5)                   # prompt reaching into the window
+    with pytest.raises(zp.ZpError):
+        s.add(3, 10, 0)
+
+
+def test_window_rows_slot_and_compression_cycle():
+    """One request: no slot until its next token is in the window, rows
+    0..w-1 recorded in order, compression at the cap, back to K_keep."""
+    n_max, b, w = 3, 16, 4
+    T = n_max * b
+    pool = zp.BlockPool(8, manual_fence=True)
+    s = zp.Scheduler(pool, n_max=n_max, block_size=b, window=w, num_query_slots=2, max_running=4)
+    s.add(7, 40, 1000)
+    p = s.plan()
+    assert p["admitted"].tolist() == [7]
+    tab, lens = s.tables([7])
+    assert lens.tolist() == [40] and (tab[0, :3] >= 0).all()
+    rows, seen_compress = [], 0
+    for step in range(30):
+        p = s.plan()
+        pool.fence()
+        if p["compress_ids"].size:
+            assert p["decode_ids"].size == 0
+            assert rows == [p["compress_qslot"][0] * w + i for i in range(w)]
+            rows = []
+            seen_compress += 1
+            _run_compress(pool, s, p, n_max)
+            assert s.tables([7])[1].tolist() == [(n_max - 1) * b]
+            assert s.stats()["free_query_slots"] == 2
+            continue
+        assert p["decode_ids"].tolist() == [7]
+        seq = int(p["decode_seq_len"][0])
+        pos = seq - 1
+        row = int(p["decode_record_row"][0])
+        if pos >= T - w:
+            assert row >= 0 and row % w == pos - (T - w)
+            rows.append(row)
+        else:
+            assert row == -1
+        # the new token's slot is in the block holding position pos
+        tab, _ = s.tables([7])
+        assert p["decode_slot"][0] == tab[0, pos // b] * b + pos % b
+    assert seen_compress >= 2
+
+
+def test_query_slots_are_limited_and_waiting_requests_stall():
+    n_max, b, w = 2, 16, 4
+    pool = zp.BlockPool(20, manual_fence=True)
+    s = zp.Scheduler(pool, n_max=n_max, block_size=b, window=w, num_query_slots=1, max_running=4)
+    s.add(0, 28, 100)
+    s.add(1, 28, 100)
+    s.plan()
+    p = s.plan()                            # both decode position 28 (window starts at 28)
+    assert p["decode_ids"].tolist() == [0]  # only one slot: request 1 waits
+    assert p["decode_record_row"].tolist() == [0]
+    for _ in range(3):
+        p = s.plan()
+        assert p["decode_ids"].tolist() == [0]
+    p = s.plan()                            # request 0 at the cap compresses
+    assert p["compress_ids"].tolist() == [0] and p["decode_ids"].tolist() == []
+    _run_compress(pool, s, p, n_max)
+    p = s.plan()                            # the slot is free again: request 1 takes it
+    assert 1 in p["decode_ids"].tolist()
+
+
+def test_preemption_takes_the_last_admitted_slotless_request_possibly_itself():
+    n_max, b, w = 4, 16, 4
+    # 0 (1 block), 1 (1 block), 2 (4 blocks, next token 60 in the window):
+    # the pool is full; 0 needs a block at position 16
+    pool = zp.BlockPool(6, manual_fence=True)
+    s = zp.Scheduler(pool, n_max=n_max, block_size=b, window=w, num_query_slots=1, max_running=4)
+    s.add(0, 16, 100)
+    s.add(1, 10, 100)
+    s.add(2, 60, 100)
+    p = s.plan()
+    assert p["admitted"].tolist() == [0, 1, 2] and pool.num_free() == 0
+    p = s.plan()
+    # 0 waits and preempts 1 (no slot, admitted after 0); 1 drops out; 2 takes
+    # the slot and decodes in its window
+    assert p["preempted"].tolist() == [1]
+    assert p["decode_ids"].tolist() == [2] and p["decode_record_row"].tolist() == [0]
+    pool.fence()
+    p = s.plan()                      # the block 1 gave back goes to 0
+    assert 0 in p["decode_ids"].tolist() and p["preempted"].size == 0
+
+
+def test_preemption_spares_slot_holders_when_a_slotless_request_exists():
+    n_max, b, w = 4, 16, 4
+    # 2 (slot holder, admitted last) and 0 (no slot, admitted first): when 1
+    # needs a block the victim is 1 itself (no slot, admitted after 0), not 2
+    pool = zp.BlockPool(6, manual_fence=True)
+    s = zp.Scheduler(pool, n_max=n_max, block_size=b, window=w, num_query_slots=1, max_running=4)
+    s.add(0, 10, 100)
+    s.add(1, 16, 100)
+    s.add(2, 60, 100)
+    s.plan()
+    p = s.plan()
+    assert p["preempted"].tolist() == [1]
+    assert sorted(p["decode_ids"].tolist()) == [0, 2]
+    # with only slot holders left, the last admitted one goes
+    pool2 = zp.BlockPool(8, manual_fence=True)
+    s2 = zp.Scheduler(pool2, n_max=n_max, block_size=b, window=w, num_query_slots=2,
+                      max_running=4)
+    s2.add(0, 60, 100)
+    s2.add(1, 60, 100)
+    s2.plan()
+    p = s2.plan()                      # both take slots, decode 60
+    assert sorted(p["decode_ids"].tolist()) == [0, 1]
+    for _ in range(3):
+        p = s2.plan()
+    # both at the cap now: compress, then position 48 starts no block... they
+    # reach 64 = N_max*b only via compression; no preemption ever needed
+    assert p["compress_ids"].size == 0 or p["preempted"].size == 0
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_workload_invariants_and_completion(seed):
+    rng = np.random.default_rng(seed)
+    n_max, b, w = int(rng.integers(3, 7)), 16, int(rng.choice([4, 16]))
+    T = n_max * b
+    nblocks = int(rng.integers(3 * n_max, 6 * n_max))
+    S = int(rng.integers(1, 4))
+    pool = zp.BlockPool(nblocks, manual_fence=True)
+    s = zp.Scheduler(pool, n_max=n_max, block_size=b, window=w, num_query_slots=S,
+                     max_running=int(rng.integers(2, 9)))
+    R = 30
+    for i in range(R):
+        s.add(i, int(rng.integers(1, T - w + 1)), int(rng.integers(1, 3 * T)))
+    done, recorded = set(), {}
+    for step in range(20000):
+        p = s.plan()
+        done |= set(p["finished"].tolist())
+        for r in p["preempted"].tolist() + p["finished"].tolist():
+            recorded.pop(r, None)  # their slot is free again
+        live = [int(x) for x in np.concatenate([p["decode_ids"], p["compress_ids"]])]
+        if live:
+            tab, lens = s.tables(live, width=n_max + 2)
+            assert np.all(tab[:, n_max:] == -1)   # never more than n_max blocks
+            for i, r in enumerate(live):
+                nb = int((tab[i] >= 0).sum())
+                assert nb <= n_max
+                assert nb in ((lens[i] + b - 1) // b, n_max)
+        # query-slot rows: recorded in window order, exactly w before compression
+        for r, row, seq in zip(p["decode_ids"].tolist(), p["decode_record_row"].tolist(),
+                               p["decode_seq_len"].tolist()):
+            pos = seq - 1
+            if pos >= T - w:
+                assert row >= 0 and row % w == pos - (T - w) and row // w < S
+                recorded.setdefault(r, []).append(row)
+            else:
+                assert row == -1
+        for r, slot in zip(p["compress_ids"].tolist(), p["compress_qslot"].tolist()):
+            assert recorded.pop(r) == [slot * w + i for i in range(w)]
+        # no two requests record into the same slot at once
+        slots = [v[0] // w for v in recorded.values() if v]
+        assert len(slots) == len(set(slots))
+        _run_compress(pool, s, p, n_max)
+        pool.fence()
+        # every block in use belongs to exactly one table
+        rc = pool.refcounts()
+        assert rc.max() <= 1
+        if len(done) == R:
+            break
+    assert len(done) == R, f"only {len(done)} of {R} finished"
+    assert pool.num_free() == nblocks
