@@ -166,7 +166,8 @@ def summarize(kt_dir: str, fetch_dir: str, write_dir: str) -> int:
 
 
 WORKLOADS = ("qwen3_8b_layer_budget2048", "structured_b32_budget4096", "mix_qwen3_8b_36layers",
-             "shared_prefix_32req_32layers", "over_cap_qwen3_8b_prompt2560")
+             "shared_prefix_32req_32layers", "over_cap_qwen3_8b_prompt2560",
+             "continuous_qwen3_8b_36layers")
 
 
 def _kernel_rows(prof: dict, alg: dict, flops: dict) -> list:
@@ -453,6 +454,160 @@ def run_single_stream(args, workload, cache, pool, tables, wq_sets, q_new, k_new
     else:
         result["cpu_baseline"] = None
     return result
+
+
+def run_continuous(args):
+    """Continuous batching over many steps, driven by the hybrid scheduler:
+    256 requests on the Qwen3-8B shape (36 layers, budget 2048, w = 16) with
+    prompts U[1536, 2032] (so the run reaches the regime where every request
+    compresses once every b steps within a few hundred steps) and generation
+    lengths U[512, 4096] tokens; a finished request is replaced by a new one.  Every step: the scheduler's plan; on
+    stream 1 the append and the paged decode of every decoding request in all
+    36 layers, the decode recording the query and its log-sum-exp into the
+    request's query-slot row while it is in its observation window; on
+    stream 2 the compression of the requests at the cap (zp_compress_lse with
+    the recorded window rows), which rejoin decoding in the next step.  The
+    caches are filled with N(0,1) rows once (a prompt's rows are whatever its
+    blocks hold).  Reported: decode tokens and compressions per second of the
+    whole run, batch sizes, preemptions and slot waits."""
+    import numpy as np
+    import torch
+    import compressed_paged_kv_amd as zp
+    dev = torch.device("cuda:0")
+    L, H, Hq, d, b, n_max, w = 36, 8, 32, 128, 16, 128, 16
+    T, k_keep = n_max * b, (n_max - 1) * b
+    R0, nb, S = 256, 32768, 256
+    rng = np.random.default_rng(107)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(107)
+    log(f"filling {L} layers x 2 pools of {nb} blocks with N(0,1) rows")
+    kp, vp = [], []
+    for _ in range(L):
+        for lst in (kp, vp):
+            t = torch.empty((nb, H, b, d), dtype=torch.bfloat16, device=dev)
+            for c0 in range(0, nb, 4096):
+                t[c0:c0 + 4096] = torch.randn((min(4096, nb - c0), H, b, d), generator=gen,
+                                              device=dev).to(torch.bfloat16)
+            lst.append(t)
+    cache = zp.KVCache(kp, vp, Hq)
+    pool = zp.BlockPool(nb)
+    sched = zp.Scheduler(pool, n_max=n_max, block_size=b, window=w, num_query_slots=S,
+                         max_running=R0)
+    next_id = [0]
+
+    def arrive():
+        sched.add(next_id[0], int(rng.integers(1536, T - w + 1)), int(rng.integers(512, 4097)))
+        next_id[0] += 1
+
+    for _ in range(R0):
+        arrive()
+    # query-slot stores per layer, and rotating decode inputs
+    q_store = [torch.zeros((S * w, Hq, d), dtype=torch.bfloat16, device=dev) for _ in range(L)]
+    lse_store = [torch.zeros((S * w, Hq), dtype=torch.float32, device=dev) for _ in range(L)]
+    NSET = 4
+    q_sets = [torch.randn((NSET, R0, Hq, d), generator=gen, device=dev).to(torch.bfloat16)
+              for _ in range(L)]
+    k_sets = [torch.randn((NSET, R0, H, d), generator=gen, device=dev).to(torch.bfloat16)
+              for _ in range(L)]
+    v_sets = [torch.randn((NSET, R0, H, d), generator=gen, device=dev).to(torch.bfloat16)
+              for _ in range(L)]
+    out = torch.empty((R0, Hq, d), dtype=torch.float32, device=dev)
+    # the decode splits a small batch over more workgroups: size for any batch
+    dws = torch.empty(max(max(zp.paged_decode_workspace_bytes(cache, r, n_max)
+                              for r in range(1, R0 + 1)), 16), dtype=torch.uint8, device=dev)
+    ws = torch.empty(zp.compress_workspace_bytes(cache, S, n_max, w), dtype=torch.uint8,
+                     device=dev)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    scale = 1.0 / float(np.sqrt(d))
+    ev_dec = [torch.cuda.Event() for _ in range(2)]
+    ev_cmp = [torch.cuda.Event() for _ in range(2)]
+    pin_i32 = [torch.empty((4, R0 * n_max), dtype=torch.int32, pin_memory=True) for _ in range(2)]
+    counters = dict(decode_tokens=0, compressions=0, preempted=0, finished=0, steps=0,
+                    decode_batch=0, slot_waits=0, decode_bytes=0)
+
+    def one_step(t: int, count: bool):
+        par = t % 2
+        plan = sched.plan()
+        R_d = int(plan["decode_ids"].size)
+        R_c = int(plan["compress_ids"].size)
+        if count:
+            counters["decode_bytes"] += int(plan["decode_seq_len"].astype(np.int64).sum()) * H * d * 2 * 2 * L
+            counters["decode_tokens"] += R_d
+            counters["compressions"] += R_c * L
+            counters["preempted"] += int(plan["preempted"].size)
+            counters["finished"] += int(plan["finished"].size)
+            counters["decode_batch"] += R_d
+            counters["slot_waits"] += sched.stats()["running"] - R_d - R_c - int(plan["admitted"].size)
+            counters["steps"] += 1
+        for _ in range(int(plan["finished"].size)):
+            arrive()
+        # decode inputs through one pinned staging buffer per parity
+        tab_d, _ = sched.tables(plan["decode_ids"]) if R_d else (np.zeros((0, n_max), np.int32), None)
+        st = pin_i32[par]
+        stv = st.numpy()
+        stv[0, : R_d * n_max] = tab_d.reshape(-1)
+        stv[1, :R_d] = plan["decode_seq_len"]
+        stv[2, :R_d] = plan["decode_slot"]
+        stv[3, :R_d] = plan["decode_record_row"]
+        with torch.cuda.stream(s1):
+            if t > 0:
+                s1.wait_event(ev_cmp[1 - par])  # step t-1's compressions rejoin here
+            if R_d:
+                dv = st.to(dev, non_blocking=True)
+                tab_t = dv[0, : R_d * n_max].view(R_d, n_max)
+                seq_t, slot_t, row_t = dv[1, :R_d], dv[2, :R_d], dv[3, :R_d]
+                k = t % NSET
+                for l in range(L):
+                    zp.append_kv(cache, l, k_sets[l][k, :R_d], v_sets[l][k, :R_d], slot_t, stream=s1)
+                    zp.paged_decode(cache, l, q_sets[l][k, :R_d], tab_t, seq_t, scale, out[:R_d],
+                                    dws, stream=s1, lse_out=lse_store[l], q_out=q_store[l],
+                                    lse_rows=row_t)
+            ev_dec[par].record(s1)
+        with torch.cuda.stream(s2):
+            if R_c:
+                s2.wait_event(ev_dec[1 - par])  # window rows recorded up to step t-1
+                tab_c, _ = sched.tables(plan["compress_ids"])
+                rows = torch.from_numpy(plan["compress_qslot"].astype(np.int64)).to(dev, non_blocking=True)
+                wq = [q_store[l].view(S, w, Hq, d).index_select(0, rows) for l in range(L)]
+                wl = [lse_store[l].view(S, w, Hq).index_select(0, rows) for l in range(L)]
+                zp.compress(cache, pool, n_max, w, tab_c, wq, ws, stream=s2, window_lse=wl)
+                sched.compress_commit(tab_c)
+            ev_cmp[par].record(s2)
+        # blocks given back by this plan were last read by step t-1
+        ev_dec[1 - par].synchronize()
+        ev_cmp[1 - par].synchronize()
+        pool.fence()
+
+    log("warm-up steps")
+    for t in range(args.warmup * 4):
+        one_step(t, False)
+    torch.cuda.synchronize()
+    steps = max(args.steps, 20)
+    log(f"timing {steps} continuous-batching steps")
+    t0 = time.perf_counter()
+    for t in range(args.warmup * 4, args.warmup * 4 + steps):
+        one_step(t, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    c = counters
+    return {
+        "metric": METRIC, "value": round(c["compressions"] / wall, 1), "unit": "compressions/s",
+        "n_gpus": 1, "steps": steps, "warmup": args.warmup * 4,
+        "ms_per_step": round(wall * 1e3 / steps, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "continuous_qwen3_8b_36layers", "requests": R0, "layers": L,
+                   "kv_heads": H, "q_heads": Hq, "head_dim": d, "block_size": b, "n_max": n_max,
+                   "window": w, "pool_blocks": nb, "query_slots": S},
+        "decode_tok_s": round(c["decode_tokens"] / wall, 1),
+        "request_compressions_per_s": round(c["compressions"] / L / wall, 1),
+        "mean_decode_batch": round(c["decode_batch"] / steps, 1),
+        "preempted": c["preempted"], "finished": c["finished"],
+        "slot_or_block_waits_per_step": round(c["slot_waits"] / steps, 2),
+        # K and V read by the decode alone (exact), over the whole run: a lower
+        # bound of the achieved HBM rate (the compressions' traffic is extra)
+        "decode_read_GBs": round(c["decode_bytes"] / wall / 1e9, 1),
+        "decode_read_hbm_frac_lower_bound": round(c["decode_bytes"] / wall / 1e9 / HBM_PEAK_GBS, 4),
+    }
 
 
 def run_mix(args):
@@ -755,6 +910,8 @@ def main() -> int:
         result = run_shared_prefix(args)
     elif args.workload == "over_cap_qwen3_8b_prompt2560":
         result = run_over_cap(args)
+    elif args.workload == "continuous_qwen3_8b_36layers":
+        result = run_continuous(args)
     elif args.workload == "structured_b32_budget4096":
         from synth.device_gen import case_structured_device
         log("generating the structured b=32 workload on the device (512 requests, budget 4096)")

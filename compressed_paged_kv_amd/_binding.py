@@ -124,7 +124,7 @@ def lib() -> ctypes.CDLL:
                                 ctypes.c_int32, _vp, ctypes.c_float, _vp, _vp, ctypes.c_size_t,
                                 _vp]),
         "zp_paged_decode_lse": (S, [ctypes.POINTER(_KVCache), ctypes.c_int32, ctypes.c_int32, _vp,
-                                    _vp, ctypes.c_int32, _vp, ctypes.c_float, _vp, _vp, _vp,
+                                    _vp, ctypes.c_int32, _vp, ctypes.c_float, _vp, _vp, _vp, _vp,
                                     ctypes.c_int32, _vp, ctypes.c_size_t, _vp]),
         "zp_sched_create": (S, [_vp, ctypes.POINTER(_SchedConfig), ctypes.POINTER(_vp)]),
         "zp_sched_destroy": (None, [_vp]),
@@ -367,20 +367,22 @@ def paged_decode_workspace_bytes(cache: KVCache, num_reqs: int, max_blocks: int)
 
 
 def paged_decode(cache: KVCache, layer: int, q, tables, seq_lens, scale: float, out, workspace,
-                 stream=None, lse_out=None, lse_rows=None) -> None:
+                 stream=None, lse_out=None, lse_rows=None, q_out=None) -> None:
     """zp_paged_decode, or zp_paged_decode_lse when ``lse_out`` (float
-    [rows][Hq]) is given; ``lse_rows`` (int32 [R]) maps requests to rows."""
+    [rows][Hq]) or ``q_out`` ([rows][Hq][d], cache dtype) is given;
+    ``lse_rows`` (int32 [R]) maps requests to rows."""
     R, max_blocks = (int(x) for x in tables.shape)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    if lse_out is None:
+    if lse_out is None and q_out is None:
         _check(lib().zp_paged_decode(cache.ref, layer, R, q.data_ptr(), tables.data_ptr(),
                                      max_blocks, seq_lens.data_ptr(), float(scale), out.data_ptr(),
                                      ws_ptr, ws_bytes, _stream_handle(stream)))
         return
+    cap = int((lse_out if lse_out is not None else q_out).shape[0])
     _check(lib().zp_paged_decode_lse(cache.ref, layer, R, q.data_ptr(), tables.data_ptr(),
                                      max_blocks, seq_lens.data_ptr(), float(scale), out.data_ptr(),
-                                     lse_out.data_ptr(), _dptr(lse_rows), int(lse_out.shape[0]),
+                                     _dptr(lse_out), _dptr(q_out), _dptr(lse_rows), cap,
                                      ws_ptr, ws_bytes, _stream_handle(stream)))
 
 

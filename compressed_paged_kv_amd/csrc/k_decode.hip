@@ -150,6 +150,19 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode(DecodeParams p) {
 #pragma unroll
     for (int v = 0; v < NV; v++) q[g][v] = ld16(qp + v * 16 * LPT);
   }
+  // optional record of the query (split 0, wave 0, token lane group 0 hold
+  // the whole row between them)
+  if (p.q_rec && split == 0 && wave == 0 && tok == 0) {
+    const int row = p.lse_rows ? p.lse_rows[r] : r;
+    if (row >= 0 && row < p.lse_cap) {
+#pragma unroll
+      for (int g = 0; g < G; g++) {
+        char* qo = static_cast<char*>(p.q_rec) + ((size_t)row * p.Hq + hq0 + g) * ROW + c * 16;
+#pragma unroll
+        for (int v = 0; v < NV; v++) stg16(qo + v * 16 * LPT, q[g][v]);
+      }
+    }
+  }
   float m[G], l[G], acc[G][NE];
 #pragma unroll
   for (int g = 0; g < G; g++) {

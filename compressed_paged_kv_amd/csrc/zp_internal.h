@@ -69,7 +69,8 @@ struct DecodeParams {
   float* out;               // [R][Hq][d]
   float* partial;           // [R][Hq][nsplit][d + 2]
   float* lse;               // optional [lse_cap][Hq]: natural-log normaliser per query head
-  const int32_t* lse_rows;  // optional [R]: row of lse for request r (default r; < 0 skips)
+  void* q_rec;              // optional [lse_cap][Hq][d]: copy of the query (cache dtype)
+  const int32_t* lse_rows;  // optional [R]: row of lse / q_rec for request r (default r; < 0 skips)
   int32_t R, H, Hq, max_blocks, nsplit, blocks_per_split, num_blocks, lse_cap;
   float scale_log2;
 };

@@ -297,22 +297,26 @@ zp_status zp_paged_decode(const zp_kv_cache* cache, int32_t layer, int32_t num_r
                           size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
- * zp_paged_decode_lse: zp_paged_decode that also returns, per request and
- * query head, the log-sum-exp of the scaled logits,
+ * zp_paged_decode_lse: zp_paged_decode that also records, per request, the
+ * query and, per query head, the log-sum-exp of the scaled logits,
  *   lse[r][hq] = ln sum over j < seq_lens[r] of exp(scale * q.k_j)
- * (-inf for an empty request).  With scale = 1/sqrt(head_dim) this is the
- * normaliser zp_compress_lse takes for a window row.
- * lse_out:      device float [lse_capacity][Hq].
- * lse_rows:     NULL (request r writes row r; then lse_capacity >= num_reqs),
- *               or device int32 [num_reqs]: the row request r writes; rows
- *               outside [0, lse_capacity) are skipped (e.g. -1 for requests
- *               that are not in their window).
+ * (-inf for an empty request), into rows of caller-owned stores -- the
+ * query slots of the hybrid scheduling (nl page Methodologie item 2).  With
+ * scale = 1/sqrt(head_dim), a window row's recorded query and normaliser
+ * are what zp_compress_lse takes.
+ * lse_out:  NULL, or device float [capacity][Hq].
+ * q_out:    NULL, or device [capacity][Hq][head_dim] in the cache dtype
+ *           (16-byte aligned): a copy of q.
+ * rows:     NULL (request r writes row r; then capacity >= num_reqs), or
+ *           device int32 [num_reqs]: the row request r writes; rows outside
+ *           [0, capacity) are skipped (e.g. -1 for requests that are not in
+ *           their window).
  * Other arguments, layouts and errors as zp_paged_decode.
  * ---------------------------------------------------------------------- */
 zp_status zp_paged_decode_lse(const zp_kv_cache* cache, int32_t layer, int32_t num_reqs,
                               const void* q, const int32_t* block_tables, int32_t max_blocks,
                               const int32_t* seq_lens, float scale, float* out, float* lse_out,
-                              const int32_t* lse_rows, int32_t lse_capacity, void* workspace,
+                              void* q_out, const int32_t* rows, int32_t capacity, void* workspace,
                               size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------

@@ -85,11 +85,20 @@ def test_decode_lse_row_map_skips_and_scatters():
                      dtype=torch.uint8, device=dev)
     out = torch.empty((R, H * G, d), device=dev)
     lse = torch.full((10, H * G), float("nan"), device=dev)
-    zp.paged_decode(cache, 0, to_tensor(c.q_new[0], dev), torch.from_numpy(c.tables).to(dev),
+    q = to_tensor(c.q_new[0], dev)
+    q_rec = torch.full((10, H * G, d), float("nan"), dtype=q.dtype, device=dev)
+    zp.paged_decode(cache, 0, q, torch.from_numpy(c.tables).to(dev),
                     torch.from_numpy(seqs).to(dev), 1.0 / np.sqrt(d), out, ws, lse_out=lse,
-                    lse_rows=torch.from_numpy(rows).to(dev))
+                    lse_rows=torch.from_numpy(rows).to(dev), q_out=q_rec)
     torch.cuda.synchronize()
     got = lse.cpu().numpy()
+    # the query is recorded bit for bit in the same rows (the query slots)
+    for rw in range(10):
+        src = [r for r, x in enumerate(rows) if x == rw]
+        if src:
+            assert torch.equal(q_rec[rw].view(torch.int16), q[src[0]].view(torch.int16))
+        else:
+            assert torch.isnan(q_rec[rw].float()).all()
     want = oracle.decode_lse(c.k_pool[0], c.q_new[0], c.tables, seqs, num_q_heads=H * G)
     written = {int(rw): r for r, rw in enumerate(rows) if 0 <= rw < 10}
     for rw in range(10):
