@@ -56,6 +56,8 @@ def _load():
     lib.zpo_decode_lse.restype = None
     lib.zpo_decode_lse.argtypes = [ctypes.c_int32] * 6 + [ctypes.c_void_p] * 2 + [
         _i32p, ctypes.c_int32, _i32p, ctypes.c_double, _f64p]
+    lib.zpo_redundancy_all.restype = None
+    lib.zpo_redundancy_all.argtypes = [ctypes.c_int32] * 6 + [ctypes.c_void_p, _i32p, _f64p]
     _lib = lib
     return lib
 
@@ -216,6 +218,20 @@ def window_lse(kpool: np.ndarray, window_q: np.ndarray, tables: np.ndarray, *, n
         lens = np.full(R, T - window + i + 1, dtype=np.int32)
         out[:, i, :] = decode_lse(kpool, np.ascontiguousarray(window_q[:, i]), tables, lens,
                                   num_q_heads=num_q_heads)
+    return out
+
+
+def redundancy_all(kpool: np.ndarray, tables: np.ndarray) -> np.ndarray:
+    """All-pairs redundancy (mean cosine with every other slot of the
+    sequence) over the T = n_blocks*b slots of each table row: [R][H][T]."""
+    lib = _load()
+    nb, H, b, d = kpool.shape
+    is_bf16 = int(kpool.dtype == np.uint16)
+    tables = np.ascontiguousarray(tables, dtype=np.int32)
+    R, n_blocks = tables.shape
+    out = np.zeros((R, H, n_blocks * b))
+    lib.zpo_redundancy_all(H, d, b, is_bf16, n_blocks, R, _vp(np.ascontiguousarray(kpool)),
+                           _i32(tables), _f64(out))
     return out
 
 

@@ -389,3 +389,44 @@ void zpo_decode_lse(int32_t H, int32_t Hq, int32_t d, int32_t b, int32_t is_bf16
     free(x);
   }
 }
+
+/* ---------------------------------------------------------------------
+ * All-pairs redundancy (the pairwise computation the Lightning Redundancy
+ * Score replaces: O(N^2 b^2) pairs instead of O(N b^2); nl page
+ * Methodologie item 5, ko page section 2.E).  Same reduction as the LRS,
+ * over the whole sequence instead of the block: for request r, head h and
+ * each of the T = n_blocks*b slots j,
+ *   R_all[j] = 1/(T-1) * sum over c != j of cos(k_j, k_c)   (0 for a zero norm).
+ * out: [R][H][T] doubles.
+ * --------------------------------------------------------------------- */
+void zpo_redundancy_all(int32_t H, int32_t d, int32_t b, int32_t is_bf16, int32_t n_blocks,
+                        int32_t R, const void* kpool, const int32_t* tables, double* out) {
+  const int32_t T = n_blocks * b;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t unit = 0; unit < (int64_t)R * H; unit++) {
+    const int32_t r = (int32_t)(unit / H), h = (int32_t)(unit % H);
+    double* K = (double*)malloc((size_t)T * d * sizeof(double));
+    double* nrm = (double*)malloc((size_t)T * sizeof(double));
+    for (int32_t j = 0; j < T; j++) {
+      size_t base = row_index(tables[(size_t)r * n_blocks + j / b], h, j % b, H, b, d);
+      double ss = 0.0;
+      for (int32_t e = 0; e < d; e++) {
+        K[(size_t)j * d + e] = widen(kpool, base + e, is_bf16);
+        ss += K[(size_t)j * d + e] * K[(size_t)j * d + e];
+      }
+      nrm[j] = sqrt(ss);
+    }
+    for (int32_t a = 0; a < T; a++) {
+      double acc = 0.0;
+      for (int32_t c = 0; c < T; c++) {
+        if (c == a || nrm[a] == 0.0 || nrm[c] == 0.0) continue;
+        double dot = 0.0;
+        for (int32_t e = 0; e < d; e++) dot += K[(size_t)a * d + e] * K[(size_t)c * d + e];
+        acc += dot / (nrm[a] * nrm[c]);
+      }
+      out[((size_t)r * H + h) * T + a] = acc / (double)(T - 1);
+    }
+    free(K);
+    free(nrm);
+  }
+}

@@ -230,6 +230,53 @@ def test_lrs_matches_sklearn_and_is_block_local_and_scale_free():
     assert N * b * (b - 1) < (N * b) * (N * b - 1)
 
 
+# ---------------------------------------------------------------- all-pairs redundancy
+
+def test_redundancy_all_closed_form_and_library():
+    """Mean cosine with all other slots equals (u_j . sum_c u_c - 1)/(T-1)
+    with u the unit keys (a different formula), and sklearn's cosine matrix."""
+    from sklearn.metrics.pairwise import cosine_similarity
+    rng = np.random.default_rng(41)
+    R, H, d, b, n = 2, 2, 8, 4, 5
+    T = n * b
+    tables, kpool, _, K, _ = _tiny_case(rng, R=R, H=H, d=d, b=b, n_max=n, w=1, pool=16)
+    got = oracle.redundancy_all(kpool, tables)
+    for r in range(R):
+        for h in range(H):
+            Kl = bf.logical_rows(kpool, tables[r], h, T)
+            U = Kl / np.linalg.norm(Kl, axis=1, keepdims=True)
+            closed = (U @ U.sum(axis=0) - 1.0) / (T - 1)
+            np.testing.assert_allclose(got[r, h], closed, atol=1e-13)
+            C = cosine_similarity(Kl)
+            np.testing.assert_allclose(got[r, h], (C.sum(axis=1) - 1.0) / (T - 1), atol=1e-13)
+
+
+def test_redundancy_all_special_cases_and_block_case():
+    d, b = 6, 4
+    # identical keys -> 1; antipodal halves -> mean of +1 and -1 terms; a
+    # zero key contributes 0 to the others and has 0 itself
+    k = np.arange(1.0, d + 1.0)
+    same = np.broadcast_to(k, (1, 1, 2 * b, d)).copy()
+    tab = np.array([[3, 1]], dtype=np.int32)
+    got = oracle.redundancy_all(synth.pool_from_logical(same, tab, 4, "f32"), tab)
+    np.testing.assert_allclose(got, 1.0, atol=1e-15)
+    anti = same.copy()
+    anti[0, 0, b:] *= -1.0
+    got = oracle.redundancy_all(synth.pool_from_logical(anti, tab, 4, "f32"), tab)
+    np.testing.assert_allclose(got, ((b - 1) - b) / (2 * b - 1), atol=1e-15)
+    zero = same.copy()
+    zero[0, 0, 0] = 0.0
+    got = oracle.redundancy_all(synth.pool_from_logical(zero, tab, 4, "f32"), tab)
+    assert got[0, 0, 0] == 0.0
+    np.testing.assert_allclose(got[0, 0, 1:], (2 * b - 2) / (2 * b - 1), atol=1e-15)
+    # one block: the all-pairs score is the Lightning Redundancy Score
+    rng = np.random.default_rng(42)
+    tables, kpool, q, _, _ = _tiny_case(rng, R=1, H=2, Hq=2, d=8, b=4, n_max=1, w=1, pool=6)
+    _, lrs, _ = oracle.scores(kpool, q, tables, num_kv_heads=2, num_q_heads=2, head_dim=8,
+                              block_size=4, window=1)
+    np.testing.assert_allclose(oracle.redundancy_all(kpool, tables), lrs, atol=1e-14)
+
+
 # ---------------------------------------------------------------- selection
 
 @pytest.mark.parametrize("seed", range(6))
