@@ -436,6 +436,24 @@ def run_single_stream(args, workload, cache, pool, tables, wq_sets, q_new, k_new
         "kernels": kernels,
         "roofline": roofline,
     }
+    # the pairwise redundancy the Lightning Redundancy Score replaces, on the
+    # same cache (every pair of the T slots of each head on MFMA)
+    log("timing the all-pairs redundancy (what the block-local score avoids)")
+    tab_full = torch.from_numpy(np.ascontiguousarray(tables)).to(dev)
+    r_all = torch.empty((R, H, T), dtype=torch.float32, device=dev)
+    for _ in range(2):
+        zp.redundancy_all(cache, 0, tab_full, r_all)
+    torch.cuda.synchronize()
+    zp.profile_enable(True)
+    zp.profile_read()
+    for _ in range(10):
+        zp.redundancy_all(cache, 0, tab_full, r_all)
+    torch.cuda.synchronize()
+    ra_ms, ra_n = zp.profile_read()["redundancy_all"]
+    zp.profile_enable(False)
+    ra_us = ra_ms * 1e3 / ra_n
+    ra_flops = 2.0 * T * T * d * R * H
+    del r_all
     rec_us = {k["phase"]: k["avg_us"] for k in _kernel_rows(rec, alg, flops)}
     rec_comp = sum(rec_us.get(p, 0.0) for p in ("upload", "score", "compact"))
     result["recorded_lse"] = {
@@ -447,6 +465,17 @@ def run_single_stream(args, workload, cache, pool, tables, wq_sets, q_new, k_new
         "compress_per_s": round(R / (rec_comp * 1e-6), 1),
         "score_hbm_frac": round(alg["score"] / (rec_us["score"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         "compress_hbm_frac": round(comp_bytes / (rec_comp * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+    }
+    result["lrs_ablation"] = {
+        "what": "all-pairs redundancy (mean cosine with every other slot, O(N^2 b^2) pairs) "
+                "against the block-local Lightning Redundancy Score (O(N b^2)) the compression "
+                "uses; per launch over all requests and heads",
+        "all_pairs_us": round(ra_us, 2),
+        "all_pairs_gram_flops": ra_flops,
+        "all_pairs_mfma_TFLOPs": round(ra_flops / (ra_us * 1e-6) / 1e12, 1),
+        "all_pairs_mfma_frac": round(ra_flops / (ra_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "lrs_gram_flops": 2.0 * H * n_max * b * b * d * R,
+        "score_kernel_us": per.get("score"),
     }
     if cpu_case is not None and not args.no_cpu_baseline:
         log("cpu baseline (oracle)")

@@ -126,6 +126,8 @@ def lib() -> ctypes.CDLL:
         "zp_paged_decode_lse": (S, [ctypes.POINTER(_KVCache), ctypes.c_int32, ctypes.c_int32, _vp,
                                     _vp, ctypes.c_int32, _vp, ctypes.c_float, _vp, _vp, _vp, _vp,
                                     ctypes.c_int32, _vp, ctypes.c_size_t, _vp]),
+        "zp_redundancy_all": (S, [ctypes.POINTER(_KVCache), ctypes.c_int32, ctypes.c_int32, _vp,
+                                  ctypes.c_int32, _vp, _vp]),
         "zp_sched_create": (S, [_vp, ctypes.POINTER(_SchedConfig), ctypes.POINTER(_vp)]),
         "zp_sched_destroy": (None, [_vp]),
         "zp_sched_add": (S, [_vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]),
@@ -386,6 +388,13 @@ def paged_decode(cache: KVCache, layer: int, q, tables, seq_lens, scale: float, 
                                      ws_ptr, ws_bytes, _stream_handle(stream)))
 
 
+def redundancy_all(cache: KVCache, layer: int, tables, out, stream=None) -> None:
+    """zp_redundancy_all: tables device int32 [R][n_blocks], out float [R][H][T]."""
+    R, n_blocks = (int(x) for x in tables.shape)
+    _check(lib().zp_redundancy_all(cache.ref, layer, R, tables.data_ptr(), n_blocks,
+                                   out.data_ptr(), _stream_handle(stream)))
+
+
 # --------------------------------------------------------------------------- scheduler
 
 class Scheduler:
@@ -449,7 +458,8 @@ class Scheduler:
 
 # --------------------------------------------------------------------------- timing
 
-PHASES = ("upload", "score_stats", "score", "select", "compact", "append", "decode", "combine")
+PHASES = ("upload", "score_stats", "score", "select", "compact", "append", "decode", "combine",
+          "redundancy_all")
 
 
 def profile_enable(on: bool = True) -> None:

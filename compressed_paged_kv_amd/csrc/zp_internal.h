@@ -75,6 +75,13 @@ struct DecodeParams {
   float scale_log2;
 };
 
+struct RedundancyParams {
+  const void* k;            // K pool of the layer
+  const int32_t* tables;    // [R][n_blocks]
+  float* out;               // [R][H][n_blocks * b]
+  int32_t R, H, n_blocks, num_blocks;
+};
+
 struct AppendParams {
   void* k;
   void* v;
@@ -93,6 +100,9 @@ hipError_t launch_compact(const CompactParams& p, int num_layers, int row_bytes,
 hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, int block_size,
                          hipStream_t s);
 hipError_t launch_append(const AppendParams& p, hipStream_t s);
+hipError_t launch_redundancy_all(const RedundancyParams& p, int dtype, int head_dim,
+                                 int block_size, hipStream_t s);
+int redundancy_max_slots();
 // Copies bytes (a multiple of 16, 16-byte aligned ends) from device-visible
 // pinned host memory to device memory with a kernel on stream s.
 hipError_t launch_upload(const void* host_src, void* dst, size_t bytes, hipStream_t s);

@@ -320,6 +320,24 @@ zp_status zp_paged_decode_lse(const zp_kv_cache* cache, int32_t layer, int32_t n
                               size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * zp_redundancy_all: the all-pairs redundancy that the Lightning Redundancy
+ * Score replaces (nl page Methodologie item 5, ko page section 2.E: the
+ * original score is O(N^2 b^2), the LRS O(N b^2)), for measuring that
+ * replacement.  For request r, KV head h and each of the T = n_blocks*b
+ * slots j of layer `layer`:
+ *   out[r][h][j] = 1/(T-1) * sum over c != j of cos(k_j, k_c),
+ * cos = 0 when either key is zero -- the LRS reduction over the whole
+ * sequence instead of the block.  Every pair is formed (MFMA Gram tiles).
+ * block_tables: device int32 [num_reqs][n_blocks], all blocks full (ids
+ *               outside the pool read as zero keys).
+ * out:          device float [num_reqs][H][T].
+ * Rejects T < 2 or T > 8192 and what zp_paged_decode rejects for the cache.
+ * ---------------------------------------------------------------------- */
+zp_status zp_redundancy_all(const zp_kv_cache* cache, int32_t layer, int32_t num_reqs,
+                            const int32_t* block_tables, int32_t n_blocks, float* out,
+                            void* stream);
+
+/* ------------------------------------------------------------------------
  * Hybrid scheduler (host object, not thread-safe).
  *
  * Requests below the block cap decode without any extra resource; a request
@@ -414,7 +432,8 @@ typedef enum {
   ZP_PHASE_APPEND = 5,      /* zp_append_kv */
   ZP_PHASE_DECODE = 6,      /* paged decode attention */
   ZP_PHASE_COMBINE = 7,     /* merge of the decode splits */
-  ZP_NUM_PHASES = 8
+  ZP_PHASE_REDUNDANCY_ALL = 8, /* zp_redundancy_all */
+  ZP_NUM_PHASES = 9
 } zp_phase;
 
 zp_status zp_profile_enable(int32_t on);
