@@ -38,7 +38,8 @@ def _load():
     lib.zpo_num_threads.restype = ctypes.c_int
     lib.zpo_plan.restype = ctypes.c_int
     lib.zpo_plan.argtypes = [ctypes.c_int32, _i32p, ctypes.c_int32, ctypes.c_int32,
-                             ctypes.c_int32, _i32p, _i32p, _i32p, _i32p, _i32p]
+                             ctypes.c_int32, _i32p, _i32p, _i32p, _i32p, _i32p, _i32p,
+                             ctypes.c_int32]
     lib.zpo_scores.restype = None
     lib.zpo_scores.argtypes = [ctypes.c_int32] * 8 + [ctypes.c_void_p, ctypes.c_void_p, _i32p,
                                                       _f64p, _f64p, _f64p]
@@ -94,9 +95,12 @@ class Plan:
     freed: np.ndarray       # freed ids in order
 
 
-def plan(refcounts: np.ndarray, tables: np.ndarray, n_max: int) -> Plan:
+def plan(refcounts: np.ndarray, tables: np.ndarray, n_max: int,
+         first_evict: Optional[np.ndarray] = None, block_size: int = 0) -> Plan:
     """Target-block plan of one compression call (inputs are not modified).
-    ``tables`` is [R][n_src] with n_src >= n_max."""
+    ``tables`` is [R][n_src] with n_src >= n_max.  ``first_evict`` ([R], the
+    lowest evicted slot of each request over its layers and heads) keeps the
+    shared blocks wholly below it shared."""
     lib = _load()
     rc = np.ascontiguousarray(refcounts, dtype=np.int32).copy()
     tab = np.ascontiguousarray(tables, dtype=np.int32).copy()
@@ -105,8 +109,11 @@ def plan(refcounts: np.ndarray, tables: np.ndarray, n_max: int) -> Plan:
     dst = np.zeros((R, max(n_max - 1, 1)), dtype=np.int32)
     freed = np.zeros(max(R * n_src, 1), dtype=np.int32)
     nfreed = np.zeros(1, dtype=np.int32)
+    fe = None
+    if first_evict is not None:
+        fe = _i32(np.ascontiguousarray(first_evict, dtype=np.int32))
     st = lib.zpo_plan(int(rc.shape[0]), _i32(rc), R, n_src, n_max, _i32(tab), _i32(src),
-                      _i32(dst), _i32(freed), _i32(nfreed))
+                      _i32(dst), _i32(freed), _i32(nfreed), fe, int(block_size))
     return Plan(int(st), tab, rc, src, dst, freed[: int(nfreed[0])].copy())
 
 
@@ -246,23 +253,54 @@ class CompressResult:
     v_pool: List[np.ndarray]
 
 
-def compress(case, layers: Optional[List[int]] = None, with_pools: bool = True) -> CompressResult:
+def first_evicted(kept: List[np.ndarray], T: int, window: int) -> np.ndarray:
+    """Lowest evicted slot of each request over all layers and heads, from
+    the kept lists ([R][H][K_keep] per layer)."""
+    C = T - window
+    out = None
+    for k in kept:
+        mask = np.ones(k.shape[:2] + (T,), dtype=bool)
+        np.put_along_axis(mask, k.astype(np.int64), False, axis=-1)
+        mask[..., C:] = False
+        first = np.where(mask.any(-1), mask.argmax(-1), C).min(axis=1)
+        out = first if out is None else np.minimum(out, first)
+    return out.astype(np.int32)
+
+
+def compress(case, layers: Optional[List[int]] = None, with_pools: bool = True,
+             keep_prefix: bool = False) -> CompressResult:
     """The whole compression call of a synthetic case, step by step
-    (``with_pools=False`` skips the out-of-place compaction of the pools)."""
+    (``with_pools=False`` skips the out-of-place compaction of the pools).
+    ``keep_prefix``: the plan is made after the selection of every layer, and
+    shared blocks below each request's first eviction stay shared."""
     g = case.geom
     n_max, w, b = case.n_max, case.window, g.block_size
     k_keep = (n_max - 1) * b
     k_sel = k_keep - w
-    p = plan(case.refcounts, case.tables, n_max)
+    T = case.tables.shape[1] * b
+    layers = list(range(g.num_layers)) if layers is None else layers
+    sel = {}
+    if keep_prefix:
+        for layer in range(g.num_layers):
+            A, Rr, s = scores(case.k_pool[layer], case.window_q[layer], case.tables,
+                              num_kv_heads=g.num_kv_heads, num_q_heads=g.num_q_heads,
+                              head_dim=g.head_dim, block_size=b, window=w)
+            sel[layer] = (A, Rr, s, select(s, w, k_sel))
+        fe = first_evicted([sel[l][3] for l in range(g.num_layers)], T, w)
+        p = plan(case.refcounts, case.tables, n_max, fe, b)
+    else:
+        p = plan(case.refcounts, case.tables, n_max)
     if p.status != OK:
         raise RuntimeError(f"oracle plan failed with status {p.status}")
-    layers = list(range(g.num_layers)) if layers is None else layers
     out = CompressResult(p, [], [], [], [], [], [])
     for layer in layers:
-        A, Rr, s = scores(case.k_pool[layer], case.window_q[layer], p.src,
-                          num_kv_heads=g.num_kv_heads, num_q_heads=g.num_q_heads,
-                          head_dim=g.head_dim, block_size=b, window=w)
-        kept = select(s, w, k_sel)
+        if layer in sel:
+            A, Rr, s, kept = sel[layer]
+        else:
+            A, Rr, s = scores(case.k_pool[layer], case.window_q[layer], p.src,
+                              num_kv_heads=g.num_kv_heads, num_q_heads=g.num_q_heads,
+                              head_dim=g.head_dim, block_size=b, window=w)
+            kept = select(s, w, k_sel)
         out.A.append(A)
         out.R.append(Rr)
         out.s.append(s)

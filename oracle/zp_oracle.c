@@ -96,10 +96,15 @@ int zpo_num_threads(void) {
  * tables: [R][n_src] in; out: the n_max new ids, then -1 for the surplus.
  * src_out: [R][n_src] (the old table).  dst_out: [R][n_max-1] (compaction
  * targets).  freed_out: capacity R*n_src.
+ *
+ * first_evict (NULL, or [R]): the request's lowest evicted slot over all
+ * layers and heads.  A shared block n < n_max-1 whose slots all lie below it
+ * is left as it is in every layer and head by the compaction, so it stays in
+ * the table, still shared (no new target, counts unchanged).
  * --------------------------------------------------------------------- */
 int zpo_plan(int32_t pool_size, int32_t* rc, int32_t R, int32_t n_src, int32_t n_max,
              int32_t* tables, int32_t* src_out, int32_t* dst_out, int32_t* freed_out,
-             int32_t* n_freed_out) {
+             int32_t* n_freed_out, const int32_t* first_evict, int32_t b) {
   if (pool_size <= 0 || R < 0 || n_max < 2 || n_src < n_max) return ZPO_INVALID;
   int32_t* seen = (int32_t*)calloc((size_t)pool_size, sizeof(int32_t));
   int32_t* rc0 = (int32_t*)malloc((size_t)pool_size * sizeof(int32_t));
@@ -119,8 +124,10 @@ int zpo_plan(int32_t pool_size, int32_t* rc, int32_t R, int32_t n_src, int32_t n
   if (bad) { free(seen); free(rc0); return ZPO_INVALID; }
   int64_t need = 0, nfree = 0;
   for (int32_t r = 0; r < R; r++)
-    for (int32_t n = 0; n < n_max; n++)
-      if (rc0[tables[(size_t)r * n_src + n]] > 1) need++;
+    for (int32_t n = 0; n < n_max; n++) {
+      const int stays = first_evict && n < n_max - 1 && (int64_t)(n + 1) * b <= first_evict[r];
+      if (rc0[tables[(size_t)r * n_src + n]] > 1 && !stays) need++;
+    }
   for (int32_t i = 0; i < pool_size; i++)
     if (rc0[i] == 0) nfree++;
   if (need > nfree) { free(seen); free(rc0); return ZPO_NO_BLOCKS; }
@@ -139,7 +146,8 @@ int zpo_plan(int32_t pool_size, int32_t* rc, int32_t R, int32_t n_src, int32_t n
         continue;
       }
       int32_t target = s;
-      if (rc0[s] > 1) {
+      const int stays = first_evict && n < n_max - 1 && (int64_t)(n + 1) * b <= first_evict[r];
+      if (rc0[s] > 1 && !stays) {
         while (rc0[next_free] != 0) next_free++;
         target = next_free++;
         rc[target] = 1;

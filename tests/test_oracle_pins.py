@@ -405,6 +405,56 @@ def test_plan_shared_reserved_block_is_replaced():
     assert p.freed.tolist() == [5]
 
 
+def test_plan_keeps_shared_blocks_below_the_first_eviction():
+    """With the first evicted slot known, a shared block wholly below it
+    stays in the table, still shared; one reaching past it is re-targeted."""
+    b = 4
+    tables = np.array([[3, 4, 5, 6], [3, 4, 7, 8]], dtype=np.int32)   # 3, 4 shared
+    rc = np.zeros(16, dtype=np.int32)
+    np.add.at(rc, tables.reshape(-1), 1)
+    # request 0: first eviction at slot 8 -> blocks 0, 1 (slots 0..7) stay;
+    # request 1: first eviction at slot 7 -> block 0 stays, block 1 (4..7) moves
+    p = oracle.plan(rc, tables, 4, first_evict=np.array([8, 7]), block_size=b)
+    assert p.status == oracle.OK
+    assert p.tables.tolist() == [[3, 4, 5, 6], [3, 0, 7, 8]]
+    assert p.dst.tolist() == [[3, 4, 5], [3, 0, 7]]
+    assert p.refcounts[3] == 2 and p.refcounts[4] == 1 and p.refcounts[0] == 1
+    assert p.freed.size == 0
+    # without it every shared position is re-targeted
+    q = oracle.plan(rc, tables, 4)
+    assert q.tables.tolist() == [[0, 1, 5, 6], [2, 9, 7, 8]]
+    assert sorted(q.freed.tolist()) == [3, 4]
+
+
+def test_keep_prefix_compression_leaves_the_shared_prefix_in_place():
+    """Exact ties (zero queries, axis-aligned keys): the evicted candidates
+    are the highest slots, far past a 2-block shared prefix, which then stays
+    shared with unchanged bytes while the rest compacts as usual."""
+    R, H, d, b, n_max, w, P = 3, 2, 16, 4, 6, 2, 2
+    c = synth.make_case("kp", 43, num_reqs=R, num_layers=2, num_kv_heads=H, num_q_heads=H,
+                        head_dim=d, block_size=b, n_max=n_max, window=w, num_blocks=40,
+                        dtype="f32", shared_prefix_blocks=P)
+    T = n_max * b
+    K = np.zeros((R, H, T, d))
+    for j in range(T):
+        K[:, :, j, j % b] = 1.0 + (j % 3)
+    for l in range(2):
+        c.k_pool[l] = synth.pool_from_logical(K, c.tables, 40, "f32")
+        c.window_q[l] = np.zeros_like(c.window_q[l])
+    res = oracle.compress(c, keep_prefix=True)
+    prefix = c.tables[0, :P]
+    assert np.all(res.plan.tables[:, :P] == prefix)
+    assert all(res.plan.refcounts[x] == R for x in prefix) and res.plan.freed.size == 0
+    C, E = T - w, b
+    for l in range(2):
+        want = list(range(C - E)) + list(range(C, T))
+        assert np.all(res.kept[l] == np.array(want))
+        np.testing.assert_array_equal(res.k_pool[l][prefix], c.k_pool[l][prefix])
+    # the plain compression re-targets the same prefix into new blocks
+    plain = oracle.compress(c)
+    assert not np.any(np.isin(plain.plan.tables[:, :P], prefix))
+
+
 def test_plan_over_cap_releases_the_surplus():
     """A request holding n_src > n_max blocks keeps its first n_max-1 blocks
     as targets and block n_max-1 as the reserved one; blocks n_max.. are
