@@ -78,7 +78,7 @@ def window_lse_on_gpu(cache, case, kp_tensors, wq_tensors, device="cuda"):
     return res
 
 
-def run_case(case, device="cuda", decode=True, recorded_lse=False) -> GpuRun:
+def run_case(case, device="cuda", decode=True, recorded_lse=False, keep_prefix=False) -> GpuRun:
     """``recorded_lse``: compress with the window rows' normalisers taken
     from zp_paged_decode_lse (the single-read scoring) instead of the
     self-contained two-pass scoring."""
@@ -99,7 +99,8 @@ def run_case(case, device="cuda", decode=True, recorded_lse=False) -> GpuRun:
                score=torch.full((L, R, H, T), float("nan"), device=device),
                kept=torch.full((L, R, H, k_keep), -1, dtype=torch.int32, device=device))
     wl = window_lse_on_gpu(cache, case, kp, wq, device) if recorded_lse else None
-    freed = zp.compress(cache, pool, n_max, w, tables, wq, ws, debug=dbg, window_lse=wl)
+    freed = zp.compress(cache, pool, n_max, w, tables, wq, ws, debug=dbg, window_lse=wl,
+                        keep_prefix=keep_prefix)
     torch.cuda.synchronize()
     run = GpuRun(tables=tables.copy(), refcounts=pool.refcounts(), freed=freed.copy(),
                  A=dbg["importance"].cpu().numpy(), R=dbg["redundancy"].cpu().numpy(),
@@ -139,7 +140,7 @@ def rel_ok(got, want, rtol, floor=FLOOR):
     return np.abs(got - want) <= rtol * np.abs(want) + floor
 
 
-def check_case(case, run: GpuRun, *, check_decode=True, layers=None) -> dict:
+def check_case(case, run: GpuRun, *, check_decode=True, layers=None, keep_prefix=False) -> dict:
     """Compare one GPU run with the oracle; raises AssertionError on failure.
     Returns a few statistics for the log."""
     g = case.geom
@@ -147,7 +148,7 @@ def check_case(case, run: GpuRun, *, check_decode=True, layers=None) -> dict:
     T, k_keep = case.n_src * b, (n_max - 1) * b
     C, k_sel = T - w, k_keep - w
     layers = list(range(g.num_layers)) if layers is None else layers
-    ref = oracle.compress(case, layers=layers, with_pools=False)
+    ref = oracle.compress(case, layers=layers, with_pools=False, keep_prefix=keep_prefix)
     # bookkeeping, exact
     np.testing.assert_array_equal(run.tables, ref.plan.tables)
     np.testing.assert_array_equal(run.refcounts, ref.plan.refcounts)

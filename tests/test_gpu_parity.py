@@ -192,3 +192,37 @@ def test_append_then_decode_one_token():
             np.testing.assert_array_equal(got[r, hq], c.v_new[0][r, hq // 2])
     blk = int(c.tables[1, 0])
     np.testing.assert_array_equal(kp[blk].cpu().numpy(), c.k_pool[0][blk])
+
+
+# ---------------------------------------------------------------- prefix-keeping compression
+
+def test_keep_prefix_leaves_a_clean_shared_prefix_shared():
+    """Exact ties put every eviction at the highest candidate slots, past a
+    3-block prefix shared by 4 requests: zp_compress_keep_prefix keeps the
+    prefix blocks in every table (still shared, bytes unchanged, nothing
+    freed) and matches the oracle's prefix-keeping plan and compaction."""
+    c = _case("kp", 240, num_reqs=4, num_layers=2, n_max=12, num_blocks=80,
+              shared_prefix_blocks=3)
+    R, H, b, d = c.num_reqs, c.geom.num_kv_heads, c.geom.block_size, c.geom.head_dim
+    T = c.n_max * b
+    K = np.zeros((R, H, T, d))
+    for j in range(T):
+        K[:, :, j, j % b] = 1.0 + (j % 3)
+    for l in range(2):
+        c.k_pool[l] = synth.pool_from_logical(K, c.tables, c.geom.num_blocks, "bf16")
+        c.window_q[l] = np.zeros_like(c.window_q[l])
+    say("[gpu parity] keep-prefix: 4 requests, 3 shared blocks, exact ties")
+    run = run_case(c, keep_prefix=True)
+    prefix = c.tables[0, :3]
+    assert np.all(run.tables[:, :3] == prefix) and run.freed.size == 0
+    assert all(run.refcounts[x] == R for x in prefix)
+    check_case(c, run, keep_prefix=True)
+
+
+@pytest.mark.parametrize("name", ["shared_prefix_2layers", "over_cap_prefix_2layers"])
+def test_keep_prefix_matches_oracle_on_random_prefixes(name):
+    case = CASES[name]()
+    say(f"[gpu parity] keep-prefix on {name}")
+    run = run_case(case, keep_prefix=True)
+    stats = check_case(case, run, keep_prefix=True)
+    say(f"[gpu parity] keep-prefix {name}: ok {stats}")
