@@ -109,6 +109,11 @@ def lib() -> ctypes.CDLL:
                               ctypes.c_int32, ctypes.c_int32, _i32p, ctypes.POINTER(_vp),
                               ctypes.POINTER(_vp), _vp, ctypes.c_size_t, _i32p, _i32p, _vp,
                               ctypes.POINTER(_Debug)]),
+        "zp_compress_keep_prefix": (S, [ctypes.POINTER(_KVCache), _vp, ctypes.c_int32,
+                                        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _i32p,
+                                        ctypes.POINTER(_vp), ctypes.POINTER(_vp), _vp,
+                                        ctypes.c_size_t, _i32p, _i32p, _vp,
+                                        ctypes.POINTER(_Debug)]),
         "zp_compress_plan_n": (S, [_vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _i32p,
                                    _i32p, _i32p, _i32p, _i32p]),
         "zp_compress_workspace_bytes_n": (ctypes.c_size_t, [ctypes.POINTER(_KVCache),
@@ -128,6 +133,12 @@ def lib() -> ctypes.CDLL:
                                     ctypes.c_int32, _vp, ctypes.c_size_t, _vp]),
         "zp_redundancy_all": (S, [ctypes.POINTER(_KVCache), ctypes.c_int32, ctypes.c_int32, _vp,
                                   ctypes.c_int32, _vp, _vp]),
+        "zp_prefix_index_create": (S, [_vp, ctypes.c_int32, ctypes.POINTER(_vp)]),
+        "zp_prefix_index_destroy": (None, [_vp]),
+        "zp_prefix_insert": (S, [_vp, _i32p, ctypes.c_int32, _i32p, ctypes.c_int32, _i32p]),
+        "zp_prefix_match": (S, [_vp, _i32p, ctypes.c_int32, _i32p, _i32p]),
+        "zp_prefix_evict": (S, [_vp, ctypes.c_int32, _i32p, _i32p]),
+        "zp_prefix_size": (ctypes.c_int32, [_vp]),
         "zp_sched_create": (S, [_vp, ctypes.POINTER(_SchedConfig), ctypes.POINTER(_vp)]),
         "zp_sched_destroy": (None, [_vp]),
         "zp_sched_add": (S, [_vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]),
@@ -318,12 +329,13 @@ def compress_workspace_bytes(cache: KVCache, num_reqs: int, n_max: int, window: 
 
 def compress(cache: KVCache, pool: BlockPool, n_max: int, window: int, tables: np.ndarray,
              window_q: List, workspace, stream=None, debug: Optional[dict] = None,
-             window_lse: Optional[List] = None) -> np.ndarray:
+             window_lse: Optional[List] = None, keep_prefix: bool = False) -> np.ndarray:
     """zp_compress (zp_compress_lse when ``window_lse``, per-layer float
     tensors [R][w][Hq] of the window rows' normalisers, is given;
     zp_compress_n when ``tables`` has n_src > n_max columns).  ``tables``
     (host int32 [R][n_src]) is rewritten on success; returns the freed block
-    ids."""
+    ids.  ``keep_prefix``: zp_compress_keep_prefix (shared blocks the
+    compaction leaves unchanged stay shared)."""
     assert tables.dtype == np.int32 and tables.flags.c_contiguous
     R, n_src = (int(x) for x in tables.shape)
     wq = (_vp * cache.num_layers)(*[t.data_ptr() for t in window_q])
@@ -336,7 +348,14 @@ def compress(cache: KVCache, pool: BlockPool, n_max: int, window: int, tables: n
     if debug:
         dbg = _Debug(_dptr(debug.get("importance")), _dptr(debug.get("redundancy")),
                      _dptr(debug.get("score")), _dptr(debug.get("kept")))
-    if n_src != n_max:
+    if keep_prefix:
+        st = lib().zp_compress_keep_prefix(
+            cache.ref, pool.handle, n_src, n_max, window, R, _i32(tables),
+            ctypes.cast(wq, ctypes.POINTER(_vp)),
+            ctypes.cast(wl, ctypes.POINTER(_vp)) if wl is not None else None,
+            workspace.data_ptr(), workspace.numel() * workspace.element_size(), _i32(freed),
+            _i32(n), _stream_handle(stream), ctypes.byref(dbg) if dbg else None)
+    elif n_src != n_max:
         st = lib().zp_compress_n(cache.ref, pool.handle, n_src, n_max, window, R, _i32(tables),
                                  ctypes.cast(wq, ctypes.POINTER(_vp)),
                                  ctypes.cast(wl, ctypes.POINTER(_vp)) if wl is not None else None,
@@ -393,6 +412,49 @@ def redundancy_all(cache: KVCache, layer: int, tables, out, stream=None) -> None
     R, n_blocks = (int(x) for x in tables.shape)
     _check(lib().zp_redundancy_all(cache.ref, layer, R, tables.data_ptr(), n_blocks,
                                    out.data_ptr(), _stream_handle(stream)))
+
+
+# --------------------------------------------------------------------------- prefix index
+
+class PrefixIndex:
+    """Prefix index (zp_prefix_*): full prompt blocks found again by tokens."""
+
+    def __init__(self, pool: BlockPool, block_size: int):
+        self.pool = pool
+        self.block_size = block_size
+        h = _vp()
+        _check(lib().zp_prefix_index_create(pool.handle, block_size, ctypes.byref(h)))
+        self.handle = h
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _lib is not None:
+            _lib.zp_prefix_index_destroy(self.handle)
+            self.handle = None
+
+    def insert(self, tokens, block_ids) -> int:
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        ids = np.ascontiguousarray(block_ids, dtype=np.int32)
+        n = np.zeros(1, dtype=np.int32)
+        _check(lib().zp_prefix_insert(self.handle, _i32(t) if t.size else None, int(t.size),
+                                      _i32(ids) if ids.size else None, int(ids.size), _i32(n)))
+        return int(n[0])
+
+    def match(self, tokens) -> np.ndarray:
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        out = np.zeros(max(t.size // self.block_size, 1), dtype=np.int32)
+        n = np.zeros(1, dtype=np.int32)
+        _check(lib().zp_prefix_match(self.handle, _i32(t) if t.size else None, int(t.size),
+                                     _i32(out), _i32(n)))
+        return out[: int(n[0])].copy()
+
+    def evict(self, max_entries: int) -> np.ndarray:
+        out = np.zeros(max(max_entries, 1), dtype=np.int32)
+        n = np.zeros(1, dtype=np.int32)
+        _check(lib().zp_prefix_evict(self.handle, int(max_entries), _i32(out), _i32(n)))
+        return out[: int(n[0])].copy()
+
+    def __len__(self) -> int:
+        return int(lib().zp_prefix_size(self.handle))
 
 
 # --------------------------------------------------------------------------- scheduler

@@ -57,7 +57,13 @@ void add_pending(zp_block_pool* pool, std::vector<int32_t> ids, hipEvent_t event
 }
 
 zp_status plan_compression(zp_block_pool* pool, int32_t n_src, int32_t n_max, int32_t num_reqs,
-                           int32_t* block_tables, PlanResult* out) {
+                           int32_t* block_tables, PlanResult* out, const int32_t* first_evict,
+                           int32_t block_size, bool dry_run) {
+  // shared block n of request r that stays: every slot of it lies below the
+  // request's first eviction in every layer and head
+  auto kept_shared = [&](int32_t r, int32_t n) {
+    return first_evict && n < n_max - 1 && (int64_t)(n + 1) * block_size <= first_evict[r];
+  };
   if (!pool) { set_error("pool is NULL"); return ZP_ERR_INVALID; }
   if (pool->poisoned) { set_error("pool unusable after an earlier HIP failure"); return ZP_ERR_STATE; }
   if (n_max < 2) { set_error("n_max must be >= 2 (got %d)", n_max); return ZP_ERR_INVALID; }
@@ -90,9 +96,10 @@ zp_status plan_compression(zp_block_pool* pool, int32_t n_src, int32_t n_max, in
         set_error("id %d listed %d times but its refcount is %d", id, seen[id], rc0[id]);
         return ZP_ERR_INVALID;
       }
-      if (n < n_max && rc0[id] > 1) need++;
+      if (n < n_max && rc0[id] > 1 && !kept_shared(r, n)) need++;
     }
   }
+  if (dry_run) return ZP_OK;  // the tables are valid; the block count is checked later
   pool->reap();
   if (need > (int64_t)pool->free_ids.size()) {
     set_error("need %lld new target blocks, %zu free", (long long)need, pool->free_ids.size());
@@ -116,7 +123,7 @@ zp_status plan_compression(zp_block_pool* pool, int32_t n_src, int32_t n_max, in
         continue;
       }
       int32_t target = s;
-      if (start_rc[s] > 1) {
+      if (start_rc[s] > 1 && !kept_shared(r, n)) {
         target = *pool->free_ids.begin();
         pool->free_ids.erase(pool->free_ids.begin());
         pool->rc[target] = 1;

@@ -42,8 +42,16 @@ struct PlanResult {
 // (n_max new ids, then -1 for the released surplus) and returns the plan
 // (freed ids are NOT yet pending: the caller attaches them with
 // add_pending).  On failure nothing changes.
+//
+// first_evict (optional, [R]): request r's lowest evicted slot over all its
+// layers and heads.  A shared block n < n_max-1 with (n+1)*b <= first_evict[r]
+// keeps its place and contents in every layer and head, so it stays in the
+// table, shared, instead of being re-targeted.  With dry_run, only the
+// checks of the tables run (not the free-block count; nothing changes).
 zp_status plan_compression(zp_block_pool* pool, int32_t n_src, int32_t n_max, int32_t num_reqs,
-                           int32_t* block_tables, PlanResult* out);
+                           int32_t* block_tables, PlanResult* out,
+                           const int32_t* first_evict = nullptr, int32_t block_size = 0,
+                           bool dry_run = false);
 
 // Attach freed ids to a pending group released by `event` (or by a fence
 // when event is null).  Takes ownership of the event.

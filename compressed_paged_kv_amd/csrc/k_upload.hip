@@ -17,7 +17,29 @@ __global__ __launch_bounds__(kUploadThreads) void k_upload(const uint4* __restri
   if (i < n16) dst[i] = src[i];
 }
 
+// Per request, the lowest evicted slot over all its (layer, head) units
+// (the evicted lists are ascending): every slot below it keeps its place in
+// every layer and head.  Written straight to host-mapped memory.
+__global__ __launch_bounds__(kUploadThreads) void k_first_evict(const int32_t* __restrict__ evicted,
+                                                                int32_t* out, int R, int H, int L,
+                                                                int E) {
+  const int r = blockIdx.x * kUploadThreads + threadIdx.x;
+  if (r >= R) return;
+  int m = 0x7fffffff;
+  for (int l = 0; l < L; l++)
+    for (int h = 0; h < H; h++) m = min(m, evicted[(((size_t)l * R + r) * H + h) * E]);
+  out[r] = m;
+}
+
 }  // namespace
+
+hipError_t launch_first_evict(const int32_t* evicted, int32_t* host_out, int R, int H, int L, int E,
+                              hipStream_t s) {
+  if (R <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_first_evict, dim3((unsigned)((R + kUploadThreads - 1) / kUploadThreads)),
+                     dim3(kUploadThreads), 0, s, evicted, host_out, R, H, L, E);
+  return hipGetLastError();
+}
 
 hipError_t launch_upload(const void* host_src, void* dst, size_t bytes, hipStream_t s) {
   if (bytes == 0) return hipSuccess;

@@ -106,6 +106,10 @@ int redundancy_max_slots();
 // Copies bytes (a multiple of 16, 16-byte aligned ends) from device-visible
 // pinned host memory to device memory with a kernel on stream s.
 hipError_t launch_upload(const void* host_src, void* dst, size_t bytes, hipStream_t s);
+// host_out[r] = min over layers l and heads h of evicted[((l*R + r)*H + h)*E]
+// (host_out: device address of host-mapped memory).
+hipError_t launch_first_evict(const int32_t* evicted, int32_t* host_out, int R, int H, int L, int E,
+                              hipStream_t s);
 
 // Kernel timing (no-ops unless enabled by zp_profile_enable): bracket one
 // phase on stream s.

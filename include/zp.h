@@ -265,6 +265,26 @@ zp_status zp_compress_n(const zp_kv_cache* cache, zp_block_pool* pool, int32_t n
                         int32_t* num_freed, void* stream, const zp_compress_debug* debug);
 
 /* ------------------------------------------------------------------------
+ * zp_compress_keep_prefix: zp_compress_n that keeps shared blocks shared
+ * when compression leaves them as they are.  New target blocks keep the
+ * shared blocks intact for their other holders (ko page section 2.C, nl
+ * page Methodologie item 3); a shared block that lies entirely below the
+ * request's first evicted slot in every layer and head is not changed by
+ * the compaction at all, so instead of a copy in a new block it stays in
+ * the table, shared, and prefix caching keeps working after the
+ * compression.  The plan therefore waits for the selection: the call
+ * synchronises the host with `stream` once, after the scoring kernel.
+ * Arguments, results and errors as zp_compress_n; ZP_ERR_NO_BLOCKS is
+ * decided after the scoring (then only the workspace has changed).
+ * ---------------------------------------------------------------------- */
+zp_status zp_compress_keep_prefix(const zp_kv_cache* cache, zp_block_pool* pool, int32_t n_src,
+                                  int32_t n_max, int32_t window, int32_t num_reqs,
+                                  int32_t* block_tables, const void* const* window_q,
+                                  const void* const* window_lse, void* workspace,
+                                  size_t workspace_bytes, int32_t* freed_ids, int32_t* num_freed,
+                                  void* stream, const zp_compress_debug* debug);
+
+/* ------------------------------------------------------------------------
  * zp_append_kv: write one new token per request into layer `layer`.
  * k_new, v_new: device [R][H][d]; slot_mapping: device int32 [R], physical
  * slot block*b + offset (negative = skip).  Tokens go into the last
@@ -414,6 +434,43 @@ zp_status zp_sched_tables(const zp_sched* sched, const int64_t* ids, int32_t n, 
 zp_status zp_sched_compress_commit(zp_sched* sched, const int32_t* new_tables);
 zp_status zp_sched_stats(const zp_sched* sched, int32_t* num_waiting, int32_t* num_running,
                          int32_t* free_query_slots);
+
+/* ------------------------------------------------------------------------
+ * Prefix index (host object, not thread-safe): full prompt blocks found
+ * again by their tokens, so that requests starting with the same tokens
+ * share the physical blocks (guide "How it works": shared blocks with
+ * reference counts; ko page section 2.C and nl page Methodologie item 3:
+ * prefix caching alongside compression).  An entry is one full block of
+ * block_size tokens keyed by its tokens and by the entry of the block before
+ * it (a block only matches after the same whole prefix); lookups hash and
+ * then compare the tokens, so there are no false matches.  The index holds
+ * one reference on each block it lists: listed blocks count as shared, so
+ * compression never rewrites them in place (it re-targets them).
+ * ---------------------------------------------------------------------- */
+typedef struct zp_prefix_index zp_prefix_index;
+
+zp_status zp_prefix_index_create(zp_block_pool* pool, int32_t block_size, zp_prefix_index** out);
+/* Gives back the index's references (blocks reaching 0 become free). */
+void zp_prefix_index_destroy(zp_prefix_index* index);
+/* List the full blocks of a prompt: block n holds tokens [n*b, (n+1)*b)
+ * (HOST arrays; only min(num_tokens / b, num_blocks) blocks are full).
+ * New entries take a reference on their block; entries already listed for
+ * the same prefix are kept (their block wins).  Call it once the prefill
+ * has written those blocks, and before any compression of the request.
+ * ZP_ERR_INVALID (nothing changed) for ids that are not allocated. */
+zp_status zp_prefix_insert(zp_prefix_index* index, const int32_t* tokens, int32_t num_tokens,
+                           const int32_t* block_ids, int32_t num_blocks, int32_t* num_added);
+/* Longest listed prefix of whole blocks of `tokens`: block_ids_out (HOST,
+ * capacity num_tokens / b) gets its blocks, each with a new reference for
+ * the caller (release it with zp_block_release), *num_matched their count. */
+zp_status zp_prefix_match(zp_prefix_index* index, const int32_t* tokens, int32_t num_tokens,
+                          int32_t* block_ids_out, int32_t* num_matched);
+/* Drop up to max_entries least-recently-used entries without children,
+ * giving back their references; freed_out (HOST, capacity max_entries, may
+ * be NULL) gets the blocks that became free, *num_freed their count. */
+zp_status zp_prefix_evict(zp_prefix_index* index, int32_t max_entries, int32_t* freed_out,
+                          int32_t* num_freed);
+int32_t zp_prefix_size(const zp_prefix_index* index);  /* listed entries */
 
 /* ------------------------------------------------------------------------
  * Kernel timing.  While enabled, every kernel launch of the calls above is
