@@ -382,9 +382,11 @@ def run_single_stream(args, workload, cache, pool, tables, wq_sets, q_new, k_new
     #    rows are computed on the current cache by zp_paged_decode_lse, as the
     #    decode steps that produced those queries would have recorded them
     #    (outside the events: that work belongs to the earlier decode steps)
-    log(f"timing {args.steps} compressions with recorded window normalisers")
-    rec = recorded_lse_compress(args.steps, cache, pool, tables, next_wq, n_max, w, R, Hq, d,
-                                dev, ws, dws, step)
+    rec = None
+    if not args.headline_only:
+        log(f"timing {args.steps} compressions with recorded window normalisers")
+        rec = recorded_lse_compress(args.steps, cache, pool, tables, next_wq, n_max, w, R, Hq, d,
+                                    dev, ws, dws, step)
     moved_after = moved_rows()
     assert tables.tolist() == tables0.tolist(), "in-place compression changed the tables"
     assert np.isfinite(out.cpu().numpy()).all()
@@ -438,22 +440,27 @@ def run_single_stream(args, workload, cache, pool, tables, wq_sets, q_new, k_new
     }
     # the pairwise redundancy the Lightning Redundancy Score replaces, on the
     # same cache (every pair of the T slots of each head on MFMA)
-    log("timing the all-pairs redundancy (what the block-local score avoids)")
-    tab_full = torch.from_numpy(np.ascontiguousarray(tables)).to(dev)
-    r_all = torch.empty((R, H, T), dtype=torch.float32, device=dev)
-    for _ in range(2):
-        zp.redundancy_all(cache, 0, tab_full, r_all)
-    torch.cuda.synchronize()
-    zp.profile_enable(True)
-    zp.profile_read()
-    for _ in range(10):
-        zp.redundancy_all(cache, 0, tab_full, r_all)
-    torch.cuda.synchronize()
-    ra_ms, ra_n = zp.profile_read()["redundancy_all"]
-    zp.profile_enable(False)
-    ra_us = ra_ms * 1e3 / ra_n
+    ra_us = None
     ra_flops = 2.0 * T * T * d * R * H
-    del r_all
+    if not args.headline_only:
+        log("timing the all-pairs redundancy (what the block-local score avoids)")
+        tab_full = torch.from_numpy(np.ascontiguousarray(tables)).to(dev)
+        r_all = torch.empty((R, H, T), dtype=torch.float32, device=dev)
+        for _ in range(2):
+            zp.redundancy_all(cache, 0, tab_full, r_all)
+        torch.cuda.synchronize()
+        zp.profile_enable(True)
+        zp.profile_read()
+        for _ in range(10):
+            zp.redundancy_all(cache, 0, tab_full, r_all)
+        torch.cuda.synchronize()
+        ra_ms, ra_n = zp.profile_read()["redundancy_all"]
+        zp.profile_enable(False)
+        ra_us = ra_ms * 1e3 / ra_n
+        del r_all
+    if args.headline_only:
+        result["cpu_baseline"] = None
+        return result
     rec_us = {k["phase"]: k["avg_us"] for k in _kernel_rows(rec, alg, flops)}
     rec_comp = sum(rec_us.get(p, 0.0) for p in ("upload", "score", "compact"))
     result["recorded_lse"] = {
@@ -945,6 +952,9 @@ def main() -> int:
                     help="the Qwen3-8B layer at budget 2048 (default, the headline line) or one of "
                          "the wider workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time only the headline step (no recorded-normaliser or ablation regions, "
+                         "no CPU baseline): what the committed rocprofv3 summaries profile")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a 1 GiB device copy (counter calibration under rocprofv3)")
     ap.add_argument("--summarize", nargs=3, metavar=("KT_DIR", "FETCH_DIR", "WRITE_DIR"),

@@ -15,6 +15,7 @@ struct Mark {
   hipEvent_t begin, end;
 };
 
+constexpr size_t kPrecreatedEvents = 2048;
 std::atomic<bool> g_on{false};
 std::mutex g_mu;
 std::vector<hipEvent_t> g_free;  // reusable events
@@ -61,6 +62,15 @@ void prof_end(int phase, hipStream_t s) {
 extern "C" {
 
 zp_status zp_profile_enable(int32_t on) {
+  if (on) {
+    // events are created ahead, so that recording them does not create any
+    std::lock_guard<std::mutex> lock(zp::g_mu);
+    while (zp::g_free.size() + 2 * zp::g_marks.size() < zp::kPrecreatedEvents) {
+      hipEvent_t e = nullptr;
+      if (hipEventCreate(&e) != hipSuccess) break;
+      zp::g_free.push_back(e);
+    }
+  }
   zp::g_on.store(on != 0);
   return ZP_OK;
 }
