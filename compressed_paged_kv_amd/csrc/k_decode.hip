@@ -7,14 +7,18 @@
 // float32 accumulation, p*v as float32 FMAs.
 //
 // Grid: x = split of the block list, y = KV head (and query-head subgroup),
-// z = request.  A workgroup has 8 waves; wave w takes the split's blocks
-// w, w+8, ...  Within a wave, lane = 8*t + c handles token t (0..7) of an
-// 8-token step and the c-th eighth of the head dimension, as 16-byte vectors
-// at byte offsets 128*v + 16*c of the row, so one load instruction covers
-// 128 contiguous bytes of 8 rows.  All G query heads of the KV head are done
-// together, so K and V are read once for the group; the next step's K and V
-// are loaded before the current one is consumed.  The eight lanes of a
-// token add their partial dot products; every lane then keeps its own
+// z = request.  A workgroup has 8 waves.  Within a wave, lane = LPT*t + c
+// handles token t of a step of 64/LPT tokens and the c-th LPT-th of the head
+// dimension, as 16-byte vectors at byte offsets 16*LPT*v + 16*c of the row,
+// so one load instruction covers whole contiguous rows.  The steps of one
+// block go to different waves (wave w takes step w % SPB of the blocks
+// w / SPB, w / SPB + 8/SPB, ...), so all of a block's tile is requested at
+// about the same time.  All G query heads of the KV head are done together,
+// so K and V are read once for the group; the next block's K and V are
+// loaded before the current one is consumed.  V is loaded non-temporally:
+// nothing reads it again soon, whereas K stays cached for the scoring of a
+// compression that follows the decode step (measured: both faster).  The
+// LPT lanes of a token add their partial dot products; every lane keeps its own
 // running softmax state (max m, sum l, accumulator) for the tokens it saw,
 // rescaled only when the max grows by more than 64 in log2 units (exact up
 // to rounding: the final normalisation divides by the same stale max; terms
@@ -175,35 +179,37 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode(DecodeParams p) {
   const char* kb = static_cast<const char*>(p.k);
   const char* vb = static_cast<const char*>(p.v);
   const size_t tile_bytes = (size_t)B * ROW;
-  const int lane_off = tok * ROW + c * 16;  // this lane's bytes inside a step
-  // This wave's blocks are blk_begin + wave + NW*i.  Lane i holds the
-  // physical id of the wave's i-th block of the current group of 64.
-  const int my_blocks = blk_end - blk_begin - wave > 0 ? (blk_end - blk_begin - wave + NW - 1) / NW : 0;
+  // SPB waves share a block, one step each, so a block's tile is requested
+  // at once; the workgroup walks NWB blocks at a time.  This wave's blocks
+  // are blk_begin + wblk + NWB*i, always at step st.
+  static_assert(NW % SPB == 0, "steps per block must divide the waves");
+  constexpr int NWB = NW / SPB;
+  const int wblk = wave / SPB, st = wave - wblk * SPB;
+  const int lane_off = (st * TPS + tok) * ROW + c * 16;  // this lane's bytes inside a block
+  const int my_blocks = blk_end - blk_begin - wblk > 0 ? (blk_end - blk_begin - wblk + NWB - 1) / NWB : 0;
   for (int g0 = 0; g0 < my_blocks; g0 += 64) {
     const int nb_here = min(64, my_blocks - g0);
     int id = -1;
     if (lane < nb_here) {
-      id = p.tables[(size_t)r * p.max_blocks + blk_begin + wave + NW * (g0 + lane)];
+      id = p.tables[(size_t)r * p.max_blocks + blk_begin + wblk + NWB * (g0 + lane)];
       if ((unsigned)id >= (unsigned)p.num_blocks) id = -1;
     }
-    const int n_items = nb_here * SPB;
-    // item -> (block i = item / SPB, step st = item % SPB).  Items past the
-    // end re-read the last item and a skipped block reads row 0 of the pool:
+    const int n_items = nb_here;
+    // item i = the wave's i-th block of the group.  Items past the end
+    // re-read the last item and a skipped block reads row 0 of the pool:
     // the loads stay unconditional (straight-line code lets the compiler
     // count outstanding loads instead of draining them) and such items are
     // masked out below.
     auto item_base = [&](int item) -> long long {
       const int it = min(item, n_items - 1);
-      const int i = it / SPB, st = it - i * SPB;
-      const int pid = __builtin_amdgcn_readlane(id, i);
+      const int pid = __builtin_amdgcn_readlane(id, it);
       if (pid < 0) return 0;
-      return (long long)(((size_t)pid * p.H + h) * tile_bytes) + (long long)st * TPS * ROW + lane_off;
+      return (long long)(((size_t)pid * p.H + h) * tile_bytes) + lane_off;
     };
     auto item_live = [&](int item) -> bool {
       if (item >= n_items) return false;
-      const int i = item / SPB, st = item - i * SPB;
-      const int pid = __builtin_amdgcn_readlane(id, i);
-      return pid >= 0 && (blk_begin + wave + NW * (g0 + i)) * B + st * TPS + tok < seq;
+      const int pid = __builtin_amdgcn_readlane(id, item);
+      return pid >= 0 && (blk_begin + wblk + NWB * (g0 + item)) * B + st * TPS + tok < seq;
     };
     // ring of PD+1 register slots: item k lives in slot k % (PD+1) and is
     // loaded PD items before it is consumed
@@ -213,7 +219,7 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode(DecodeParams p) {
 #pragma unroll
       for (int v = 0; v < NV; v++) {
         kd[v] = ld16(kb + o + v * 16 * LPT);
-        vd[v] = ld16(vb + o + v * 16 * LPT);
+        vd[v] = ldg16_stream(vb + o + v * 16 * LPT);
       }
     };
 #pragma unroll
