@@ -450,7 +450,8 @@ zp_status zp_sched_stats(const zp_sched* sched, int32_t* num_waiting, int32_t* n
 typedef struct zp_prefix_index zp_prefix_index;
 
 zp_status zp_prefix_index_create(zp_block_pool* pool, int32_t block_size, zp_prefix_index** out);
-/* Gives back the index's references (blocks reaching 0 become free). */
+/* Gives back the index's references (blocks reaching 0 become free at
+ * once, as with zp_block_release). */
 void zp_prefix_index_destroy(zp_prefix_index* index);
 /* List the full blocks of a prompt: block n holds tokens [n*b, (n+1)*b)
  * (HOST arrays; only min(num_tokens / b, num_blocks) blocks are full).
@@ -467,7 +468,9 @@ zp_status zp_prefix_match(zp_prefix_index* index, const int32_t* tokens, int32_t
                           int32_t* block_ids_out, int32_t* num_matched);
 /* Drop up to max_entries least-recently-used entries without children,
  * giving back their references; freed_out (HOST, capacity max_entries, may
- * be NULL) gets the blocks that became free, *num_freed their count. */
+ * be NULL) gets the blocks that became free, *num_freed their count.  Like
+ * zp_block_release, blocks reaching 0 are free at once: the caller
+ * guarantees no queued GPU work still reads them. */
 zp_status zp_prefix_evict(zp_prefix_index* index, int32_t max_entries, int32_t* freed_out,
                           int32_t* num_freed);
 int32_t zp_prefix_size(const zp_prefix_index* index);  /* listed entries */
@@ -482,9 +485,9 @@ int32_t zp_prefix_size(const zp_prefix_index* index);  /* listed entries */
  * ---------------------------------------------------------------------- */
 typedef enum {
   ZP_PHASE_UPLOAD = 0,      /* table / pointer upload of zp_compress */
-  ZP_PHASE_SCORE_STATS = 1, /* per-chunk softmax statistics */
-  ZP_PHASE_SCORE = 2,       /* importance, redundancy, combined score */
-  ZP_PHASE_SELECT = 3,      /* per-head survivor selection */
+  ZP_PHASE_SCORE_STATS = 1, /* not used: the statistics pass is inside the scoring kernel */
+  ZP_PHASE_SCORE = 2,       /* importance, redundancy, combined score and survivor selection */
+  ZP_PHASE_SELECT = 3,      /* not used: the selection is inside the scoring kernel */
   ZP_PHASE_COMPACT = 4,     /* order-preserving gather of K and V */
   ZP_PHASE_APPEND = 5,      /* zp_append_kv */
   ZP_PHASE_DECODE = 6,      /* paged decode attention */
