@@ -79,6 +79,14 @@ def lib() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is missing: build it first "
                            "(python -c 'import __graft_entry__; __graft_entry__.build()')")
+    # One HIP runtime per process: PyTorch ships its own libamdhip64, and
+    # libzp.so binds to whichever copy is loaded first.  Loading torch first
+    # makes it the same one; a second runtime loaded beside torch's sees no
+    # device.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     L = ctypes.CDLL(LIB_PATH)
     S = ctypes.c_int  # zp_status
     sig = {
