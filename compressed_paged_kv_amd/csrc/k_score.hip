@@ -175,10 +175,6 @@ __global__ __launch_bounds__(64 * score_waves<RG>(), (kMaxWaves / score_waves<RG
   constexpr int kPrefetch = ZP_SCORE_RING_VGPRS / (FL * 4) < 2   ? 2
                             : ZP_SCORE_RING_VGPRS / (FL * 4) > 4 ? 4
                                                                  : ZP_SCORE_RING_VGPRS / (FL * 4);
-  // Gram split: with shared tiles and two sub-tiles, each wave of a pair
-  // takes the diagonal tiles (norms) and the off-diagonal tile of its own
-  // column sub-tile; otherwise the pair alternates whole blocks.
-  constexpr bool GSPLIT = SH && NST == 2;
 
   const size_t unit = blockIdx.x;
   const int h = (int)(unit % p.H);
@@ -437,24 +433,22 @@ __global__ __launch_bounds__(64 * score_waves<RG>(), (kMaxWaves / score_waves<RG
 #pragma unroll
       for (int st = 0; st < NST; st++) dst[n * B + st * 16 + col] = A[st];
     }
-    // the two row groups see the same blocks: they share or take turns on
-    // the Gram work
-    if (GSPLIT || RG == 1 || (k & 1) == rg) {
+    // the two row groups see the same blocks: they take turns on the Gram
+    // work, whole blocks each (splitting a block's Gram between the pair
+    // costs more: both waves then need the diagonal tiles for the norms)
+    if (RG == 1 || (k & 1) == rg) {
       // redundancy: column sums of the in-block cosine matrix, diagonal
       // excluded.  gm[s1][s2] holds the dot products of keys 16*s1 + 4*grp + i
       // (rows) with keys 16*s2 + col; the diagonal tiles give the squared
       // norms, and the inverse norms of a lane's rows come through LDS.
-      auto mine = [&](int s2) { return !GSPLIT || s2 == rg; };  // column sub-tiles this wave sums
       f32x4_t gm[NST][NST];
 #pragma unroll
       for (int s1 = 0; s1 < NST; s1++)
 #pragma unroll
         for (int s2 = 0; s2 < NST; s2++) {
           gm[s1][s2] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-          if (s1 == s2 || mine(s2)) {
 #pragma unroll
-            for (int v = 0; v < NV; v++) gm[s1][s2] = Mma<DT>::step(kt[s1][v], kt[s2][v], gm[s1][s2]);
-          }
+          for (int v = 0; v < NV; v++) gm[s1][s2] = Mma<DT>::step(kt[s1][v], kt[s2][v], gm[s1][s2]);
         }
       float nrm[NST];
 #pragma unroll
@@ -482,6 +476,8 @@ __global__ __launch_bounds__(64 * score_waves<RG>(), (kMaxWaves / score_waves<RG
       float Rd[NST];
 #pragma unroll
       for (int s2 = 0; s2 < NST; s2++) {
+        // the column's inverse norm is common to all its terms (every lane
+        // of the column holds the same one), so it multiplies the sum
         float cs = 0.f;
         const float rc = nrm[s2] > 0.f ? rsqrtf(nrm[s2]) : 0.f;
 #pragma unroll
@@ -489,9 +485,9 @@ __global__ __launch_bounds__(64 * score_waves<RG>(), (kMaxWaves / score_waves<RG
 #pragma unroll
           for (int i = 0; i < 4; i++) {
             const bool diag = (s1 == s2) && (4 * grp + i == col);
-            cs += diag ? 0.f : gm[s1][s2][i] * ra[s1][i] * rc;
+            cs += diag ? 0.f : gm[s1][s2][i] * ra[s1][i];
           }
-        Rd[s2] = sum_rows(cs) * inv_bm1;
+        Rd[s2] = sum_rows(cs * rc) * inv_bm1;
       }
       if (grp == 0) {
 #pragma unroll
@@ -505,7 +501,7 @@ __global__ __launch_bounds__(64 * score_waves<RG>(), (kMaxWaves / score_waves<RG
             if (p.dbg_importance) p.dbg_importance[o] = a;
             if (p.dbg_redundancy) p.dbg_redundancy[o] = Rd[st];
             if (p.dbg_score && j < p.C) p.dbg_score[o] = s;
-          } else if (mine(st)) {
+          } else {
             s_rr[j] = Rd[st];
           }
         }
