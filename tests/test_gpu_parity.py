@@ -77,6 +77,15 @@ CASES = {
                                           num_q_heads=8, n_max=8, n_src=20, num_blocks=48),
     "over_cap_f32_d64_many": lambda: _case("o4", 217, dtype="f32", head_dim=64, n_max=6,
                                            n_src=60, num_blocks=130),
+    # the limits the host accepts: 8192 cached slots (512 blocks of 16) with one
+    # row group, 4096 slots with 128 window rows (two row groups), and 1024
+    # evictions per head (a cache 63 blocks past the cap)
+    "max_slots_8192": lambda: _case("m1", 218, num_reqs=1, num_kv_heads=1, num_q_heads=4,
+                                    n_max=512, num_blocks=520),
+    "max_slots_4096_rows128": lambda: _case("m2", 219, num_reqs=1, num_kv_heads=1,
+                                            num_q_heads=8, n_max=256, num_blocks=260),
+    "max_evictions_1024": lambda: _case("m3", 220, num_reqs=2, head_dim=64, n_max=20, n_src=83,
+                                        num_blocks=180),
 }
 
 
@@ -167,6 +176,34 @@ def test_paged_decode_ragged_lengths(dtype, d, b, G):
     np.testing.assert_array_equal(got[0], 0.0)      # empty sequence -> zeros
     err = np.abs(got - want)
     assert err.max() <= DECODE_ATOL, err.max()
+
+
+def test_empty_batches_do_nothing():
+    """Zero requests: compression and decode enqueue nothing and change
+    nothing (no tables, no freed blocks)."""
+    import compressed_paged_kv_amd as zp
+    from synth.device import to_numpy, to_tensor
+    c = _case("empty", 221, num_reqs=1, n_max=4, num_blocks=8)
+    dev = "cuda"
+    say("[gpu parity] empty batches")
+    kp, vp = to_tensor(c.k_pool[0], dev), to_tensor(c.v_pool[0], dev)
+    cache = zp.KVCache([kp], [vp], c.geom.num_q_heads)
+    pool = zp.BlockPool.from_refcounts(c.refcounts)
+    before = pool.refcounts()
+    tables = np.zeros((0, c.n_max), dtype=np.int32)
+    wq = [torch.empty((0, c.window, c.geom.num_q_heads, c.geom.head_dim), dtype=kp.dtype,
+                      device=dev)]
+    ws = torch.empty(256, dtype=torch.uint8, device=dev)
+    freed = zp.compress(cache, pool, c.n_max, c.window, tables, wq, ws)
+    assert freed.size == 0
+    out = torch.empty((0, c.geom.num_q_heads, c.geom.head_dim), device=dev)
+    zp.paged_decode(cache, 0, torch.empty((0, c.geom.num_q_heads, c.geom.head_dim),
+                                          dtype=kp.dtype, device=dev),
+                    torch.zeros((0, c.n_max), dtype=torch.int32, device=dev),
+                    torch.zeros(0, dtype=torch.int32, device=dev), 0.125, out, None)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(pool.refcounts(), before)
+    np.testing.assert_array_equal(to_numpy(kp), c.k_pool[0])
 
 
 def test_append_then_decode_one_token():
