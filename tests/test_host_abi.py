@@ -283,3 +283,24 @@ def test_decode_and_append_reject_bad_arguments():
     lib = zp.lib()
     assert lib.zp_append_kv(cache.ref, 3, 1, t.data_ptr(), t.data_ptr(), t.data_ptr(), None) == \
         zp.ZP_ERR_INVALID
+
+
+def test_size_limits_are_checked_before_any_work():
+    """The largest shapes the kernels take are accepted; one step past any of
+    them is rejected with a message (no work is ever enqueued for them)."""
+    lib = zp.lib()
+    c16 = _fake_cache(H=1, Hq=4, d=128, b=16, nb=1024, dtype="torch.bfloat16")
+    c32 = _fake_cache(H=1, Hq=4, d=128, b=32, nb=1024, dtype="torch.bfloat16")
+    c16g8 = _fake_cache(H=1, Hq=8, d=128, b=16, nb=1024, dtype="torch.bfloat16")
+    ok = [(c16, 512, 512, 16),      # 8192 cached slots, one row group
+          (c16g8, 256, 256, 16),    # 128 window rows at 4096 slots
+          (c16, 83, 20, 16)]        # 1024 evictions per head
+    bad = [(c16, 513, 513, 16, "n_max"),
+           (c32, 257, 257, 32, "n_src*block_size"),
+           (c16g8, 257, 257, 16, "beyond the scoring kernel"),
+           (c16, 84, 20, 16, "evictions per head")]
+    for c, n_src, n_max, w in ok:
+        assert lib.zp_compress_workspace_bytes_n(c.ref, 1, n_src, n_max, w) > 0, zp.last_error()
+    for c, n_src, n_max, w, msg in bad:
+        assert lib.zp_compress_workspace_bytes_n(c.ref, 1, n_src, n_max, w) == 0
+        assert msg in zp.last_error(), zp.last_error()
