@@ -77,7 +77,7 @@ def cpu_baseline(case, min_seconds: float = 10.0) -> dict:
     k_keep = (n_max - 1) * b
     R = case.num_reqs
     times = []
-    while sum(times) < min_seconds and len(times) < 10:
+    while sum(times) < min_seconds and len(times) < 30:
         t0 = time.perf_counter()
         res = oracle.compress(case)
         kp, vp = res.k_pool[0], res.v_pool[0]
