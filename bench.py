@@ -140,11 +140,17 @@ def summarize(kt_dir: str, fetch_dir: str, write_dir: str) -> int:
 
     fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
     gib_kib = (1 << 30) / 1024.0
-    def is_cal(name):
-        return "elementwise" in name.lower() and "mul" in name.lower()
 
-    cal_f = [v for k, v in fetch.items() if is_cal(k)]
-    cal_w = [v for k, v in write.items() if is_cal(k)]
+    def calibration(d, counter):
+        # the three elementwise multiplies of calibrate_copy(), which runs
+        # before any other work of the process: the first such dispatches
+        rows = [r for r in _read_csv(glob.glob(os.path.join(d, "*counter_collection.csv"))[0])
+                if r["Counter_Name"] == counter and "elementwise" in r["Kernel_Name"].lower()
+                and "mul" in r["Kernel_Name"].lower()]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        return [float(r["Counter_Value"]) for r in rows[:3]]
+
+    cal_f, cal_w = calibration(fetch_dir, "FETCH_SIZE"), calibration(write_dir, "WRITE_SIZE")
     f_scale = gib_kib / max(cal_f) if cal_f else None
     w_scale = gib_kib / max(cal_w) if cal_w else None
     print()
