@@ -34,7 +34,8 @@ sys.path.insert(0, ROOT)
 METRIC = "KV compressions/sec + decode tok/s at budget 2048; % of HBM peak GB/s"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
-PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "hot_path_kernels_qwen3_8b_layer_budget2048.txt")
+# committed rocprofv3 summaries, one per workload: profiles/hot_path_kernels_<workload>.txt
+PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "upload": "compressed_paged_kv_amd/csrc/k_upload.hip",
     "score": "compressed_paged_kv_amd/csrc/k_score.hip",
@@ -54,12 +55,13 @@ def source_sha(rel: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def read_counters(kernel: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when absent or taken on a different kernel source."""
-    if not os.path.exists(PROFILE_COUNTERS):
+def read_counters(kernel: str, workload: str):
+    """HBM bytes per launch from the workload's committed rocprofv3 counter
+    summary, or None when absent or taken on a different kernel source."""
+    path = os.path.join(PROFILE_DIR, f"hot_path_kernels_{workload}.txt")
+    if not os.path.exists(path):
         return None
-    text = open(PROFILE_COUNTERS).read()
+    text = open(path).read()
     m = re.search(rf"^phase {kernel}: fetch_bytes=(\d+) write_bytes=(\d+) source_sha=(\w+)", text,
                   re.M)
     if not m or m.group(3) != source_sha(KERNEL_SOURCES[kernel]):
@@ -404,7 +406,7 @@ def run_single_stream(args, workload, cache, pool, tables, wq_sets, q_new, k_new
     kernels = _kernel_rows(prof, alg, flops)
     gpu_kernels = [k for k in kernels if k["phase"] != "upload"]
     dom = max(gpu_kernels, key=lambda k: k["avg_us"] * k["launches"])
-    traffic = read_counters(dom["phase"]) if workload == WORKLOADS[0] else None
+    traffic = read_counters(dom["phase"], workload)
     roofline = {"bound": "hbm", "kernel": dom["phase"], "achieved": dom["alg_GBs"],
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dom["hbm_frac"],
                 "traffic": traffic}
