@@ -413,7 +413,8 @@ typedef struct zp_sched_step {
 } zp_sched_step;
 
 /* Rejects n_max < 2, block_size not in {16,32}, window outside [1, b],
- * num_query_slots < 1, max_running < 1.  The pool is borrowed. */
+ * num_query_slots < 1, max_running < 1.  The pool is borrowed: it must
+ * outlive the scheduler. */
 zp_status zp_sched_create(zp_block_pool* pool, const zp_sched_config* cfg, zp_sched** out);
 void zp_sched_destroy(zp_sched* sched);
 /* Queue a request; prompt_len in [1, N_max*b - w] (longer prompts are
@@ -449,6 +450,7 @@ zp_status zp_sched_stats(const zp_sched* sched, int32_t* num_waiting, int32_t* n
  * ---------------------------------------------------------------------- */
 typedef struct zp_prefix_index zp_prefix_index;
 
+/* The pool is borrowed (it must outlive the index); block_size >= 1. */
 zp_status zp_prefix_index_create(zp_block_pool* pool, int32_t block_size, zp_prefix_index** out);
 /* Gives back the index's references (blocks reaching 0 become free at
  * once, as with zp_block_release). */
