@@ -10,7 +10,8 @@
 // One workgroup (8 waves) per (request, head).  The inverse norms of all T
 // keys go to LDS first.  Then, round by round, every wave holds RB row tiles
 // of 16 keys in registers while the workgroup streams the keys in chunks of
-// 128 through LDS; each (row tile, column tile) pair is a 16x16 MFMA Gram
+// 128 through two LDS buffers (the next chunk's loads are in flight while
+// this one is used); each (row tile, column tile) pair is a 16x16 MFMA Gram
 // tile, scaled by the column keys' inverse norms and added to per-lane row
 // sums, which 16-lane DPP reductions finish.  The diagonal (|k_j|^2 times
 // its inverse norm squared, 1 up to rounding) is subtracted as 1.
@@ -23,7 +24,7 @@ namespace {
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kChunk = 128;        // keys staged in LDS at a time
+constexpr int kChunk = 128;        // keys staged in LDS at a time (64 for 512-byte rows)
 constexpr int kMaxSlots = 8192;    // T bound (inverse norms in LDS)
 
 template <int CTRL>
@@ -45,8 +46,12 @@ __global__ __launch_bounds__(kThreads) void k_redundancy_all(RedundancyParams p)
   constexpr int EB = Mma<DT>::kElemBytes;
   constexpr int ROWB = D * EB;             // bytes per key row
   constexpr int NV = ROWB / 64;            // 16-byte fragments per lane per row
-  constexpr int RB = NV >= 16 ? 1 : 16 / NV;  // row tiles a wave holds (<= 64 registers)
+  constexpr int RB = NV >= 32 ? 1 : 32 / NV;  // row tiles a wave holds (<= 128 registers)
   constexpr int PITCH = ROWB + 16;         // LDS row pitch (breaks bank alignment)
+  constexpr int CH = ROWB > 256 ? kChunk / 2 : kChunk;  // keys per chunk (two buffers fit LDS)
+  constexpr int PIECES = CH * (ROWB / 16);      // 16-byte pieces of a chunk
+  constexpr int PPT = PIECES / kThreads;        // pieces per thread
+  static_assert(PIECES % kThreads == 0, "a chunk is whole pieces per thread");
   const int h = blockIdx.x, r = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -62,7 +67,7 @@ __global__ __launch_bounds__(kThreads) void k_redundancy_all(RedundancyParams p)
   };
 
   __shared__ float s_rinv[kMaxSlots + kChunk];
-  __shared__ __attribute__((aligned(16))) char s_k[kChunk * PITCH];
+  __shared__ __attribute__((aligned(16))) char s_k[2][CH * PITCH];  // double buffer
 
   // inverse norms (0 for a zero key and past the end)
   for (int j = tid; j < T + kChunk; j += kThreads) {
@@ -78,8 +83,18 @@ __global__ __launch_bounds__(kThreads) void k_redundancy_all(RedundancyParams p)
   }
   __syncthreads();
 
+  // the 16-byte pieces this thread loads for a chunk starting at slot c0
+  auto load_chunk = [&](int c0, uint4 (&pf)[PPT]) {
+#pragma unroll
+    for (int u = 0; u < PPT; u++) {
+      const int x = tid + u * kThreads;
+      const int j = c0 + x / (ROWB / 16), piece = x % (ROWB / 16);
+      pf[u] = (j < T && key_ok(j)) ? ldg16(key_row(j) + piece * 16) : make_uint4(0, 0, 0, 0);
+    }
+  };
   const int n_tiles = T / 16;
   const int per_round = kWaves * RB;
+  int par = 0;
   for (int t0 = 0; t0 < n_tiles; t0 += per_round) {
     // this wave's row tiles: t0 + wave*RB + k
     uint4 a[RB][NV];
@@ -98,19 +113,26 @@ __global__ __launch_bounds__(kThreads) void k_redundancy_all(RedundancyParams p)
         for (int v = 0; v < NV; v++) a[k][v] = make_uint4(0, 0, 0, 0);
       }
     }
-    for (int c0 = 0; c0 < T; c0 += kChunk) {
-      __syncthreads();  // the previous chunk is no longer read
-      for (int x = tid; x < kChunk * (ROWB / 16); x += kThreads) {
-        const int jj = x / (ROWB / 16), piece = x % (ROWB / 16);
-        const int j = c0 + jj;
-        const uint4 v = (j < T && key_ok(j)) ? ldg16(key_row(j) + piece * 16) : make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4*>(s_k + jj * PITCH + piece * 16) = v;
+    // Chunks go through two LDS buffers: chunk c is stored into buffer
+    // par, then (after one barrier) the loads of chunk c+1 are issued and
+    // chunk c is consumed.  Buffer par is next written two chunks later,
+    // after a barrier every wave passes only once done with chunk c; the
+    // parity runs on across rounds for the same reason.
+    uint4 pf[PPT];
+    load_chunk(0, pf);
+    for (int c0 = 0; c0 < T; c0 += CH, par ^= 1) {
+      char* buf = s_k[par];
+#pragma unroll
+      for (int u = 0; u < PPT; u++) {
+        const int x = tid + u * kThreads;
+        *reinterpret_cast<uint4*>(buf + (x / (ROWB / 16)) * PITCH + (x % (ROWB / 16)) * 16) = pf[u];
       }
       __syncthreads();
-      const int nct = min(kChunk, T - c0) / 16;
+      if (c0 + CH < T) load_chunk(c0 + CH, pf);
+      const int nct = min(CH, T - c0) / 16;
       for (int ct = 0; ct < nct; ct++) {
         uint4 bf[NV];
-        const char* brow = s_k + (ct * 16 + col) * PITCH + grp * 16;
+        const char* brow = buf + (ct * 16 + col) * PITCH + grp * 16;
 #pragma unroll
         for (int v = 0; v < NV; v++) bf[v] = *reinterpret_cast<const uint4*>(brow + v * 64);
         const float rc = s_rinv[c0 + ct * 16 + col];
