@@ -309,7 +309,10 @@ size_t zp_paged_decode_workspace_bytes(const zp_kv_cache* cache, int32_t num_req
  * [R][max_blocks]; seq_lens: device int32 [R], 0 <= seq_len <= max_blocks*b
  * (0 gives a zero output); out: device float32 [R][Hq][d]; workspace:
  * device, >= zp_paged_decode_workspace_bytes().  Entries of a table beyond
- * ceil(seq_len/b) are never read.
+ * ceil(seq_len/b) are never read.  Device-side guards (the host cannot see
+ * device tables): a seq_len outside [0, max_blocks*b] is clamped into it,
+ * and a table entry outside [0, num_blocks) is skipped -- its slots add
+ * nothing -- so no load ever leaves the pools.
  * ---------------------------------------------------------------------- */
 zp_status zp_paged_decode(const zp_kv_cache* cache, int32_t layer, int32_t num_reqs,
                           const void* q, const int32_t* block_tables, int32_t max_blocks,

@@ -206,6 +206,39 @@ def test_empty_batches_do_nothing():
     np.testing.assert_array_equal(to_numpy(kp), c.k_pool[0])
 
 
+def test_decode_skips_table_entries_outside_the_pool():
+    """A block id outside [0, num_blocks) (negative or too large) is skipped
+    by the kernel's own guard: the output is the attention over the other
+    blocks' slots, which the oracle gets from the table without them (the
+    attention is a sum over the set of slots, so their order is free)."""
+    import compressed_paged_kv_amd as zp
+    from synth.device import to_tensor
+    b, H, Hq, d = 16, 2, 8, 128
+    c = _case("guard", 222, num_reqs=2, num_kv_heads=H, num_q_heads=Hq, head_dim=d,
+              block_size=b, n_max=6, window=1, num_blocks=20)
+    say("[gpu parity] decode with table entries outside the pool")
+    dev = "cuda"
+    kp, vp = to_tensor(c.k_pool[0], dev), to_tensor(c.v_pool[0], dev)
+    cache = zp.KVCache([kp], [vp], Hq)
+    tab = c.tables.copy()
+    tab[0, 1] = 20 + 5          # past the pool
+    tab[1, 3] = -7              # negative
+    seq = np.array([5 * b + 7, 4 * b], dtype=np.int32)
+    out = torch.full((2, Hq, d), float("nan"), device=dev)
+    zp.paged_decode(cache, 0, to_tensor(c.q_new[0], dev), torch.from_numpy(tab).to(dev),
+                    torch.from_numpy(seq).to(dev), 1.0 / np.sqrt(d), out, None)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    # request 0: blocks 0, 2..5 (the last holds 7 slots); request 1: blocks 0..2
+    keep0 = np.array([c.tables[0, i] for i in (0, 2, 3, 4, 5)], dtype=np.int32)
+    want0 = oracle.decode(c.k_pool[0], c.v_pool[0], c.q_new[0][:1], keep0[None],
+                          np.array([4 * b + 7], dtype=np.int32), num_q_heads=Hq)
+    want1 = oracle.decode(c.k_pool[0], c.v_pool[0], c.q_new[0][1:], c.tables[1:, :3],
+                          np.array([3 * b], dtype=np.int32), num_q_heads=Hq)
+    assert np.abs(got[0] - want0[0]).max() <= DECODE_ATOL
+    assert np.abs(got[1] - want1[0]).max() <= DECODE_ATOL
+
+
 def test_append_then_decode_one_token():
     """A request of length 1: the appended row is the only key, so the output
     equals the appended value exactly (softmax over one slot)."""
