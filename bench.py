@@ -633,6 +633,21 @@ def run_continuous(args):
         one_step(t, True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # GPU time by phase over a further stretch of steps, from HIP events
+    # around every kernel on its own stream (the two streams overlap, so
+    # each duration includes the slowdown from sharing the GPU)
+    n_prof = min(50, steps)
+    log(f"{n_prof} more steps with per-kernel events")
+    zp.profile_enable(True)
+    zp.profile_read()
+    t_base = args.warmup * 4 + steps
+    for t in range(t_base, t_base + n_prof):
+        one_step(t, False)
+    torch.cuda.synchronize()
+    prof = zp.profile_read()
+    zp.profile_enable(False)
+    comp_ms = sum(prof[k][0] for k in ("upload", "score", "compact"))
+    dec_ms = sum(prof[k][0] for k in ("append", "decode", "combine"))
     c = counters
     return {
         "metric": METRIC, "value": round(c["compressions"] / wall, 1), "unit": "compressions/s",
@@ -651,6 +666,10 @@ def run_continuous(args):
         # bound of the achieved HBM rate (the compressions' traffic is extra)
         "decode_read_GBs": round(c["decode_bytes"] / wall / 1e9, 1),
         "decode_read_hbm_frac_lower_bound": round(c["decode_bytes"] / wall / 1e9 / HBM_PEAK_GBS, 4),
+        "gpu_ms_per_step_by_phase": {"compression": round(comp_ms / n_prof, 3),
+                                     "decode": round(dec_ms / n_prof, 3),
+                                     "compression_share": round(comp_ms / max(comp_ms + dec_ms, 1e-9), 4),
+                                     "steps": n_prof},
     }
 
 
