@@ -40,7 +40,7 @@
  * force, closed forms, library routines or invariants, except the choices
  * of combination (s = A(1-R)), aggregation (mean over the group) and LRS
  * reduction (mean cosine), which the pages leave open and which are pinned
- * only by their definitions.
+ * only by their definitions: parity unpinned for those three choices.
  */
 #include <math.h>
 #include <stdint.h>
