@@ -15,7 +15,9 @@ from typing import List, Optional, Sequence
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libzp.so")
+# ZP_LIBRARY names another build of the same library (the host-side
+# sanitizer test loads an instrumented one); by default the in-tree build.
+LIB_PATH = os.environ.get("ZP_LIBRARY") or os.path.join(HERE, "libzp.so")
 
 ZP_OK, ZP_ERR_INVALID, ZP_ERR_NO_BLOCKS, ZP_ERR_HIP, ZP_ERR_STATE = range(5)
 ZP_F32, ZP_BF16 = 0, 1

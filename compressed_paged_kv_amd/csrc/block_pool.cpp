@@ -311,7 +311,7 @@ zp_status zp_compress_plan_n(zp_block_pool* pool, int32_t n_src, int32_t n_max, 
   if (num_reqs > 0) {
     std::memcpy(src_out, plan.src.data(), plan.src.size() * sizeof(int32_t));
     std::memcpy(dst_out, plan.dst.data(), plan.dst.size() * sizeof(int32_t));
-    std::memcpy(freed_ids, plan.freed.data(), plan.freed.size() * sizeof(int32_t));
+    std::copy(plan.freed.begin(), plan.freed.end(), freed_ids);  // may be empty
   }
   if (num_freed) *num_freed = (int32_t)plan.freed.size();
   zp::add_pending(pool, std::move(plan.freed), nullptr);

@@ -25,7 +25,7 @@ namespace {
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kChunk = 128;        // keys staged in LDS at a time (64 for 512-byte rows)
-constexpr int kMaxSlots = 8192;    // T bound (inverse norms in LDS)
+constexpr int kMaxSlots = kMaxRedundancySlots;  // T bound (inverse norms in LDS)
 
 template <int CTRL>
 __device__ inline float dpp_f(float x) {
@@ -184,8 +184,6 @@ hipError_t launch_dt(const RedundancyParams& p, int head_dim, int block_size, hi
 }
 
 }  // namespace
-
-int redundancy_max_slots() { return kMaxSlots; }
 
 hipError_t launch_redundancy_all(const RedundancyParams& p, int dtype, int head_dim,
                                  int block_size, hipStream_t s) {

@@ -593,12 +593,6 @@ __global__ __launch_bounds__(64 * score_waves<RG>(), (kMaxWaves / score_waves<RG
   }
 }
 
-// More than 64 rows take two row groups, which keep three T-long arrays in
-// LDS (T <= 4096, which also keeps a wave's block count within one id per
-// lane).  At 64 rows or fewer one group is faster: with two, each block is
-// read by two waves and the second read often misses L2.
-bool score_two_groups(int row_tiles, int T) { return row_tiles > 4 && T <= 4096; }
-
 template <int DT, int D, int B, int RT, int RG>
 hipError_t launch_rt(const ScoreParams& p, int units, hipStream_t s) {
   prof_begin(ZP_PHASE_SCORE, s);
@@ -636,19 +630,6 @@ hipError_t launch_dt(const ScoreParams& p, int head_dim, int block_size, int row
 
 }  // namespace
 
-int score_row_tiles(int rows) {
-  if (rows <= 0 || rows > kMaxScoreRows) return 0;
-  const int t = (rows + 15) / 16;
-  int p2 = 1;
-  while (p2 < t) p2 <<= 1;
-  return p2;
-}
-
-bool score_fits(int rows, int T) {
-  const int rt = score_row_tiles(rows);
-  if (rt == 0 || T > kMaxScoreSlots) return false;
-  return rt <= 4 || score_two_groups(rt, T);
-}
 
 hipError_t launch_score(const ScoreParams& p, int dtype, int head_dim, int block_size, int units,
                         hipStream_t s) {

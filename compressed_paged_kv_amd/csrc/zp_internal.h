@@ -29,6 +29,8 @@ constexpr int kMaxScoreSlots = 8192;
 // Largest eviction count per (layer, request, head) the compaction's LDS list
 // holds: E = block_size * (n_src - n_max + 1).
 constexpr int kMaxEvicted = 1024;
+// Largest T of the all-pairs redundancy (inverse norms of all keys in LDS).
+constexpr int kMaxRedundancySlots = 8192;
 // Paged decode: threads per workgroup, and the workgroup count below which
 // a request's block list is split over several workgroups.
 #ifndef ZP_DECODE_THREADS
@@ -102,7 +104,6 @@ hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, int blo
 hipError_t launch_append(const AppendParams& p, hipStream_t s);
 hipError_t launch_redundancy_all(const RedundancyParams& p, int dtype, int head_dim,
                                  int block_size, hipStream_t s);
-int redundancy_max_slots();
 // Copies bytes (a multiple of 16, 16-byte aligned ends) from device-visible
 // pinned host memory to device memory with a kernel on stream s.
 hipError_t launch_upload(const void* host_src, void* dst, size_t bytes, hipStream_t s);
@@ -116,8 +117,25 @@ hipError_t launch_first_evict(const int32_t* evicted, int32_t* host_out, int R, 
 void prof_begin(int phase, hipStream_t s);
 void prof_end(int phase, hipStream_t s);
 
-// Geometry helpers shared by the validation and the workspace layout.
-int score_row_tiles(int rows);     // 1, 2, 4 or 8 tiles of 16 rows; 0 if rows > kMaxScoreRows
-bool score_fits(int rows, int T);  // the fused scoring + selection kernel handles this shape
+// Geometry of the scoring kernel, shared by the host validation and the
+// launcher.  Window rows come in 1, 2, 4 or 8 tiles of 16 (0: too many).
+inline int score_row_tiles(int rows) {
+  if (rows <= 0 || rows > kMaxScoreRows) return 0;
+  const int t = (rows + 15) / 16;
+  int p2 = 1;
+  while (p2 < t) p2 <<= 1;
+  return p2;
+}
+// More than 64 rows take two row groups, which keep three T-long arrays in
+// LDS (T <= 4096, which also keeps a wave's block count within one id per
+// lane).  At 64 rows or fewer one group is faster: with two, each block is
+// read by two waves and the second read often misses L2.
+inline bool score_two_groups(int row_tiles, int T) { return row_tiles > 4 && T <= 4096; }
+// The fused scoring + selection kernel handles this shape.
+inline bool score_fits(int rows, int T) {
+  const int rt = score_row_tiles(rows);
+  if (rt == 0 || T > kMaxScoreSlots) return false;
+  return rt <= 4 || score_two_groups(rt, T);
+}
 
 }  // namespace zp

@@ -32,9 +32,12 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_build.LIB):
-        _build.build()
-    lib = ctypes.CDLL(_build.LIB)
+    path = os.environ.get("ZP_ORACLE_LIBRARY")  # an instrumented build (sanitizer test)
+    if not path:
+        path = _build.LIB
+        if not os.path.exists(path):
+            _build.build()
+    lib = ctypes.CDLL(path)
     lib.zpo_num_threads.restype = ctypes.c_int
     lib.zpo_plan.restype = ctypes.c_int
     lib.zpo_plan.argtypes = [ctypes.c_int32, _i32p, ctypes.c_int32, ctypes.c_int32,
