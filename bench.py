@@ -568,6 +568,7 @@ def run_continuous(args):
     pin_i32 = [torch.empty((4, R0 * n_max), dtype=torch.int32, pin_memory=True) for _ in range(2)]
     counters = dict(decode_tokens=0, compressions=0, preempted=0, finished=0, steps=0,
                     decode_batch=0, slot_waits=0, decode_bytes=0)
+    done_ids = set()
 
     def one_step(t: int, count: bool):
         par = t % 2
@@ -583,6 +584,7 @@ def run_continuous(args):
             counters["decode_batch"] += R_d
             counters["slot_waits"] += sched.stats()["running"] - R_d - R_c - int(plan["admitted"].size)
             counters["steps"] += 1
+        done_ids.update(int(i) for i in plan["finished"])
         for _ in range(int(plan["finished"].size)):
             arrive()
         # decode inputs through one pinned staging buffer per parity
@@ -646,6 +648,15 @@ def run_continuous(args):
     torch.cuda.synchronize()
     prof = zp.profile_read()
     zp.profile_enable(False)
+    # integrity after the whole run: every block's reference count equals the
+    # number of live requests' tables holding it (nothing leaked, nothing
+    # freed while referenced)
+    pool.fence()
+    live = np.array([i for i in range(next_id[0]) if i not in done_ids], dtype=np.int64)
+    tabs, _ = sched.tables(live)
+    want_rc = np.bincount(tabs[tabs >= 0].reshape(-1), minlength=nb)
+    rc_mismatch = int((pool.refcounts() != want_rc).sum())
+    log(f"pool check over {live.size} live requests: {rc_mismatch} blocks with a wrong count")
     comp_ms = sum(prof[k][0] for k in ("upload", "score", "compact"))
     dec_ms = sum(prof[k][0] for k in ("append", "decode", "combine"))
     c = counters
@@ -666,6 +677,8 @@ def run_continuous(args):
         # bound of the achieved HBM rate (the compressions' traffic is extra)
         "decode_read_GBs": round(c["decode_bytes"] / wall / 1e9, 1),
         "decode_read_hbm_frac_lower_bound": round(c["decode_bytes"] / wall / 1e9 / HBM_PEAK_GBS, 4),
+        "pool_refcount_mismatches_after_run": rc_mismatch,
+        "free_blocks_after_run": pool.num_free(),
         "gpu_ms_per_step_by_phase": {"compression": round(comp_ms / n_prof, 3),
                                      "decode": round(dec_ms / n_prof, 3),
                                      "compression_share": round(comp_ms / max(comp_ms + dec_ms, 1e-9), 4),
