@@ -136,6 +136,37 @@ def test_exact_ties_keep_the_lower_slots(dtype, d, b, n_max, w):
     check_case(case, run)
 
 
+def _max_shift_case():
+    """Window queries along one direction u per head and the keys of every
+    request's first block along -2u: those 16 slots get by far the smallest
+    importance, so the whole first block is evicted and every survivor moves
+    up by b slots -- the largest in-place shift, where each compaction tile
+    reads the rows the tile after it overwrites."""
+    c = _case("shift", 223, num_reqs=2, n_max=20, num_kv_heads=2, num_q_heads=8, num_blocks=64)
+    g = c.geom
+    H, Hq, d, b = g.num_kv_heads, g.num_q_heads, g.head_dim, g.block_size
+    G = Hq // H
+    rng = np.random.default_rng(2230)
+    u = rng.standard_normal((H, d))
+    wq = np.repeat(u, G, axis=0)[None, None] + 0.3 * rng.standard_normal((c.num_reqs, c.window, Hq, d))
+    c.window_q[0] = synth.f32_to_bf16_bits(wq.astype(np.float32))
+    for r in range(c.num_reqs):
+        blk = int(c.tables[r, 0])
+        keys = -2.0 * u[:, None, :] + 0.3 * rng.standard_normal((H, b, d))
+        c.k_pool[0][blk] = synth.f32_to_bf16_bits(keys.astype(np.float32))
+    return c
+
+
+def test_first_block_evicted_whole_every_row_moves():
+    case = _max_shift_case()
+    say("[gpu parity] maximum in-place shift: every head evicts its first block")
+    run = run_case(case)
+    b = case.geom.block_size
+    first = run.kept[0][..., 0]
+    assert np.all(first == b), first            # slots 0..b-1 gone: every kept row moved
+    check_case(case, run)
+
+
 def test_qwen3_8b_layer_full_size():
     """64 requests at budget 2048 (N_max=128, b=16, w=16), 8 KV / 32 query
     heads, d=128, bf16, pool of 16384 blocks: every output compared."""

@@ -174,21 +174,24 @@ def test_shared_prefix_full_size_sampled():
 
 def test_compress_overlapped_with_decode():
     """Compression of two requests on one stream while the others append and
-    decode on another (the decode of the next step waiting on an event):
-    results bit-identical to running the same work serially, and equal to
-    the oracle."""
-    say("overlap: 8 requests x 3 layers, 2 compress on stream A, 6 decode on stream B")
+    decode on another (the decode of the next step waiting on an event); all
+    eight requests share a 4-block prefix, which the compression re-targets
+    while the decode reads it: results bit-identical to running the same
+    work serially, the shared blocks unchanged, and equal to the oracle."""
+    say("overlap: 8 requests x 3 layers sharing 4 blocks, 2 compress on stream A, 6 decode on B")
     dev = torch.device("cuda:0")
+    P = 4
     base = synth.make_case("overlap", 301, num_reqs=8, num_layers=3, num_kv_heads=2, num_q_heads=8,
                            head_dim=128, block_size=16, n_max=24, window=16, num_blocks=256,
-                           dtype="bf16", key_scale_range=(0.5, 2.0))
+                           dtype="bf16", key_scale_range=(0.5, 2.0), shared_prefix_blocks=P)
     g = base.geom
     L, H, Hq, d, b = g.num_layers, g.num_kv_heads, g.num_q_heads, g.head_dim, g.block_size
     n_max, w = base.n_max, base.window
     T, k_keep = n_max * b, (n_max - 1) * b
     comp, dec = np.array([1, 5]), np.array([0, 2, 3, 4, 6, 7])
     rng = np.random.default_rng(3011)
-    lens = rng.integers(1, T - 1, size=len(dec)).astype(np.int32)
+    # appends land past the shared prefix (a shared block is never written)
+    lens = rng.integers(P * b, T - 1, size=len(dec)).astype(np.int32)
     lens[0] = T - 1                      # a full last block but for the appended slot
     tables_c = np.ascontiguousarray(base.tables[comp])
     tables_d = np.ascontiguousarray(base.tables[dec])
@@ -246,6 +249,12 @@ def test_compress_overlapped_with_decode():
         assert np.array_equal(words(ser[2][l]), words(ovl[2][l]))
         assert np.array_equal(words(ser[3][l]), words(ovl[3][l]))
     np.testing.assert_array_equal(ser[4].view(np.uint32), ovl[4].view(np.uint32))
+    shared = base.tables[0, :P]
+    assert np.all(base.tables[:, :P] == shared)
+    assert not np.any(np.isin(ovl[0], shared))        # the compressed requests left the prefix
+    for l in range(L):                                 # ... and never wrote it
+        assert np.array_equal(words(ovl[2][l][shared]), words(base.k_pool[l][shared]))
+        assert np.array_equal(words(ovl[3][l][shared]), words(base.v_pool[l][shared]))
     # the compressing requests against the oracle (their own sub-batch)
     sub = synth.CompressCase("overlap_comp", base.seed, g, n_max, w, tables_c,
                              np.bincount(tables_c.reshape(-1), minlength=g.num_blocks).astype(np.int32),
