@@ -108,6 +108,12 @@ def run_case(case, device="cuda", decode=True, recorded_lse=False, keep_prefix=F
                  k_pool=[to_numpy(t) for t in kp], v_pool=[to_numpy(t) for t in vp],
                  out=None, appended_k=None, appended_v=None)
     if decode:
+        # poison the reserved blocks' slots past the one about to be appended:
+        # a decode that strayed past the length would turn its output NaN
+        reserved = torch.from_numpy(tables[:, n_max - 1].astype(np.int64)).to(device)
+        for layer in range(L):
+            for t in (kp[layer], vp[layer]):
+                t[reserved, :, 1:, :] = float("nan")
         slot = tables[:, k_keep // b] * b + k_keep % b
         slot_t = torch.from_numpy(slot.astype(np.int32)).to(device)
         tab_t = torch.from_numpy(np.ascontiguousarray(tables[:, :n_max])).to(device)
@@ -203,6 +209,10 @@ def check_case(case, run: GpuRun, *, check_decode=True, layers=None, keep_prefix
             kp, vp = run.k_pool[layer].copy(), run.v_pool[layer].copy()
             slot = (run.tables[:, k_keep // b] * b + k_keep % b).astype(np.int32)
             oracle.append(kp, vp, case.k_new[layer], case.v_new[layer], slot)
+            # run_case poisoned the reserved blocks' slots past the appended one
+            res = run.tables[:, n_max - 1]
+            kp[res, :, 1:, :] = run.appended_k[layer][res, :, 1:, :]
+            vp[res, :, 1:, :] = run.appended_v[layer][res, :, 1:, :]
             assert np.array_equal(words(run.appended_k[layer]), words(kp))
             assert np.array_equal(words(run.appended_v[layer]), words(vp))
             want = oracle.decode(kp, vp, case.q_new[layer],
