@@ -327,3 +327,43 @@ def test_keep_prefix_matches_oracle_on_random_prefixes(name):
     run = run_case(case, keep_prefix=True)
     stats = check_case(case, run, keep_prefix=True)
     say(f"[gpu parity] keep-prefix {name}: ok {stats}")
+
+
+def _random_configs(n, seed):
+    """Seeded random shapes inside the host's limits, including the corner
+    n_max = 2 (one target block plus the reserved one; with w = b every
+    candidate is evicted)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        b = int(rng.choice([16, 32]))
+        w = int(rng.integers(1, b + 1))
+        G = int(rng.choice([1, 2, 4, 8]))
+        H = int(rng.integers(1, 3))
+        n_max = 2 if len(out) < 3 else int(rng.integers(2, 33))
+        n_src = n_max + int(rng.integers(0, 4)) if rng.random() < 0.3 else n_max
+        if G * w > 128 or (G * w > 64 and n_src * b > 4096):
+            continue
+        if (n_src - n_max + 1) * b > 1024:
+            continue
+        R = int(rng.integers(1, 4))
+        L = int(rng.integers(1, 3))
+        P = int(rng.integers(0, min(n_max - 1, 3) + 1)) if R > 1 and rng.random() < 0.4 else 0
+        nb = P + R * (n_src - P) + R * n_max + 4
+        out.append(dict(num_reqs=R, num_layers=L, num_kv_heads=H, num_q_heads=H * G,
+                        head_dim=int(rng.choice([64, 128])), block_size=b, n_max=n_max,
+                        window=w, num_blocks=nb, dtype=str(rng.choice(["bf16", "f32"])),
+                        shared_prefix_blocks=P, n_src=n_src))
+    # n_max = 2 with w = b: no candidate survives (K_sel = 0)
+    out.append(dict(num_reqs=2, num_layers=1, num_kv_heads=2, num_q_heads=4, head_dim=128,
+                    block_size=16, n_max=2, window=16, num_blocks=12, dtype="bf16",
+                    shared_prefix_blocks=0, n_src=2))
+    return out
+
+
+@pytest.mark.parametrize("i,cfg", list(enumerate(_random_configs(24, 4242))))
+def test_random_shapes_match_oracle(i, cfg):
+    case = synth.make_case(f"rand{i}", 5000 + i, **cfg)
+    say(f"[gpu parity] random shape {i}: {cfg}")
+    run = run_case(case)
+    check_case(case, run)
