@@ -373,6 +373,9 @@ def run_single_stream(args, workload, cache, pool, tables, wq_sets, q_new, k_new
     # 2) the same K steps again with HIP events recorded around every kernel
     #    on its launch stream, for per-kernel durations (the events add small
     #    gaps between kernels, so this region's wall time is reported apart)
+    # the rows the compaction moves drift slowly from step to step: count
+    # them right around the region the per-kernel durations come from
+    moved_pre = moved_rows()
     log(f"timing {args.steps} steps with per-kernel events")
     zp.profile_enable(True)
     zp.profile_read()
@@ -385,6 +388,7 @@ def run_single_stream(args, workload, cache, pool, tables, wq_sets, q_new, k_new
     prof = zp.profile_read()
     zp.profile_enable(False)
     ms_per_step_events = (t3 - t2) * 1e3 / args.steps
+    moved_post = moved_rows()
     # 3) the compression fed with recorded window normalisers (the scoring
     #    reads K once): before each step the normalisers of the step's window
     #    rows are computed on the current cache by zp_paged_decode_lse, as the
@@ -399,7 +403,7 @@ def run_single_stream(args, workload, cache, pool, tables, wq_sets, q_new, k_new
     assert tables.tolist() == tables0.tolist(), "in-place compression changed the tables"
     assert np.isfinite(out.cpu().numpy()).all()
 
-    moved = 0.5 * (moved_before + moved_after)
+    moved = 0.5 * (moved_pre + moved_post)
     nsplit = zp.paged_decode_workspace_bytes(cache, R, n_max) // (R * Hq * (d + 2) * 4)
     alg, flops = _alg_bytes(R, R, 1, H, Hq, d, b, n_max, w, moved, R * seq, nsplit=nsplit,
                             append_rows=R * b)
@@ -442,7 +446,8 @@ def run_single_stream(args, workload, cache, pool, tables, wq_sets, q_new, k_new
         "decode_us": round(dec_us, 2),
         "decode_hbm_frac": round(dec_bytes / (dec_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         "moved_rows_per_step": int(moved),
-        "moved_rows_before_after": [moved_before, moved_after],
+        "moved_rows_before_after": [moved_pre, moved_post],
+        "moved_rows_first_last": [moved_before, moved_after],
         "kernels": kernels,
         "roofline": roofline,
     }
