@@ -367,3 +367,46 @@ def test_random_shapes_match_oracle(i, cfg):
     say(f"[gpu parity] random shape {i}: {cfg}")
     run = run_case(case)
     check_case(case, run)
+
+
+def _random_decode_configs(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        b, d = int(rng.choice([16, 32])), int(rng.choice([64, 128]))
+        G, H = int(rng.choice([1, 2, 4, 8])), int(rng.integers(1, 4))
+        R, mb = int(rng.integers(1, 40)), int(rng.integers(1, 70))
+        seqs = rng.integers(0, mb * b + 1, size=R).astype(np.int32)
+        out.append((b, d, G, H, R, mb, str(rng.choice(["bf16", "f32"])), seqs))
+    return out
+
+
+@pytest.mark.parametrize("i,cfg", list(enumerate(_random_decode_configs(20, 31))))
+def test_random_decode_shapes_match_oracle(i, cfg):
+    """Seeded random batches (with and without splits of the block list):
+    output and log-sum-exp against the oracle."""
+    import compressed_paged_kv_amd as zp
+    from synth.device import to_tensor
+    b, d, G, H, R, mb, dtype, seqs = cfg
+    c = synth.make_case(f"dec{i}", 70000 + i, num_reqs=R, num_layers=1, num_kv_heads=H,
+                        num_q_heads=H * G, head_dim=d, block_size=b, n_max=mb, window=1,
+                        num_blocks=R * mb + 3, dtype=dtype)
+    say(f"[gpu parity] random decode {i}: R={R} H={H} G={G} d={d} b={b} max_blocks={mb} {dtype}")
+    dev = "cuda"
+    kp, vp = to_tensor(c.k_pool[0], dev), to_tensor(c.v_pool[0], dev)
+    cache = zp.KVCache([kp], [vp], H * G)
+    out = torch.full((R, H * G, d), float("nan"), device=dev)
+    lse = torch.full((R, H * G), float("nan"), device=dev)
+    ws = torch.empty(max(zp.paged_decode_workspace_bytes(cache, R, mb), 16), dtype=torch.uint8,
+                     device=dev)
+    zp.paged_decode(cache, 0, to_tensor(c.q_new[0], dev), torch.from_numpy(c.tables).to(dev),
+                    torch.from_numpy(seqs).to(dev), 1.0 / np.sqrt(d), out, ws, lse_out=lse)
+    torch.cuda.synchronize()
+    want = oracle.decode(c.k_pool[0], c.v_pool[0], c.q_new[0], c.tables, seqs, num_q_heads=H * G)
+    want_lse = oracle.decode_lse(c.k_pool[0], c.q_new[0], c.tables, seqs, num_q_heads=H * G)
+    got, got_lse = out.cpu().numpy(), lse.cpu().numpy()
+    assert np.isfinite(got).all() and np.abs(got - want).max() <= DECODE_ATOL
+    fin = np.isfinite(want_lse)
+    np.testing.assert_array_equal(np.isfinite(got_lse), fin)      # -inf for empty requests
+    if fin.any():
+        assert np.abs(got_lse[fin] - want_lse[fin]).max() <= 1e-4 * max(1.0, np.abs(want_lse[fin]).max())
