@@ -134,13 +134,213 @@ __device__ inline int block_incl_sum(int v, int* scratch) {
   return v + before;
 }
 
-template <int NW>
-__device__ inline int block_broadcast_last(int v, int* scratch) {
-  if (threadIdx.x == 64 * NW - 1) scratch[NW] = v;
+// Minimum over the wave: DPP inside 16-lane rows, then the row swaps.
+template <int CTRL>
+__device__ inline uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, true);
+}
+__device__ inline uint32_t wave_min_u32(uint32_t x) {
+  x = min(x, dpp_u32<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = min(x, dpp_u32<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = min(x, dpp_u32<0x141>(x));  // row_half_mirror
+  x = min(x, dpp_u32<0x140>(x));  // row_mirror
+  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = min(a[0], a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return min(b[0], b[1]);
+}
+
+// Selection state in LDS.  Histograms are triple-buffered: pass p counts
+// into buffer p % 3 and clears buffer (p + 1) % 3, which every wave finished
+// scanning before the barrier of pass p - 1, so each pass needs a single
+// barrier.  Small target bins are resolved in `list`.
+constexpr int kSelList = 64;
+struct SelectLds {
+  int hist[3][256];
+  unsigned long long list[kSelList];  // (key << 32) | ~slot of the target bin's candidates
+  uint32_t evict_bits[kMaxScoreSlots / 32];
+  uint32_t wave_min[kMaxWaves], wave_max[kMaxWaves];
+  int count;
+};
+
+// Evicts the E candidates (slots j < C) with the smallest order keys, equal
+// keys taking the higher slot first, and writes them ascending.  Thread t
+// owns the contiguous slots [t*per, t*per + per); PER >= per.
+//   1. The block's smallest and largest key share a prefix, which the
+//      E-th smallest key shares too.
+//   2. Radix passes of up to 8 bits below the known prefix narrow the
+//      bin that holds the E-th smallest key; every wave reads the histogram
+//      and finds the bin itself (4 bins a lane, one wave-wide scan).
+//   3. Once that bin holds at most kSelList keys, each of them is ranked
+//      against the others by (key, higher slot first) and the first `rank`
+//      are marked; if all 32 bits are fixed and the bin is still larger,
+//      its keys are all equal and the highest `rank` slots of them go.
+//   4. One workgroup prefix sum gives every thread its output position.
+template <int PER, int NW>
+__device__ inline void select_evicted(const float* s_sc, SelectLds& L, int* s_scr,
+                                      const ScoreParams& p, size_t unit) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int per = (p.T + 64 * NW - 1) / (64 * NW);
+  const int j0 = tid * per;
+  uint32_t key[PER];
+  if (per == PER) {  // 16-byte groups; a range past T stays inside s_buf (threads * PER floats)
+#pragma unroll
+    for (int i = 0; i < PER; i += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(s_sc + j0 + i);
+      key[i] = order_key(v.x);
+      key[i + 1] = order_key(v.y);
+      key[i + 2] = order_key(v.z);
+      key[i + 3] = order_key(v.w);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < PER; i++) key[i] = (i < per && j0 + i < p.T) ? order_key(s_sc[j0 + i]) : 0u;
+  }
+  auto valid = [&](int i) { return i < per && j0 + i < p.C; };
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+  for (int i = 0; i < PER; i++)
+    if (valid(i)) {
+      kmin = min(kmin, key[i]);
+      kmax = max(kmax, key[i]);
+    }
+  for (int t = tid; t < 256; t += 64 * NW) L.hist[0][t] = 0;
+  for (int t = tid; t < kMaxScoreSlots / 32; t += 64 * NW) L.evict_bits[t] = 0u;
+  if (tid == 0) L.count = 0;
+  kmin = wave_min_u32(kmin);
+  kmax = ~wave_min_u32(~kmax);
+  if (lane == 0) {
+    L.wave_min[wave] = kmin;
+    L.wave_max[wave] = kmax;
+  }
   __syncthreads();
-  const int t = scratch[NW];
-  __syncthreads();
-  return t;
+#pragma unroll
+  for (int w = 0; w < NW; w++) {
+    kmin = min(kmin, L.wave_min[w]);
+    kmax = max(kmax, L.wave_max[w]);
+  }
+  const uint32_t diff = kmin ^ kmax;
+  int done = diff ? __clz((int)diff) : 32;  // leading bits every candidate key shares
+  uint32_t mask = done == 0 ? 0u : done == 32 ? 0xFFFFFFFFu : 0xFFFFFFFFu << (32 - done);
+  uint32_t prefix = kmin & mask;
+  int rank = p.E;   // the E-th smallest key is the rank-th smallest of the bin
+  int cnt = p.C;    // candidates in the bin
+  int pass = 0;
+  while (cnt > kSelList && done < 32) {
+    const int nb = min(8, 32 - done), shift = 32 - done - nb;
+    int* h = L.hist[pass % 3];
+#pragma unroll
+    for (int i = 0; i < PER; i++)
+      if (valid(i) && (key[i] & mask) == prefix) atomicAdd(&h[(key[i] >> shift) & ((1u << nb) - 1u)], 1);
+    for (int t = tid; t < 256; t += 64 * NW) L.hist[(pass + 1) % 3][t] = 0;
+    __syncthreads();
+    const int4 hv = *reinterpret_cast<const int4*>(&h[lane * 4]);
+    const int c4 = hv.x + hv.y + hv.z + hv.w;
+    int incl = c4;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(incl, off);
+      if (lane >= off) incl += t;
+    }
+    const int excl = incl - c4;
+    const unsigned long long hit = __ballot(excl < rank && incl >= rank);
+    const int src = hit ? __builtin_ctzll(hit) : 0;
+    int sb = 0, below = excl, cb = hv.x;
+    if (below + hv.x < rank) {
+      below += hv.x; sb = 1; cb = hv.y;
+      if (below + hv.y < rank) {
+        below += hv.y; sb = 2; cb = hv.z;
+        if (below + hv.z < rank) { below += hv.z; sb = 3; cb = hv.w; }
+      }
+    }
+    const uint32_t bin = (uint32_t)__builtin_amdgcn_readlane(lane * 4 + sb, src);
+    rank -= __builtin_amdgcn_readlane(below, src);
+    cnt = __builtin_amdgcn_readlane(cb, src);
+    prefix |= bin << shift;
+    mask |= ((1u << nb) - 1u) << shift;
+    done += nb;
+    pass++;
+  }
+  const bool listed = cnt <= kSelList;
+  if (listed) {
+    // the bin's candidates into the list: one atomic per wave
+    int mine = 0;
+#pragma unroll
+    for (int i = 0; i < PER; i++) mine += (valid(i) && (key[i] & mask) == prefix) ? 1 : 0;
+    int incl = mine;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(incl, off);
+      if (lane >= off) incl += t;
+    }
+    int base = 0;
+    if (lane == 63 && incl > 0) base = atomicAdd(&L.count, incl);
+    base = __shfl(base, 63) + incl - mine;
+#pragma unroll
+    for (int i = 0; i < PER; i++)
+      if (valid(i) && (key[i] & mask) == prefix) {
+        if (base < kSelList)
+          L.list[base] = ((unsigned long long)key[i] << 32) | (uint32_t)(~(uint32_t)(j0 + i));
+        base++;
+      }
+    __syncthreads();
+    if (tid < cnt) {
+      const unsigned long long me = L.list[tid];
+      int below = 0;
+      for (int u = 0; u < cnt; u++) below += L.list[u] < me ? 1 : 0;
+      if (below < rank) {
+        const uint32_t j = ~(uint32_t)me;
+        atomicOr(&L.evict_bits[j >> 5], 1u << (j & 31));
+      }
+    }
+    __syncthreads();
+  }
+  // per thread: evicted slots decided so far, and (equal-key case) the
+  // keys equal to the bin's key, packed in one prefix sum
+  int sure = 0, ties = 0;
+#pragma unroll
+  for (int i = 0; i < PER; i++) {
+    if (!valid(i)) continue;
+    if (key[i] < prefix) {
+      sure++;
+    } else if ((key[i] & mask) == prefix) {
+      const int j = j0 + i;
+      if (listed) sure += (L.evict_bits[j >> 5] >> (j & 31)) & 1u;
+      else ties++;
+    }
+  }
+  const int packed = sure | (ties << 16);  // both sums stay below 2^16 (T <= 8192)
+  const int excl = block_incl_sum(packed, s_scr) - packed;
+  const int tie_from = cnt - rank;  // tie index (slot order) from which equal keys go
+  int tie_idx = excl >> 16;
+  int pos = (excl & 0xFFFF) + (listed ? 0 : max(0, tie_idx - tie_from));
+  int kept_pos = j0 - pos;  // survivors below j0
+  int32_t* out = p.evicted + unit * p.E;
+#pragma unroll
+  for (int i = 0; i < PER; i++) {
+    const int j = j0 + i;
+    if (i >= per || j >= p.T) continue;
+    bool ev = false;
+    if (j < p.C) {
+      if (key[i] < prefix) {
+        ev = true;
+      } else if ((key[i] & mask) == prefix) {
+        if (listed) {
+          ev = (L.evict_bits[j >> 5] >> (j & 31)) & 1u;
+        } else {
+          ev = tie_idx >= tie_from;
+          tie_idx++;
+        }
+      }
+    }
+    if (ev) {
+      if (pos < p.E) out[pos] = j;
+      pos++;
+    } else {
+      if (p.dbg_kept && kept_pos >= 0 && kept_pos < p.K_keep) p.dbg_kept[unit * p.K_keep + kept_pos] = j;
+      kept_pos++;
+    }
+  }
 }
 
 // Sixteen waves fit a CU when a wave's Q fragments and K ring stay small
@@ -187,13 +387,12 @@ __global__ __launch_bounds__(64 * score_waves<RG>(), (kMaxWaves / score_waves<RG
   const char* kbase = static_cast<const char*>(p.layer_ptrs[l * kPtrsPerLayer + 0]);
   const char* qbase = static_cast<const char*>(p.layer_ptrs[l * kPtrsPerLayer + 2]);
 
-  __shared__ float s_buf[lds_floats<RG>()];
+  __shared__ __align__(16) float s_buf[lds_floats<RG>()];
   __shared__ float s_wst[kWaves][RPW][2];
   __shared__ float s_off[RT * 16];
   __shared__ float s_nrm[kWaves][B];
-  __shared__ int s_hist[256];
   __shared__ int s_scr[kWaves + 1];
-  __shared__ int s_sel[2];
+  __shared__ __align__(16) SelectLds s_sel;
   __shared__ uint4 s_x[SH ? 2 : 1][SH ? WPG : 1][SH ? F : 1][64];  // [parity][pair][fragment][lane]
   float* s_sc = s_buf;          // scores (with two row groups: group 0's partial importance)
   float* s_aux = s_buf + 4096;  // group 1's partial importance (two row groups only)
@@ -523,74 +722,10 @@ __global__ __launch_bounds__(64 * score_waves<RG>(), (kMaxWaves / score_waves<RG
   }
 
   // ---------------------------------------------------------------- select
-  // thread t owns the contiguous slots [t*per, (t+1)*per)
   const int per = (p.T + kThreads - 1) / kThreads;
-  const int j0 = tid * per, j1 = min(j0 + per, p.C);
-  uint32_t prefix = 0, pmask = 0;
-  int rank = p.E;  // the E-th smallest candidate key, counted from 1
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    if (tid < 256) s_hist[tid] = 0;
-    __syncthreads();
-    for (int j = j0; j < j1; j++) {
-      const uint32_t key = order_key(s_sc[j]);
-      if ((key & pmask) == prefix) atomicAdd(&s_hist[(key >> shift) & 0xFFu], 1);
-    }
-    __syncthreads();
-    const int cnt = tid < 256 ? s_hist[tid] : 0;
-    const int incl = block_incl_sum(cnt, s_scr);
-    if (tid < 256 && incl - cnt < rank && incl >= rank) {
-      s_sel[0] = tid;
-      s_sel[1] = incl - cnt;
-    }
-    __syncthreads();
-    prefix |= (uint32_t)s_sel[0] << shift;
-    pmask |= 0xFFu << shift;
-    rank -= s_sel[1];
-    __syncthreads();
-  }
-  const uint32_t tau = prefix;  // the E-th smallest key
-  const int evict_ties = rank;  // how many keys equal to tau are evicted
-  int my_ties = 0;
-  for (int j = j0; j < j1; j++) my_ties += order_key(s_sc[j]) == tau ? 1 : 0;
-  const int ties_incl = block_incl_sum(my_ties, s_scr);
-  const int ties_total = block_broadcast_last<kWaves>(ties_incl, s_scr);
-  // evicted: keys below tau, and the evict_ties highest slots equal to tau
-  int tie_rank = ties_incl - my_ties;
-  int my_ev = 0;
-  for (int j = j0; j < j1; j++) {
-    const uint32_t key = order_key(s_sc[j]);
-    if (key < tau) {
-      my_ev++;
-    } else if (key == tau) {
-      my_ev += tie_rank >= ties_total - evict_ties ? 1 : 0;
-      tie_rank++;
-    }
-  }
-  const int ev_incl = block_incl_sum(my_ev, s_scr);
-  int pos = ev_incl - my_ev;
-  int32_t* out = p.evicted + unit * p.E;
-  tie_rank = ties_incl - my_ties;
-  int kept_pos = j0 - pos;  // survivors below j0
-  const int jend = min(j0 + per, p.T);
-  for (int j = j0; j < jend; j++) {
-    bool ev = false;
-    if (j < p.C) {
-      const uint32_t key = order_key(s_sc[j]);
-      if (key < tau) {
-        ev = true;
-      } else if (key == tau) {
-        ev = tie_rank >= ties_total - evict_ties;
-        tie_rank++;
-      }
-    }
-    if (ev) {
-      if (pos < p.E) out[pos] = j;
-      pos++;
-    } else {
-      if (p.dbg_kept && kept_pos >= 0 && kept_pos < p.K_keep) p.dbg_kept[unit * p.K_keep + kept_pos] = j;
-      kept_pos++;
-    }
-  }
+  if (per <= 8) select_evicted<8, kWaves>(s_sc, s_sel, s_scr, p, unit);
+  else if (per <= 16) select_evicted<16, kWaves>(s_sc, s_sel, s_scr, p, unit);
+  else select_evicted<32, kWaves>(s_sc, s_sel, s_scr, p, unit);
 }
 
 template <int DT, int D, int B, int RT, int RG>

@@ -118,7 +118,7 @@ def _exact_tie_case(dtype, d, b, n_max, w):
 
 
 @pytest.mark.parametrize("dtype,d,b,n_max,w", [("bf16", 128, 16, 20, 16), ("f32", 64, 16, 8, 8),
-                                               ("bf16", 64, 32, 9, 7)])
+                                               ("bf16", 64, 32, 9, 7), ("f32", 64, 16, 4, 8)])
 def test_exact_ties_keep_the_lower_slots(dtype, d, b, n_max, w):
     case = _exact_tie_case(dtype, d, b, n_max, w)
     say(f"[gpu parity] exact tie {dtype} d={d} b={b} n_max={n_max} w={w}")
@@ -132,6 +132,35 @@ def test_exact_ties_keep_the_lower_slots(dtype, d, b, n_max, w):
     assert np.all(cand == cand[..., :1])          # bit-identical scores
     for r in range(case.num_reqs):
         for h in range(case.geom.num_kv_heads):
+            np.testing.assert_array_equal(run.kept[0, r, h], want)
+    check_case(case, run)
+
+
+def test_ties_at_the_threshold_below_some_lower_scores():
+    """The exact-tie cache with, in the second block of every head, keys
+    0..7 made equal: their cosines are 1, so they score below every other
+    candidate and go first, and the remaining E - 8 evictions fall among
+    the equal scores -- the highest slots of those."""
+    case = _exact_tie_case("bf16", 128, 16, 20, 16)
+    say("[gpu parity] 8 lower scores, then exact ties at the threshold")
+    g = case.geom
+    b, d = g.block_size, g.head_dim
+    for r in range(case.num_reqs):
+        blk = int(case.tables[r, 1])
+        for h in range(g.num_kv_heads):
+            row = np.zeros(d, dtype=np.float32)
+            row[0] = 1.0
+            case.k_pool[0][blk, h, :8] = synth.f32_to_bf16_bits(np.tile(row, (8, 1)))
+    run = run_case(case)
+    n_max, w = case.n_max, case.window
+    T, k_keep = n_max * b, (n_max - 1) * b
+    C = T - w
+    E = C - (k_keep - w)
+    gone = set(range(b, b + 8)) | set(range(C - (E - 8), C))
+    want = np.array([j for j in range(T) if j not in gone])
+    assert len(want) == k_keep
+    for r in range(case.num_reqs):
+        for h in range(g.num_kv_heads):
             np.testing.assert_array_equal(run.kept[0, r, h], want)
     check_case(case, run)
 
