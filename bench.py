@@ -116,6 +116,68 @@ def _read_csv(path):
         return list(csv.DictReader(f))
 
 
+HOT_PHASES = {"k_upload": "upload", "k_score_select": "score", "k_compact": "compact",
+              "k_append": "append", "k_decode<": "decode", "k_decode_combine": "combine"}
+SIMDS = 256 * 4   # MI355X: 256 CUs of 4 SIMDs
+XCDS = 8
+
+
+def summarize_counters(dirs) -> int:
+    """Per-dispatch averages of rocprofv3 --pmc counters for the hot-path
+    kernels (several runs, one counter group each), and the ratios derived
+    from them.  SQ_WAVE_CYCLES, SQ_ACTIVE_INST_* and SQ_WAIT_ANY are all in
+    quad-cycles summed over the waves, so their ratios are shares of the
+    waves' resident time.  GRBM_GUI_ACTIVE is summed over the 8 XCDs: divided
+    by 8 and by the dispatch duration it gives the clock, and divided by 8
+    it is the dispatch's cycle count, against which SQ_VALU_MFMA_BUSY_CYCLES
+    (summed over the SIMDs) gives the share of SIMD-cycles the matrix units
+    were busy."""
+    import glob
+    acc, dur, wgs = {}, {}, {}
+    for d in dirs:
+        for r in _read_csv(glob.glob(os.path.join(d, "*counter_collection.csv"))[0]):
+            phase = next((ph for key, ph in HOT_PHASES.items() if key in r["Kernel_Name"]), None)
+            if phase is None:
+                continue
+            acc.setdefault(phase, {}).setdefault(r["Counter_Name"], []).append(
+                float(r["Counter_Value"]))
+            dur.setdefault(phase, {})[(d, r["Dispatch_Id"])] = (
+                int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+            wgs[phase] = int(r["Grid_Size"]) // max(1, int(r["Workgroup_Size"]))
+    print("# Counters per dispatch (rocprofv3 --pmc; averages over the dispatches of each run)")
+    for phase in HOT_PHASES.values():
+        if phase not in acc:
+            continue
+        c = {k: sum(v) / len(v) for k, v in acc[phase].items()}
+        t = sum(dur[phase].values()) / len(dur[phase])
+        print(f"phase {phase}: dispatches {len(dur[phase])}, {t * 1e6:.1f} us each under the "
+              f"profiler, {wgs[phase]} workgroups")
+        for k in sorted(c):
+            print(f"  {k:32s} {c[k]:.6g}")
+        wc = c.get("SQ_WAVE_CYCLES")
+        derived = []
+        if wc:
+            for k, name in (("SQ_ACTIVE_INST_ANY", "issuing any instruction"),
+                            ("SQ_ACTIVE_INST_VALU", "issuing VALU (incl. MFMA) instructions"),
+                            ("SQ_WAIT_ANY", "waiting")):
+                if k in c:
+                    derived.append(f"{name}: {c[k] / wc:.1%} of wave-resident time")
+        gui = c.get("GRBM_GUI_ACTIVE")
+        if gui and t >= 20e-6:  # a short dispatch is dominated by what surrounds it
+            cyc = gui / XCDS
+            derived.append(f"clock {cyc / t / 1e9:.2f} GHz ({cyc:.0f} cycles per dispatch)")
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+                derived.append(f"matrix units busy {c['SQ_VALU_MFMA_BUSY_CYCLES'] / (cyc * SIMDS):.1%}"
+                               f" of SIMD-cycles")
+        for k in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_LDS",
+                  "SQ_INSTS_SALU"):
+            if k in c and wgs[phase]:
+                derived.append(f"{k} per workgroup {c[k] / wgs[phase]:.0f}")
+        for line in derived:
+            print(f"  -> {line}")
+    return 0
+
+
 def summarize(kt_dir: str, fetch_dir: str, write_dir: str) -> int:
     """Summary text of rocprofv3 outputs: kernel-trace statistics of the
     bench run, and HBM bytes per dispatch of each hot-path kernel from the
@@ -128,8 +190,7 @@ def summarize(kt_dir: str, fetch_dir: str, write_dir: str) -> int:
     for r in stats:
         print(f"{r['Name'][:70]:70s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
               f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f}")
-    phases = {"k_upload": "upload", "k_score_select": "score", "k_compact": "compact",
-              "k_append": "append", "k_decode<": "decode", "k_decode_combine": "combine"}
+    phases = HOT_PHASES
 
     def per_kernel(d, counter):
         rows = _read_csv(glob.glob(os.path.join(d, "*counter_collection.csv"))[0])
@@ -1004,9 +1065,14 @@ def main() -> int:
                     help="first run a 1 GiB device copy (counter calibration under rocprofv3)")
     ap.add_argument("--summarize", nargs=3, metavar=("KT_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="print the summary of rocprofv3 csv outputs and exit")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="PMC_DIR",
+                    help="print per-kernel averages of rocprofv3 --pmc runs (SQ/GRBM counters) "
+                         "and exit")
     args = ap.parse_args()
     if args.summarize:
         return summarize(*args.summarize)
+    if args.summarize_counters:
+        return summarize_counters(args.summarize_counters)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this path runs without sharding or "
               f"collectives, so --gpus {args.gpus} is not supported", file=sys.stderr)

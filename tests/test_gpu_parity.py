@@ -86,6 +86,12 @@ CASES = {
                                             num_q_heads=8, n_max=256, num_blocks=260),
     "max_evictions_1024": lambda: _case("m3", 220, num_reqs=2, head_dim=64, n_max=20, n_src=83,
                                         num_blocks=180),
+    # 16 keys per selecting thread: 4096 slots exactly, and a ragged 3200
+    "slots_4096_rows64": lambda: _case("m4", 224, num_reqs=2, num_kv_heads=1, num_q_heads=4,
+                                       n_max=256, num_blocks=520),
+    "slots_3200_rows32_f32": lambda: _case("m5", 225, dtype="f32", head_dim=64, num_reqs=1,
+                                           num_kv_heads=2, num_q_heads=4, n_max=200,
+                                           num_blocks=210),
 }
 
 
