@@ -135,7 +135,11 @@ def summarize_counters(dirs) -> int:
     import glob
     acc, dur, wgs = {}, {}, {}
     for d in dirs:
-        for r in _read_csv(glob.glob(os.path.join(d, "*counter_collection.csv"))[0]):
+        found = glob.glob(os.path.join(d, "*counter_collection.csv"))
+        if not found:
+            print(f"no rocprofv3 counter_collection.csv under {d}", file=sys.stderr)
+            return 1
+        for r in _read_csv(found[0]):
             phase = next((ph for key, ph in HOT_PHASES.items() if key in r["Kernel_Name"]), None)
             if phase is None:
                 continue
