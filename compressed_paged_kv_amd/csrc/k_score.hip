@@ -21,9 +21,11 @@
 //   2. the same blocks again (now in cache): probabilities summed over the
 //      rows in a fixed order (so equal inputs give bit-equal importances),
 //      the in-block Gram matrix for the cosines, and s into LDS;
-//   3. a radix select (4 passes of 8 bits over order-preserving 32-bit keys)
-//      finds the E-th smallest score and how many equal scores go; prefix
-//      counts in slot order give the ascending evicted list.
+//   3. the selection (select_evicted): radix passes over order-preserving
+//      32-bit keys, starting below the prefix all keys share, narrow the bin
+//      of the E-th smallest score; a small bin is ranked exactly, a large
+//      bin of equal keys gives up its highest slots; one prefix sum in slot
+//      order places the ascending evicted list.
 // The rows x b logit tiles and the b x b Gram tiles are 16x16 MFMA tiles:
 // v_mfma_f32_16x16x32_bf16 for bfloat16 caches, v_mfma_f32_16x16x4f32 for
 // float32 ones.  A lane holds operand row (lane % 16) and a 16-byte slice of
@@ -40,9 +42,10 @@ namespace zp {
 namespace {
 
 
-// Waves per workgroup: four with one row group (two workgroups share a CU,
-// so one selects while the other streams K); eight with two row groups,
-// whose paired waves exchange K tiles through LDS.
+// Waves per workgroup: four with one row group (two workgroups share a CU;
+// with more units than workgroup slots one selects while another streams
+// K); eight with two row groups, whose paired waves exchange K tiles
+// through LDS.
 template <int RG>
 constexpr int score_waves() { return RG == 2 ? 8 : 4; }
 constexpr int kMaxWaves = 8;
