@@ -509,7 +509,14 @@ def run_single_stream(args, workload, cache, pool, tables, wq_sets, q_new, k_new
         "decode_tok_s_per_layer": round(R / (dec_us * 1e-6), 1),
         f"decode_tok_s_{layers_model}_layers": round(R / (layers_model * dec_us * 1e-6), 1),
         "decode_us": round(dec_us, 2),
+        # the append here writes the whole reserved block (the pending token
+        # and the b-1 rows that keep the steps alike); the attention kernel's
+        # own fraction is decode_attention_hbm_frac
         "decode_hbm_frac": round(dec_bytes / (dec_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "decode_attention_hbm_frac": round(
+            sum(alg[p] for p in ("decode", "combine"))
+            / (max(sum(per.get(p, 0.0) for p in ("decode", "combine")), 1e-9) * 1e-6)
+            / 1e9 / HBM_PEAK_GBS, 4),
         "moved_rows_per_step": int(moved),
         "moved_rows_before_after": [moved_pre, moved_post],
         "moved_rows_first_last": [moved_before, moved_after],
