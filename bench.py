@@ -40,10 +40,16 @@ KERNEL_SOURCES = {
     "upload": "compressed_paged_kv_amd/csrc/k_upload.hip",
     "score": "compressed_paged_kv_amd/csrc/k_score.hip",
     "compact": "compressed_paged_kv_amd/csrc/k_compact.hip",
+    "score_compact": "compressed_paged_kv_amd/csrc/k_score.hip",
     "decode": "compressed_paged_kv_amd/csrc/k_decode.hip",
     "combine": "compressed_paged_kv_amd/csrc/k_decode.hip",
     "append": "compressed_paged_kv_amd/csrc/k_decode.hip",
 }
+
+
+# phases of a compression call: the scoring kernel either selects only (then
+# the compaction kernel follows) or also compacts ("score_compact")
+COMPRESS_PHASES = ("upload", "score", "compact", "score_compact")
 
 
 def log(msg: str) -> None:
@@ -117,7 +123,8 @@ def _read_csv(path):
 
 
 HOT_PHASES = {"k_upload": "upload", "k_score_select": "score", "k_compact": "compact",
-              "k_append": "append", "k_decode<": "decode", "k_decode_combine": "combine"}
+              "k_score_compact": "score_compact", "k_append": "append", "k_decode<": "decode",
+              "k_decode_combine": "combine"}
 SIMDS = 256 * 4   # MI355X: 256 CUs of 4 SIMDs
 XCDS = 8
 
@@ -280,7 +287,9 @@ def _alg_bytes(R_c, R_d, L, H, Hq, d, b, n_max, w, moved_rows, dec_tokens, eb=2,
         "decode": dec_tokens * H * kv_row * 2 + R_d * Hq * kv_row,
         "combine": R_d * Hq * nsplit * (d + 2) * 4 + R_d * Hq * d * 4,
     }
+    alg["score_compact"] = alg["score"] + alg["compact"]
     flops = {"score": L * (2 * Hq * w * T * d * R_c + 2 * H * n_max * b * b * d * R_c)}
+    flops["score_compact"] = flops["score"]
     return alg, flops
 
 
@@ -480,9 +489,9 @@ def run_single_stream(args, workload, cache, pool, tables, wq_sets, q_new, k_new
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dom["hbm_frac"],
                 "traffic": traffic}
     per = {k["phase"]: k["avg_us"] for k in kernels}
-    comp_us = sum(per.get(p, 0.0) for p in ("upload", "score", "compact"))
+    comp_us = sum(per.get(p, 0.0) for p in COMPRESS_PHASES)
     dec_us = sum(per.get(p, 0.0) for p in ("append", "decode", "combine"))
-    comp_bytes = sum(alg[p] for p in ("upload", "score", "compact"))
+    comp_bytes = sum(alg[p] for p in COMPRESS_PHASES if p in per)
     dec_bytes = sum(alg[p] for p in ("append", "decode", "combine"))
     layers_model = 36 if b == 16 else 32
     result = {
@@ -547,16 +556,16 @@ def run_single_stream(args, workload, cache, pool, tables, wq_sets, q_new, k_new
         result["cpu_baseline"] = None
         return result
     rec_us = {k["phase"]: k["avg_us"] for k in _kernel_rows(rec, alg, flops)}
-    rec_comp = sum(rec_us.get(p, 0.0) for p in ("upload", "score", "compact"))
+    rec_comp = sum(rec_us.get(p, 0.0) for p in COMPRESS_PHASES)
+    rec_bytes = sum(alg[p] for p in COMPRESS_PHASES if p in rec_us)
     result["recorded_lse"] = {
         "what": "compression with the window rows' softmax normalisers recorded by the decode "
                 "steps that produced the window queries (zp_compress_lse): the scoring reads K "
                 "once; per-phase HIP-event averages",
-        "score_us": rec_us.get("score"), "compact_us": rec_us.get("compact"),
+        "kernel_us": {p: rec_us[p] for p in COMPRESS_PHASES if p in rec_us},
         "compress_us": round(rec_comp, 2),
         "compress_per_s": round(R / (rec_comp * 1e-6), 1),
-        "score_hbm_frac": round(alg["score"] / (rec_us["score"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-        "compress_hbm_frac": round(comp_bytes / (rec_comp * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "compress_hbm_frac": round(rec_bytes / (rec_comp * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
     }
     result["lrs_ablation"] = {
         "what": "all-pairs redundancy (mean cosine with every other slot, O(N^2 b^2) pairs) "
@@ -567,7 +576,9 @@ def run_single_stream(args, workload, cache, pool, tables, wq_sets, q_new, k_new
         "all_pairs_mfma_TFLOPs": round(ra_flops / (ra_us * 1e-6) / 1e12, 1),
         "all_pairs_mfma_frac": round(ra_flops / (ra_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "lrs_gram_flops": 2.0 * H * n_max * b * b * d * R,
-        "score_kernel_us": per.get("score"),
+        # the scoring kernel, with the compaction when that is fused into it
+        "score_kernel_us": per.get("score", per.get("score_compact")),
+        "score_kernel_compacts": "score_compact" in per,
     }
     if cpu_case is not None and not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
@@ -734,7 +745,7 @@ def run_continuous(args):
     want_rc = np.bincount(tabs[tabs >= 0].reshape(-1), minlength=nb)
     rc_mismatch = int((pool.refcounts() != want_rc).sum())
     log(f"pool check over {live.size} live requests: {rc_mismatch} blocks with a wrong count")
-    comp_ms = sum(prof[k][0] for k in ("upload", "score", "compact"))
+    comp_ms = sum(prof[k][0] for k in COMPRESS_PHASES)
     dec_ms = sum(prof[k][0] for k in ("append", "decode", "combine"))
     c = counters
     return {
@@ -931,11 +942,10 @@ def run_over_cap(args):
     prof = zp.profile_read()
     zp.profile_enable(False)
     t_c = float(np.median(times))
-    gpu_us = sum(k["avg_us"] for k in _kernel_rows(prof, {}, {})
-                 if k["phase"] in ("upload", "score", "compact"))
+    gpu_us = sum(k["avg_us"] for k in _kernel_rows(prof, {}, {}) if k["phase"] in COMPRESS_PHASES)
     alg, flops = _alg_bytes(R, 0, 1, H, Hq, d, b, n_src, w, moved, 0, n_max_keep=n_max)
-    kernels = [k for k in _kernel_rows(prof, alg, flops) if k["phase"] in ("upload", "score", "compact")]
-    comp_bytes = alg["upload"] + alg["score"] + alg["compact"]
+    kernels = [k for k in _kernel_rows(prof, alg, flops) if k["phase"] in COMPRESS_PHASES]
+    comp_bytes = sum(alg[k["phase"]] for k in kernels)
     return {
         "metric": METRIC, "value": round(R / (t_c * 1e-3), 1), "unit": "compressions/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(t_c, 4),

@@ -531,7 +531,7 @@ class Scheduler:
 # --------------------------------------------------------------------------- timing
 
 PHASES = ("upload", "score_stats", "score", "select", "compact", "append", "decode", "combine",
-          "redundancy_all")
+          "redundancy_all", "score_compact")
 
 
 def profile_enable(on: bool = True) -> None:

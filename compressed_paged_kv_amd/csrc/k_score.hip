@@ -67,6 +67,10 @@ constexpr int lds_floats() { return RG == 2 ? 3 * 4096 : 8192; }
 #define ZP_SCORE_REVERSE 1
 #endif
 constexpr bool kReversePass2 = ZP_SCORE_REVERSE != 0;
+#ifndef ZP_FUSED_UNROLL
+#define ZP_FUSED_UNROLL 6
+#endif
+constexpr int kFusedUnroll = ZP_FUSED_UNROLL;  // rows per thread per tile of the fused compaction
 
 template <bool V>
 struct BoolC {
@@ -179,9 +183,10 @@ struct SelectLds {
 //      are marked; if all 32 bits are fixed and the bin is still larger,
 //      its keys are all equal and the highest `rank` slots of them go.
 //   4. One workgroup prefix sum gives every thread its output position.
+// s_f (LDS, may be null) also gets f_i = e_i - i for the i-th evicted slot.
 template <int PER, int NW>
 __device__ inline void select_evicted(const float* s_sc, SelectLds& L, int* s_scr,
-                                      const ScoreParams& p, size_t unit) {
+                                      const ScoreParams& p, size_t unit, int* s_f) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int per = (p.T + 64 * NW - 1) / (64 * NW);
   const int j0 = tid * per;
@@ -337,11 +342,109 @@ __device__ inline void select_evicted(const float* s_sc, SelectLds& L, int* s_sc
       }
     }
     if (ev) {
-      if (pos < p.E) out[pos] = j;
+      if (pos < p.E) {
+        out[pos] = j;
+        if (s_f) s_f[pos] = j - pos;
+      }
       pos++;
     } else {
       if (p.dbg_kept && kept_pos >= 0 && kept_pos < p.K_keep) p.dbg_kept[unit * p.K_keep + kept_pos] = j;
       kept_pos++;
+    }
+  }
+}
+
+// Compaction of one (layer, request, head) unit right after its selection,
+// by the workgroup that scored it: logical slot r < K_keep of the target
+// blocks receives old slot kept[r], for K and V, with kept rebuilt from the
+// evicted list as kept[r] = r + #{i : f_i <= r}, f_i = e_i - i (nl page
+// Methodologie item 1, ko page section 2.C: survivors move in order into the
+// first N_max-1 blocks; shared sources are never written).
+//
+// Units never touch each other's rows: a unit writes only rows of its own
+// head and layer, in blocks private to its request or freshly allocated, and
+// every other unit reads other heads, layers or requests.  Inside the unit
+// the in-place rule of the standalone compaction holds: target slot r is old
+// slot r or a fresh block, old slot r is read only by rows r' <= r, and the
+// workgroup walks ascending tiles whose loads all return before the barrier
+// and whose stores all come after it.  Rows below the first evicted slot and
+// the first re-targeted block stay where they are.
+//
+// LDS (inside the score array, free once the keys are in registers): f from
+// the selection, then kept, and the request's source and target block ids.
+template <int VPR, int B, int NTH, int U>
+__device__ inline void compact_unit(const ScoreParams& p, float* lds, int* s_first, int l, int r,
+                                    int h) {
+  constexpr int kRowsPerPass = NTH / VPR;
+  constexpr int kRowsPerTile = kRowsPerPass * U;
+  constexpr size_t kRowBytes = (size_t)VPR * 16;
+  const int tid = threadIdx.x;
+  const int vec = tid % VPR, rsub = tid / VPR;
+  const int* f = reinterpret_cast<const int*>(lds);
+  unsigned short* kept = reinterpret_cast<unsigned short*>(lds + kMaxEvicted);
+  int* srcb = reinterpret_cast<int*>(lds + kMaxEvicted + kMaxScoreSlots / 2);
+  int* dstb = srcb + kMaxScoreSlots / 16;
+  for (int n = tid; n < p.n_src; n += NTH) srcb[n] = p.src[(size_t)r * p.n_src + n];
+  for (int n = tid; n < p.n_max - 1; n += NTH) dstb[n] = p.dst[(size_t)r * (p.n_max - 1) + n];
+  if (tid == 0) *s_first = p.K_keep;
+  __syncthreads();  // f (written by the selection) and the block ids are in LDS
+  // the first re-targeted block (a new block for a shared source) ...
+  for (int n = tid; n < p.n_max - 1; n += NTH)
+    if (dstb[n] != srcb[n]) atomicMin(s_first, n * B);
+  for (int row = tid; row < p.K_keep; row += NTH) {
+    int lo = 0, hi = p.E;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (f[mid] <= row) lo = mid + 1; else hi = mid;
+    }
+    kept[row] = (unsigned short)(row + lo);
+  }
+  __syncthreads();
+  // ... and the first evicted slot (f_0 = e_0): nothing below both moves
+  const int first = min(min(*s_first, p.E > 0 ? f[0] : p.K_keep), p.K_keep);
+  if (first >= p.K_keep) return;  // nothing moves (uniform)
+
+  char* const kbase = static_cast<char*>(p.layer_ptrs[l * kPtrsPerLayer + 0]) + vec * 16;
+  char* const vbase = static_cast<char*>(p.layer_ptrs[l * kPtrsPerLayer + 1]) + vec * 16;
+  auto row_of = [&](int blk, int off) -> int { return (blk * p.H + h) * B + off; };
+  auto off_of = [&](int row) -> size_t { return (size_t)(unsigned)row * kRowBytes; };
+  // rows past the end are clamped to the last row; unmoved rows are read
+  // but not written (target -1)
+  auto load_tile = [&](int t0, uint4 (&kb)[U], uint4 (&vb)[U], int (&to)[U]) {
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const int row = min(t0 + rsub + u * kRowsPerPass, p.K_keep - 1);
+      const int j = kept[row];
+      const int from = row_of(srcb[j / B], j % B);
+      const int dst = row_of(dstb[row / B], row % B);
+      kb[u] = ldg16_stream(kbase + off_of(from));
+      vb[u] = ldg16_stream(vbase + off_of(from));
+      to[u] = (dst != from && t0 + rsub + u * kRowsPerPass < p.K_keep) ? dst : -1;
+    }
+  };
+  uint4 ck[U], cv[U], nk[U], nv[U];
+  int cto[U], nto[U];
+  load_tile(first, ck, cv, cto);
+  for (int t0 = first; t0 < p.K_keep; t0 += kRowsPerTile) {
+    load_tile(min(t0 + kRowsPerTile, p.K_keep - 1), nk, nv, nto);
+    // every load of this tile has returned before any thread stores
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      asm volatile("" ::"v"(ck[u].x), "v"(ck[u].y), "v"(ck[u].z), "v"(ck[u].w));
+      asm volatile("" ::"v"(cv[u].x), "v"(cv[u].y), "v"(cv[u].z), "v"(cv[u].w));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < U; u++)
+      if (cto[u] >= 0) {
+        stg16_stream(kbase + off_of(cto[u]), ck[u]);
+        stg16_stream(vbase + off_of(cto[u]), cv[u]);
+      }
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      ck[u] = nk[u];
+      cv[u] = nv[u];
+      cto[u] = nto[u];
     }
   }
 }
@@ -356,8 +459,10 @@ constexpr int score_min_blocks() {
 // RG row groups: with two, waves 0-3 take the first half of the row tiles and
 // waves 4-7 the second, both over all blocks, which halves the Q fragments a
 // wave holds.
-template <int DT, int D, int B, int RT, int RG>
-__global__ __launch_bounds__(64 * score_waves<RG>(), (kMaxWaves / score_waves<RG>()) * (score_min_blocks<DT, D, RT / RG, B>())) void k_score_select(ScoreParams p) {
+// FUSE: the workgroup also compacts its unit (compact_unit) after the
+// selection.
+template <int DT, int D, int B, int RT, int RG, bool FUSE>
+__device__ __forceinline__ void score_unit(const ScoreParams& p) {
   constexpr int kWaves = score_waves<RG>();
   constexpr int kThreads = 64 * kWaves;
   constexpr int EB = Mma<DT>::kElemBytes;
@@ -726,16 +831,38 @@ __global__ __launch_bounds__(64 * score_waves<RG>(), (kMaxWaves / score_waves<RG
 
   // ---------------------------------------------------------------- select
   const int per = (p.T + kThreads - 1) / kThreads;
-  if (per <= 8) select_evicted<8, kWaves>(s_sc, s_sel, s_scr, p, unit);
-  else if (per <= 16) select_evicted<16, kWaves>(s_sc, s_sel, s_scr, p, unit);
-  else select_evicted<32, kWaves>(s_sc, s_sel, s_scr, p, unit);
+  int* s_f = FUSE ? reinterpret_cast<int*>(s_buf) : nullptr;  // the scores are in registers by then
+  if (per <= 8) select_evicted<8, kWaves>(s_sc, s_sel, s_scr, p, unit, s_f);
+  else if (per <= 16) select_evicted<16, kWaves>(s_sc, s_sel, s_scr, p, unit, s_f);
+  else select_evicted<32, kWaves>(s_sc, s_sel, s_scr, p, unit, s_f);
+  if constexpr (FUSE) {
+    __shared__ int s_first;
+    compact_unit<ROWB / 16, B, kThreads, kFusedUnroll>(p, s_buf, &s_first, l, r, h);
+  }
+}
+
+template <int DT, int D, int B, int RT, int RG>
+__global__ __launch_bounds__(64 * score_waves<RG>(), (kMaxWaves / score_waves<RG>()) * (score_min_blocks<DT, D, RT / RG, B>())) void k_score_select(ScoreParams p) {
+  score_unit<DT, D, B, RT, RG, false>(p);
+}
+
+template <int DT, int D, int B, int RT, int RG>
+__global__ __launch_bounds__(64 * score_waves<RG>(), (kMaxWaves / score_waves<RG>()) * (score_min_blocks<DT, D, RT / RG, B>())) void k_score_compact(ScoreParams p) {
+  score_unit<DT, D, B, RT, RG, true>(p);
 }
 
 template <int DT, int D, int B, int RT, int RG>
 hipError_t launch_rt(const ScoreParams& p, int units, hipStream_t s) {
-  prof_begin(ZP_PHASE_SCORE, s);
-  hipLaunchKernelGGL((k_score_select<DT, D, B, RT, RG>), dim3(units), dim3(64 * score_waves<RG>()), 0, s, p);
-  prof_end(ZP_PHASE_SCORE, s);
+  const dim3 grid(units), block(64 * score_waves<RG>());
+  if (p.dst) {
+    prof_begin(ZP_PHASE_SCORE_COMPACT, s);
+    hipLaunchKernelGGL((k_score_compact<DT, D, B, RT, RG>), grid, block, 0, s, p);
+    prof_end(ZP_PHASE_SCORE_COMPACT, s);
+  } else {
+    prof_begin(ZP_PHASE_SCORE, s);
+    hipLaunchKernelGGL((k_score_select<DT, D, B, RT, RG>), grid, block, 0, s, p);
+    prof_end(ZP_PHASE_SCORE, s);
+  }
   return hipGetLastError();
 }
 
@@ -773,6 +900,10 @@ hipError_t launch_score(const ScoreParams& p, int dtype, int head_dim, int block
                         hipStream_t s) {
   if (units <= 0) return hipSuccess;
   if (!score_fits(p.rows, p.T)) return hipErrorInvalidValue;
+  // the fused compaction's LDS lists: E evicted slots, n_src <= 512 blocks
+  if (p.dst && (p.E < 0 || p.E > kMaxEvicted || p.n_src > kMaxScoreSlots / 16 || p.n_max < 2 ||
+                p.n_max > p.n_src || p.K_keep != (p.n_max - 1) * block_size))
+    return hipErrorInvalidValue;
   const int rt = score_row_tiles(p.rows);
   if (dtype == ZP_BF16) return launch_dt<ZP_BF16>(p, head_dim, block_size, rt, units, s);
   if (dtype == ZP_F32) return launch_dt<ZP_F32>(p, head_dim, block_size, rt, units, s);

@@ -50,7 +50,8 @@ struct ScoreParams {
   float* dbg_redundancy;    // optional [L*R*H][T]
   float* dbg_score;         // optional [L*R*H][T]
   int32_t* dbg_kept;        // optional [L*R*H][K_keep]
-  int32_t R, H, Hq, G, w, n_src, T, C, E, K_keep, rows;  // T = n_src * b
+  const int32_t* dst;       // device [R][n_max-1] target blocks: compact in the same kernel; null: select only
+  int32_t R, H, Hq, G, w, n_src, n_max, T, C, E, K_keep, rows;  // T = n_src * b
   float scale_log2;  // log2(e) / sqrt(d)
 };
 

@@ -498,7 +498,8 @@ typedef enum {
   ZP_PHASE_DECODE = 6,      /* paged decode attention */
   ZP_PHASE_COMBINE = 7,     /* merge of the decode splits */
   ZP_PHASE_REDUNDANCY_ALL = 8, /* zp_redundancy_all */
-  ZP_NUM_PHASES = 9
+  ZP_PHASE_SCORE_COMPACT = 9,  /* scoring, selection and compaction in one kernel */
+  ZP_NUM_PHASES = 10
 } zp_phase;
 
 zp_status zp_profile_enable(int32_t on);
