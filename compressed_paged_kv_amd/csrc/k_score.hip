@@ -408,8 +408,10 @@ __device__ inline void compact_unit(const ScoreParams& p, float* lds, int* s_fir
   char* const vbase = static_cast<char*>(p.layer_ptrs[l * kPtrsPerLayer + 1]) + vec * 16;
   auto row_of = [&](int blk, int off) -> int { return (blk * p.H + h) * B + off; };
   auto off_of = [&](int row) -> size_t { return (size_t)(unsigned)row * kRowBytes; };
-  // rows past the end are clamped to the last row; unmoved rows are read
-  // but not written (target -1)
+  // Rows past the end are clamped to the last row; unmoved rows are read
+  // but not written (target -1).  K rows are loaded normally: the scoring
+  // has just read them, and they are often still cached (non-temporal loads
+  // made the fused kernel 6 % slower); V rows and all stores are streamed.
   auto load_tile = [&](int t0, uint4 (&kb)[U], uint4 (&vb)[U], int (&to)[U]) {
 #pragma unroll
     for (int u = 0; u < U; u++) {
@@ -417,7 +419,7 @@ __device__ inline void compact_unit(const ScoreParams& p, float* lds, int* s_fir
       const int j = kept[row];
       const int from = row_of(srcb[j / B], j % B);
       const int dst = row_of(dstb[row / B], row % B);
-      kb[u] = ldg16_stream(kbase + off_of(from));
+      kb[u] = ldg16(kbase + off_of(from));
       vb[u] = ldg16_stream(vbase + off_of(from));
       to[u] = (dst != from && t0 + rsub + u * kRowsPerPass < p.K_keep) ? dst : -1;
     }
