@@ -372,7 +372,7 @@ __device__ inline void select_evicted(const float* s_sc, SelectLds& L, int* s_sc
 //
 // LDS (inside the score array, free once the keys are in registers): f from
 // the selection, then kept, and the request's source and target block ids.
-template <int VPR, int B, int NTH, int U>
+template <int VPR, int B, int NTH, int U, bool KCACHED>
 __device__ inline void compact_unit(const ScoreParams& p, float* lds, int* s_first, int l, int r,
                                     int h) {
   constexpr int kRowsPerPass = NTH / VPR;
@@ -409,9 +409,11 @@ __device__ inline void compact_unit(const ScoreParams& p, float* lds, int* s_fir
   auto row_of = [&](int blk, int off) -> int { return (blk * p.H + h) * B + off; };
   auto off_of = [&](int row) -> size_t { return (size_t)(unsigned)row * kRowBytes; };
   // Rows past the end are clamped to the last row; unmoved rows are read
-  // but not written (target -1).  K rows are loaded normally: the scoring
-  // has just read them, and they are often still cached (non-temporal loads
-  // made the fused kernel 6 % slower); V rows and all stores are streamed.
+  // but not written (target -1).  V rows and all stores are streamed.  K
+  // rows are loaded normally (KCACHED) when every unit of the call is
+  // resident at once: the scoring has just read them and many are still
+  // cached.  With several rounds of workgroups, normal loads only crowd out
+  // what the later rounds' scoring reads, and K is streamed too.
   auto load_tile = [&](int t0, uint4 (&kb)[U], uint4 (&vb)[U], int (&to)[U]) {
 #pragma unroll
     for (int u = 0; u < U; u++) {
@@ -419,7 +421,7 @@ __device__ inline void compact_unit(const ScoreParams& p, float* lds, int* s_fir
       const int j = kept[row];
       const int from = row_of(srcb[j / B], j % B);
       const int dst = row_of(dstb[row / B], row % B);
-      kb[u] = ldg16(kbase + off_of(from));
+      kb[u] = KCACHED ? ldg16(kbase + off_of(from)) : ldg16_stream(kbase + off_of(from));
       vb[u] = ldg16_stream(vbase + off_of(from));
       to[u] = (dst != from && t0 + rsub + u * kRowsPerPass < p.K_keep) ? dst : -1;
     }
@@ -839,7 +841,10 @@ __device__ __forceinline__ void score_unit(const ScoreParams& p) {
   else select_evicted<32, kWaves>(s_sc, s_sel, s_scr, p, unit, s_f);
   if constexpr (FUSE) {
     __shared__ int s_first;
-    compact_unit<ROWB / 16, B, kThreads, kFusedUnroll>(p, s_buf, &s_first, l, r, h);
+    if (p.k_cached)  // uniform: one tile loop or the other, each straight-line
+      compact_unit<ROWB / 16, B, kThreads, kFusedUnroll, true>(p, s_buf, &s_first, l, r, h);
+    else
+      compact_unit<ROWB / 16, B, kThreads, kFusedUnroll, false>(p, s_buf, &s_first, l, r, h);
   }
 }
 

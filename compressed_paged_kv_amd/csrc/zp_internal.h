@@ -51,6 +51,7 @@ struct ScoreParams {
   float* dbg_score;         // optional [L*R*H][T]
   int32_t* dbg_kept;        // optional [L*R*H][K_keep]
   const int32_t* dst;       // device [R][n_max-1] target blocks: compact in the same kernel; null: select only
+  int32_t k_cached;         // fused compaction: load K normally (1) or non-temporally (0)
   int32_t R, H, Hq, G, w, n_src, n_max, T, C, E, K_keep, rows;  // T = n_src * b
   float scale_log2;  // log2(e) / sqrt(d)
 };
