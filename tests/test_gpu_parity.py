@@ -86,6 +86,11 @@ CASES = {
                                             num_q_heads=8, n_max=256, num_blocks=260),
     "max_evictions_1024": lambda: _case("m3", 220, num_reqs=2, head_dim=64, n_max=20, n_src=83,
                                         num_blocks=180),
+    # more (layer, request, head) units than two per compute unit (576 on a
+    # 256-CU MI355X): the fused compaction streams K instead of loading it
+    # normally
+    "units_576_streamed_k": lambda: _case("m6", 226, num_reqs=24, num_layers=3, num_kv_heads=8,
+                                          num_q_heads=16, head_dim=64, n_max=6, num_blocks=200),
     # 16 keys per selecting thread: 4096 slots exactly, and a ragged 3200
     "slots_4096_rows64": lambda: _case("m4", 224, num_reqs=2, num_kv_heads=1, num_q_heads=4,
                                        n_max=256, num_blocks=520),
