@@ -450,3 +450,24 @@ def test_random_decode_shapes_match_oracle(i, cfg):
     np.testing.assert_array_equal(np.isfinite(got_lse), fin)      # -inf for empty requests
     if fin.any():
         assert np.abs(got_lse[fin] - want_lse[fin]).max() <= 1e-4 * max(1.0, np.abs(want_lse[fin]).max())
+
+
+@pytest.mark.parametrize("name", ["bf16_d128_b16_ragged", "bf16_d64_b32_rows128",
+                                  "f32_d128_b32_w5", "over_cap_bf16_3_extra",
+                                  "units_576_streamed_k"])
+def test_fused_compaction_equals_the_standalone_kernel(name):
+    """Without shared blocks the prefix-keeping call makes the same plan as
+    the plain one, but runs the selection and the compaction as two kernels
+    (its plan waits for the selection), while the plain call compacts inside
+    the scoring kernel: the pools and tables must come out bit-identical."""
+    case = CASES[name]()
+    assert np.all(case.refcounts <= 1), "the case must have no shared blocks"
+    say(f"[gpu parity] fused vs standalone compaction: {name}")
+    fused = run_case(case, decode=False)
+    split = run_case(case, decode=False, keep_prefix=True)
+    np.testing.assert_array_equal(fused.tables, split.tables)
+    np.testing.assert_array_equal(fused.refcounts, split.refcounts)
+    np.testing.assert_array_equal(fused.kept, split.kept)
+    for a, b in zip(fused.k_pool + fused.v_pool, split.k_pool + split.v_pool):
+        assert np.array_equal(np.ascontiguousarray(a).view(np.uint8),
+                              np.ascontiguousarray(b).view(np.uint8))
