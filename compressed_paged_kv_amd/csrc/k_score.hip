@@ -409,11 +409,12 @@ __device__ inline void compact_unit(const ScoreParams& p, float* lds, int* s_fir
   auto row_of = [&](int blk, int off) -> int { return (blk * p.H + h) * B + off; };
   auto off_of = [&](int row) -> size_t { return (size_t)(unsigned)row * kRowBytes; };
   // Rows past the end are clamped to the last row; unmoved rows are read
-  // but not written (target -1).  V rows and all stores are streamed.  K
-  // rows are loaded normally (KCACHED) when every unit of the call is
+  // but not written (target -1).  V rows are streamed both ways.  K rows
+  // are loaded and stored normally (KCACHED) when every unit of the call is
   // resident at once: the scoring has just read them and many are still
-  // cached.  With several rounds of workgroups, normal loads only crowd out
-  // what the later rounds' scoring reads, and K is streamed too.
+  // cached, and the decode that follows finds some of the stored rows
+  // there.  With several rounds of workgroups, normal accesses only crowd
+  // out what the later rounds' scoring reads, and K is streamed too.
   auto load_tile = [&](int t0, uint4 (&kb)[U], uint4 (&vb)[U], int (&to)[U]) {
 #pragma unroll
     for (int u = 0; u < U; u++) {
@@ -441,7 +442,8 @@ __device__ inline void compact_unit(const ScoreParams& p, float* lds, int* s_fir
 #pragma unroll
     for (int u = 0; u < U; u++)
       if (cto[u] >= 0) {
-        stg16_stream(kbase + off_of(cto[u]), ck[u]);
+        if constexpr (KCACHED) stg16(kbase + off_of(cto[u]), ck[u]);
+        else stg16_stream(kbase + off_of(cto[u]), ck[u]);
         stg16_stream(vbase + off_of(cto[u]), cv[u]);
       }
 #pragma unroll
