@@ -63,6 +63,12 @@ class _SchedStep(ctypes.Structure):
                 ("num_released", ctypes.c_int32)]
 
 
+class _CompressInfo(ctypes.Structure):
+    _fields_ = [("units", ctypes.c_int32), ("threads", ctypes.c_int32),
+                ("resident_per_cu", ctypes.c_int32), ("compute_units", ctypes.c_int32),
+                ("k_cached", ctypes.c_int32)]
+
+
 class _Debug(ctypes.Structure):
     _fields_ = [("importance", ctypes.c_void_p), ("redundancy", ctypes.c_void_p),
                 ("score", ctypes.c_void_p), ("kept", ctypes.c_void_p)]
@@ -129,6 +135,8 @@ def lib() -> ctypes.CDLL:
         "zp_compress_workspace_bytes_n": (ctypes.c_size_t, [ctypes.POINTER(_KVCache),
                                                             ctypes.c_int32, ctypes.c_int32,
                                                             ctypes.c_int32, ctypes.c_int32]),
+        "zp_compress_query": (S, [ctypes.POINTER(_KVCache), ctypes.c_int32, ctypes.c_int32,
+                                  ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(_CompressInfo)]),
         "zp_append_kv": (S, [ctypes.POINTER(_KVCache), ctypes.c_int32, ctypes.c_int32, _vp, _vp,
                              _vp, _vp]),
         "zp_paged_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(_KVCache),
@@ -188,6 +196,35 @@ def _stream_handle(stream) -> Optional[int]:
 
 def _dptr(t) -> Optional[int]:
     return None if t is None else int(t.data_ptr())
+
+
+def _want(t, name: str, device, dtype, shape) -> None:
+    """Raise ValueError unless ``t`` is a contiguous tensor on ``device`` with
+    ``dtype`` and ``shape`` (None entries of ``shape`` match any size).  The
+    kernels take raw pointers: a CPU tensor, a wrong element type or a short
+    buffer would send them to invalid addresses, which the C layer cannot
+    see."""
+    if not hasattr(t, "data_ptr") or not hasattr(t, "is_contiguous"):
+        raise ValueError(f"{name}: expected a tensor, got {type(t).__name__}")
+    if t.device != device:
+        raise ValueError(f"{name}: on {t.device}, the cache is on {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if shape is not None:
+        got = tuple(int(x) for x in t.shape)
+        if len(got) != len(shape) or any(w is not None and g != w for g, w in zip(got, shape)):
+            want = tuple("*" if w is None else w for w in shape)
+            raise ValueError(f"{name}: shape {got}, expected {want}")
+
+
+def _want_bytes(t, name: str, device, nbytes: int) -> None:
+    """A contiguous device buffer of at least ``nbytes`` bytes (workspaces)."""
+    _want(t, name, device, None, None)
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError(f"{name}: {have} bytes, needs {nbytes}")
 
 
 # --------------------------------------------------------------------------- pool
@@ -314,6 +351,12 @@ class KVCache:
         for t in self.k_pools + self.v_pools:
             if tuple(t.shape) != (nb, H, b, d) or t.dtype != k0.dtype or not t.is_contiguous():
                 raise ValueError("every pool must be a contiguous tensor of the same shape and dtype")
+        self.device = k0.device
+        self.torch_dtype = k0.dtype
+        if self.device.type != "cuda":
+            raise ValueError(f"the pools must be GPU tensors, got {self.device}")
+        if any(t.device != self.device for t in self.k_pools + self.v_pools):
+            raise ValueError("every pool must be on the same device")
         n = self.num_layers
         self._k_arr = (_vp * n)(*[t.data_ptr() for t in self.k_pools])
         self._v_arr = (_vp * n)(*[t.data_ptr() for t in self.v_pools])
@@ -337,6 +380,17 @@ def compress_workspace_bytes(cache: KVCache, num_reqs: int, n_max: int, window: 
     return n
 
 
+def compress_query(cache: KVCache, num_reqs: int, n_max: int, window: int,
+                   n_src: Optional[int] = None) -> dict:
+    """zp_compress_query: how a compression call of this shape runs on the
+    current device (units, threads, resident workgroups per compute unit,
+    compute units, and whether the fused compaction loads K normally)."""
+    info = _CompressInfo()
+    _check(lib().zp_compress_query(cache.ref, num_reqs, n_max if n_src is None else n_src, n_max,
+                                   window, ctypes.byref(info)))
+    return {f: int(getattr(info, f)) for f, _ in _CompressInfo._fields_}
+
+
 def compress(cache: KVCache, pool: BlockPool, n_max: int, window: int, tables: np.ndarray,
              window_q: List, workspace, stream=None, debug: Optional[dict] = None,
              window_lse: Optional[List] = None, keep_prefix: bool = False) -> np.ndarray:
@@ -346,8 +400,31 @@ def compress(cache: KVCache, pool: BlockPool, n_max: int, window: int, tables: n
     (host int32 [R][n_src]) is rewritten on success; returns the freed block
     ids.  ``keep_prefix``: zp_compress_keep_prefix (shared blocks the
     compaction leaves unchanged stay shared)."""
-    assert tables.dtype == np.int32 and tables.flags.c_contiguous
+    import torch
+    if not (isinstance(tables, np.ndarray) and tables.dtype == np.int32 and tables.ndim == 2
+            and tables.flags.c_contiguous):
+        raise ValueError("tables: expected a C-contiguous host int32 [R][n_src] array")
     R, n_src = (int(x) for x in tables.shape)
+    L, H, Hq, d, b = (cache.num_layers, cache.num_kv_heads, cache.num_q_heads, cache.head_dim,
+                      cache.block_size)
+    dev = cache.device
+    if len(window_q) != L:
+        raise ValueError(f"window_q: {len(window_q)} entries for {L} layers")
+    for l, t in enumerate(window_q):
+        _want(t, f"window_q[{l}]", dev, cache.torch_dtype, (R, window, Hq, d))
+    if window_lse is not None:
+        if len(window_lse) != L:
+            raise ValueError(f"window_lse: {len(window_lse)} entries for {L} layers")
+        for l, t in enumerate(window_lse):
+            _want(t, f"window_lse[{l}]", dev, torch.float32, (R, window, Hq))
+    _want(workspace, "workspace", dev, None, None)
+    if debug:
+        T, k_keep = n_src * b, (n_max - 1) * b
+        for key in ("importance", "redundancy", "score"):
+            if debug.get(key) is not None:
+                _want(debug[key], f"debug[{key!r}]", dev, torch.float32, (L, R, H, T))
+        if debug.get("kept") is not None:
+            _want(debug["kept"], "debug['kept']", dev, torch.int32, (L, R, H, k_keep))
     wq = (_vp * cache.num_layers)(*[t.data_ptr() for t in window_q])
     wl = None
     if window_lse is not None:
@@ -389,6 +466,13 @@ def compress(cache: KVCache, pool: BlockPool, n_max: int, window: int, tables: n
 
 
 def append_kv(cache: KVCache, layer: int, k_new, v_new, slot_mapping, stream=None) -> None:
+    """zp_append_kv: k_new, v_new [R][H][d] (cache dtype), slot_mapping int32 [R]."""
+    import torch
+    dev = cache.device
+    _want(slot_mapping, "slot_mapping", dev, torch.int32, (None,))
+    kv = (int(slot_mapping.shape[0]), cache.num_kv_heads, cache.head_dim)
+    _want(k_new, "k_new", dev, cache.torch_dtype, kv)
+    _want(v_new, "v_new", dev, cache.torch_dtype, kv)
     _check(lib().zp_append_kv(cache.ref, layer, int(slot_mapping.shape[0]), k_new.data_ptr(),
                               v_new.data_ptr(), slot_mapping.data_ptr(), _stream_handle(stream)))
 
@@ -402,7 +486,23 @@ def paged_decode(cache: KVCache, layer: int, q, tables, seq_lens, scale: float, 
     """zp_paged_decode, or zp_paged_decode_lse when ``lse_out`` (float
     [rows][Hq]) or ``q_out`` ([rows][Hq][d], cache dtype) is given;
     ``lse_rows`` (int32 [R]) maps requests to rows."""
+    import torch
+    dev, Hq, d = cache.device, cache.num_q_heads, cache.head_dim
+    _want(tables, "tables", dev, torch.int32, (None, None))
     R, max_blocks = (int(x) for x in tables.shape)
+    _want(q, "q", dev, cache.torch_dtype, (R, Hq, d))
+    _want(seq_lens, "seq_lens", dev, torch.int32, (R,))
+    _want(out, "out", dev, torch.float32, (R, Hq, d))
+    if workspace is not None:
+        _want(workspace, "workspace", dev, None, None)
+    if lse_out is not None:
+        _want(lse_out, "lse_out", dev, torch.float32, (None, Hq))
+    if q_out is not None:
+        _want(q_out, "q_out", dev, cache.torch_dtype, (None, Hq, d))
+        if lse_out is not None and int(q_out.shape[0]) != int(lse_out.shape[0]):
+            raise ValueError("q_out and lse_out must have the same number of rows")
+    if lse_rows is not None:
+        _want(lse_rows, "lse_rows", dev, torch.int32, (R,))
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     if lse_out is None and q_out is None:
@@ -419,7 +519,10 @@ def paged_decode(cache: KVCache, layer: int, q, tables, seq_lens, scale: float, 
 
 def redundancy_all(cache: KVCache, layer: int, tables, out, stream=None) -> None:
     """zp_redundancy_all: tables device int32 [R][n_blocks], out float [R][H][T]."""
+    import torch
+    _want(tables, "tables", cache.device, torch.int32, (None, None))
     R, n_blocks = (int(x) for x in tables.shape)
+    _want(out, "out", cache.device, torch.float32, (R, cache.num_kv_heads, n_blocks * cache.block_size))
     _check(lib().zp_redundancy_all(cache.ref, layer, R, tables.data_ptr(), n_blocks,
                                    out.data_ptr(), _stream_handle(stream)))
 

@@ -28,13 +28,26 @@ void zp_block_pool::reap() {
     }
     if (done) {
       for (int32_t id : p.ids) free_ids.insert(id);
-      (void)hipEventDestroy(p.event);
+      give_back_event(p.event);
     } else {
       if (keep != i) pending[keep] = std::move(p);
       keep++;
     }
   }
   pending.resize(keep);
+}
+
+hipError_t zp_block_pool::take_event(hipEvent_t* out) {
+  if (!spare_events.empty()) {
+    *out = spare_events.back();
+    spare_events.pop_back();
+    return hipSuccess;
+  }
+  return hipEventCreateWithFlags(out, hipEventDisableTiming);
+}
+
+void zp_block_pool::give_back_event(hipEvent_t e) {
+  if (e) spare_events.push_back(e);
 }
 
 int32_t zp_block_pool::pending_count() const {
@@ -47,7 +60,7 @@ namespace zp {
 
 void add_pending(zp_block_pool* pool, std::vector<int32_t> ids, hipEvent_t event) {
   if (ids.empty()) {
-    if (event) (void)hipEventDestroy(event);
+    pool->give_back_event(event);
     return;
   }
   zp_block_pool::Pending p;
@@ -161,6 +174,7 @@ void zp_block_pool_destroy(zp_block_pool* pool) {
       (void)hipEventSynchronize(p.event);
       (void)hipEventDestroy(p.event);
     }
+  for (hipEvent_t e : pool->spare_events) (void)hipEventDestroy(e);
   delete pool;
 }
 
@@ -284,7 +298,7 @@ zp_status zp_block_pool_sync(zp_block_pool* pool) {
   }
   for (auto& p : pool->pending) {
     for (int32_t id : p.ids) pool->free_ids.insert(id);
-    if (p.event) (void)hipEventDestroy(p.event);
+    pool->give_back_event(p.event);
   }
   pool->pending.clear();
   return ZP_OK;

@@ -21,10 +21,17 @@ struct zp_block_pool {
   std::vector<int32_t> rc;
   std::set<int32_t> free_ids;
   std::vector<Pending> pending;
+  // Events of completed groups, kept for the next group instead of being
+  // destroyed and created again (event creation is a driver call per
+  // compression otherwise).
+  std::vector<hipEvent_t> spare_events;
 
   bool manual_fence() const { return (flags & ZP_POOL_MANUAL_FENCE) != 0; }
   // Move every pending group whose GPU work is done into the free set.
   void reap();
+  // An event for a new pending group (a spare one, else a new one).
+  hipError_t take_event(hipEvent_t* out);
+  void give_back_event(hipEvent_t e);
   int32_t pending_count() const;
 };
 

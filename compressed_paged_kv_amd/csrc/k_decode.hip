@@ -232,6 +232,9 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode(DecodeParams p) {
         // a skipped block, a token past the end or an item past the end
         // contributes nothing
         const bool live = item_live(item);
+        // (its probability is forced to exactly 0 below: while a lane has
+        // seen no live token its max is still kInitMax, and 2^(x - m) would
+        // count a dead one as 1)
         float x[G];
 #pragma unroll
         for (int g = 0; g < G; g++) {
@@ -258,7 +261,7 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode(DecodeParams p) {
             for (int e = 0; e < NE; e++) acc[g][e] *= cr;
             m[g] = x[g];
           }
-          const float pr = fast_exp2(x[g] - m[g]);
+          const float pr = live ? fast_exp2(x[g] - m[g]) : 0.f;
           l[g] += pr;
 #pragma unroll
           for (int e = 0; e < NE; e++) acc[g][e] = fmaf(pr, vf[e], acc[g][e]);

@@ -860,6 +860,15 @@ __global__ __launch_bounds__(64 * score_waves<RG>(), (kMaxWaves / score_waves<RG
   score_unit<DT, D, B, RT, RG, true>(p);
 }
 
+// Workgroups of one instantiation that a compute unit holds at once (from
+// the compiled kernel's registers, LDS and launch bounds).
+template <int DT, int D, int B, int RT, int RG>
+hipError_t resident_rt(bool fused, int* per_cu) {
+  const auto fn = fused ? reinterpret_cast<const void*>(&k_score_compact<DT, D, B, RT, RG>)
+                        : reinterpret_cast<const void*>(&k_score_select<DT, D, B, RT, RG>);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, fn, 64 * score_waves<RG>(), 0);
+}
+
 template <int DT, int D, int B, int RT, int RG>
 hipError_t launch_rt(const ScoreParams& p, int units, hipStream_t s) {
   const dim3 grid(units), block(64 * score_waves<RG>());
@@ -873,6 +882,18 @@ hipError_t launch_rt(const ScoreParams& p, int units, hipStream_t s) {
     prof_end(ZP_PHASE_SCORE, s);
   }
   return hipGetLastError();
+}
+
+template <int DT, int D, int B>
+hipError_t resident_b(bool fused, int row_tiles, int T, int* per_cu) {
+  switch (row_tiles) {
+    case 1: return resident_rt<DT, D, B, 1, 1>(fused, per_cu);
+    case 2: return resident_rt<DT, D, B, 2, 1>(fused, per_cu);
+    case 4: return resident_rt<DT, D, B, 4, 1>(fused, per_cu);
+    case 8: return score_two_groups(8, T) ? resident_rt<DT, D, B, 8, 2>(fused, per_cu)
+                                          : hipErrorInvalidValue;
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int DT, int D, int B>
@@ -902,8 +923,25 @@ hipError_t launch_dt(const ScoreParams& p, int head_dim, int block_size, int row
   return hipErrorInvalidValue;
 }
 
+template <int DT>
+hipError_t resident_dt(bool fused, int head_dim, int block_size, int row_tiles, int T, int* per_cu) {
+  if (head_dim == 64 && block_size == 16) return resident_b<DT, 64, 16>(fused, row_tiles, T, per_cu);
+  if (head_dim == 64 && block_size == 32) return resident_b<DT, 64, 32>(fused, row_tiles, T, per_cu);
+  if (head_dim == 128 && block_size == 16) return resident_b<DT, 128, 16>(fused, row_tiles, T, per_cu);
+  if (head_dim == 128 && block_size == 32) return resident_b<DT, 128, 32>(fused, row_tiles, T, per_cu);
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
 
+hipError_t score_resident_per_cu(int dtype, int head_dim, int block_size, int rows, int T,
+                                 bool fused, int* per_cu) {
+  if (!score_fits(rows, T)) return hipErrorInvalidValue;
+  const int rt = score_row_tiles(rows);
+  if (dtype == ZP_BF16) return resident_dt<ZP_BF16>(fused, head_dim, block_size, rt, T, per_cu);
+  if (dtype == ZP_F32) return resident_dt<ZP_F32>(fused, head_dim, block_size, rt, T, per_cu);
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_score(const ScoreParams& p, int dtype, int head_dim, int block_size, int units,
                         hipStream_t s) {

@@ -99,6 +99,10 @@ struct AppendParams {
 // dispatch and enqueue.  Return hipSuccess or the launch error.
 hipError_t launch_score(const ScoreParams& p, int dtype, int head_dim, int block_size, int units,
                         hipStream_t s);
+// Workgroups of the scoring kernel (fused with the compaction, or selecting
+// only) that one compute unit of the current device holds at once.
+hipError_t score_resident_per_cu(int dtype, int head_dim, int block_size, int rows, int T,
+                                 bool fused, int* per_cu);
 hipError_t launch_compact(const CompactParams& p, int num_layers, int row_bytes, int block_size,
                           hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, int block_size,

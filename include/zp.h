@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define ZP_VERSION 1
+#define ZP_VERSION 2
 
 typedef enum {
   ZP_OK = 0,
@@ -264,6 +264,25 @@ zp_status zp_compress_n(const zp_kv_cache* cache, zp_block_pool* pool, int32_t n
                         void* workspace, size_t workspace_bytes, int32_t* freed_ids,
                         int32_t* num_freed, void* stream, const zp_compress_debug* debug);
 
+/* How zp_compress / zp_compress_lse / zp_compress_n run a call of this
+ * shape on the current device (a host query; it enqueues nothing).  One
+ * workgroup scores, selects and compacts each (layer, request, KV head)
+ * unit; when every unit of the call is resident at once, the compaction
+ * loads K normally (the scoring has just read it and much of it is still
+ * cached), otherwise it streams K past the caches. */
+typedef struct zp_compress_info {
+  int32_t units;            /* num_layers * num_reqs * num_kv_heads workgroups */
+  int32_t threads;          /* threads per workgroup */
+  int32_t resident_per_cu;  /* such workgroups one compute unit holds at once */
+  int32_t compute_units;    /* of the current device */
+  int32_t k_cached;         /* 1: K loaded normally by the compaction; 0: streamed */
+} zp_compress_info;
+
+/* Rejects (ZP_ERR_INVALID) the shapes zp_compress_n rejects; ZP_ERR_HIP
+ * without a device. */
+zp_status zp_compress_query(const zp_kv_cache* cache, int32_t num_reqs, int32_t n_src,
+                            int32_t n_max, int32_t window, zp_compress_info* out);
+
 /* ------------------------------------------------------------------------
  * zp_compress_keep_prefix: zp_compress_n that keeps shared blocks shared
  * when compression leaves them as they are.  New target blocks keep the
@@ -287,9 +306,11 @@ zp_status zp_compress_keep_prefix(const zp_kv_cache* cache, zp_block_pool* pool,
 /* ------------------------------------------------------------------------
  * zp_append_kv: write one new token per request into layer `layer`.
  * k_new, v_new: device [R][H][d]; slot_mapping: device int32 [R], physical
- * slot block*b + offset (negative = skip).  Tokens go into the last
- * partially filled block, as in paged attention ("How it works": a new block
- * only when the previous ones are full).
+ * slot block*b + offset (negative = skip).  The caller picks the slot:
+ * the next free offset of the request's last block, the paged cache taking
+ * a further block on demand once that one has filled (upskillscore.com
+ * guide, "How it works").  A slot whose block lies outside the pool is
+ * skipped.
  * ---------------------------------------------------------------------- */
 zp_status zp_append_kv(const zp_kv_cache* cache, int32_t layer, int32_t num_reqs,
                        const void* k_new, const void* v_new, const int32_t* slot_mapping,

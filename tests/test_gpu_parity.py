@@ -176,6 +176,38 @@ def test_ties_at_the_threshold_below_some_lower_scores():
     check_case(case, run)
 
 
+def _zero_key_case(dtype, d, b):
+    """Keys of zero norm (cosine 0 with every other key, so they add nothing
+    to their neighbours' redundancy and have redundancy 0 themselves): in
+    request 0 three rows of its third block (every head) and the whole of
+    its fifth block; in request 1 the first row of head 1 only, and the row
+    just before the window."""
+    c = _case("zero", 227, dtype=dtype, head_dim=d, block_size=b, n_max=12, window=16,
+              num_q_heads=8, num_blocks=64)
+    zero = np.float32(0) if dtype == "f32" else np.uint16(0)
+    T, w = c.n_max * b, c.window
+    rows = {0: [(2, h, o) for h in range(2) for o in (1, 5, 6)] + [(4, h, o) for h in range(2)
+                                                                  for o in range(b)],
+            1: [(0, 1, 0), ((T - w - 1) // b, 0, (T - w - 1) % b)]}
+    for r, lst in rows.items():
+        for n, h, o in lst:
+            c.k_pool[0][c.tables[r, n], h, o, :] = zero
+    return c, rows
+
+
+@pytest.mark.parametrize("dtype,d,b", [("bf16", 128, 16), ("f32", 64, 32), ("bf16", 64, 32)])
+def test_zero_norm_keys_have_zero_cosines(dtype, d, b):
+    case, rows = _zero_key_case(dtype, d, b)
+    say(f"[gpu parity] zero-norm keys {dtype} d={d} b={b}")
+    run = run_case(case)
+    for r, lst in rows.items():
+        for n, h, o in lst:
+            assert run.R[0, r, h, n * b + o] == 0.0, (r, h, n, o)
+    # the all-zero block: every cosine in it is 0
+    np.testing.assert_array_equal(run.R[0, 0, :, 4 * b:5 * b], 0.0)
+    check_case(case, run)
+
+
 def _max_shift_case():
     """Window queries along one direction u per head and the keys of every
     request's first block along -2u: those 16 slots get by far the smallest
@@ -281,33 +313,56 @@ def test_decode_skips_table_entries_outside_the_pool():
     """A block id outside [0, num_blocks) (negative or too large) is skipped
     by the kernel's own guard: the output is the attention over the other
     blocks' slots, which the oracle gets from the table without them (the
-    attention is a sum over the set of slots, so their order is free)."""
+    attention is a sum over the set of slots, so their order is free).  A
+    request whose every entry is outside the pool attends over nothing: its
+    output is 0 and its log-sum-exp -inf, as for an empty request.  Three
+    requests alone split their 20-block lists over three workgroups each;
+    the same requests repeated 100 times fill the GPU without splits."""
     import compressed_paged_kv_amd as zp
     from synth.device import to_tensor
-    b, H, Hq, d = 16, 2, 8, 128
-    c = _case("guard", 222, num_reqs=2, num_kv_heads=H, num_q_heads=Hq, head_dim=d,
-              block_size=b, n_max=6, window=1, num_blocks=20)
+    b, H, Hq, d, nb = 16, 2, 8, 128, 20
+    c = _case("guard", 222, num_reqs=3, num_kv_heads=H, num_q_heads=Hq, head_dim=d,
+              block_size=b, n_max=nb, window=1, num_blocks=64)
     say("[gpu parity] decode with table entries outside the pool")
     dev = "cuda"
     kp, vp = to_tensor(c.k_pool[0], dev), to_tensor(c.v_pool[0], dev)
     cache = zp.KVCache([kp], [vp], Hq)
     tab = c.tables.copy()
-    tab[0, 1] = 20 + 5          # past the pool
+    tab[0, 1] = 64 + 5          # past the pool
     tab[1, 3] = -7              # negative
-    seq = np.array([5 * b + 7, 4 * b], dtype=np.int32)
-    out = torch.full((2, Hq, d), float("nan"), device=dev)
-    zp.paged_decode(cache, 0, to_tensor(c.q_new[0], dev), torch.from_numpy(tab).to(dev),
-                    torch.from_numpy(seq).to(dev), 1.0 / np.sqrt(d), out, None)
-    torch.cuda.synchronize()
-    got = out.cpu().numpy()
-    # request 0: blocks 0, 2..5 (the last holds 7 slots); request 1: blocks 0..2
-    keep0 = np.array([c.tables[0, i] for i in (0, 2, 3, 4, 5)], dtype=np.int32)
+    tab[2, :] = np.where(np.arange(nb) % 2 == 0, -1 - np.arange(nb), 64 + np.arange(nb))
+    tab[2, 5] = 1 << 30
+    seq = np.array([17 * b + 7, 12 * b, nb * b], dtype=np.int32)
+    # request 0: blocks 0, 2..17 (the last holds 7 slots); request 1: blocks 0..2, 4..11
+    keep0 = np.array([c.tables[0, i] for i in [0] + list(range(2, 18))], dtype=np.int32)
+    keep1 = np.array([c.tables[1, i] for i in [0, 1, 2] + list(range(4, 12))], dtype=np.int32)
     want0 = oracle.decode(c.k_pool[0], c.v_pool[0], c.q_new[0][:1], keep0[None],
-                          np.array([4 * b + 7], dtype=np.int32), num_q_heads=Hq)
-    want1 = oracle.decode(c.k_pool[0], c.v_pool[0], c.q_new[0][1:], c.tables[1:, :3],
-                          np.array([3 * b], dtype=np.int32), num_q_heads=Hq)
-    assert np.abs(got[0] - want0[0]).max() <= DECODE_ATOL
-    assert np.abs(got[1] - want1[0]).max() <= DECODE_ATOL
+                          np.array([16 * b + 7], dtype=np.int32), num_q_heads=Hq)
+    want1 = oracle.decode(c.k_pool[0], c.v_pool[0], c.q_new[0][1:2], keep1[None],
+                          np.array([11 * b], dtype=np.int32), num_q_heads=Hq)
+    lse0 = oracle.decode_lse(c.k_pool[0], c.q_new[0][:1], keep0[None],
+                             np.array([16 * b + 7], dtype=np.int32), num_q_heads=Hq)
+    q = to_tensor(c.q_new[0], dev)
+    for reps in (1, 100):
+        R = 3 * reps
+        qs = q.repeat(reps, 1, 1).contiguous()
+        tabs = np.ascontiguousarray(np.tile(tab, (reps, 1)))
+        seqs = np.ascontiguousarray(np.tile(seq, reps))
+        out = torch.full((R, Hq, d), float("nan"), device=dev)
+        lse = torch.full((R, Hq), float("nan"), device=dev)
+        ws_bytes = zp.paged_decode_workspace_bytes(cache, R, nb)
+        assert (ws_bytes > 0) == (reps == 1), ws_bytes      # split only when alone
+        ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+        zp.paged_decode(cache, 0, qs, torch.from_numpy(tabs).to(dev),
+                        torch.from_numpy(seqs).to(dev), 1.0 / np.sqrt(d), out, ws, lse_out=lse)
+        torch.cuda.synchronize()
+        got, got_lse = out.cpu().numpy(), lse.cpu().numpy()
+        for k in range(reps):
+            assert np.abs(got[3 * k] - want0[0]).max() <= DECODE_ATOL
+            assert np.abs(got[3 * k + 1] - want1[0]).max() <= DECODE_ATOL
+            np.testing.assert_array_equal(got[3 * k + 2], 0.0)
+            assert np.all(np.isneginf(got_lse[3 * k + 2])), got_lse[3 * k + 2]
+            assert np.abs(got_lse[3 * k] - lse0[0]).max() <= 1e-4 * max(1.0, np.abs(lse0).max())
 
 
 def test_append_then_decode_one_token():
@@ -452,17 +507,18 @@ def test_random_decode_shapes_match_oracle(i, cfg):
         assert np.abs(got_lse[fin] - want_lse[fin]).max() <= 1e-4 * max(1.0, np.abs(want_lse[fin]).max())
 
 
-@pytest.mark.parametrize("name", ["bf16_d128_b16_ragged", "bf16_d64_b32_rows128",
-                                  "f32_d128_b32_w5", "over_cap_bf16_3_extra",
-                                  "units_576_streamed_k"])
-def test_fused_compaction_equals_the_standalone_kernel(name):
-    """Without shared blocks the prefix-keeping call makes the same plan as
-    the plain one, but runs the selection and the compaction as two kernels
-    (its plan waits for the selection), while the plain call compacts inside
-    the scoring kernel: the pools and tables must come out bit-identical."""
-    case = CASES[name]()
+def _fused_equals_standalone(case, want_k_cached):
+    import compressed_paged_kv_amd as zp
+    from synth.device import to_tensor
+    g = case.geom
     assert np.all(case.refcounts <= 1), "the case must have no shared blocks"
-    say(f"[gpu parity] fused vs standalone compaction: {name}")
+    cache = zp.KVCache([to_tensor(x, "cuda") for x in case.k_pool[:1]] * g.num_layers,
+                       [to_tensor(x, "cuda") for x in case.v_pool[:1]] * g.num_layers,
+                       g.num_q_heads)
+    info = zp.compress_query(cache, case.num_reqs, case.n_max, case.window, n_src=case.n_src)
+    say(f"[gpu parity]   launch: {info}")
+    assert info["k_cached"] == want_k_cached, info
+    del cache
     fused = run_case(case, decode=False)
     split = run_case(case, decode=False, keep_prefix=True)
     np.testing.assert_array_equal(fused.tables, split.tables)
@@ -471,3 +527,39 @@ def test_fused_compaction_equals_the_standalone_kernel(name):
     for a, b in zip(fused.k_pool + fused.v_pool, split.k_pool + split.v_pool):
         assert np.array_equal(np.ascontiguousarray(a).view(np.uint8),
                               np.ascontiguousarray(b).view(np.uint8))
+
+
+@pytest.mark.parametrize("name", ["bf16_d128_b16_ragged", "bf16_d64_b32_rows128",
+                                  "f32_d128_b32_w5", "over_cap_bf16_3_extra"])
+def test_fused_compaction_equals_the_standalone_kernel(name):
+    """Without shared blocks the prefix-keeping call makes the same plan as
+    the plain one, but runs the selection and the compaction as two kernels
+    (its plan waits for the selection), while the plain call compacts inside
+    the scoring kernel: the pools and tables must come out bit-identical.
+    These small calls have every unit resident at once, so the fused
+    compaction loads K normally."""
+    case = CASES[name]()
+    say(f"[gpu parity] fused vs standalone compaction: {name}")
+    _fused_equals_standalone(case, want_k_cached=1)
+
+
+def test_fused_compaction_streaming_k_equals_the_standalone_kernel():
+    """The other branch of the fused compaction: a call with more units than
+    the GPU holds at once (sized from the device's own resident count for
+    this shape) streams K; pools and tables bit-identical to the two-kernel
+    path, and the kept lists to the oracle's rule on the GPU's scores."""
+    import compressed_paged_kv_amd as zp
+    from synth.device import to_tensor
+    kw = dict(num_layers=3, num_kv_heads=8, num_q_heads=16, head_dim=64, n_max=6)
+    probe = _case("m6probe", 226, num_reqs=1, num_blocks=8, **kw)
+    cache = zp.KVCache([to_tensor(probe.k_pool[0], "cuda")] * 3,
+                       [to_tensor(probe.v_pool[0], "cuda")] * 3, 16)
+    info = zp.compress_query(cache, 1, 6, 16)
+    del cache
+    fit = info["resident_per_cu"] * info["compute_units"]
+    R = fit // (3 * 8) + 1                 # one more request than fits at once
+    say(f"[gpu parity] fused vs standalone, streamed K: {info}, {R} requests "
+        f"({3 * 8 * R} units for {fit} resident)")
+    case = _case("m6", 226, num_reqs=R, num_blocks=R * 6 + 8, **kw)
+    _fused_equals_standalone(case, want_k_cached=0)
+    check_case(case, run_case(case))

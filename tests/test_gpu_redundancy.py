@@ -65,3 +65,34 @@ def test_redundancy_all_qwen3_layer_sampled():
     want = oracle.redundancy_all(case.k_pool[0], case.tables[rs])
     err = np.abs(out.cpu().numpy()[rs] - want)
     assert err.max() <= R_ATOL, err.max()
+
+
+@pytest.mark.parametrize("dtype,d,b", [("bf16", 128, 16), ("f32", 64, 32)])
+def test_redundancy_all_with_zero_norm_keys(dtype, d, b):
+    """Zero keys (cosine 0 with everything, redundancy 0 themselves): a few
+    rows of one block and one whole block of request 0, one row of head 1 of
+    request 1; the other keys' means still divide by T - 1."""
+    import compressed_paged_kv_amd as zp
+    n_blocks = 24
+    c = synth.make_case("rall0", 260, num_reqs=2, num_layers=1, num_kv_heads=2, num_q_heads=2,
+                        head_dim=d, block_size=b, n_max=n_blocks, window=1,
+                        num_blocks=2 * n_blocks + 5, dtype=dtype)
+    zero = np.float32(0) if dtype == "f32" else np.uint16(0)
+    for h in range(2):
+        c.k_pool[0][c.tables[0, 3], h, [0, 2, b - 1], :] = zero
+        c.k_pool[0][c.tables[0, 7], h] = zero
+    c.k_pool[0][c.tables[1, 0], 1, 0, :] = zero
+    T = n_blocks * b
+    say(f"[gpu redundancy] zero-norm keys {dtype} d={d} b={b} T={T}")
+    dev = "cuda"
+    cache = zp.KVCache([to_tensor(c.k_pool[0], dev)], [to_tensor(c.v_pool[0], dev)], 2)
+    out = torch.full((2, 2, T), float("nan"), device=dev)
+    zp.redundancy_all(cache, 0, torch.from_numpy(c.tables).to(dev), out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    want = oracle.redundancy_all(c.k_pool[0], c.tables)
+    np.testing.assert_array_equal(got[0, :, 7 * b:8 * b], 0.0)
+    np.testing.assert_array_equal(got[0, :, 3 * b + np.array([0, 2, b - 1])], 0.0)
+    assert got[1, 1, 0] == 0.0
+    err = np.abs(got - want)
+    assert np.isfinite(got).all() and err.max() <= R_ATOL, err.max()

@@ -278,3 +278,176 @@ def test_compress_overlapped_with_decode():
         err = float(np.abs(ovl[4][l] - want).max())
         assert err <= DECODE_ATOL, f"layer {l}: decode error {err}"
     say("overlap: ok")
+
+
+def _poison_past(pool_t, tables, upto, b):
+    """NaN into every slot at or past logical slot upto[r] of each request
+    (whole blocks past it, and the tail of the block it falls in): a decode
+    that read past a request's length would turn its output NaN."""
+    full = [tables[r, (int(upto[r]) + b - 1) // b:] for r in range(tables.shape[0])]
+    ids = np.concatenate(full) if full else np.zeros(0, np.int32)
+    if ids.size:
+        pool_t.index_fill_(0, torch.from_numpy(ids.astype(np.int64)).to(pool_t.device),
+                           float("nan"))
+    part = {}
+    for r in range(tables.shape[0]):
+        o = int(upto[r]) % b
+        if o:
+            part.setdefault(o, []).append(int(tables[r, int(upto[r]) // b]))
+    for o, lst in part.items():
+        idx = torch.tensor(lst, dtype=torch.int64, device=pool_t.device)
+        pool_t[idx, :, o:, :] = float("nan")
+
+
+def test_mix_full_size_two_streams_sampled():
+    """The continuous-batching mix at its full size: 256 requests x 36 layers
+    of the Qwen3-8B shape (pool 32768 blocks, 72 GiB of K/V).  A seeded 10 %
+    of the requests (26) sit at the cap and compress on one stream while the
+    other 230, with ragged cached lengths in [64, 2048), append one token and
+    decode in every layer on a second stream, the two joined by events; then
+    the compressed requests rejoin decoding (append at slot 2032, decode over
+    2033).  The plan, refcounts and freed ids are compared exactly for the
+    whole batch; sampled (layer, request) compressions -- scores, survivor
+    sets, compacted rows -- and sampled decodes of both groups against the
+    oracle.  Slots past every decoding request's length are NaN, so a decode
+    reading past it would fail."""
+    from synth.device_gen import case_mix_device
+    dev = torch.device("cuda:0")
+    say("mix_qwen3_8b_36layers: generating 256 requests x 36 layers on the device")
+    case = case_mix_device(dev)
+    g = case.geom
+    L, H, Hq, d, b = g.num_layers, g.num_kv_heads, g.num_q_heads, g.head_dim, g.block_size
+    n_max, w = case.n_max, case.window
+    T, k_keep = n_max * b, (n_max - 1) * b
+    C, k_sel = T - w, k_keep - w
+    lens = case.seq_lens
+    comp = np.nonzero(lens == T)[0]
+    dec = np.nonzero(lens < T)[0]
+    Rc, Rd = len(comp), len(dec)
+    assert Rc == 26 and Rd == 230, (Rc, Rd)
+    tables_c = np.ascontiguousarray(case.tables[comp])
+    tables_d = np.ascontiguousarray(case.tables[dec])
+    ld = lens[dec].astype(np.int32)
+    say(f"mix: poisoning slots past the {Rd} decoding requests' lengths")
+    for l in range(L):
+        for t in (case.k_pool[l], case.v_pool[l]):
+            _poison_past(t, tables_d, ld + 1, b)
+    comp_t = torch.from_numpy(comp.astype(np.int64)).to(dev)
+    dec_t = torch.from_numpy(dec.astype(np.int64)).to(dev)
+    wq = [q.index_select(0, comp_t).contiguous() for q in case.window_q]
+    qd = [q.index_select(0, dec_t).contiguous() for q in case.q_new]
+    kd = [k.index_select(0, dec_t).contiguous() for k in case.k_new]
+    vd = [v.index_select(0, dec_t).contiguous() for v in case.v_new]
+    qc = [q.index_select(0, comp_t).contiguous() for q in case.q_new]
+    kc = [k.index_select(0, comp_t).contiguous() for k in case.k_new]
+    vc = [v.index_select(0, comp_t).contiguous() for v in case.v_new]
+
+    c_samples = [(0, 0), (11, 7), (23, 13), (35, 25)]           # (layer, index into comp)
+    order = np.argsort(ld)
+    d_samples = [(0, int(order[0])), (7, int(order[-1])), (18, int(order[len(order) // 2])),
+                 (35, 101), (29, 3)]                             # (layer, index into dec)
+    snap_c = {(l, i): (_blocks(case.k_pool[l], tables_c[i]), _blocks(case.v_pool[l], tables_c[i]))
+              for l, i in c_samples}
+    snap_d = {(l, i): (_blocks(case.k_pool[l], tables_d[i]), _blocks(case.v_pool[l], tables_d[i]))
+              for l, i in d_samples}
+
+    cache = zp.KVCache(case.k_pool, case.v_pool, Hq)
+    pool = zp.BlockPool.from_refcounts(case.refcounts)
+    tables = tables_c.copy()
+    ws = torch.empty(zp.compress_workspace_bytes(cache, Rc, n_max, w), dtype=torch.uint8, device=dev)
+    # one workspace for both decodes on stream B (the 26 rejoining requests
+    # split their block lists, the 230 others do not)
+    dws = torch.empty(max(zp.paged_decode_workspace_bytes(cache, Rd, n_max),
+                          zp.paged_decode_workspace_bytes(cache, Rc, n_max), 16),
+                      dtype=torch.uint8, device=dev)
+    dbg = dict(importance=torch.full((L, Rc, H, T), float("nan"), device=dev),
+               redundancy=torch.full((L, Rc, H, T), float("nan"), device=dev),
+               score=torch.full((L, Rc, H, T), float("nan"), device=dev),
+               kept=torch.full((L, Rc, H, k_keep), -1, dtype=torch.int32, device=dev))
+    tab_d = torch.from_numpy(tables_d).to(dev)
+    slot_d = torch.from_numpy((tables_d[np.arange(Rd), ld // b] * b + ld % b).astype(np.int32)).to(dev)
+    seq_d = torch.from_numpy(ld + 1).to(dev)
+    out_d = torch.full((L, Rd, Hq, d), float("nan"), device=dev)
+    s_c, s_d = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    say(f"mix: {Rc} requests compress 36 layers on stream A, {Rd} append + decode on stream B")
+    start = torch.cuda.Event()
+    start.record(torch.cuda.current_stream())
+    s_c.wait_event(start)
+    s_d.wait_event(start)
+    freed = zp.compress(cache, pool, n_max, w, tables, wq, ws, stream=s_c, debug=dbg)
+    for l in range(L):
+        zp.append_kv(cache, l, kd[l], vd[l], slot_d, stream=s_d)
+        zp.paged_decode(cache, l, qd[l], tab_d, seq_d, 1.0 / np.sqrt(d), out_d[l], dws, stream=s_d)
+    done_c = torch.cuda.Event()
+    done_c.record(s_c)
+    # the compressed requests rejoin decoding after the compression
+    s_d.wait_event(done_c)
+    tab_c_t = torch.from_numpy(np.ascontiguousarray(tables)).to(dev)
+    slot_c = torch.from_numpy((tables[:, k_keep // b] * b + k_keep % b).astype(np.int32)).to(dev)
+    seq_c = torch.full((Rc,), k_keep + 1, dtype=torch.int32, device=dev)
+    out_c = torch.full((L, Rc, Hq, d), float("nan"), device=dev)
+    for l in range(L):
+        zp.append_kv(cache, l, kc[l], vc[l], slot_c, stream=s_d)
+        zp.paged_decode(cache, l, qc[l], tab_c_t, seq_c, 1.0 / np.sqrt(d), out_c[l], dws, stream=s_d)
+    torch.cuda.synchronize()
+    say("mix: checking the plan of the whole batch")
+    ref = oracle.plan(case.refcounts[:], tables_c, n_max)
+    assert ref.status == oracle.OK
+    np.testing.assert_array_equal(tables, ref.tables)
+    pool.sync()
+    # the decoding requests still hold their blocks: the pool counts every table
+    np.testing.assert_array_equal(pool.refcounts(), ref.refcounts)
+    np.testing.assert_array_equal(np.sort(freed), np.sort(ref.freed))
+    assert np.isfinite(out_d.cpu().numpy()).all() and np.isfinite(out_c.cpu().numpy()).all()
+    near = 0
+    for l, i in c_samples:
+        tag = f"mix compress layer {l} req {int(comp[i])}"
+        say(f"  oracle on {tag}")
+        kb, vb = snap_c[(l, i)]
+        src = np.arange(n_max, dtype=np.int32)[None, :]
+        Ao, Ro, so = oracle.scores(kb, to_numpy(wq[l][i:i + 1]), src, num_kv_heads=H,
+                                   num_q_heads=Hq, head_dim=d, block_size=b, n_max=n_max, window=w)
+        A = dbg["importance"][l, i].cpu().numpy()
+        Rr = dbg["redundancy"][l, i].cpu().numpy()
+        s = dbg["score"][l, i].cpu().numpy()
+        _check_unit_scores(A, Rr, s, Ao[0], Ro[0], so[0], C, tag)
+        kept = dbg["kept"][l, i].cpu().numpy()
+        _check_unit_kept(kept, s, so[0], w, k_sel, C, tag)
+        near += int(np.count_nonzero(kept != oracle.select(so[0], w, k_sel)))
+        ck, cv = _blocks(case.k_pool[l], tables[i]), _blocks(case.v_pool[l], tables[i])
+        hi = np.arange(H)[:, None]
+        kk = np.arange(k_keep)[None, :]
+        for before, after in ((kb, ck), (vb, cv)):
+            want = words(before)[kept // b, hi, kept % b]
+            got = words(after)[kk // b, hi, kk % b]
+            assert np.array_equal(got, want), f"{tag}: compacted rows differ"
+        # the rejoining decode: compacted rows + the token appended at slot
+        # k_keep (offset 0 of the reserved block), which must be bit-exact
+        kp, vp = ck.copy(), cv.copy()
+        oracle.append(kp, vp, to_numpy(kc[l][i:i + 1]), to_numpy(vc[l][i:i + 1]),
+                      np.array([k_keep], dtype=np.int32))
+        assert np.array_equal(words(kp), words(ck)) and np.array_equal(words(vp), words(cv)), \
+            f"{tag}: rejoining append"
+        want = oracle.decode(kp, vp, to_numpy(qc[l][i:i + 1]), src,
+                             np.array([k_keep + 1], dtype=np.int32), num_q_heads=Hq)
+        err = float(np.abs(out_c[l, i:i + 1].cpu().numpy() - want).max())
+        assert err <= DECODE_ATOL, f"{tag}: rejoining decode error {err}"
+    for l, i in d_samples:
+        tag = f"mix decode layer {l} req {int(dec[i])} (len {int(ld[i])})"
+        say(f"  oracle on {tag}")
+        kb, vb = snap_d[(l, i)]
+        src = np.arange(n_max, dtype=np.int32)[None, :]
+        kp, vp = kb.copy(), vb.copy()
+        oracle.append(kp, vp, to_numpy(kd[l][i:i + 1]), to_numpy(vd[l][i:i + 1]),
+                      np.array([int(ld[i])], dtype=np.int32))
+        after_k, after_v = _blocks(case.k_pool[l], tables_d[i]), _blocks(case.v_pool[l], tables_d[i])
+        assert np.array_equal(words(after_k), words(kp)), f"{tag}: append wrote elsewhere"
+        assert np.array_equal(words(after_v), words(vp)), f"{tag}: append wrote elsewhere"
+        want = oracle.decode(kp, vp, to_numpy(qd[l][i:i + 1]), src,
+                             np.array([int(ld[i]) + 1], dtype=np.int32), num_q_heads=Hq)
+        err = float(np.abs(out_d[l, i:i + 1].cpu().numpy() - want).max())
+        assert err <= DECODE_ATOL, f"{tag}: decode error {err}"
+    say(f"mix: ok ({len(c_samples)} compressions, {len(c_samples) + len(d_samples)} decodes "
+        f"sampled, {near} near-tie slot differences)")
+    pool.close()

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_function():
                          text=True, check=True).stdout
     exported = set(re.findall(r" T (zp_\w+)", out))
     assert set(names) <= exported
-    assert zp.lib().zp_version() == 1
+    assert zp.lib().zp_version() == 2
 
 
 def test_library_links_no_oracle():
@@ -189,12 +189,15 @@ def test_planner_shared_prefix_case_conserves_refcounts():
 # ------------------------------------------------------------------ validation
 
 class _FakeTensor:
-    """Host buffer posing as a device tensor for calls that must fail in
+    """Host buffer posing as a device tensor (a cuda:0 device and a real torch
+    dtype, so the binding's own checks pass) for calls that must fail in
     validation before touching any device memory."""
 
     def __init__(self, shape, dtype_name, nbytes=64):
-        self.shape = shape
-        self.dtype = dtype_name
+        import torch
+        self.shape = tuple(shape)
+        self.dtype = getattr(torch, dtype_name.split(".")[-1])
+        self.device = torch.device("cuda", 0)
         self._buf = ctypes.create_string_buffer(max(nbytes, 64) + 256)
         self._ptr = (ctypes.addressof(self._buf) + 255) // 256 * 256
 
@@ -217,6 +220,20 @@ def _fake_cache(L=1, H=2, Hq=4, d=64, b=16, nb=16, dtype="torch.float32"):
     return zp.KVCache(ks, vs, Hq)
 
 
+def _raw_compress(cache, pool, n_max, window, tables, wq, ws):
+    """zp_compress through the C ABI alone (no binding checks): the library's
+    own validation is what these tests pin."""
+    lib = zp.lib()
+    arr = (ctypes.c_void_p * cache.num_layers)(*[t.data_ptr() for t in wq])
+    freed = np.zeros(max(tables.size, 1), dtype=np.int32)
+    n = np.zeros(1, dtype=np.int32)
+    i32 = ctypes.POINTER(ctypes.c_int32)
+    return lib.zp_compress(cache.ref, pool.handle, n_max, window, int(tables.shape[0]),
+                           tables.ctypes.data_as(i32), ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)),
+                           ws.data_ptr(), ws.numel() * ws.element_size(),
+                           freed.ctypes.data_as(i32), n.ctypes.data_as(i32), None, None)
+
+
 def test_compress_rejects_bad_arguments_before_any_work():
     cache = _fake_cache()
     n_max = 8
@@ -229,9 +246,8 @@ def test_compress_rejects_bad_arguments_before_any_work():
         args = dict(n_max=n_max, window=8)
         args.update(kwargs)
         t = tables.copy()
-        with pytest.raises(zp.ZpError) as e:
-            zp.compress(cache, pool, args["n_max"], args["window"], t, wq, ws, stream=0)
-        assert e.value.status == zp.ZP_ERR_INVALID
+        st = _raw_compress(cache, pool, args["n_max"], args["window"], t, wq, ws)
+        assert st == zp.ZP_ERR_INVALID, (kwargs, zp.last_error())
         np.testing.assert_array_equal(t, tables)
     # workspace too small (the fake reports 64 bytes)
     with pytest.raises(zp.ZpError) as e:
@@ -242,6 +258,55 @@ def test_compress_rejects_bad_arguments_before_any_work():
     mpool = zp.BlockPool(16, manual_fence=True)
     with pytest.raises(zp.ZpError):
         zp.compress(cache, mpool, n_max, 8, tables.copy(), wq, ws, stream=0)
+
+
+def test_binding_rejects_tensors_the_kernels_cannot_take():
+    """The binding checks device, element type, contiguity and shape of every
+    tensor before a pointer reaches the library (the C layer sees only
+    addresses): a CPU tensor, an int64 table, a short window-query tensor or
+    a strided view raise ValueError and nothing is called."""
+    import torch
+    cache = _fake_cache()
+    pool = zp.BlockPool(16)
+    tables = np.arange(8, dtype=np.int32)[None].copy()
+    pool.alloc(8)
+    ws = _FakeTensor((1,), "torch.uint8")
+    good_wq = [_FakeTensor((1, 8, 4, 64), "torch.float32")]
+    bad_wq = {
+        "on the CPU": [torch.zeros((1, 8, 4, 64))],
+        "dtype": [_FakeTensor((1, 8, 4, 64), "torch.bfloat16")],
+        "shape": [_FakeTensor((1, 7, 4, 64), "torch.float32")],
+    }
+    for why, wq in bad_wq.items():
+        with pytest.raises(ValueError):
+            zp.compress(cache, pool, 8, 8, tables.copy(), wq, ws, stream=0)
+    with pytest.raises(ValueError):
+        zp.compress(cache, pool, 8, 8, tables.astype(np.int64), good_wq, ws, stream=0)
+    with pytest.raises(ValueError):   # one entry per layer
+        zp.compress(cache, pool, 8, 8, tables.copy(), good_wq * 2, ws, stream=0)
+    assert [pool.refcount(i) for i in range(8)] == [1] * 8
+
+    q = _FakeTensor((2, 4, 64), "torch.float32")
+    tab = _FakeTensor((2, 8), "torch.int32")
+    seq = _FakeTensor((2,), "torch.int32")
+    out = _FakeTensor((2, 4, 64), "torch.float32")
+    for args in ((torch.zeros((2, 4, 64)), tab, seq, out),                 # q on the CPU
+                 (q, _FakeTensor((2, 8), "torch.int64"), seq, out),         # int64 table
+                 (q, tab, _FakeTensor((3,), "torch.int32"), out),           # lengths of another batch
+                 (q, tab, seq, _FakeTensor((2, 4, 64), "torch.bfloat16")),  # output not float32
+                 (_FakeTensor((2, 4, 32), "torch.float32"), tab, seq, out)):
+        with pytest.raises(ValueError):
+            zp.paged_decode(cache, 0, *args, 0.125, None, stream=0)
+    strided = torch.zeros((2, 4, 128))[..., ::2]
+    with pytest.raises(ValueError):
+        zp.paged_decode(cache, 0, strided, tab, seq, 0.125, out, None, stream=0)
+    kv = _FakeTensor((2, 2, 64), "torch.float32")
+    with pytest.raises(ValueError):
+        zp.append_kv(cache, 0, kv, kv, _FakeTensor((2,), "torch.int64"), stream=0)
+    with pytest.raises(ValueError):
+        zp.append_kv(cache, 0, _FakeTensor((2, 4, 64), "torch.float32"), kv, seq, stream=0)
+    with pytest.raises(ValueError):   # pools must live on a GPU
+        zp.KVCache([torch.zeros((4, 2, 16, 64))], [torch.zeros((4, 2, 16, 64))], 4)
 
 
 @pytest.mark.parametrize("field,value", [("head_dim", 96), ("block_size", 8), ("num_q_heads", 6),
@@ -270,18 +335,20 @@ def test_workspace_sizes_grow_with_the_batch():
 
 def test_decode_and_append_reject_bad_arguments():
     cache = _fake_cache()
-    t = _FakeTensor((1,), "torch.int32")
+    q = _FakeTensor((1, 4, 64), "torch.float32")
+    seq = _FakeTensor((1,), "torch.int32")
+    out = _FakeTensor((1, 4, 64), "torch.float32")
     tab = _FakeTensor((1, 8), "torch.int32")
     with pytest.raises(zp.ZpError):
-        zp.paged_decode(cache, 1, t, tab, t, 0.125, t, None, stream=0)      # layer out of range
+        zp.paged_decode(cache, 1, q, tab, seq, 0.125, out, None, stream=0)      # layer out of range
     with pytest.raises(zp.ZpError):
-        zp.paged_decode(cache, 0, t, tab, t, -1.0, t, None, stream=0)       # bad scale
+        zp.paged_decode(cache, 0, q, tab, seq, -1.0, out, None, stream=0)       # bad scale
     tab_big = _FakeTensor((1, 64), "torch.int32")
     with pytest.raises(zp.ZpError) as e:
-        zp.paged_decode(cache, 0, t, tab_big, t, 0.125, t, None, stream=0)  # needs a workspace
+        zp.paged_decode(cache, 0, q, tab_big, seq, 0.125, out, None, stream=0)  # needs a workspace
     assert "workspace" in str(e.value)
     lib = zp.lib()
-    assert lib.zp_append_kv(cache.ref, 3, 1, t.data_ptr(), t.data_ptr(), t.data_ptr(), None) == \
+    assert lib.zp_append_kv(cache.ref, 3, 1, q.data_ptr(), q.data_ptr(), seq.data_ptr(), None) == \
         zp.ZP_ERR_INVALID
 
 

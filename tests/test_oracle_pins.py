@@ -426,6 +426,39 @@ def test_plan_keeps_shared_blocks_below_the_first_eviction():
     assert sorted(q.freed.tolist()) == [3, 4]
 
 
+def test_first_evicted_takes_the_lowest_slot_over_layers_and_heads():
+    """Hand-built kept lists (T = 16, w = 2, so C = 14 candidates; 12 kept,
+    4 evicted per head) whose first evictions differ by layer and head.
+    Request 0: layer 0 first evicts 5 (head 0) and 3 (head 1), layer 1 4 and
+    7 -> 3.  Request 1: 10, 9 | 10, 6 -> 6, the minimum sitting in the other
+    layer and head.  Request 2: every head evicts 10..13 -> 10.  Evicted
+    sets that are not runs (head 1 of request 0, layer 0: {3, 9, 10, 11})
+    make a slip to the last eviction, or to the first kept slot, fail."""
+    T, w = 16, 2
+    evicted = {  # (layer, request, head) -> evicted candidate slots
+        (0, 0, 0): {5, 6, 7, 8}, (0, 0, 1): {3, 9, 10, 11},
+        (1, 0, 0): {4, 5, 12, 13}, (1, 0, 1): {7, 8, 9, 10},
+        (0, 1, 0): {10, 11, 12, 13}, (0, 1, 1): {9, 11, 12, 13},
+        (1, 1, 0): {10, 11, 12, 13}, (1, 1, 1): {6, 13, 12, 8},
+        (0, 2, 0): {10, 11, 12, 13}, (0, 2, 1): {10, 11, 12, 13},
+        (1, 2, 0): {10, 11, 12, 13}, (1, 2, 1): {10, 11, 12, 13},
+    }
+    kept = []
+    for layer in range(2):
+        k = np.zeros((3, 2, T - 4), dtype=np.int32)
+        for r in range(3):
+            for h in range(2):
+                ev = evicted[(layer, r, h)]
+                assert len(ev) == 4 and max(ev) < T - w
+                k[r, h] = sorted(set(range(T)) - ev)
+        kept.append(k)
+    np.testing.assert_array_equal(oracle.first_evicted(kept, T, w), [3, 6, 10])
+    # one layer alone: request 0 -> min(5, 3), request 1 -> min(10, 9)
+    np.testing.assert_array_equal(oracle.first_evicted(kept[:1], T, w), [3, 9, 10])
+    # the other alone: request 0 -> min(4, 7), request 1 -> min(10, 6)
+    np.testing.assert_array_equal(oracle.first_evicted(kept[1:], T, w), [4, 6, 10])
+
+
 def test_keep_prefix_compression_leaves_the_shared_prefix_in_place():
     """Exact ties (zero queries, axis-aligned keys): the evicted candidates
     are the highest slots, far past a 2-block shared prefix, which then stays

@@ -31,6 +31,7 @@ hipError_t launch_append(const AppendParams&, hipStream_t) { return hipErrorInva
 hipError_t launch_redundancy_all(const RedundancyParams&, int, int, int, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_upload(const void*, void*, size_t, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_first_evict(const int32_t*, int32_t*, int, int, int, int, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t score_resident_per_cu(int, int, int, int, int, bool, int*) { return hipErrorInvalidValue; }
 }  // namespace zp
 """
 
@@ -63,7 +64,9 @@ def test_host_code_and_oracle_are_clean_under_sanitizers(instrumented):
     env.update({
         "ZP_LIBRARY": host_lib,
         "ZP_ORACLE_LIBRARY": oracle_lib,
-        "LD_PRELOAD": f"{_runtime('libasan.so')}:{_runtime('libubsan.so')}",
+        # the sanitizer runtimes first, anything already preloaded kept after them
+        "LD_PRELOAD": ":".join(x for x in (_runtime('libasan.so'), _runtime('libubsan.so'),
+                                           os.environ.get("LD_PRELOAD", "")) if x),
         # the interpreter itself is not instrumented: no leak report for it
         "ASAN_OPTIONS": "detect_leaks=0:halt_on_error=1:abort_on_error=0",
         "UBSAN_OPTIONS": "halt_on_error=1:print_stacktrace=1",
