@@ -7,6 +7,6 @@ from ._binding import (  # noqa: F401
     ZP_BF16, ZP_ERR_HIP, ZP_ERR_INVALID, ZP_ERR_NO_BLOCKS, ZP_ERR_STATE, ZP_F32, ZP_OK,
     BlockPool, KVCache, PrefixIndex, Scheduler, ZpError, append_kv, compress, compress_plan,
     compress_query, compress_workspace_bytes,
-    last_error, lib, paged_decode, paged_decode_workspace_bytes, profile_enable, profile_read,
+    last_error, lib, paged_decode, paged_decode_noalloc, paged_decode_workspace_bytes, profile_enable, profile_read,
     redundancy_all,
 )

@@ -149,6 +149,9 @@ def lib() -> ctypes.CDLL:
         "zp_paged_decode_lse": (S, [ctypes.POINTER(_KVCache), ctypes.c_int32, ctypes.c_int32, _vp,
                                     _vp, ctypes.c_int32, _vp, ctypes.c_float, _vp, _vp, _vp, _vp,
                                     ctypes.c_int32, _vp, ctypes.c_size_t, _vp]),
+        "zp_paged_decode_noalloc": (S, [ctypes.POINTER(_KVCache), ctypes.c_int32, ctypes.c_int32,
+                                        _vp, _vp, ctypes.c_int32, _vp, ctypes.c_float, _vp, _vp,
+                                        _vp, _vp, ctypes.c_int32, _vp]),
         "zp_redundancy_all": (S, [ctypes.POINTER(_KVCache), ctypes.c_int32, ctypes.c_int32, _vp,
                                   ctypes.c_int32, _vp, _vp]),
         "zp_prefix_index_create": (S, [_vp, ctypes.c_int32, ctypes.POINTER(_vp)]),
@@ -515,6 +518,34 @@ def paged_decode(cache: KVCache, layer: int, q, tables, seq_lens, scale: float, 
                                      max_blocks, seq_lens.data_ptr(), float(scale), out.data_ptr(),
                                      _dptr(lse_out), _dptr(q_out), _dptr(lse_rows), cap,
                                      ws_ptr, ws_bytes, _stream_handle(stream)))
+
+
+def paged_decode_noalloc(cache: KVCache, layer: int, q, tables, seq_lens, scale: float, out,
+                         stream=None, lse_out=None, lse_rows=None, q_out=None) -> None:
+    """zp_paged_decode_noalloc: paged_decode with the split partials in the
+    library's fixed device scratch (no workspace; nothing is allocated).
+    Calls whose work overlaps on one GPU race on that scratch."""
+    import torch
+    dev, Hq, d = cache.device, cache.num_q_heads, cache.head_dim
+    _want(tables, "tables", dev, torch.int32, (None, None))
+    R, max_blocks = (int(x) for x in tables.shape)
+    _want(q, "q", dev, cache.torch_dtype, (R, Hq, d))
+    _want(seq_lens, "seq_lens", dev, torch.int32, (R,))
+    _want(out, "out", dev, torch.float32, (R, Hq, d))
+    if lse_out is not None:
+        _want(lse_out, "lse_out", dev, torch.float32, (None, Hq))
+    if q_out is not None:
+        _want(q_out, "q_out", dev, cache.torch_dtype, (None, Hq, d))
+        if lse_out is not None and int(q_out.shape[0]) != int(lse_out.shape[0]):
+            raise ValueError("q_out and lse_out must have the same number of rows")
+    if lse_rows is not None:
+        _want(lse_rows, "lse_rows", dev, torch.int32, (R,))
+    rows_src = lse_out if lse_out is not None else q_out
+    cap = int(rows_src.shape[0]) if rows_src is not None else 0
+    _check(lib().zp_paged_decode_noalloc(cache.ref, layer, R, q.data_ptr(), tables.data_ptr(),
+                                         max_blocks, seq_lens.data_ptr(), float(scale),
+                                         out.data_ptr(), _dptr(lse_out), _dptr(q_out),
+                                         _dptr(lse_rows), cap, _stream_handle(stream)))
 
 
 def redundancy_all(cache: KVCache, layer: int, tables, out, stream=None) -> None:

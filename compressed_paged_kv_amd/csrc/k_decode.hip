@@ -24,11 +24,20 @@
 // to rounding: the final normalisation divides by the same stale max; terms
 // stay below 2^64, far inside the float range), and the states of
 // lanes, waves and splits are merged by log-sum-exp at the end.
+#include <mutex>
+
 #include "zp_device.h"
 #include "zp_internal.h"
 
 namespace zp {
 namespace {
+
+// Split partials of zp_paged_decode_noalloc, for callers that cannot
+// allocate device memory.  Every GPU the library runs on holds its own copy
+// until the process ends.  Host code never passes this name to a kernel (on
+// the host it only stands for the variable): decode_static_scratch() looks
+// up each device's address once and the kernels get that address.
+static __device__ __align__(256) unsigned char scratch[kDecodeStaticScratchBytes];
 
 constexpr float kInitMax = -1.0e30f;
 constexpr float kLazy = 64.0f;
@@ -412,6 +421,25 @@ hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, int blo
   if (dtype == ZP_BF16) return launch_dt<ZP_BF16>(p, head_dim, block_size, s);
   if (dtype == ZP_F32) return launch_dt<ZP_F32>(p, head_dim, block_size, s);
   return hipErrorInvalidValue;
+}
+
+hipError_t decode_static_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_append(const AppendParams& p, hipStream_t s) {

@@ -41,6 +41,16 @@ constexpr int kDecodeThreads = ZP_DECODE_THREADS;
 #define ZP_DECODE_TARGET_WORKGROUPS 512
 #endif
 constexpr int kDecodeTargetWorkgroups = ZP_DECODE_TARGET_WORKGROUPS;
+// Fixed device scratch of the allocation-free decode entry point: the split
+// partials [R][Hq][nsplit][d + 2] floats.  A list is split only while the
+// (request, KV head, query subgroup) units number fewer than
+// kDecodeTargetWorkgroups, so R*Hq*nsplit < 2 * 4 * kDecodeTargetWorkgroups
+// (at most 4 query heads per unit) and the partials never exceed the bound
+// below at head_dim 128.
+constexpr size_t kDecodeStaticScratchBytes = size_t(4) << 20;
+static_assert((size_t)2 * 4 * kDecodeTargetWorkgroups * (128 + 2) * sizeof(float) <=
+                  kDecodeStaticScratchBytes,
+              "the static decode scratch must hold the largest split partials");
 
 struct ScoreParams {
   void* const* layer_ptrs;  // device [L][kPtrsPerLayer]
@@ -108,6 +118,9 @@ hipError_t launch_compact(const CompactParams& p, int num_layers, int row_bytes,
 hipError_t launch_decode(const DecodeParams& p, int dtype, int head_dim, int block_size,
                          hipStream_t s);
 hipError_t launch_append(const AppendParams& p, hipStream_t s);
+// Device address of the current device's copy of the fixed decode scratch
+// (kDecodeStaticScratchBytes, 256-byte aligned), looked up once per device.
+hipError_t decode_static_scratch(void** ptr);
 hipError_t launch_redundancy_all(const RedundancyParams& p, int dtype, int head_dim,
                                  int block_size, hipStream_t s);
 // Copies bytes (a multiple of 16, 16-byte aligned ends) from device-visible

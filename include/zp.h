@@ -364,6 +364,27 @@ zp_status zp_paged_decode_lse(const zp_kv_cache* cache, int32_t layer, int32_t n
                               size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * zp_paged_decode_noalloc: zp_paged_decode_lse for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  It takes no workspace: the
+ * split partials go to a fixed 4 MiB device array inside the library, one
+ * copy per GPU, held until the process ends; the call itself allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine).  Its
+ * device address is looked up on the first call on each device.
+ * Every argument, layout and result as zp_paged_decode_lse.  Calls on one
+ * GPU share that array: two calls whose work overlaps on the GPU (on
+ * different streams) race on it and must be ordered by the caller.
+ * Rejects (ZP_ERR_INVALID) a batch whose partials would exceed the array
+ * (none does at the library's split rule: at most about 2.1 MB at
+ * head_dim 128), besides what zp_paged_decode_lse rejects.
+ * ---------------------------------------------------------------------- */
+zp_status zp_paged_decode_noalloc(const zp_kv_cache* cache, int32_t layer, int32_t num_reqs,
+                                  const void* q, const int32_t* block_tables, int32_t max_blocks,
+                                  const int32_t* seq_lens, float scale, float* out,
+                                  float* lse_out, void* q_out, const int32_t* rows,
+                                  int32_t capacity, void* stream);
+
+/* ------------------------------------------------------------------------
  * zp_redundancy_all: the all-pairs redundancy that the Lightning Redundancy
  * Score replaces (nl page Methodologie item 5, ko page section 2.E: the
  * original score is O(N^2 b^2), the LRS O(N b^2)), for measuring that
