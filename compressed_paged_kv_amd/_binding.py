@@ -74,6 +74,19 @@ class _Debug(ctypes.Structure):
                 ("score", ctypes.c_void_p), ("kept", ctypes.c_void_p)]
 
 
+ZP_COMPRESS_KEEP_PREFIX = 1
+
+
+class _CompressArgs(ctypes.Structure):
+    _fields_ = [("n_src", ctypes.c_int32), ("n_max", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("num_reqs", ctypes.c_int32), ("block_tables", ctypes.POINTER(ctypes.c_int32)),
+                ("device_tables", ctypes.c_void_p), ("window_q", ctypes.POINTER(ctypes.c_void_p)),
+                ("window_lse", ctypes.POINTER(ctypes.c_void_p)), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t), ("freed_ids", ctypes.POINTER(ctypes.c_int32)),
+                ("num_freed", ctypes.POINTER(ctypes.c_int32)), ("stream", ctypes.c_void_p),
+                ("debug", ctypes.POINTER(_Debug)), ("flags", ctypes.c_uint32)]
+
+
 _i32p = ctypes.POINTER(ctypes.c_int32)
 _vp = ctypes.c_void_p
 _lib = None
@@ -135,6 +148,7 @@ def lib() -> ctypes.CDLL:
         "zp_compress_workspace_bytes_n": (ctypes.c_size_t, [ctypes.POINTER(_KVCache),
                                                             ctypes.c_int32, ctypes.c_int32,
                                                             ctypes.c_int32, ctypes.c_int32]),
+        "zp_compress_ex": (S, [ctypes.POINTER(_KVCache), _vp, ctypes.POINTER(_CompressArgs)]),
         "zp_compress_query": (S, [ctypes.POINTER(_KVCache), ctypes.c_int32, ctypes.c_int32,
                                   ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(_CompressInfo)]),
         "zp_append_kv": (S, [ctypes.POINTER(_KVCache), ctypes.c_int32, ctypes.c_int32, _vp, _vp,
@@ -396,13 +410,16 @@ def compress_query(cache: KVCache, num_reqs: int, n_max: int, window: int,
 
 def compress(cache: KVCache, pool: BlockPool, n_max: int, window: int, tables: np.ndarray,
              window_q: List, workspace, stream=None, debug: Optional[dict] = None,
-             window_lse: Optional[List] = None, keep_prefix: bool = False) -> np.ndarray:
+             window_lse: Optional[List] = None, keep_prefix: bool = False,
+             device_tables=None) -> np.ndarray:
     """zp_compress (zp_compress_lse when ``window_lse``, per-layer float
     tensors [R][w][Hq] of the window rows' normalisers, is given;
     zp_compress_n when ``tables`` has n_src > n_max columns).  ``tables``
     (host int32 [R][n_src]) is rewritten on success; returns the freed block
     ids.  ``keep_prefix``: zp_compress_keep_prefix (shared blocks the
-    compaction leaves unchanged stay shared)."""
+    compaction leaves unchanged stay shared).  ``device_tables`` (device
+    int32 [R][n_src], the same ids as ``tables``): zp_compress_ex with the
+    caller's device copy, so an in-place plan uploads nothing."""
     import torch
     if not (isinstance(tables, np.ndarray) and tables.dtype == np.int32 and tables.ndim == 2
             and tables.flags.c_contiguous):
@@ -421,6 +438,8 @@ def compress(cache: KVCache, pool: BlockPool, n_max: int, window: int, tables: n
         for l, t in enumerate(window_lse):
             _want(t, f"window_lse[{l}]", dev, torch.float32, (R, window, Hq))
     _want(workspace, "workspace", dev, None, None)
+    if device_tables is not None:
+        _want(device_tables, "device_tables", dev, torch.int32, (R, n_src))
     if debug:
         T, k_keep = n_src * b, (n_max - 1) * b
         for key in ("importance", "redundancy", "score"):
@@ -438,7 +457,16 @@ def compress(cache: KVCache, pool: BlockPool, n_max: int, window: int, tables: n
     if debug:
         dbg = _Debug(_dptr(debug.get("importance")), _dptr(debug.get("redundancy")),
                      _dptr(debug.get("score")), _dptr(debug.get("kept")))
-    if keep_prefix:
+    if device_tables is not None:
+        a = _CompressArgs(n_src, n_max, window, R, _i32(tables), device_tables.data_ptr(),
+                          ctypes.cast(wq, ctypes.POINTER(_vp)),
+                          ctypes.cast(wl, ctypes.POINTER(_vp)) if wl is not None else None,
+                          workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                          _i32(freed), _i32(n), _stream_handle(stream),
+                          ctypes.pointer(dbg) if dbg else None,
+                          ZP_COMPRESS_KEEP_PREFIX if keep_prefix else 0)
+        st = lib().zp_compress_ex(cache.ref, pool.handle, ctypes.byref(a))
+    elif keep_prefix:
         st = lib().zp_compress_keep_prefix(
             cache.ref, pool.handle, n_src, n_max, window, R, _i32(tables),
             ctypes.cast(wq, ctypes.POINTER(_vp)),

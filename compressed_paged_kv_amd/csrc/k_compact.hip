@@ -46,7 +46,7 @@ __global__ __launch_bounds__(kThreads, 4) void k_compact(CompactParams p) {
   constexpr int kRowsPerPass = kThreads / VPR;
   constexpr int kRowsPerTile = kRowsPerPass * kUnroll;
   const int h = blockIdx.x >> 1, kv = blockIdx.x & 1;
-  const int lr = blockIdx.y;
+  const int lr = p.layer0 * p.R + blockIdx.y;   // (layer, request) over the whole call
   const int l = lr / p.R, r = lr - l * p.R;
   const int tid = threadIdx.x;
   const int vec = tid % VPR, rsub = tid / VPR;
@@ -61,8 +61,8 @@ __global__ __launch_bounds__(kThreads, 4) void k_compact(CompactParams p) {
   __shared__ int s_first;
   const int32_t* ev = p.evicted + unit * p.E;
   for (int i = tid; i < p.E; i += kThreads) f[i] = ev[i] - i;
-  for (int n = tid; n < p.n_src; n += kThreads) srcb[n] = p.src[(size_t)r * p.n_src + n];
-  for (int n = tid; n < p.n_max - 1; n += kThreads) dstb[n] = p.dst[(size_t)r * (p.n_max - 1) + n];
+  for (int n = tid; n < p.n_src; n += kThreads) srcb[n] = p.src[(size_t)r * p.src_stride + n];
+  for (int n = tid; n < p.n_max - 1; n += kThreads) dstb[n] = p.dst[(size_t)r * p.dst_stride + n];
   if (tid == 0) s_first = p.E > 0 ? ev[0] : p.K_keep;  // rows below the first eviction stay put
   __syncthreads();
   // ... unless their block is re-targeted (a new block for a shared source)
@@ -83,7 +83,8 @@ __global__ __launch_bounds__(kThreads, 4) void k_compact(CompactParams p) {
 
   // a row of the pool as one index (block, head, offset), below 2^31 for
   // any pool the host accepts; the byte address is formed at the access
-  char* const base = static_cast<char*>(p.layer_ptrs[l * kPtrsPerLayer + kv]) + vec * 16;
+  const LayerArgs& la = p.layers[l - p.layer0];
+  char* const base = static_cast<char*>(kv ? la.v : la.k) + vec * 16;
   auto row_of = [&](int blk, int off) -> int { return (blk * p.H + h) * b + off; };
   auto addr = [&](int row) -> char* { return base + (size_t)(unsigned)row * row_bytes; };
   // Rows past the end are clamped to the last row; an unmoved row is read
@@ -144,7 +145,8 @@ hipError_t launch_compact(const CompactParams& p, int num_layers, int row_bytes,
     return hipErrorInvalidValue;
   if (block_size != 16 && block_size != 32) return hipErrorInvalidValue;
   if (p.K_keep != (p.n_max - 1) * block_size) return hipErrorInvalidValue;
-  dim3 grid(2 * p.H, num_layers * p.R);
+  if (num_layers < 1 || num_layers > kArgLayers) return hipErrorInvalidValue;
+  dim3 grid(2 * p.H, num_layers * p.R);   // layers layer0 .. layer0 + num_layers - 1
   const int vpr = row_bytes / 16;
   if (vpr != 8 && vpr != 16 && vpr != 32) return hipErrorInvalidValue;
   prof_begin(ZP_PHASE_COMPACT, s);

@@ -384,8 +384,8 @@ __device__ inline void compact_unit(const ScoreParams& p, float* lds, int* s_fir
   unsigned short* kept = reinterpret_cast<unsigned short*>(lds + kMaxEvicted);
   int* srcb = reinterpret_cast<int*>(lds + kMaxEvicted + kMaxScoreSlots / 2);
   int* dstb = srcb + kMaxScoreSlots / 16;
-  for (int n = tid; n < p.n_src; n += NTH) srcb[n] = p.src[(size_t)r * p.n_src + n];
-  for (int n = tid; n < p.n_max - 1; n += NTH) dstb[n] = p.dst[(size_t)r * (p.n_max - 1) + n];
+  for (int n = tid; n < p.n_src; n += NTH) srcb[n] = p.src[(size_t)r * p.src_stride + n];
+  for (int n = tid; n < p.n_max - 1; n += NTH) dstb[n] = p.dst[(size_t)r * p.dst_stride + n];
   if (tid == 0) *s_first = p.K_keep;
   __syncthreads();  // f (written by the selection) and the block ids are in LDS
   // the first re-targeted block (a new block for a shared source) ...
@@ -404,8 +404,8 @@ __device__ inline void compact_unit(const ScoreParams& p, float* lds, int* s_fir
   const int first = min(min(*s_first, p.E > 0 ? f[0] : p.K_keep), p.K_keep);
   if (first >= p.K_keep) return;  // nothing moves (uniform)
 
-  char* const kbase = static_cast<char*>(p.layer_ptrs[l * kPtrsPerLayer + 0]) + vec * 16;
-  char* const vbase = static_cast<char*>(p.layer_ptrs[l * kPtrsPerLayer + 1]) + vec * 16;
+  char* const kbase = static_cast<char*>(p.layers[l - p.layer0].k) + vec * 16;
+  char* const vbase = static_cast<char*>(p.layers[l - p.layer0].v) + vec * 16;
   auto row_of = [&](int blk, int off) -> int { return (blk * p.H + h) * B + off; };
   auto off_of = [&](int row) -> size_t { return (size_t)(unsigned)row * kRowBytes; };
   // Rows past the end are clamped to the last row; unmoved rows are read
@@ -490,7 +490,7 @@ __device__ __forceinline__ void score_unit(const ScoreParams& p) {
                             : ZP_SCORE_RING_VGPRS / (FL * 4) > 4 ? 4
                                                                  : ZP_SCORE_RING_VGPRS / (FL * 4);
 
-  const size_t unit = blockIdx.x;
+  const size_t unit = (size_t)p.layer0 * p.R * p.H + blockIdx.x;  // over the whole call
   const int h = (int)(unit % p.H);
   const int lr = (int)(unit / p.H);
   const int l = lr / p.R, r = lr - l * p.R;
@@ -498,8 +498,8 @@ __device__ __forceinline__ void score_unit(const ScoreParams& p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
   const int rg = wave / WPG, wl = wave - rg * WPG;
-  const char* kbase = static_cast<const char*>(p.layer_ptrs[l * kPtrsPerLayer + 0]);
-  const char* qbase = static_cast<const char*>(p.layer_ptrs[l * kPtrsPerLayer + 2]);
+  const char* kbase = static_cast<const char*>(p.layers[l - p.layer0].k);
+  const char* qbase = static_cast<const char*>(p.layers[l - p.layer0].q);
 
   __shared__ __align__(16) float s_buf[lds_floats<RG>()];
   __shared__ float s_wst[kWaves][RPW][2];
@@ -537,7 +537,7 @@ __device__ __forceinline__ void score_unit(const ScoreParams& p) {
   // this wave's blocks are wl + WPG*k; lane k holds the physical id of the k-th
   const int nbw = p.n_src > wl ? (p.n_src - wl + WPG - 1) / WPG : 0;
   // (a wave has at most 128 blocks: n_src <= 512 at four waves per row group)
-  const int32_t* tab = p.src + (size_t)r * p.n_src + wl;
+  const int32_t* tab = p.src + (size_t)r * p.src_stride + wl;
   const int ids0 = lane < nbw ? tab[WPG * lane] : 0;
   const int ids1 = lane + 64 < nbw ? tab[WPG * (lane + 64)] : 0;
   const int row_off = col * ROWB + grp * 16;
@@ -619,7 +619,7 @@ __device__ __forceinline__ void score_unit(const ScoreParams& p) {
   // (the log-sum-exp the decode steps of those rows computed over the same
   // slots): then K is read once.
   const float sl2 = p.scale_log2;
-  const float* lse = static_cast<const float*>(p.layer_ptrs[l * kPtrsPerLayer + 3]);
+  const float* lse = p.layers[l - p.layer0].lse;
   if (lse != nullptr) {
     if (tid < RT * 16) {
       float o = 1.0e30f;  // padding rows: probability 0

@@ -17,10 +17,17 @@ void clear_error();
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Per-layer device pointers uploaded for the compression kernels:
-// entry [l*4 + 0] = K pool, [l*4 + 1] = V pool, [l*4 + 2] = window queries,
-// [l*4 + 3] = recorded window normalisers (or null).
-constexpr int kPtrsPerLayer = 4;
+// Per-layer device pointers of the compression kernels, passed in the
+// kernel arguments (no upload): K pool, V pool, window queries and the
+// recorded window normalisers (or null).  One launch covers at most
+// kArgLayers layers; more layers take several launches.
+struct LayerArgs {
+  void* k;
+  void* v;
+  const void* q;
+  const float* lse;
+};
+constexpr int kArgLayers = 48;
 
 // Largest number of (query head, window row) pairs per KV head, and the
 // largest cached length the in-LDS scoring and selection handle.
@@ -53,23 +60,28 @@ static_assert((size_t)2 * 4 * kDecodeTargetWorkgroups * (128 + 2) * sizeof(float
               "the static decode scratch must hold the largest split partials");
 
 struct ScoreParams {
-  void* const* layer_ptrs;  // device [L][kPtrsPerLayer]
-  const int32_t* src;       // device [R][n_src]: the request's blocks, n_src >= n_max
+  LayerArgs layers[kArgLayers];  // layers layer0 .. layer0 + launched layers - 1
+  int32_t layer0;           // first layer of this launch; unit = layer0*R*H + blockIdx.x
+  const int32_t* src;       // device, row r at src + r*src_stride: the request's n_src >= n_max blocks
+  int32_t src_stride;
+  int32_t dst_stride;       // row stride of dst
   int32_t* evicted;         // [L*R*H][E], ascending
   float* dbg_importance;    // optional [L*R*H][T]
   float* dbg_redundancy;    // optional [L*R*H][T]
   float* dbg_score;         // optional [L*R*H][T]
   int32_t* dbg_kept;        // optional [L*R*H][K_keep]
-  const int32_t* dst;       // device [R][n_max-1] target blocks: compact in the same kernel; null: select only
+  const int32_t* dst;       // device, row r at dst + r*dst_stride: the n_max-1 target blocks; compact in the same kernel; null: select only
   int32_t k_cached;         // fused compaction: load K normally (1) or non-temporally (0)
   int32_t R, H, Hq, G, w, n_src, n_max, T, C, E, K_keep, rows;  // T = n_src * b
   float scale_log2;  // log2(e) / sqrt(d)
 };
 
 struct CompactParams {
-  void* const* layer_ptrs;  // device [L][kPtrsPerLayer]
-  const int32_t* src;       // device [R][n_src]
-  const int32_t* dst;       // device [R][n_max-1]
+  LayerArgs layers[kArgLayers];  // layers layer0 .. layer0 + launched layers - 1
+  int32_t layer0;
+  const int32_t* src;       // device, row r at src + r*src_stride (n_src entries)
+  const int32_t* dst;       // device, row r at dst + r*dst_stride (n_max-1 entries)
+  int32_t src_stride, dst_stride;
   const int32_t* evicted;   // [L*R*H][E]
   int32_t R, H, n_src, n_max, E, K_keep;
 };

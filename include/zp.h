@@ -264,6 +264,60 @@ zp_status zp_compress_n(const zp_kv_cache* cache, zp_block_pool* pool, int32_t n
                         void* workspace, size_t workspace_bytes, int32_t* freed_ids,
                         int32_t* num_freed, void* stream, const zp_compress_debug* debug);
 
+/* ------------------------------------------------------------------------
+ * zp_compress_ex: every compression call above, with its options in one
+ * struct, and one more: the caller's device copy of the block tables.
+ *
+ * Serving engines keep the block tables on the GPU for decode anyway.
+ * Given that copy, a call whose plan compacts every request in place (no
+ * shared block re-targeted -- the usual case) uploads nothing and records
+ * no event: the kernels read the sources and, in place, the targets from
+ * the device table, and the per-layer pointers travel in the kernel
+ * arguments.  Plans that re-target shared blocks still upload their target
+ * table (host staging ring, one event).  Without the device copy the source
+ * table is uploaded, and the target table only when it differs from it.
+ *
+ * Fields (results exactly as the entry point each combination names):
+ *   n_src, n_max    blocks each request holds (>= n_max; n_src = n_max is
+ *                   zp_compress / zp_compress_lse, larger is zp_compress_n)
+ *   window, num_reqs, block_tables (HOST int32 [num_reqs][n_src], rewritten
+ *                   on success), window_q, window_lse (may be NULL),
+ *                   workspace, workspace_bytes, freed_ids, num_freed,
+ *                   stream, debug (may be NULL): as zp_compress_n.
+ *   device_tables   NULL, or DEVICE int32 [num_reqs][n_src] (row stride
+ *                   n_src, 4-byte aligned) holding the same ids as
+ *                   block_tables at the call.  The library cannot compare
+ *                   the two: a copy that differs gives wrong results (every
+ *                   id is read as a block of the pool).  Not written; after
+ *                   a plan that re-targets blocks the caller refreshes it
+ *                   from the rewritten host tables.
+ *   flags           0, or ZP_COMPRESS_KEEP_PREFIX (zp_compress_keep_prefix).
+ * Rejects what the named entry points reject, unknown flags and a
+ * misaligned device_tables.
+ * ---------------------------------------------------------------------- */
+#define ZP_COMPRESS_KEEP_PREFIX 1u
+
+typedef struct zp_compress_args {
+  int32_t n_src;
+  int32_t n_max;
+  int32_t window;
+  int32_t num_reqs;
+  int32_t* block_tables;
+  const int32_t* device_tables;
+  const void* const* window_q;
+  const void* const* window_lse;
+  void* workspace;
+  size_t workspace_bytes;
+  int32_t* freed_ids;
+  int32_t* num_freed;
+  void* stream;
+  const zp_compress_debug* debug;
+  uint32_t flags;
+} zp_compress_args;
+
+zp_status zp_compress_ex(const zp_kv_cache* cache, zp_block_pool* pool,
+                         const zp_compress_args* args);
+
 /* How zp_compress / zp_compress_lse / zp_compress_n run a call of this
  * shape on the current device (a host query; it enqueues nothing).  One
  * workgroup scores, selects and compacts each (layer, request, KV head)

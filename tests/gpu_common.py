@@ -78,10 +78,12 @@ def window_lse_on_gpu(cache, case, kp_tensors, wq_tensors, device="cuda"):
     return res
 
 
-def run_case(case, device="cuda", decode=True, recorded_lse=False, keep_prefix=False) -> GpuRun:
+def run_case(case, device="cuda", decode=True, recorded_lse=False, keep_prefix=False,
+             device_tables=False) -> GpuRun:
     """``recorded_lse``: compress with the window rows' normalisers taken
     from zp_paged_decode_lse (the single-read scoring) instead of the
-    self-contained two-pass scoring."""
+    self-contained two-pass scoring.  ``device_tables``: zp_compress_ex with
+    a device copy of the tables (no upload when the plan is in place)."""
     g = case.geom
     L, H, b, n_max, w = g.num_layers, g.num_kv_heads, g.block_size, case.n_max, case.window
     R, n_src = case.num_reqs, case.n_src
@@ -99,8 +101,9 @@ def run_case(case, device="cuda", decode=True, recorded_lse=False, keep_prefix=F
                score=torch.full((L, R, H, T), float("nan"), device=device),
                kept=torch.full((L, R, H, k_keep), -1, dtype=torch.int32, device=device))
     wl = window_lse_on_gpu(cache, case, kp, wq, device) if recorded_lse else None
+    dtab = torch.from_numpy(np.ascontiguousarray(case.tables)).to(device) if device_tables else None
     freed = zp.compress(cache, pool, n_max, w, tables, wq, ws, debug=dbg, window_lse=wl,
-                        keep_prefix=keep_prefix)
+                        keep_prefix=keep_prefix, device_tables=dtab)
     torch.cuda.synchronize()
     run = GpuRun(tables=tables.copy(), refcounts=pool.refcounts(), freed=freed.copy(),
                  A=dbg["importance"].cpu().numpy(), R=dbg["redundancy"].cpu().numpy(),

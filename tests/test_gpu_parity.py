@@ -91,6 +91,11 @@ CASES = {
     # normally
     "units_576_streamed_k": lambda: _case("m6", 226, num_reqs=24, num_layers=3, num_kv_heads=8,
                                           num_q_heads=16, head_dim=64, n_max=6, num_blocks=200),
+    # more layers than one launch carries (48): the compression runs in two
+    # launches over layer chunks
+    "layers_50_two_launches": lambda: _case("m7", 228, num_reqs=2, num_layers=50, num_kv_heads=1,
+                                            num_q_heads=2, head_dim=64, n_max=4, window=4,
+                                            num_blocks=12),
     # 16 keys per selecting thread: 4096 slots exactly, and a ragged 3200
     "slots_4096_rows64": lambda: _case("m4", 224, num_reqs=2, num_kv_heads=1, num_q_heads=4,
                                        n_max=256, num_blocks=520),
@@ -563,3 +568,32 @@ def test_fused_compaction_streaming_k_equals_the_standalone_kernel():
     case = _case("m6", 226, num_reqs=R, num_blocks=R * 6 + 8, **kw)
     _fused_equals_standalone(case, want_k_cached=0)
     check_case(case, run_case(case))
+
+
+@pytest.mark.parametrize("name,keep_prefix", [
+    ("tiny", False),                          # in place: nothing uploaded
+    ("bf16_d128_b16_ragged", False),
+    ("shared_prefix_2layers", False),         # re-targets: the target table is uploaded
+    ("over_cap_prefix_2layers", False),       # past the cap, shared prefix
+    ("over_cap_bf16_3_extra", False),         # past the cap, in place
+    ("layers_50_two_launches", False),        # two launches of layer chunks
+    ("shared_prefix_2layers", True),          # prefix keeping with device sources
+    ("bf16_d128_b16_ragged", True),
+])
+def test_device_tables_equal_the_uploaded_tables(name, keep_prefix):
+    """zp_compress_ex with the caller's device copy of the tables: the same
+    pools, tables, survivor lists and decode outputs, bit for bit, as the
+    call that uploads its tables, and the oracle's results."""
+    case = CASES[name]()
+    say(f"[gpu parity] device tables: {name}, keep_prefix={keep_prefix}")
+    up = run_case(case, keep_prefix=keep_prefix)
+    dv = run_case(case, keep_prefix=keep_prefix, device_tables=True)
+    np.testing.assert_array_equal(up.tables, dv.tables)
+    np.testing.assert_array_equal(up.refcounts, dv.refcounts)
+    np.testing.assert_array_equal(np.sort(up.freed), np.sort(dv.freed))
+    np.testing.assert_array_equal(up.kept, dv.kept)
+    for a, b in zip(up.appended_k + up.appended_v, dv.appended_k + dv.appended_v):
+        assert np.array_equal(np.ascontiguousarray(a).view(np.uint8),
+                              np.ascontiguousarray(b).view(np.uint8))
+    np.testing.assert_array_equal(up.out.view(np.uint32), dv.out.view(np.uint32))
+    check_case(case, dv, keep_prefix=keep_prefix)

@@ -32,6 +32,7 @@ hipError_t launch_redundancy_all(const RedundancyParams&, int, int, int, hipStre
 hipError_t launch_upload(const void*, void*, size_t, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_first_evict(const int32_t*, int32_t*, int, int, int, int, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t score_resident_per_cu(int, int, int, int, int, bool, int*) { return hipErrorInvalidValue; }
+hipError_t decode_static_scratch(void**) { return hipErrorInvalidValue; }
 }  // namespace zp
 """
 
