@@ -44,7 +44,7 @@ class _KVCache(ctypes.Structure):
 class _SchedConfig(ctypes.Structure):
     _fields_ = [("n_max", ctypes.c_int32), ("block_size", ctypes.c_int32),
                 ("window", ctypes.c_int32), ("num_query_slots", ctypes.c_int32),
-                ("max_running", ctypes.c_int32)]
+                ("max_running", ctypes.c_int32), ("prefill_chunk", ctypes.c_int32)]
 
 
 _i64p_t = ctypes.POINTER(ctypes.c_int64)
@@ -57,7 +57,10 @@ class _SchedStep(ctypes.Structure):
                 ("decode_slot", _i32p_t), ("decode_seq_len", _i32p_t),
                 ("decode_record_row", _i32p_t),
                 ("num_compress", ctypes.c_int32), ("compress_ids", _i64p_t),
-                ("compress_qslot", _i32p_t),
+                ("compress_qslot", _i32p_t), ("compress_n_src", _i32p_t),
+                ("num_prefill", ctypes.c_int32), ("prefill_ids", _i64p_t),
+                ("prefill_start", _i32p_t), ("prefill_len", _i32p_t),
+                ("prefill_record_row", _i32p_t),
                 ("num_preempted", ctypes.c_int32), ("preempted", _i64p_t),
                 ("num_finished", ctypes.c_int32), ("finished", _i64p_t),
                 ("num_released", ctypes.c_int32)]
@@ -636,10 +639,11 @@ class Scheduler:
     observation window, preemption of slot-less requests first."""
 
     def __init__(self, pool: BlockPool, n_max: int, block_size: int, window: int,
-                 num_query_slots: int, max_running: int):
+                 num_query_slots: int, max_running: int, prefill_chunk: int = 0):
         self.pool = pool  # keeps the pool alive
         self.n_max, self.block_size, self.window = n_max, block_size, window
-        cfg = _SchedConfig(n_max, block_size, window, num_query_slots, max_running)
+        self.prefill_chunk = prefill_chunk
+        cfg = _SchedConfig(n_max, block_size, window, num_query_slots, max_running, prefill_chunk)
         h = _vp()
         _check(lib().zp_sched_create(pool.handle, ctypes.byref(cfg), ctypes.byref(h)))
         self.handle = h
@@ -666,6 +670,11 @@ class Scheduler:
             "decode_record_row": arr(st.decode_record_row, st.num_decode, np.int32),
             "compress_ids": arr(st.compress_ids, st.num_compress, np.int64),
             "compress_qslot": arr(st.compress_qslot, st.num_compress, np.int32),
+            "compress_n_src": arr(st.compress_n_src, st.num_compress, np.int32),
+            "prefill_ids": arr(st.prefill_ids, st.num_prefill, np.int64),
+            "prefill_start": arr(st.prefill_start, st.num_prefill, np.int32),
+            "prefill_len": arr(st.prefill_len, st.num_prefill, np.int32),
+            "prefill_record_row": arr(st.prefill_record_row, st.num_prefill, np.int32),
             "preempted": arr(st.preempted, st.num_preempted, np.int64),
             "finished": arr(st.finished, st.num_finished, np.int64),
             "num_released": int(st.num_released),

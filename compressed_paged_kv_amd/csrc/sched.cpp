@@ -27,11 +27,28 @@
 // a slot admitted last; possibly itself), never one compressing this step.
 // A preempted request gives back its blocks and slot and returns to the
 // front of the queue to start over.
-// Then waiting requests are admitted in order while their prompt blocks and
-// the concurrency cap allow.  Blocks given back are released to the pool as
-// a pending group (reference count 0, not allocatable) that the caller
-// releases with zp_block_pool_fence once the GPU work of the step has
-// completed.
+// Chunked prefill (config prefill_chunk > 0): a prompt is written chunk by
+// chunk, one chunk per step, so a prompt longer than the budget never holds
+// more than a chunk beyond it (the ko page, section 5, names chunked
+// prefilling as the next step; the nl page's problem statement faults
+// compressing only the input for the prefill cost it leaves).  Between steps
+// a prefilling request's cache ends at or below the window start T - w
+// (T = N_max*b).  The next chunk, of c = min(prefill_chunk, rest) prompt
+// tokens from cache position t:
+//   * ends at or below T - w: written as it is;
+//   * else, if the rest of the prompt reaches T: cut (or stretched) to end
+//     at the block boundary max(T, floor((t + c)/b)*b) and compressed in the
+//     same step, n_src = that boundary / b blocks (zp_compress_n, the window
+//     being the chunk's last w queries); the cache is then back to
+//     (N_max-1)*b <= T - w;
+//   * else the rest ends inside the window band (T - w, T): it is written
+//     whole, its positions at or past T - w recorded in a query slot (the
+//     request waits for one like a decoding request), and decode continues.
+// Then waiting requests are admitted in order while their prompt blocks (the
+// first chunk's, with chunked prefill) and the concurrency cap allow.
+// Blocks given back are released to the pool as a pending group (reference
+// count 0, not allocatable) that the caller releases with
+// zp_block_pool_fence once the GPU work of the step has completed.
 #include <algorithm>
 #include <cstring>
 #include <deque>
@@ -48,6 +65,8 @@ struct Req {
   int64_t id = 0;
   int32_t prompt_len = 0, max_new = 0, generated = 0;
   int32_t seq_len = 0;
+  int32_t prompt_done = 0;       // prompt tokens written (chunked prefill)
+  int32_t compress_n_src = 0;    // blocks held by a request compressing this step
   std::vector<int32_t> table;
   int32_t qslot = -1;
   int64_t admit_order = -1;
@@ -69,14 +88,32 @@ struct zp_sched {
   int64_t admit_counter = 0;
   int64_t step = 0;
   // outputs of the last plan
-  std::vector<int64_t> admitted, decode_ids, compress_ids, preempted, finished;
-  std::vector<int32_t> decode_slot, decode_seq, decode_row, compress_qslot;
+  std::vector<int64_t> admitted, decode_ids, compress_ids, preempted, finished, prefill_ids;
+  std::vector<int32_t> decode_slot, decode_seq, decode_row, compress_qslot, compress_n_src;
+  std::vector<int32_t> prefill_start, prefill_len, prefill_row;
   std::vector<int32_t> to_release;
 };
 
 namespace {
 
 int32_t cap_tokens(const zp_sched* s) { return s->cfg.n_max * s->cfg.block_size; }
+
+bool prefilling(const Req& q) { return q.prompt_done < q.prompt_len; }
+
+// Length of the next prefill chunk of q (cache at t = q.seq_len, t <= T - w)
+// and whether the request compresses right after it (see the header).
+int32_t next_chunk(const zp_sched* s, const Req& q, bool* compress) {
+  const int32_t b = s->cfg.block_size, w = s->cfg.window, T = cap_tokens(s);
+  const int32_t t = q.seq_len, rest = q.prompt_len - q.prompt_done;
+  const int32_t c = std::min(s->cfg.prefill_chunk, rest);
+  *compress = false;
+  if (t + c <= T - w) return c;
+  if (t + rest >= T) {
+    *compress = true;
+    return std::max(T, (t + c) / b * b) - t;
+  }
+  return rest;
+}
 
 // Drop a request's references to its blocks; blocks reaching 0 wait in the
 // pool for zp_block_pool_fence.
@@ -125,6 +162,7 @@ void preempt(zp_sched* s, int64_t id) {
   give_back_blocks(s, q);
   q.running = false;
   q.seq_len = 0;
+  q.prompt_done = 0;
   q.generated = 0;
   q.admit_order = -1;
   q.slot_wait_since = -1;
@@ -146,6 +184,21 @@ zp_status zp_sched_create(zp_block_pool* pool, const zp_sched_config* cfg, zp_sc
                   "num_query_slots >= 1, max_running >= 1");
     return ZP_ERR_INVALID;
   }
+  // a chunk spans at most prefill_chunk + b tokens past the cache (the
+  // stretch to the next block boundary), so its compression holds at most
+  // n_max - 1 + prefill_chunk/b + 1 blocks and evicts at most
+  // prefill_chunk + 2b slots per head
+  if (cfg->prefill_chunk < 0 || cfg->prefill_chunk % cfg->block_size != 0 ||
+      (cfg->prefill_chunk > 0 &&
+       (cfg->n_max + cfg->prefill_chunk / cfg->block_size > zp::kMaxCompressBlocks ||
+        (int64_t)(cfg->n_max + cfg->prefill_chunk / cfg->block_size) * cfg->block_size >
+            zp::kMaxScoreSlots ||
+        cfg->prefill_chunk + 2 * cfg->block_size > zp::kMaxEvicted))) {
+    zp::set_error("prefill_chunk %d: a multiple of block_size, with n_max + prefill_chunk/b <= %d "
+                  "blocks of at most %d tokens and prefill_chunk + 2*block_size <= %d",
+                  cfg->prefill_chunk, zp::kMaxCompressBlocks, zp::kMaxScoreSlots, zp::kMaxEvicted);
+    return ZP_ERR_INVALID;
+  }
   zp_sched* s = new zp_sched();
   s->pool = pool;
   s->cfg = *cfg;
@@ -160,9 +213,14 @@ zp_status zp_sched_add(zp_sched* s, int64_t id, int32_t prompt_len, int32_t max_
   zp::clear_error();
   if (!s) { zp::set_error("scheduler is NULL"); return ZP_ERR_INVALID; }
   if (s->reqs.count(id)) { zp::set_error("request %lld already exists", (long long)id); return ZP_ERR_INVALID; }
-  if (prompt_len < 1 || prompt_len > cap_tokens(s) - s->cfg.window || max_new_tokens < 1) {
-    zp::set_error("prompt_len must be in [1, N_max*b - w = %d] and max_new_tokens >= 1",
-                  cap_tokens(s) - s->cfg.window);
+  if (s->cfg.prefill_chunk == 0 &&
+      (prompt_len < 1 || prompt_len > cap_tokens(s) - s->cfg.window || max_new_tokens < 1)) {
+    zp::set_error("prompt_len must be in [1, N_max*b - w = %d] and max_new_tokens >= 1 (longer "
+                  "prompts need prefill_chunk > 0)", cap_tokens(s) - s->cfg.window);
+    return ZP_ERR_INVALID;
+  }
+  if (prompt_len < 1 || max_new_tokens < 1) {
+    zp::set_error("prompt_len and max_new_tokens must be >= 1");
     return ZP_ERR_INVALID;
   }
   Req q;
@@ -193,6 +251,11 @@ zp_status zp_sched_plan(zp_sched* s, zp_sched_step* out) {
   s->decode_row.clear();
   s->compress_ids.clear();
   s->compress_qslot.clear();
+  s->compress_n_src.clear();
+  s->prefill_ids.clear();
+  s->prefill_start.clear();
+  s->prefill_len.clear();
+  s->prefill_row.clear();
   s->preempted.clear();
   s->finished.clear();
   s->to_release.clear();
@@ -217,8 +280,10 @@ zp_status zp_sched_plan(zp_sched* s, zp_sched_step* out) {
   std::vector<int64_t> need_slot;
   for (int64_t id : s->running) {
     Req& q = s->reqs[id];
+    if (prefilling(q)) continue;  // chunks are planned in 2c
     if (q.seq_len == T) {
       q.compress_now = true;
+      q.compress_n_src = s->cfg.n_max;
       s->compress_ids.push_back(id);
     } else if (q.seq_len >= T - w && q.qslot < 0) {
       if (q.slot_wait_since < 0) q.slot_wait_since = s->step;
@@ -238,7 +303,7 @@ zp_status zp_sched_plan(zp_sched* s, zp_sched_step* out) {
   std::vector<int64_t> order;
   for (int64_t id : s->running) {
     const Req& q = s->reqs[id];
-    if (q.compress_now || (q.seq_len >= T - w && q.qslot < 0)) continue;
+    if (prefilling(q) || q.compress_now || (q.seq_len >= T - w && q.qslot < 0)) continue;
     order.push_back(id);
   }
   // 2b. in admission order: one token each, a new block when it starts one
@@ -286,26 +351,121 @@ zp_status zp_sched_plan(zp_sched* s, zp_sched_step* out) {
     q.seq_len = p + 1;
     q.generated += 1;
   }
-  for (int64_t id : s->compress_ids) s->compress_qslot.push_back(s->reqs[id].qslot);
+  // 2c. chunked prefill, in admission order: one chunk each (see the header)
+  std::vector<int64_t> pre;
+  for (int64_t id : s->running)
+    if (prefilling(s->reqs[id])) pre.push_back(id);
+  for (int64_t id : pre) {
+    if (!s->reqs[id].running) continue;  // preempted earlier in this step
+    Req& q = s->reqs[id];
+    bool comp = false;
+    const int32_t c = next_chunk(s, q, &comp);
+    const int32_t t = q.seq_len;
+    const bool band = !comp && t + c > T - w;  // ends inside the window band
+    if (band && q.qslot < 0) {
+      if (s->free_qslots.empty()) continue;  // waits for a query slot
+      q.qslot = *s->free_qslots.begin();
+      s->free_qslots.erase(s->free_qslots.begin());
+    }
+    const int32_t need = (t + c + b - 1) / b - (int32_t)q.table.size();
+    s->pool->reap();
+    if (need > (int32_t)s->pool->free_ids.size()) {
+      // as for a decoding request: wait, and preempt unless blocks given
+      // back in this step cover it
+      if (promised >= need) {
+        promised -= need;
+        continue;
+      }
+      const int64_t v = pick_victim(s, -1);
+      if (v < 0) {
+        zp::set_error("request %lld needs %d blocks and none can be freed", (long long)id, need);
+        return ZP_ERR_NO_BLOCKS;
+      }
+      auto it = std::find(s->decode_ids.begin(), s->decode_ids.end(), v);
+      if (it != s->decode_ids.end()) {
+        const size_t k = (size_t)(it - s->decode_ids.begin());
+        s->decode_ids.erase(it);
+        s->decode_slot.erase(s->decode_slot.begin() + (long)k);
+        s->decode_seq.erase(s->decode_seq.begin() + (long)k);
+        s->decode_row.erase(s->decode_row.begin() + (long)k);
+      }
+      auto jt = std::find(s->prefill_ids.begin(), s->prefill_ids.end(), v);
+      if (jt != s->prefill_ids.end()) {
+        const size_t k = (size_t)(jt - s->prefill_ids.begin());
+        s->prefill_ids.erase(jt);
+        s->prefill_start.erase(s->prefill_start.begin() + (long)k);
+        s->prefill_len.erase(s->prefill_len.begin() + (long)k);
+        s->prefill_row.erase(s->prefill_row.begin() + (long)k);
+      }
+      const size_t before = s->to_release.size();
+      preempt(s, v);
+      promised += (int64_t)(s->to_release.size() - before);
+      continue;
+    }
+    for (int32_t i = 0; i < need; i++) {
+      int32_t blk = -1;
+      alloc_block(s, &blk);
+      q.table.push_back(blk);
+    }
+    s->prefill_ids.push_back(id);
+    s->prefill_start.push_back(t);
+    s->prefill_len.push_back(c);
+    s->prefill_row.push_back(band ? q.qslot * w : -1);
+    q.seq_len = t + c;
+    q.prompt_done += c;
+    if (comp) {
+      q.compress_now = true;
+      q.compress_n_src = (t + c) / b;
+      s->compress_ids.push_back(id);
+    }
+  }
 
-  // 3. admission in arrival order, while the prompt blocks fit
+  // 3. admission in arrival order, while the prompt blocks (with chunked
+  //    prefill: the first chunk's) fit; a chunked request's first chunk is
+  //    written in this step
   while (!s->waiting.empty() && (int32_t)s->running.size() < s->cfg.max_running) {
     Req& q = s->reqs[s->waiting.front()];
-    const int32_t nb = (q.prompt_len + b - 1) / b;
+    const bool chunked = s->cfg.prefill_chunk > 0;
+    bool comp = false;
+    q.seq_len = 0;
+    q.prompt_done = 0;
+    const int32_t c = chunked ? next_chunk(s, q, &comp) : q.prompt_len;
+    const bool band = chunked && !comp && c > T - w;
+    const int32_t nb = (c + b - 1) / b;
     s->pool->reap();
-    if ((int32_t)s->pool->free_ids.size() < nb) break;
+    if ((int32_t)s->pool->free_ids.size() < nb || (band && s->free_qslots.empty())) break;
     s->waiting.pop_front();
     for (int32_t i = 0; i < nb; i++) {
       int32_t blk = -1;
       alloc_block(s, &blk);
       q.table.push_back(blk);
     }
-    q.seq_len = q.prompt_len;
+    q.seq_len = c;
+    q.prompt_done = c;
     q.generated = 0;
     q.running = true;
     q.admit_order = s->admit_counter++;
     s->running.push_back(q.id);
     s->admitted.push_back(q.id);
+    if (chunked) {
+      if (band) {
+        q.qslot = *s->free_qslots.begin();
+        s->free_qslots.erase(s->free_qslots.begin());
+      }
+      s->prefill_ids.push_back(q.id);
+      s->prefill_start.push_back(0);
+      s->prefill_len.push_back(c);
+      s->prefill_row.push_back(band ? q.qslot * w : -1);
+      if (comp) {
+        q.compress_now = true;
+        q.compress_n_src = c / b;
+        s->compress_ids.push_back(q.id);
+      }
+    }
+  }
+  for (int64_t id : s->compress_ids) {
+    s->compress_qslot.push_back(s->reqs[id].qslot);
+    s->compress_n_src.push_back(s->reqs[id].compress_n_src);
   }
   zp::add_pending(s->pool, s->to_release, nullptr);
   s->step++;
@@ -320,6 +480,12 @@ zp_status zp_sched_plan(zp_sched* s, zp_sched_step* out) {
   out->num_compress = (int32_t)s->compress_ids.size();
   out->compress_ids = s->compress_ids.data();
   out->compress_qslot = s->compress_qslot.data();
+  out->compress_n_src = s->compress_n_src.data();
+  out->num_prefill = (int32_t)s->prefill_ids.size();
+  out->prefill_ids = s->prefill_ids.data();
+  out->prefill_start = s->prefill_start.data();
+  out->prefill_len = s->prefill_len.data();
+  out->prefill_record_row = s->prefill_row.data();
   out->num_preempted = (int32_t)s->preempted.size();
   out->preempted = s->preempted.data();
   out->num_finished = (int32_t)s->finished.size();

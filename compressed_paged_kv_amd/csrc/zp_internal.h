@@ -36,6 +36,8 @@ constexpr int kMaxScoreSlots = 8192;
 // Largest eviction count per (layer, request, head) the compaction's LDS list
 // holds: E = block_size * (n_src - n_max + 1).
 constexpr int kMaxEvicted = 1024;
+// Largest block count of one request in a compression call (n_src).
+constexpr int kMaxCompressBlocks = 512;
 // Largest T of the all-pairs redundancy (inverse norms of all keys in LDS).
 constexpr int kMaxRedundancySlots = 8192;
 // Paged decode: threads per workgroup, and the workgroup count below which

@@ -480,6 +480,23 @@ zp_status zp_redundancy_all(const zp_kv_cache* cache, int32_t layer, int32_t num
  * Blocks a step gives back (finished or preempted requests) reach reference
  * count 0 but stay pending in the pool until zp_block_pool_fence(), which
  * the caller calls once the GPU work that last read them has completed.
+ *
+ * Chunked prefill (prefill_chunk > 0; the ko page, section 5, names chunked
+ * prefilling as the next step): prompts of any length are written one
+ * chunk per step, and a prompt longer than the budget is compressed as its
+ * chunks go, so it never holds more than about a chunk past the cap.
+ * Between steps a prefilling request's cache ends at or below the window
+ * start T - w (T = N_max*b).  From cache position t, the next chunk of
+ * c = min(prefill_chunk, rest of the prompt) tokens
+ *   - ending at or below T - w is written as it is;
+ *   - else, when the rest of the prompt reaches T, is cut or stretched to end
+ *     at the block boundary max(T, floor((t + c)/b)*b), and the request
+ *     compresses in the same step with n_src = that boundary / b blocks
+ *     (zp_compress_n; window = the queries of the chunk's last w tokens),
+ *     which leaves (N_max-1)*b cached tokens;
+ *   - else (the rest ends inside (T - w, T)) is written whole, its positions
+ *     p >= T - w recorded in a query slot (the request waits for a free one)
+ *     at row prefill_record_row + p - (T - w), and decode follows.
  * ---------------------------------------------------------------------- */
 typedef struct zp_sched zp_sched;
 
@@ -489,21 +506,33 @@ typedef struct zp_sched_config {
   int32_t window;          /* w, 1..b */
   int32_t num_query_slots; /* query slots (each holds w rows), >= 1 */
   int32_t max_running;     /* concurrency cap, >= 1 */
+  int32_t prefill_chunk;   /* 0: whole prompts at admission (length <= N_max*b - w);
+                              else tokens per prefill chunk, a multiple of b */
 } zp_sched_config;
 
 /* One step's plan; arrays are owned by the scheduler and valid until the
  * next zp_sched_plan. */
 typedef struct zp_sched_step {
-  int32_t num_admitted;  /* prefilled this step: prompt in the request's blocks */
+  int32_t num_admitted;  /* admitted this step: whole prompt in the request's blocks, or
+                            (chunked prefill) its first chunk, listed with the prefills */
   const int64_t* admitted;
   int32_t num_decode;    /* decode one token each */
   const int64_t* decode_ids;
   const int32_t* decode_slot;        /* physical slot (block*b + offset) of the new token */
   const int32_t* decode_seq_len;     /* length including the new token */
   const int32_t* decode_record_row;  /* query-slot row slot*w + i for window position i, or -1 */
-  int32_t num_compress;  /* at the cap: compress this step (zp_sched_tables, then commit) */
+  int32_t num_compress;  /* compress this step (zp_sched_tables, then commit) */
   const int64_t* compress_ids;
-  const int32_t* compress_qslot;     /* their query slots, rows slot*w .. slot*w + w-1 */
+  const int32_t* compress_qslot;     /* their query slots, rows slot*w .. slot*w + w-1; -1 after
+                                        a prefill chunk (window = the chunk's last w queries) */
+  const int32_t* compress_n_src;     /* blocks each holds: N_max at the cap, more after a chunk
+                                        (zp_compress_n; one call per distinct value) */
+  int32_t num_prefill;   /* prefill chunks of this step (after the decodes, before the
+                            compressions of the requests that wrote them) */
+  const int64_t* prefill_ids;
+  const int32_t* prefill_start;      /* first cache position of the chunk */
+  const int32_t* prefill_len;        /* its tokens (prompt tokens prefill_start.. of the cache) */
+  const int32_t* prefill_record_row; /* query-slot row of position T - w, or -1 (see above) */
   int32_t num_preempted;
   const int64_t* preempted;
   int32_t num_finished;
@@ -512,12 +541,16 @@ typedef struct zp_sched_step {
 } zp_sched_step;
 
 /* Rejects n_max < 2, block_size not in {16,32}, window outside [1, b],
- * num_query_slots < 1, max_running < 1.  The pool is borrowed: it must
- * outlive the scheduler. */
+ * num_query_slots < 1, max_running < 1, and a prefill_chunk that is
+ * negative, not a multiple of b, or beyond the compression's limits
+ * (n_max + prefill_chunk/b <= 512 blocks of at most 8192 tokens,
+ * prefill_chunk + 2b <= 1024 evictions per head).  The pool is borrowed: it
+ * must outlive the scheduler. */
 zp_status zp_sched_create(zp_block_pool* pool, const zp_sched_config* cfg, zp_sched** out);
 void zp_sched_destroy(zp_sched* sched);
-/* Queue a request; prompt_len in [1, N_max*b - w] (longer prompts are
- * compressed after prefill with zp_compress_n), max_new_tokens >= 1. */
+/* Queue a request; max_new_tokens >= 1; prompt_len >= 1, and without
+ * chunked prefill at most N_max*b - w (longer prompts then go through
+ * zp_compress_n after their prefill). */
 zp_status zp_sched_add(zp_sched* sched, int64_t id, int32_t prompt_len, int32_t max_new_tokens);
 /* Plan the next step (see above).  ZP_ERR_STATE if the previous plan's
  * compressions were not committed; ZP_ERR_NO_BLOCKS if a request needs a
@@ -527,10 +560,13 @@ zp_status zp_sched_plan(zp_sched* sched, zp_sched_step* out);
  * blocks) and lengths (may be NULL) of the given requests. */
 zp_status zp_sched_tables(const zp_sched* sched, const int64_t* ids, int32_t n, int32_t width,
                           int32_t* tables_out, int32_t* seq_lens_out);
-/* After the step's compression call (zp_compress or zp_compress_lse on
- * zp_sched_tables(compress_ids, width = n_max), which rewrote those tables):
- * new_tables HOST int32 [num_compress][n_max]; each request's length
- * becomes (N_max-1)*b and its query slot is free again. */
+/* After the step's compression calls (zp_compress / zp_compress_lse on
+ * zp_sched_tables(ids, width = n_max) for the requests at the cap,
+ * zp_compress_n on width = n_src for those past it after a prefill chunk,
+ * which rewrote those tables): new_tables HOST int32 [num_compress][n_max]
+ * in compress_ids order (the first n_max entries of each rewritten row);
+ * each request's length becomes (N_max-1)*b and its query slot is free
+ * again. */
 zp_status zp_sched_compress_commit(zp_sched* sched, const int32_t* new_tables);
 zp_status zp_sched_stats(const zp_sched* sched, int32_t* num_waiting, int32_t* num_running,
                          int32_t* free_query_slots);

@@ -198,3 +198,146 @@ def test_random_workload_invariants_and_completion(seed):
             break
     assert len(done) == R, f"only {len(done)} of {R} finished"
     assert pool.num_free() == nblocks
+
+
+# ------------------------------------------------------------------ chunked prefill
+
+def _drive_prefill(s, pool, n_max, steps, on_step=None):
+    """Run plans; compress (host planner, per n_src group) and commit each
+    step's compressions; return the per-step plans."""
+    plans = []
+    for _ in range(steps):
+        p = s.plan()
+        if on_step:
+            on_step(p)
+        if p["compress_ids"].size:
+            news = []
+            for i, rid in enumerate(p["compress_ids"]):
+                n_src = int(p["compress_n_src"][i])
+                tab, lens = s.tables([rid], width=n_src)
+                assert lens.tolist() == [n_src * s.block_size]
+                assert np.all(tab[0] >= 0)                 # every block held, all full
+                zp.compress_plan(pool, n_max, tab)
+                news.append(tab[0, :n_max])
+            s.compress_commit(np.stack(news))
+        pool.fence()
+        plans.append(p)
+    return plans
+
+
+def test_chunked_prefill_validation():
+    pool = zp.BlockPool(64, manual_fence=True)
+    kw = dict(n_max=8, block_size=16, window=16, num_query_slots=2, max_running=4)
+    for bad in (-16, 24, 16 * 600):           # negative, not a multiple of b, past the limits
+        with pytest.raises(zp.ZpError):
+            zp.Scheduler(pool, prefill_chunk=bad, **kw)
+    s = zp.Scheduler(pool, prefill_chunk=48, **kw)
+    s.add(1, 5000, 3)                          # any prompt length with chunked prefill
+    with pytest.raises(zp.ZpError):
+        s.add(2, 0, 3)
+
+
+def test_chunked_prefill_of_a_long_prompt():
+    """n_max = 8, b = 16 (T = 128), w = 16, chunks of 48, a 300-token prompt.
+    Worked by hand from the rule in the header: chunks 0..47, 48..95 (the
+    cache ends at 96 <= T - w = 112); then 96 + 48 = 144 > 112 and the rest
+    reaches T, so the chunk ends at the block boundary 144: compress 9 blocks
+    -> 112; then 112 + 48 = 160, boundary 160: 10 blocks -> 112, twice
+    (prompt tokens 144..191 and 192..239); then 48 tokens are left: 112 + 48
+    = 160 again (10 blocks) -> 112 with 12 left; 112 + 12 = 124 lies in the
+    window band (112, 128): written whole, positions 112..123 recorded in
+    query-slot rows 0..11, and decode goes on from 124: positions 124..127
+    recorded in rows 12..15, then the cap compression (8 blocks)."""
+    n_max, b, w = 8, 16, 16
+    pool = zp.BlockPool(64, manual_fence=True)
+    s = zp.Scheduler(pool, n_max=n_max, block_size=b, window=w, num_query_slots=1, max_running=2,
+                     prefill_chunk=48)
+    s.add(5, 300, 10)
+    chunks, comps, rows = [], [], []
+
+    def look(p):
+        for i in range(p["prefill_ids"].size):
+            chunks.append((int(p["prefill_start"][i]), int(p["prefill_len"][i]),
+                           int(p["prefill_record_row"][i])))
+        for i in range(p["compress_ids"].size):
+            comps.append(int(p["compress_n_src"][i]))
+            assert p["compress_qslot"][i] == (-1 if p["prefill_ids"].size else 0)
+        for i in range(p["decode_ids"].size):
+            rows.append(int(p["decode_record_row"][i]))
+        # a request writes a chunk or decodes, never both in one step
+        assert not (set(p["prefill_ids"].tolist()) & set(p["decode_ids"].tolist()))
+
+    _drive_prefill(s, pool, n_max, 12, look)
+    assert chunks == [(0, 48, -1), (48, 48, -1), (96, 48, -1), (112, 48, -1), (112, 48, -1),
+                      (112, 48, -1), (112, 12, 0)]
+    assert comps == [9, 10, 10, 10, 8]
+    # decode after the prefill: 124..127 in rows 12..15, then the cap, then
+    # 112.. again outside the window
+    assert rows[:4] == [12, 13, 14, 15] and rows[4:] == [-1] * (len(rows) - 4)
+    tab, lens = s.tables([5])
+    assert int(lens[0]) == 112 + len(rows) - 4
+    # every block held is counted once, the rest of the pool free
+    assert sum(pool.refcount(i) for i in range(64)) == int((tab[0] >= 0).sum())
+
+
+def test_chunked_prefill_batch_by_hand():
+    """n_max = 8, b = 16 (T = 128, K_keep = 112), w = 8 (window start 120),
+    chunks of 64; four requests admitted together, worked by hand:
+      1: 200 tokens: (0, 64); (64, 64) ends at 128 = T -> compress 8 blocks;
+         (112, 64) ends at 176, a block boundary -> compress 11; (112, 8)
+         ends at 120 <= 120, plain; then decodes from 120 with a query slot.
+      2: 30 tokens: (0, 30), then decodes.
+      3: 124 tokens: (0, 64); (64, 60) ends at 124, inside the band
+         (120, 128) with no more prompt to reach T: written whole with its
+         positions 120..123 in query-slot rows 0..3 (slot 0), then decodes
+         124.. into rows 4..7.
+      4: 150 tokens: (0, 64); (64, 64) -> compress 8; then 22 left: 112 + 22
+         = 134 floors to the boundary 128 -> (112, 16), compress 8; (112, 6)
+         plain; decodes from 118."""
+    n_max, b, w = 8, 16, 8
+    pool = zp.BlockPool(64, manual_fence=True)
+    s = zp.Scheduler(pool, n_max=n_max, block_size=b, window=w, num_query_slots=4, max_running=4,
+                     prefill_chunk=64)
+    for rid, P in ((1, 200), (2, 30), (3, 124), (4, 150)):
+        s.add(rid, P, 50)
+    seen = []
+
+    def look(p):
+        pre = {int(i): (int(a), int(l), int(r)) for i, a, l, r in
+               zip(p["prefill_ids"], p["prefill_start"], p["prefill_len"], p["prefill_record_row"])}
+        comp = dict(zip(p["compress_ids"].tolist(), p["compress_n_src"].tolist()))
+        dec = {int(i): (int(l) - 1, int(r)) for i, l, r in
+               zip(p["decode_ids"], p["decode_seq_len"], p["decode_record_row"])}
+        seen.append((pre, comp, dec))
+
+    _drive_prefill(s, pool, n_max, 5, look)
+    assert seen[0] == ({1: (0, 64, -1), 2: (0, 30, -1), 3: (0, 64, -1), 4: (0, 64, -1)}, {}, {})
+    assert seen[1] == ({1: (64, 64, -1), 3: (64, 60, 0), 4: (64, 64, -1)}, {1: 8, 4: 8},
+                       {2: (30, -1)})
+    assert seen[2] == ({1: (112, 64, -1), 4: (112, 16, -1)}, {1: 11, 4: 8},
+                       {2: (31, -1), 3: (124, 4)})
+    assert seen[3] == ({1: (112, 8, -1), 4: (112, 6, -1)}, {}, {2: (32, -1), 3: (125, 5)})
+    assert seen[4] == ({}, {}, {1: (120, 8), 2: (33, -1), 3: (126, 6), 4: (118, -1)})
+    tab, lens = s.tables([1, 2, 3, 4], width=n_max)
+    assert lens.tolist() == [121, 34, 127, 119]
+    assert sum(pool.refcount(i) for i in range(64)) == int((tab >= 0).sum())
+
+
+def test_chunked_prefill_waits_for_blocks_and_preempts():
+    """A pool too small for two long prompts: the second request's chunk
+    finds no block, preempts the last-admitted request without a query slot
+    (itself here), and restarts its prefill from the queue later."""
+    n_max, b, w = 4, 16, 16
+    pool = zp.BlockPool(9, manual_fence=True)
+    s = zp.Scheduler(pool, n_max=n_max, block_size=b, window=w, num_query_slots=2, max_running=2,
+                     prefill_chunk=32)
+    s.add(1, 100, 3)
+    s.add(2, 100, 3)
+    preempted = []
+    plans = _drive_prefill(s, pool, n_max, 12, lambda p: preempted.extend(p["preempted"].tolist()))
+    assert 2 in preempted
+    # everything either finished or still holds consistent counts
+    held = sum(pool.refcount(i) for i in range(9))
+    ids = [r for r in (1, 2)]
+    tab, _ = s.tables(ids, width=n_max + 2)
+    assert held == int((tab >= 0).sum())
