@@ -62,15 +62,19 @@ def source_sha(rel: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def read_counters(kernel: str, workload: str):
-    """HBM bytes per launch from the workload's committed rocprofv3 counter
-    summary, or None when absent or taken on a different kernel source."""
+def read_counters(kernel: str, workload: str, what: str = "egress"):
+    """Bytes per launch from the workload's committed rocprofv3 counter
+    summary, or None when absent or taken on a different kernel source:
+    "egress" = FETCH_SIZE + WRITE_SIZE scaled by the calibration copy (bytes
+    leaving L2 for the memory fabric), "dram" = the bytes of requests bound
+    for DRAM (32-byte unit counters, memory-side cache hits included)."""
     path = os.path.join(PROFILE_DIR, f"hot_path_kernels_{workload}.txt")
     if not os.path.exists(path):
         return None
     text = open(path).read()
-    m = re.search(rf"^phase {kernel}: fetch_bytes=(\d+) write_bytes=(\d+) source_sha=(\w+)", text,
-                  re.M)
+    pat = (rf"^phase {kernel}: fetch_bytes=(\d+) write_bytes=(\d+) source_sha=(\w+)" if what == "egress"
+           else rf"^phase {kernel}: dram_read_bytes=(\d+) dram_write_bytes=(\d+) source_sha=(\w+)")
+    m = re.search(pat, text, re.M)
     if not m or m.group(3) != source_sha(KERNEL_SOURCES[kernel]):
         return None
     return int(m.group(1)) + int(m.group(2))
@@ -190,11 +194,18 @@ def summarize_counters(dirs) -> int:
     return 0
 
 
-def summarize(kt_dir: str, fetch_dir: str, write_dir: str) -> int:
+def summarize(kt_dir: str, fetch_dir: str, write_dir: str, req_dir: str = None,
+              dram_dir: str = None) -> int:
     """Summary text of rocprofv3 outputs: kernel-trace statistics of the
-    bench run, and HBM bytes per dispatch of each hot-path kernel from the
-    FETCH_SIZE / WRITE_SIZE runs, scaled by what the same counters read for
-    the calibration copy (1 GiB each way)."""
+    bench run, and bytes per dispatch of each hot-path kernel leaving L2 for
+    the memory fabric, from the FETCH_SIZE / WRITE_SIZE runs scaled by what
+    the same counters read for the calibration copy (1 GiB each way).  With
+    ``req_dir`` (TCC_EA0_RDREQ, TCC_BUBBLE, TCC_EA0_RDREQ_32B and
+    TCC_EA0_RDREQ_128B) the read bytes are also derived from the request
+    sizes, which explains the copy's scale factor; with ``dram_dir``
+    (TCC_EA0_RDREQ_DRAM_32B, TCC_EA0_WRREQ_WRITE_DRAM_32B, counted in 32-byte
+    units by definition) the bytes of requests bound for DRAM, which still
+    include hits in the memory-side cache in front of HBM."""
     import glob
     stats = _read_csv(glob.glob(os.path.join(kt_dir, "*kernel_stats.csv"))[0])
     print("# kernel-trace statistics (rocprofv3 --kernel-trace --stats)")
@@ -243,6 +254,76 @@ def summarize(kt_dir: str, fetch_dir: str, write_dir: str) -> int:
         src = KERNEL_SOURCES[phase]
         print(f"phase {phase}: fetch_bytes={fb} write_bytes={wb} source_sha={source_sha(src)} "
               f"(raw FETCH_SIZE {fk[0]:.1f} KiB, WRITE_SIZE {wk[0]:.1f} KiB; {src})")
+
+    def per_kernel_all(d):
+        rows = _read_csv(glob.glob(os.path.join(d, "*counter_collection.csv"))[0])
+        acc = {}
+        for r in rows:
+            acc.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], []).append(
+                float(r["Counter_Value"]))
+        return {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in acc.items()}
+
+    def first_copies(d):
+        rows = _read_csv(glob.glob(os.path.join(d, "*counter_collection.csv"))[0])
+        rows = [r for r in rows if "elementwise" in r["Kernel_Name"].lower()
+                and "mul" in r["Kernel_Name"].lower()]
+        ids = sorted({int(r["Dispatch_Id"]) for r in rows})[:3]
+        acc = {}
+        for r in rows:
+            if int(r["Dispatch_Id"]) in ids:
+                acc.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        return {c: max(v) for c, v in acc.items()}
+
+    def get(c, name):
+        for k in (name, name + "_sum"):
+            if k in c:
+                return c[k]
+        return None
+
+    if req_dir:
+        req = per_kernel_all(req_dir)
+        print()
+        print("# Read requests leaving L2, by size (rocprofv3 --pmc TCC_EA0_RDREQ_sum TCC_BUBBLE_sum "
+              "TCC_EA0_RDREQ_32B_sum TCC_EA0_RDREQ_128B_sum; per dispatch).  FETCH_SIZE's gfx950 "
+              "definition is 128*BUBBLE + 64*(RDREQ - BUBBLE - RDREQ_32B) + 32*RDREQ_32B bytes; "
+              "the bytes the requests carry are 128*RDREQ_128B + 64*(RDREQ - RDREQ_128B - "
+              "RDREQ_32B) + 32*RDREQ_32B.  Where TCC_BUBBLE misses the 128-byte requests, "
+              "FETCH_SIZE prices each at 64 bytes: half the true bytes, the copy's factor of 2.")
+        targets = [("copy calibration (1 GiB read)", first_copies(req_dir))]
+        for key, phase in phases.items():
+            ks = [c for k, c in req.items() if key in k]
+            if ks:
+                targets.append((f"phase {phase}", ks[0]))
+        for name, c in targets:
+            rq, bb = get(c, "TCC_EA0_RDREQ"), get(c, "TCC_BUBBLE")
+            r32, r128 = get(c, "TCC_EA0_RDREQ_32B"), get(c, "TCC_EA0_RDREQ_128B")
+            if None in (rq, bb, r32, r128):
+                continue
+            by_size = 128 * r128 + 64 * (rq - r128 - r32) + 32 * r32
+            by_fetch = 128 * bb + 64 * (rq - bb - r32) + 32 * r32
+            print(f"{name}: read_bytes_by_size={int(by_size)} fetch_size_formula_bytes="
+                  f"{int(by_fetch)} ratio={by_size / max(by_fetch, 1):.4f} (requests {rq:.0f}: "
+                  f"128B {r128:.0f}, 32B {r32:.0f}, bubble {bb:.0f})")
+    if dram_dir:
+        dram = per_kernel_all(dram_dir)
+        print()
+        print("# Bytes of requests bound for DRAM (rocprofv3 --pmc TCC_EA0_RDREQ_DRAM_32B_sum "
+              "TCC_EA0_WRREQ_WRITE_DRAM_32B_sum: 32-byte units by definition, a 128-byte request "
+              "counting 4; no scale).  Hits in the memory-side cache in front of HBM are still "
+              "among them: an upper bound on HBM bytes.")
+        targets = [("copy calibration (1 GiB each way)", first_copies(dram_dir))]
+        for key, phase in phases.items():
+            ks = [c for k, c in dram.items() if key in k]
+            if ks:
+                targets.append((f"phase {phase}", ks[0]))
+        for name, c in targets:
+            rd, wr = get(c, "TCC_EA0_RDREQ_DRAM_32B"), get(c, "TCC_EA0_WRREQ_WRITE_DRAM_32B")
+            if rd is None or wr is None:
+                continue
+            extra = ""
+            if name.startswith("phase"):
+                extra = f" source_sha={source_sha(KERNEL_SOURCES[name.split()[1]])}"
+            print(f"{name}: dram_read_bytes={int(32 * rd)} dram_write_bytes={int(32 * wr)}{extra}")
     return 0
 
 
@@ -292,6 +373,111 @@ def _alg_bytes(R_c, R_d, L, H, Hq, d, b, n_max, w, moved_rows, dec_tokens, eb=2,
     flops = {"score": L * (2 * Hq * w * T * d * R_c + 2 * H * n_max * b * b * d * R_c)}
     flops["score_compact"] = flops["score"]
     return alg, flops
+
+
+def _ceilings_lib():
+    import ctypes
+    import torch  # noqa: F401  (the HIP runtime torch ships, loaded first)
+    from compressed_paged_kv_amd import build as B
+    lib = ctypes.CDLL(B.CEILINGS_LIB)
+    vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    lib.zpc_read.argtypes = [vp, sz, vp, vp]
+    lib.zpc_copy.argtypes = [vp, vp, sz, vp]
+    lib.zpc_read_tiles.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp]
+    return lib
+
+
+def measure_ceilings(cache, tab_t, seq_t, reps: int = 10) -> dict:
+    """What plain memory traffic reaches on this GPU, measured in the same
+    run: a 1 GiB linear read, a 1 GiB copy, and a read-only pass over the
+    exact (block, head) K and V tiles the decode of the step reads.  Each rep
+    is timed alone with HIP events, after a 1 GiB read of another buffer
+    (outside the events) that leaves nothing of the measured data in the
+    caches ("cold"); the tile pass is also timed back to back ("warm", as
+    the step's decode meets a cache the compression just touched)."""
+    import numpy as np
+    import torch
+    lib = _ceilings_lib()
+    dev = tab_t.device
+    st = torch.cuda.current_stream()
+    h = st.cuda_stream
+    gib = 1 << 30
+    flush = torch.ones(gib // 4, dtype=torch.float32, device=dev)
+    src = torch.ones(gib // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    sink = torch.zeros(16, dtype=torch.int32, device=dev)
+    kp, vp = cache.k_pools[0], cache.v_pools[0]
+    R, mb = (int(x) for x in tab_t.shape)
+    H, b = cache.num_kv_heads, cache.block_size
+    tile = b * cache.head_dim * kp.element_size()
+    seqs = seq_t.cpu().numpy()
+    tile_bytes_total = float(H * tile * 2 * int(np.sum((seqs + b - 1) // b)))
+
+    def run(name, fn):
+        assert fn() == 0, name
+    ops = {
+        "read": (float(gib), lambda: lib.zpc_read(src.data_ptr(), gib, sink.data_ptr(), h)),
+        "copy": (2.0 * gib, lambda: lib.zpc_copy(src.data_ptr(), dst.data_ptr(), gib, h)),
+        "decode_tiles": (tile_bytes_total, lambda: lib.zpc_read_tiles(
+            kp.data_ptr(), vp.data_ptr(), tab_t.data_ptr(), seq_t.data_ptr(), R, mb, H, b, tile,
+            cache.num_blocks, sink.data_ptr(), h)),
+    }
+    out = {"what": "plain read / copy / the decode's own (block, head) K+V tiles read-only, on "
+                   "this GPU in this run; cold = 1 GiB of other data read before each rep, warm = "
+                   "reps back to back"}
+    for name, (nbytes, fn) in ops.items():
+        for _ in range(2):
+            run(name, fn)
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(reps):
+            run("flush", lambda: lib.zpc_read(flush.data_ptr(), gib, sink.data_ptr(), h))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            run(name, fn)
+            e1.record(st)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e3)
+        us = float(np.median(times))
+        out[f"{name}_cold_us"] = round(us, 2)
+        out[f"{name}_GBs"] = round(nbytes / (us * 1e-6) / 1e9, 1)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(reps):
+        run("decode_tiles", ops["decode_tiles"][1])
+    e1.record(st)
+    e1.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    out["decode_tiles_warm_us"] = round(us, 2)
+    out["decode_tiles_warm_GBs"] = round(tile_bytes_total / (us * 1e-6) / 1e9, 1)
+    del flush, src, dst
+    return out
+
+
+def cold_decode_us(cache, q, tab_t, seq_t, scale, out, dws, reps: int = 10) -> float:
+    """Median duration of the decode kernels (HIP events on the launch
+    stream) when the memory-side cache holds nothing of the pools: 1 GiB of
+    other data is read before each decode, outside the events."""
+    import numpy as np
+    import torch
+    import compressed_paged_kv_amd as zp
+    lib = _ceilings_lib()
+    h = torch.cuda.current_stream().cuda_stream
+    gib = 1 << 30
+    flush = torch.ones(gib // 4, dtype=torch.float32, device=tab_t.device)
+    sink = torch.zeros(16, dtype=torch.int32, device=tab_t.device)
+    times = []
+    for _ in range(reps):
+        assert lib.zpc_read(flush.data_ptr(), gib, sink.data_ptr(), h) == 0
+        zp.profile_enable(True)
+        zp.profile_read()
+        zp.paged_decode(cache, 0, q, tab_t, seq_t, scale, out, dws)
+        torch.cuda.synchronize()
+        prof = zp.profile_read()
+        zp.profile_enable(False)
+        times.append(sum(prof[p][0] for p in ("decode", "combine")) * 1e3)
+    del flush
+    return float(np.median(times))
 
 
 def window_query_sets(first, n: int, seed: int, dev) -> list:
@@ -495,6 +681,14 @@ def run_single_stream(args, workload, cache, pool, tables, wq_sets, q_new, k_new
     assert tables.tolist() == tables0.tolist(), "in-place compression changed the tables"
     assert np.isfinite(out.cpu().numpy()).all()
 
+    # the decode once more with the memory-side cache emptied before each
+    # run, and what plain traffic of the same shapes reaches on this GPU
+    dec_cold_us, ceilings = None, None
+    if not args.headline_only:
+        log("timing the decode from a cold memory-side cache, and the box's bandwidth ceilings")
+        dec_cold_us = cold_decode_us(cache, q_new, tab_t, seq_t, scale, out, dws)
+        ceilings = measure_ceilings(cache, tab_t, seq_t)
+
     moved = 0.5 * (moved_pre + moved_post)
     nsplit = zp.paged_decode_workspace_bytes(cache, R, n_max) // (R * Hq * (d + 2) * 4)
     alg, flops = _alg_bytes(R, R, 1, H, Hq, d, b, n_max, w, moved, R * seq, nsplit=nsplit,
@@ -505,7 +699,12 @@ def run_single_stream(args, workload, cache, pool, tables, wq_sets, q_new, k_new
     traffic = read_counters(dom["phase"], workload)
     roofline = {"bound": "hbm", "kernel": dom["phase"], "achieved": dom["alg_GBs"],
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dom["hbm_frac"],
-                "traffic": traffic}
+                "traffic": traffic,
+                # requests bound for DRAM (memory-side cache hits included)
+                "traffic_dram": read_counters(dom["phase"], workload, "dram"),
+                # the same achieved rate against the best plain copy of this GPU
+                "frac_of_copy_ceiling": round(dom["alg_GBs"] / ceilings["copy_GBs"], 4)
+                if ceilings else None}
     per = {k["phase"]: k["avg_us"] for k in kernels}
     comp_us = sum(per.get(p, 0.0) for p in COMPRESS_PHASES)
     dec_us = sum(per.get(p, 0.0) for p in ("append", "decode", "combine"))
@@ -544,6 +743,14 @@ def run_single_stream(args, workload, cache, pool, tables, wq_sets, q_new, k_new
             sum(alg[p] for p in ("decode", "combine"))
             / (max(sum(per.get(p, 0.0) for p in ("decode", "combine")), 1e-9) * 1e-6)
             / 1e9 / HBM_PEAK_GBS, 4),
+        # the same decode with nothing of the pools left in the memory-side
+        # cache (the step's decode follows a compression that just read and
+        # wrote much of K)
+        "decode_attention_cold_us": round(dec_cold_us, 2) if dec_cold_us else None,
+        "decode_attention_cold_hbm_frac": round(
+            sum(alg[p] for p in ("decode", "combine")) / (dec_cold_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+            if dec_cold_us else None,
+        "ceilings": ceilings,
         "moved_rows_per_step": int(moved),
         "moved_rows_before_after": [moved_pre, moved_post],
         "moved_rows_first_last": [moved_before, moved_after],
@@ -1104,8 +1311,9 @@ def main() -> int:
                          "no CPU baseline): what the committed rocprofv3 summaries profile")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a 1 GiB device copy (counter calibration under rocprofv3)")
-    ap.add_argument("--summarize", nargs=3, metavar=("KT_DIR", "FETCH_DIR", "WRITE_DIR"),
-                    help="print the summary of rocprofv3 csv outputs and exit")
+    ap.add_argument("--summarize", nargs="+", metavar="DIR",
+                    help="KT_DIR FETCH_DIR WRITE_DIR [REQ_DIR [DRAM_DIR]]: print the summary "
+                         "of rocprofv3 csv outputs and exit")
     ap.add_argument("--summarize-counters", nargs="+", metavar="PMC_DIR",
                     help="print per-kernel averages of rocprofv3 --pmc runs (SQ/GRBM counters) "
                          "and exit")

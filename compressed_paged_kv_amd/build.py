@@ -3,7 +3,8 @@
 Every source under csrc/ is compiled to an object with hipcc (device code for
 gfx950 only, packed-FP32 instructions disabled) and linked into
 ``compressed_paged_kv_amd/libzp.so``.  Objects go to ``_build/`` next to
-this file.  ``build()`` always recompiles.
+this file.  The benchmark's bandwidth-ceiling kernels (ceilings/) become
+``libzp_ceilings.so`` beside it.  ``build()`` always recompiles.
 """
 from __future__ import annotations
 
@@ -19,6 +20,9 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libzp.so")
+# bandwidth ceilings of the box, for the benchmark only (not part of libzp.so)
+CEILINGS_SRC = os.path.join(HERE, "ceilings", "ceilings.hip")
+CEILINGS_LIB = os.path.join(HERE, "libzp_ceilings.so")
 ARCH = "gfx950"
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"--offload-arch={ARCH}",
@@ -70,6 +74,12 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}{res.stderr}")
     os.replace(tmp, LIB)
+    tmp = CEILINGS_LIB + ".tmp"
+    cmd = [_hipcc(), *COMMON, *DEVICE_ONLY, "-shared", "-o", tmp, CEILINGS_SRC]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {CEILINGS_SRC}:\n{res.stdout}{res.stderr}")
+    os.replace(tmp, CEILINGS_LIB)
     return LIB
 
 
