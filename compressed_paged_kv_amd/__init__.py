@@ -8,5 +8,6 @@ from ._binding import (  # noqa: F401
     BlockPool, KVCache, PrefixIndex, Scheduler, ZpError, append_kv, compress, compress_plan,
     compress_query, compress_workspace_bytes,
     last_error, lib, paged_decode, paged_decode_noalloc, paged_decode_workspace_bytes, profile_enable, profile_read,
-    redundancy_all,
+    redundancy_all, ZP_DEBUG_POISON, ZP_DEBUG_TRACE, ZP_DEBUG_VALIDATE, debug_flags,
+    set_debug_flags, trace_available,
 )

@@ -158,6 +158,9 @@ def lib() -> ctypes.CDLL:
                              _vp, _vp]),
         "zp_paged_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(_KVCache),
                                                               ctypes.c_int32, ctypes.c_int32]),
+        "zp_debug_flags": (ctypes.c_uint32, []),
+        "zp_set_debug_flags": (S, [ctypes.c_uint32]),
+        "zp_trace_available": (ctypes.c_int32, []),
         "zp_profile_enable": (S, [ctypes.c_int32]),
         "zp_profile_read": (S, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
         "zp_paged_decode": (S, [ctypes.POINTER(_KVCache), ctypes.c_int32, ctypes.c_int32, _vp, _vp,
@@ -697,6 +700,24 @@ class Scheduler:
         w, r, f = (np.zeros(1, dtype=np.int32) for _ in range(3))
         _check(lib().zp_sched_stats(self.handle, _i32(w), _i32(r), _i32(f)))
         return {"waiting": int(w[0]), "running": int(r[0]), "free_query_slots": int(f[0])}
+
+
+# --------------------------------------------------------------------------- debug switches
+
+ZP_DEBUG_TRACE, ZP_DEBUG_POISON, ZP_DEBUG_VALIDATE = 1, 2, 4
+
+
+def debug_flags() -> int:
+    """The debug switches in effect (ZP_DEBUG_* bits)."""
+    return int(lib().zp_debug_flags())
+
+
+def set_debug_flags(flags: int) -> None:
+    _check(lib().zp_set_debug_flags(int(flags)))
+
+
+def trace_available() -> bool:
+    return bool(lib().zp_trace_available())
 
 
 # --------------------------------------------------------------------------- timing

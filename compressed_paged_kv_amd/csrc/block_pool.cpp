@@ -314,6 +314,7 @@ zp_status zp_compress_plan(zp_block_pool* pool, int32_t n_max, int32_t num_reqs,
 zp_status zp_compress_plan_n(zp_block_pool* pool, int32_t n_src, int32_t n_max, int32_t num_reqs,
                              int32_t* block_tables, int32_t* src_out, int32_t* dst_out,
                              int32_t* freed_ids, int32_t* num_freed) {
+  zp::TraceRange trace("zp.compress_plan");
   zp::clear_error();
   if (num_reqs > 0 && (!src_out || !dst_out || !freed_ids || !num_freed)) {
     zp::set_error("output pointers must not be NULL");

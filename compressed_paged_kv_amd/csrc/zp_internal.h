@@ -145,6 +145,22 @@ hipError_t launch_upload(const void* host_src, void* dst, size_t bytes, hipStrea
 hipError_t launch_first_evict(const int32_t* evicted, int32_t* host_out, int R, int H, int L, int E,
                               hipStream_t s);
 
+// Debug switches (ZP_DEBUG_* of zp.h), read from the environment on first
+// use; roctx ranges on the host timeline while ZP_DEBUG_TRACE is set (a
+// no-op otherwise, or when no roctx library can be loaded).
+uint32_t debug_flags();
+bool trace_available();
+class TraceRange {
+ public:
+  explicit TraceRange(const char* name);
+  ~TraceRange();
+  TraceRange(const TraceRange&) = delete;
+  TraceRange& operator=(const TraceRange&) = delete;
+
+ private:
+  bool active_ = false;
+};
+
 // Kernel timing (no-ops unless enabled by zp_profile_enable): bracket one
 // phase on stream s.
 void prof_begin(int phase, hipStream_t s);

@@ -613,6 +613,35 @@ zp_status zp_prefix_evict(zp_prefix_index* index, int32_t max_entries, int32_t* 
 int32_t zp_prefix_size(const zp_prefix_index* index);  /* listed entries */
 
 /* ------------------------------------------------------------------------
+ * Debug switches.  The environment sets them when the library first needs
+ * them (ZP_TRACE, ZP_DEBUG_POISON, ZP_VALIDATE: any value but "" and "0");
+ * zp_set_debug_flags() replaces them at run time (not thread-safe against
+ * calls in flight on other threads).
+ *   ZP_DEBUG_TRACE     roctx ranges around the host side of every call (the
+ *                      plan, each kernel launch), shown by rocprofv3's marker
+ *                      trace; the roctx library is loaded on first use and
+ *                      tracing stays off without one (zp_trace_available).
+ *   ZP_DEBUG_POISON    after every compression, on its stream: NaN into the
+ *                      blocks the call frees and into every slot of each
+ *                      request's reserved block (all past the new length),
+ *                      K and V of every layer, so that any later read of
+ *                      stale rows turns outputs NaN.  Slow; checking only.
+ *   ZP_DEBUG_VALIDATE  zp_compress_ex with device_tables reads that copy back
+ *                      (one host synchronisation with the call's stream) and
+ *                      returns ZP_ERR_INVALID, changing nothing, when it
+ *                      differs from block_tables.
+ * ---------------------------------------------------------------------- */
+#define ZP_DEBUG_TRACE 1u
+#define ZP_DEBUG_POISON 2u
+#define ZP_DEBUG_VALIDATE 4u
+
+uint32_t zp_debug_flags(void);
+/* Rejects unknown bits (ZP_ERR_INVALID). */
+zp_status zp_set_debug_flags(uint32_t flags);
+/* 1 if a roctx library could be loaded (tracing can be shown), else 0. */
+int32_t zp_trace_available(void);
+
+/* ------------------------------------------------------------------------
  * Kernel timing.  While enabled, every kernel launch of the calls above is
  * bracketed by HIP events recorded on the caller's stream (a few events per
  * call, no synchronisation).  zp_profile_read() waits for the recorded

@@ -597,3 +597,81 @@ def test_device_tables_equal_the_uploaded_tables(name, keep_prefix):
                               np.ascontiguousarray(b).view(np.uint8))
     np.testing.assert_array_equal(up.out.view(np.uint32), dv.out.view(np.uint32))
     check_case(case, dv, keep_prefix=keep_prefix)
+
+
+def test_debug_poison_changes_nothing_a_correct_reader_sees():
+    """With ZP_DEBUG_POISON the compression leaves NaN in the blocks it frees
+    and in every slot of the reserved blocks; everything else -- tables,
+    compacted targets, the appended token and the decode output -- is bit
+    for bit what the same call gives without it."""
+    import compressed_paged_kv_amd as zp
+    case = CASES["shared_prefix_2layers"]()      # 4 requests re-target a shared 3-block prefix
+    say("[gpu parity] debug poison on the shared-prefix case")
+    before = zp.debug_flags()
+    plain = run_case(case, decode=False)
+    try:
+        zp.set_debug_flags(zp.ZP_DEBUG_POISON)
+        poisoned = run_case(case, decode=False)
+    finally:
+        zp.set_debug_flags(before)
+    np.testing.assert_array_equal(plain.tables, poisoned.tables)
+    freed = np.asarray(poisoned.freed)
+    assert freed.size == 3
+    reserved = poisoned.tables[:, case.n_max - 1]
+    bad = set(freed.tolist()) | set(reserved.tolist())
+    for a, b in zip(plain.k_pool + plain.v_pool, poisoned.k_pool + poisoned.v_pool):
+        fa = a.astype(np.float32) if a.dtype == np.float32 else synth.bf16_bits_to_f32(a)
+        fb = b.astype(np.float32) if b.dtype == np.float32 else synth.bf16_bits_to_f32(b)
+        for blk in range(a.shape[0]):
+            if blk in bad:
+                assert np.isnan(fb[blk]).all(), blk
+            else:
+                assert np.array_equal(a[blk].view(np.uint8), b[blk].view(np.uint8)), blk
+    # the decode after the append reads only slots up to the new length
+    zp.set_debug_flags(zp.ZP_DEBUG_POISON)
+    try:
+        dec = run_case(case)
+    finally:
+        zp.set_debug_flags(before)
+    ref = run_case(case)
+    np.testing.assert_array_equal(dec.out.view(np.uint32), ref.out.view(np.uint32))
+
+
+def test_validate_rejects_a_device_table_that_differs():
+    """ZP_DEBUG_VALIDATE: zp_compress_ex reads the device copy back and
+    rejects a call whose copy differs from the host tables, changing nothing
+    (tables, reference counts, pools)."""
+    import compressed_paged_kv_amd as zp
+    from synth.device import to_numpy, to_tensor
+    case = CASES["bf16_d128_b16_ragged"]()
+    g = case.geom
+    say("[gpu parity] validate device tables")
+    kp = [to_tensor(x, "cuda") for x in case.k_pool]
+    vp = [to_tensor(x, "cuda") for x in case.v_pool]
+    wq = [to_tensor(x, "cuda") for x in case.window_q]
+    cache = zp.KVCache(kp, vp, g.num_q_heads)
+    pool = zp.BlockPool.from_refcounts(case.refcounts)
+    ws = torch.empty(zp.compress_workspace_bytes(cache, case.num_reqs, case.n_max, case.window),
+                     dtype=torch.uint8, device="cuda")
+    wrong = case.tables.copy()
+    wrong[1, 5], wrong[1, 6] = wrong[1, 6], wrong[1, 5]
+    before = zp.debug_flags()
+    zp.set_debug_flags(zp.ZP_DEBUG_VALIDATE)
+    try:
+        tables = case.tables.copy()
+        with pytest.raises(zp.ZpError) as e:
+            zp.compress(cache, pool, case.n_max, case.window, tables, wq, ws,
+                        device_tables=torch.from_numpy(wrong).to("cuda"))
+        assert e.value.status == zp.ZP_ERR_INVALID and "device_tables differ" in str(e.value)
+        np.testing.assert_array_equal(tables, case.tables)
+        np.testing.assert_array_equal(pool.refcounts(), case.refcounts)
+        torch.cuda.synchronize()
+        for l in range(g.num_layers):
+            assert np.array_equal(to_numpy(kp[l]).view(np.uint8), case.k_pool[l].view(np.uint8))
+        # the matching copy goes through
+        zp.compress(cache, pool, case.n_max, case.window, tables, wq, ws,
+                    device_tables=torch.from_numpy(np.ascontiguousarray(case.tables)).to("cuda"))
+        torch.cuda.synchronize()
+    finally:
+        zp.set_debug_flags(before)
+    pool.sync()

@@ -4,6 +4,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import numpy as np
 import pytest
@@ -371,3 +372,33 @@ def test_size_limits_are_checked_before_any_work():
     for c, n_src, n_max, w, msg in bad:
         assert lib.zp_compress_workspace_bytes_n(c.ref, 1, n_src, n_max, w) == 0
         assert msg in zp.last_error(), zp.last_error()
+
+
+# ------------------------------------------------------------------ debug switches
+
+def test_debug_flags_round_trip_and_reject_unknown_bits():
+    before = zp.debug_flags()
+    try:
+        zp.set_debug_flags(zp.ZP_DEBUG_TRACE | zp.ZP_DEBUG_VALIDATE)
+        assert zp.debug_flags() == zp.ZP_DEBUG_TRACE | zp.ZP_DEBUG_VALIDATE
+        with pytest.raises(zp.ZpError):
+            zp.set_debug_flags(8)
+        assert zp.debug_flags() == zp.ZP_DEBUG_TRACE | zp.ZP_DEBUG_VALIDATE
+        # tracing on: the planner runs inside a roctx range when a roctx
+        # library is there, and without one nothing changes
+        pool = zp.BlockPool(16, manual_fence=True)
+        tab = pool.alloc(8).reshape(2, 4).astype(np.int32).copy()
+        src, dst, freed = zp.compress_plan(pool, 4, tab)
+        assert src.shape == (2, 4) and freed.size == 0
+        assert isinstance(zp.trace_available(), bool)
+    finally:
+        zp.set_debug_flags(before)
+
+
+def test_debug_flags_come_from_the_environment():
+    code = ("import compressed_paged_kv_amd as zp; "
+            "print(zp.debug_flags(), flush=True)")
+    env = dict(os.environ, ZP_TRACE="1", ZP_DEBUG_POISON="0", ZP_VALIDATE="yes")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True,
+                         text=True, check=True).stdout.strip().splitlines()[-1]
+    assert int(out) == zp.ZP_DEBUG_TRACE | zp.ZP_DEBUG_VALIDATE

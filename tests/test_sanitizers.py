@@ -49,10 +49,10 @@ def instrumented(tmp_path_factory):
     stub.write_text(STUBS)
     host_lib = str(d / "libzp_host_san.so")
     srcs = [os.path.join(CSRC, f) for f in ("api.cpp", "block_pool.cpp", "sched.cpp",
-                                             "prefix_index.cpp", "profile.cpp")] + [str(stub)]
+                                             "prefix_index.cpp", "profile.cpp", "debug.cpp")] + [str(stub)]
     subprocess.run(["g++", "-std=c++17", "-shared", *SAN, "-D__HIP_PLATFORM_AMD__",
                     "-I/opt/rocm/include", f"-I{ROOT}/include", f"-I{CSRC}", "-o", host_lib, *srcs,
-                    "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib"], check=True)
+                    "-L/opt/rocm/lib", "-lamdhip64", "-ldl", "-Wl,-rpath,/opt/rocm/lib"], check=True)
     oracle_lib = str(d / "libzp_oracle_san.so")
     subprocess.run(["gcc", "-std=c11", "-shared", *SAN, "-o", oracle_lib,
                     os.path.join(ROOT, "oracle", "zp_oracle.c"), "-lm"], check=True)
