@@ -80,6 +80,16 @@ class _Debug(ctypes.Structure):
 ZP_COMPRESS_KEEP_PREFIX = 1
 
 
+class _DecodeArgs(ctypes.Structure):
+    _fields_ = [("layer", ctypes.c_int32), ("num_reqs", ctypes.c_int32), ("q", ctypes.c_void_p),
+                ("block_tables", ctypes.c_void_p), ("max_blocks", ctypes.c_int32),
+                ("seq_lens", ctypes.c_void_p), ("scale", ctypes.c_float), ("out", ctypes.c_void_p),
+                ("out_dtype", ctypes.c_int32), ("lse_out", ctypes.c_void_p),
+                ("q_out", ctypes.c_void_p), ("rows", ctypes.c_void_p), ("capacity", ctypes.c_int32),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("stream", ctypes.c_void_p)]
+
+
 class _CompressArgs(ctypes.Structure):
     _fields_ = [("n_src", ctypes.c_int32), ("n_max", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("num_reqs", ctypes.c_int32), ("block_tables", ctypes.POINTER(ctypes.c_int32)),
@@ -169,6 +179,7 @@ def lib() -> ctypes.CDLL:
         "zp_paged_decode_lse": (S, [ctypes.POINTER(_KVCache), ctypes.c_int32, ctypes.c_int32, _vp,
                                     _vp, ctypes.c_int32, _vp, ctypes.c_float, _vp, _vp, _vp, _vp,
                                     ctypes.c_int32, _vp, ctypes.c_size_t, _vp]),
+        "zp_paged_decode_ex": (S, [ctypes.POINTER(_KVCache), ctypes.POINTER(_DecodeArgs)]),
         "zp_paged_decode_noalloc": (S, [ctypes.POINTER(_KVCache), ctypes.c_int32, ctypes.c_int32,
                                         _vp, _vp, ctypes.c_int32, _vp, ctypes.c_float, _vp, _vp,
                                         _vp, _vp, ctypes.c_int32, _vp]),
@@ -522,14 +533,16 @@ def paged_decode(cache: KVCache, layer: int, q, tables, seq_lens, scale: float, 
                  stream=None, lse_out=None, lse_rows=None, q_out=None) -> None:
     """zp_paged_decode, or zp_paged_decode_lse when ``lse_out`` (float
     [rows][Hq]) or ``q_out`` ([rows][Hq][d], cache dtype) is given;
-    ``lse_rows`` (int32 [R]) maps requests to rows."""
+    ``lse_rows`` (int32 [R]) maps requests to rows.  A bfloat16 ``out`` goes
+    through zp_paged_decode_ex with out_dtype ZP_BF16."""
     import torch
     dev, Hq, d = cache.device, cache.num_q_heads, cache.head_dim
     _want(tables, "tables", dev, torch.int32, (None, None))
     R, max_blocks = (int(x) for x in tables.shape)
     _want(q, "q", dev, cache.torch_dtype, (R, Hq, d))
     _want(seq_lens, "seq_lens", dev, torch.int32, (R,))
-    _want(out, "out", dev, torch.float32, (R, Hq, d))
+    out_bf16 = hasattr(out, "dtype") and out.dtype == torch.bfloat16
+    _want(out, "out", dev, torch.bfloat16 if out_bf16 else torch.float32, (R, Hq, d))
     if workspace is not None:
         _want(workspace, "workspace", dev, None, None)
     if lse_out is not None:
@@ -542,6 +555,14 @@ def paged_decode(cache: KVCache, layer: int, q, tables, seq_lens, scale: float, 
         _want(lse_rows, "lse_rows", dev, torch.int32, (R,))
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if out_bf16:
+        rows_src = lse_out if lse_out is not None else q_out
+        a = _DecodeArgs(layer, R, q.data_ptr(), tables.data_ptr(), max_blocks, seq_lens.data_ptr(),
+                        float(scale), out.data_ptr(), ZP_BF16, _dptr(lse_out), _dptr(q_out),
+                        _dptr(lse_rows), int(rows_src.shape[0]) if rows_src is not None else 0,
+                        ws_ptr, ws_bytes, _stream_handle(stream))
+        _check(lib().zp_paged_decode_ex(cache.ref, ctypes.byref(a)))
+        return
     if lse_out is None and q_out is None:
         _check(lib().zp_paged_decode(cache.ref, layer, R, q.data_ptr(), tables.data_ptr(),
                                      max_blocks, seq_lens.data_ptr(), float(scale), out.data_ptr(),

@@ -118,6 +118,18 @@ __device__ inline float group_sum(float x) {
 // to zero, which only drops probabilities far below the output tolerance).
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// One output element, as float32 or (out_bf16) bfloat16 rounded to nearest
+// even; NaN stays NaN.
+__device__ inline void store_out(const DecodeParams& p, size_t idx, float x) {
+  if (p.out_bf16) {
+    const uint32_t u = __float_as_uint(x);
+    const uint32_t r = (x != x) ? 0x7FC0u : (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    static_cast<uint16_t*>(p.out)[idx] = (uint16_t)r;
+  } else {
+    static_cast<float*>(p.out)[idx] = x;
+  }
+}
+
 // Optional output: the log-sum-exp of the scaled logits of query head hq,
 // ln sum_j exp(scale * q.k_j), from the merged (max M, sum L) in log2 units.
 __device__ inline void store_lse(const DecodeParams& p, int r, int hq, float M, float L) {
@@ -328,7 +340,7 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode(DecodeParams p) {
     }
     const int hq = hq0 + g;
     if (p.nsplit == 1) {
-      p.out[((size_t)r * p.Hq + hq) * D + d] = L > 0.f ? o / L : 0.f;
+      store_out(p, ((size_t)r * p.Hq + hq) * D + d, L > 0.f ? o / L : 0.f);
       if (d == 0) store_lse(p, r, hq, M, L);
     } else {
       float* part = p.partial + (((size_t)r * p.Hq + hq) * p.nsplit + split) * (D + 2);
@@ -355,7 +367,7 @@ __global__ __launch_bounds__(D) void k_decode_combine(DecodeParams p) {
     L = fmaf(ps[1], c, L);
     o = fmaf(ps[2 + d], c, o);
   }
-  p.out[(size_t)rh * D + d] = L > 0.f ? o / L : 0.f;
+  store_out(p, (size_t)rh * D + d, L > 0.f ? o / L : 0.f);
   if (d == 0) store_lse(p, rh / p.Hq, rh % p.Hq, M, L);
 }
 

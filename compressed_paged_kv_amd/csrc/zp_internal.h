@@ -94,7 +94,8 @@ struct DecodeParams {
   const void* q;            // [R][Hq][d]
   const int32_t* tables;    // [R][max_blocks]
   const int32_t* seq_lens;  // [R]
-  float* out;               // [R][Hq][d]
+  void* out;                // [R][Hq][d], float32, or bfloat16 when out_bf16
+  int32_t out_bf16;
   float* partial;           // [R][Hq][nsplit][d + 2]
   float* lse;               // optional [lse_cap][Hq]: natural-log normaliser per query head
   void* q_rec;              // optional [lse_cap][Hq][d]: copy of the query (cache dtype)

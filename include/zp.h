@@ -418,6 +418,36 @@ zp_status zp_paged_decode_lse(const zp_kv_cache* cache, int32_t layer, int32_t n
                               size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * zp_paged_decode_ex: zp_paged_decode_lse with its arguments in a struct,
+ * and the output element type to choose.
+ *   out_dtype   ZP_F32 (out: float [R][Hq][d], exactly zp_paged_decode_lse)
+ *               or ZP_BF16 (out: bfloat16 [R][Hq][d], 2-byte aligned: the
+ *               same float32 result rounded to nearest even).
+ * Every other field, result and error as zp_paged_decode_lse (lse_out,
+ * q_out and rows may be NULL); an unknown out_dtype is ZP_ERR_INVALID.
+ * ---------------------------------------------------------------------- */
+typedef struct zp_decode_args {
+  int32_t layer;
+  int32_t num_reqs;
+  const void* q;
+  const int32_t* block_tables;
+  int32_t max_blocks;
+  const int32_t* seq_lens;
+  float scale;
+  void* out;
+  int32_t out_dtype; /* zp_dtype */
+  float* lse_out;
+  void* q_out;
+  const int32_t* rows;
+  int32_t capacity;
+  void* workspace;
+  size_t workspace_bytes;
+  void* stream;
+} zp_decode_args;
+
+zp_status zp_paged_decode_ex(const zp_kv_cache* cache, const zp_decode_args* args);
+
+/* ------------------------------------------------------------------------
  * zp_paged_decode_noalloc: zp_paged_decode_lse for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving
  * loops, harnesses that forbid allocation).  It takes no workspace: the

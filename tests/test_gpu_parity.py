@@ -675,3 +675,39 @@ def test_validate_rejects_a_device_table_that_differs():
     finally:
         zp.set_debug_flags(before)
     pool.sync()
+
+
+@pytest.mark.parametrize("dtype,d,b,G,R,mb", [("bf16", 128, 16, 4, 3, 40),    # split lists
+                                              ("bf16", 128, 16, 4, 300, 9),   # no split
+                                              ("f32", 64, 32, 8, 5, 12)])
+def test_decode_bfloat16_output_is_the_rounded_float32_output(dtype, d, b, G, R, mb):
+    """zp_paged_decode_ex with out_dtype ZP_BF16: every element is the
+    float32 result of the same call rounded to nearest even (bit for bit),
+    log-sum-exp unchanged."""
+    import compressed_paged_kv_amd as zp
+    from synth.device import to_tensor
+    H = 2
+    c = synth.make_case("dec_bf16", 6100 + R, num_reqs=R, num_layers=1, num_kv_heads=H,
+                        num_q_heads=H * G, head_dim=d, block_size=b, n_max=mb, window=1,
+                        num_blocks=R * mb + 3, dtype=dtype)
+    say(f"[gpu parity] bf16 decode output {dtype} d={d} b={b} G={G} R={R} max_blocks={mb}")
+    rng = np.random.default_rng(61)
+    seqs = rng.integers(0, mb * b + 1, size=R).astype(np.int32)
+    dev = "cuda"
+    kp, vp = to_tensor(c.k_pool[0], dev), to_tensor(c.v_pool[0], dev)
+    cache = zp.KVCache([kp], [vp], H * G)
+    q, tab = to_tensor(c.q_new[0], dev), torch.from_numpy(c.tables).to(dev)
+    seq_t = torch.from_numpy(seqs).to(dev)
+    ws = torch.empty(max(zp.paged_decode_workspace_bytes(cache, R, mb), 16), dtype=torch.uint8,
+                     device=dev)
+    o32 = torch.full((R, H * G, d), float("nan"), device=dev)
+    o16 = torch.full((R, H * G, d), float("nan"), dtype=torch.bfloat16, device=dev)
+    l32 = torch.full((R, H * G), float("nan"), device=dev)
+    l16 = torch.full((R, H * G), float("nan"), device=dev)
+    zp.paged_decode(cache, 0, q, tab, seq_t, 1.0 / np.sqrt(d), o32, ws, lse_out=l32)
+    zp.paged_decode(cache, 0, q, tab, seq_t, 1.0 / np.sqrt(d), o16, ws, lse_out=l16)
+    torch.cuda.synchronize()
+    want = synth.f32_to_bf16_bits(o32.cpu().numpy())
+    got = o16.cpu().view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(got, want)
+    np.testing.assert_array_equal(l16.cpu().numpy().view(np.uint32), l32.cpu().numpy().view(np.uint32))
