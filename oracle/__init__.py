@@ -42,7 +42,7 @@ def _load():
     lib.zpo_plan.restype = ctypes.c_int
     lib.zpo_plan.argtypes = [ctypes.c_int32, _i32p, ctypes.c_int32, ctypes.c_int32,
                              ctypes.c_int32, _i32p, _i32p, _i32p, _i32p, _i32p, _i32p,
-                             ctypes.c_int32]
+                             ctypes.c_int32, _i32p]
     lib.zpo_scores.restype = None
     lib.zpo_scores.argtypes = [ctypes.c_int32] * 8 + [ctypes.c_void_p, ctypes.c_void_p, _i32p,
                                                       _f64p, _f64p, _f64p]
@@ -99,11 +99,13 @@ class Plan:
 
 
 def plan(refcounts: np.ndarray, tables: np.ndarray, n_max: int,
-         first_evict: Optional[np.ndarray] = None, block_size: int = 0) -> Plan:
+         first_evict: Optional[np.ndarray] = None, block_size: int = 0,
+         n_blocks: Optional[np.ndarray] = None) -> Plan:
     """Target-block plan of one compression call (inputs are not modified).
     ``tables`` is [R][n_src] with n_src >= n_max.  ``first_evict`` ([R], the
     lowest evicted slot of each request over its layers and heads) keeps the
-    shared blocks wholly below it shared."""
+    shared blocks wholly below it shared.  ``n_blocks`` ([R]): request r holds
+    only the first n_blocks[r] entries of its row, the rest being -1."""
     lib = _load()
     rc = np.ascontiguousarray(refcounts, dtype=np.int32).copy()
     tab = np.ascontiguousarray(tables, dtype=np.int32).copy()
@@ -112,11 +114,15 @@ def plan(refcounts: np.ndarray, tables: np.ndarray, n_max: int,
     dst = np.zeros((R, max(n_max - 1, 1)), dtype=np.int32)
     freed = np.zeros(max(R * n_src, 1), dtype=np.int32)
     nfreed = np.zeros(1, dtype=np.int32)
-    fe = None
+    fe = nb = None
     if first_evict is not None:
-        fe = _i32(np.ascontiguousarray(first_evict, dtype=np.int32))
+        fe_a = np.ascontiguousarray(first_evict, dtype=np.int32)
+        fe = _i32(fe_a)
+    if n_blocks is not None:
+        nb_a = np.ascontiguousarray(n_blocks, dtype=np.int32)
+        nb = _i32(nb_a)
     st = lib.zpo_plan(int(rc.shape[0]), _i32(rc), R, n_src, n_max, _i32(tab), _i32(src),
-                      _i32(dst), _i32(freed), _i32(nfreed), fe, int(block_size))
+                      _i32(dst), _i32(freed), _i32(nfreed), fe, int(block_size), nb)
     return Plan(int(st), tab, rc, src, dst, freed[: int(nfreed[0])].copy())
 
 
@@ -256,18 +262,79 @@ class CompressResult:
     v_pool: List[np.ndarray]
 
 
-def first_evicted(kept: List[np.ndarray], T: int, window: int) -> np.ndarray:
+def first_evicted(kept: List[np.ndarray], T, window: int) -> np.ndarray:
     """Lowest evicted slot of each request over all layers and heads, from
-    the kept lists ([R][H][K_keep] per layer)."""
-    C = T - window
+    the kept lists ([R][H][K_keep] per layer); ``T`` is the cached slots of
+    every request, or an array of them per request."""
+    R = kept[0].shape[0]
+    Ts = np.broadcast_to(np.asarray(T, dtype=np.int64), (R,))
+    Tm = int(Ts.max())
+    C = Ts - window
     out = None
     for k in kept:
-        mask = np.ones(k.shape[:2] + (T,), dtype=bool)
+        mask = np.ones(k.shape[:2] + (Tm,), dtype=bool)
         np.put_along_axis(mask, k.astype(np.int64), False, axis=-1)
-        mask[..., C:] = False
-        first = np.where(mask.any(-1), mask.argmax(-1), C).min(axis=1)
+        mask &= np.arange(Tm)[None, None, :] < C[:, None, None]
+        first = np.where(mask.any(-1), mask.argmax(-1), C[:, None]).min(axis=1)
         out = first if out is None else np.minimum(out, first)
     return out.astype(np.int32)
+
+
+def _compress_ragged(case, layers, with_pools, keep_prefix) -> "CompressResult":
+    """compress() for requests holding different numbers of blocks
+    (``case.num_blocks``): one plan for the whole call, then every request on
+    its own T = num_blocks[r]*b (scores and selection are per (request,
+    head) anyway); the compaction writes only each request's own targets, so
+    the per-request results merge without overlap.  A, R and s come back
+    padded to the longest T with NaN."""
+    g = case.geom
+    n_max, w, b = case.n_max, case.window, g.block_size
+    k_sel = (n_max - 1) * b - w
+    nbk = np.asarray(case.num_blocks, dtype=np.int32)
+    R, Tm = case.num_reqs, int(nbk.max()) * b
+    layers = list(range(g.num_layers)) if layers is None else layers
+    kw = dict(num_kv_heads=g.num_kv_heads, num_q_heads=g.num_q_heads, head_dim=g.head_dim,
+              block_size=b, window=w)
+
+    def unit_scores(layer, src):
+        A = np.full((R, g.num_kv_heads, Tm), np.nan)
+        Rr, s = A.copy(), A.copy()
+        kept = np.zeros((R, g.num_kv_heads, (n_max - 1) * b), dtype=np.int32)
+        for r in range(R):
+            n = int(nbk[r])
+            a, rr, ss = scores(case.k_pool[layer], case.window_q[layer][r:r + 1],
+                               np.ascontiguousarray(src[r:r + 1, :n]), **kw)
+            A[r, :, :n * b], Rr[r, :, :n * b], s[r, :, :n * b] = a[0], rr[0], ss[0]
+            kept[r] = select(ss[0], w, k_sel)
+        return A, Rr, s, kept
+
+    sel = {}
+    if keep_prefix:
+        for layer in range(g.num_layers):
+            sel[layer] = unit_scores(layer, case.tables)
+        fe = first_evicted([sel[l][3] for l in range(g.num_layers)], nbk * b, w)
+        p = plan(case.refcounts, case.tables, n_max, fe, b, n_blocks=nbk)
+    else:
+        p = plan(case.refcounts, case.tables, n_max, n_blocks=nbk)
+    if p.status != OK:
+        raise RuntimeError(f"oracle plan failed with status {p.status}")
+    out = CompressResult(p, [], [], [], [], [], [])
+    for layer in layers:
+        A, Rr, s, kept = sel[layer] if layer in sel else unit_scores(layer, p.src)
+        out.A.append(A)
+        out.R.append(Rr)
+        out.s.append(s)
+        out.kept.append(kept)
+        if with_pools:
+            for pools, res in ((case.k_pool, out.k_pool), (case.v_pool, out.v_pool)):
+                merged = pools[layer].copy()
+                for r in range(R):
+                    n = int(nbk[r])
+                    one = compact(pools[layer], np.ascontiguousarray(p.src[r:r + 1, :n]),
+                                  p.dst[r:r + 1], kept[r:r + 1], n_max=n_max)
+                    merged[p.dst[r]] = one[p.dst[r]]
+                res.append(merged)
+    return out
 
 
 def compress(case, layers: Optional[List[int]] = None, with_pools: bool = True,
@@ -276,6 +343,8 @@ def compress(case, layers: Optional[List[int]] = None, with_pools: bool = True,
     (``with_pools=False`` skips the out-of-place compaction of the pools).
     ``keep_prefix``: the plan is made after the selection of every layer, and
     shared blocks below each request's first eviction stay shared."""
+    if getattr(case, "num_blocks", None) is not None:
+        return _compress_ragged(case, layers, with_pools, keep_prefix)
     g = case.geom
     n_max, w, b = case.n_max, case.window, g.block_size
     k_keep = (n_max - 1) * b

@@ -101,18 +101,33 @@ int zpo_num_threads(void) {
  * layers and heads.  A shared block n < n_max-1 whose slots all lie below it
  * is left as it is in every layer and head by the compaction, so it stays in
  * the table, still shared (no new target, counts unchanged).
+ *
+ * n_blocks (NULL, or [R]): requests past the cap by different amounts in one
+ * call; request r holds the first n_blocks[r] entries of its row (between
+ * n_max and n_src) and the rest of the row is -1.  Everything above then
+ * reads n_blocks[r] for n_src, request by request, in the same order.
  * --------------------------------------------------------------------- */
 int zpo_plan(int32_t pool_size, int32_t* rc, int32_t R, int32_t n_src, int32_t n_max,
              int32_t* tables, int32_t* src_out, int32_t* dst_out, int32_t* freed_out,
-             int32_t* n_freed_out, const int32_t* first_evict, int32_t b) {
+             int32_t* n_freed_out, const int32_t* first_evict, int32_t b,
+             const int32_t* n_blocks) {
   if (pool_size <= 0 || R < 0 || n_max < 2 || n_src < n_max) return ZPO_INVALID;
+  /* n_blocks (optional): request r holds the first n_blocks[r] entries of
+   * its row, n_max <= n_blocks[r] <= n_src; the rest of the row is -1 */
+  if (n_blocks)
+    for (int32_t r = 0; r < R; r++) {
+      if (n_blocks[r] < n_max || n_blocks[r] > n_src) return ZPO_INVALID;
+      for (int32_t n = n_blocks[r]; n < n_src; n++)
+        if (tables[(size_t)r * n_src + n] != -1) return ZPO_INVALID;
+    }
   int32_t* seen = (int32_t*)calloc((size_t)pool_size, sizeof(int32_t));
   int32_t* rc0 = (int32_t*)malloc((size_t)pool_size * sizeof(int32_t));
   if (!seen || !rc0) { free(seen); free(rc0); return ZPO_INVALID; }
   memcpy(rc0, rc, (size_t)pool_size * sizeof(int32_t));
   int bad = 0;
   for (int32_t r = 0; r < R && !bad; r++) {
-    for (int32_t n = 0; n < n_src && !bad; n++) {
+    const int32_t nr = n_blocks ? n_blocks[r] : n_src;
+    for (int32_t n = 0; n < nr && !bad; n++) {
       int32_t id = tables[(size_t)r * n_src + n];
       if (id < 0 || id >= pool_size || rc0[id] < 1) { bad = 1; break; }
       for (int32_t m = 0; m < n; m++)
@@ -136,8 +151,9 @@ int zpo_plan(int32_t pool_size, int32_t* rc, int32_t R, int32_t n_src, int32_t n
   int32_t nfreed = 0;
   for (int32_t r = 0; r < R; r++) {
     int32_t* row = tables + (size_t)r * n_src;
+    const int32_t nr = n_blocks ? n_blocks[r] : n_src;
     for (int32_t n = 0; n < n_src; n++) src_out[(size_t)r * n_src + n] = row[n];
-    for (int32_t n = 0; n < n_src; n++) {
+    for (int32_t n = 0; n < nr; n++) {
       int32_t s = row[n];
       if (n >= n_max) { /* surplus: released */
         rc[s] -= 1;

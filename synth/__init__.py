@@ -91,6 +91,7 @@ class CompressCase:
     v_new: List[np.ndarray]     # [R][H][d]
     notes: str = ""
     extra: dict = field(default_factory=dict)
+    num_blocks: Optional[np.ndarray] = None  # int32 [R] when requests hold different counts
 
     @property
     def num_reqs(self) -> int:
@@ -118,7 +119,7 @@ def make_case(name: str, seed: int, *, num_reqs: int, num_layers: int, num_kv_he
               num_blocks: int, dtype: str, key_scale_range: Optional[tuple] = None,
               shared_prefix_blocks: int = 0, key_kind: str = "iid", ar_rho: float = 0.9,
               planted_frac: float = 0.0, planted_scale: float = 8.0,
-              n_src: Optional[int] = None) -> CompressCase:
+              n_src=None) -> CompressCase:
     """Build a seeded case.
 
     key_kind "iid": K ~ N(0,1) (optionally times a per (layer, head) scale
@@ -129,24 +130,32 @@ def make_case(name: str, seed: int, *, num_reqs: int, num_layers: int, num_kv_he
     ``shared_prefix_blocks`` > 0: every request's first blocks are the same
     physical ids with the same contents (refcount = num_reqs).
     ``n_src`` (default n_max): blocks each request holds, all full; more than
-    n_max is a cache past the cap (e.g. a long prompt).
+    n_max is a cache past the cap (e.g. a long prompt).  A list gives each
+    request its own count: the table rows are then as long as the largest,
+    each padded with -1, and ``num_blocks`` holds the counts.
     """
     geom = Geometry(num_layers, num_kv_heads, num_q_heads, head_dim, block_size, num_blocks, dtype)
     rng = np.random.default_rng(seed)
     R, H, Hq, d, b = num_reqs, num_kv_heads, num_q_heads, head_dim, block_size
     P = shared_prefix_blocks
-    nb_req = n_max if n_src is None else int(n_src)
-    if nb_req < n_max:
-        raise ValueError("n_src must be >= n_max")
-    need = P + R * (nb_req - P)
+    ragged = isinstance(n_src, (list, tuple, np.ndarray))
+    counts = (np.asarray(n_src, dtype=np.int32) if ragged
+              else np.full(R, n_max if n_src is None else int(n_src), dtype=np.int32))
+    if len(counts) != R or counts.min() < n_max:
+        raise ValueError("n_src must be >= n_max for every request")
+    nb_req = int(counts.max())
+    need = P + int(np.sum(counts - P))
     if need > num_blocks:
         raise ValueError(f"pool of {num_blocks} blocks cannot hold {need}")
     perm = rng.permutation(num_blocks).astype(np.int32)
-    tables = np.empty((R, nb_req), dtype=np.int32)
+    tables = np.full((R, nb_req), -1, dtype=np.int32)
     tables[:, :P] = perm[:P]
-    tables[:, P:] = perm[P:need].reshape(R, nb_req - P)
+    at = P
+    for r in range(R):
+        tables[r, P:counts[r]] = perm[at:at + counts[r] - P]
+        at += counts[r] - P
     refcounts = np.zeros(num_blocks, dtype=np.int32)
-    np.add.at(refcounts, tables.reshape(-1), 1)
+    np.add.at(refcounts, tables[tables >= 0], 1)
 
     T = nb_req * b
     k_pool, v_pool, wq, qn, kn, vn = [], [], [], [], [], []
@@ -181,8 +190,9 @@ def make_case(name: str, seed: int, *, num_reqs: int, num_layers: int, num_kv_he
                     shared_k, shared_v = k[:P].copy(), v[:P].copy()
                 k[:P] = shared_k
                 v[:P] = shared_v
-            kp[tables[r]] = _to_storage(k, dtype)
-            vp[tables[r]] = _to_storage(v, dtype)
+            n = int(counts[r])
+            kp[tables[r, :n]] = _to_storage(k[:n], dtype)
+            vp[tables[r, :n]] = _to_storage(v[:n], dtype)
         k_pool.append(kp)
         v_pool.append(vp)
         wq.append(_to_storage(rng.standard_normal((R, window, Hq, d)), dtype))
@@ -190,7 +200,8 @@ def make_case(name: str, seed: int, *, num_reqs: int, num_layers: int, num_kv_he
         kn.append(_to_storage(rng.standard_normal((R, H, d)) * sigma[None, :, None], dtype))
         vn.append(_to_storage(rng.standard_normal((R, H, d)), dtype))
     return CompressCase(name, seed, geom, n_max, window, tables, refcounts,
-                        k_pool, v_pool, wq, qn, kn, vn)
+                        k_pool, v_pool, wq, qn, kn, vn,
+                        num_blocks=counts.copy() if ragged else None)
 
 
 def pool_from_logical(logical: np.ndarray, tables: np.ndarray, num_blocks: int,

@@ -716,3 +716,62 @@ def test_bf16_inputs_are_widened_exactly():
     b = oracle.scores(kpool32, q32, tables, **kw)
     for x, y in zip(a, b):
         np.testing.assert_array_equal(x, y)
+
+
+# ---------------------------------------------------------------- requests holding different counts
+
+def test_plan_with_per_request_block_counts_by_hand():
+    """n_max = 3.  Request 0 holds 3 blocks [2, 3, 4]; request 1 holds 5
+    blocks [5, 6, 7, 8, 9], block 6 also held by someone outside the call.
+    Request 0 compacts in place.  Request 1: block 5 in place; block 6 is
+    shared, so it gets the smallest free id, 0, and drops to count 1 (not
+    freed); block 7 is its reserved block; blocks 8 and 9 are surplus, count
+    0: freed.  Rows stay padded with -1 past each request's blocks."""
+    tables = np.array([[2, 3, 4, -1, -1], [5, 6, 7, 8, 9]], dtype=np.int32)
+    rc = np.zeros(16, dtype=np.int32)
+    np.add.at(rc, tables[tables >= 0], 1)
+    rc[6] += 1
+    p = oracle.plan(rc, tables, 3, n_blocks=np.array([3, 5]))
+    assert p.status == oracle.OK
+    assert p.tables.tolist() == [[2, 3, 4, -1, -1], [5, 0, 7, -1, -1]]
+    assert p.dst.tolist() == [[2, 3], [5, 0]]
+    assert sorted(p.freed.tolist()) == [8, 9]
+    assert p.refcounts[0] == 1 and p.refcounts[6] == 1 and p.refcounts[8] == 0
+    # a row not padded with -1 past its count, or a count outside [n_max, n_src]
+    bad = tables.copy()
+    bad[0, 3] = 11
+    assert oracle.plan(rc, bad, 3, n_blocks=np.array([3, 5])).status == oracle.INVALID
+    assert oracle.plan(rc, tables, 3, n_blocks=np.array([2, 5])).status == oracle.INVALID
+    assert oracle.plan(rc, tables, 3, n_blocks=np.array([3, 6])).status == oracle.INVALID
+
+
+def test_ragged_compression_is_each_request_on_its_own():
+    """Requests holding 4, 6 and 5 blocks (n_max = 4) in one call, no block
+    shared (so no allocation order is involved): the scores, survivors and
+    compacted rows of each request equal those of the request compressed
+    alone."""
+    case = synth.make_case("ragged", 91, num_reqs=3, num_layers=2, num_kv_heads=2, num_q_heads=4,
+                           head_dim=16, block_size=4, n_max=4, window=3, num_blocks=24,
+                           dtype="f32", n_src=[4, 6, 5])
+    assert case.num_blocks.tolist() == [4, 6, 5] and case.tables.shape == (3, 6)
+    assert np.all(case.tables[0, 4:] == -1) and np.all(case.tables[2, 5:] == -1)
+    res = oracle.compress(case)
+    b = 4
+    for r, n in enumerate(case.num_blocks.tolist()):
+        alone = synth.CompressCase("alone", 0, case.geom, case.n_max, case.window,
+                                   np.ascontiguousarray(case.tables[r:r + 1, :n]),
+                                   case.refcounts, case.k_pool, case.v_pool,
+                                   [q[r:r + 1] for q in case.window_q], [], [], [])
+        one = oracle.compress(alone)
+        assert one.plan.tables[0, :4].tolist() == res.plan.tables[r, :4].tolist()
+        for l in range(2):
+            np.testing.assert_array_equal(res.A[l][r, :, :n * b], one.A[l][0])
+            np.testing.assert_array_equal(res.s[l][r, :, :n * b], one.s[l][0])
+            assert np.isnan(res.A[l][r, :, n * b:]).all()
+            np.testing.assert_array_equal(res.kept[l][r], one.kept[l][0])
+            for a, c in ((res.k_pool[l], one.k_pool[l]), (res.v_pool[l], one.v_pool[l])):
+                tgt = res.plan.dst[r]
+                np.testing.assert_array_equal(a[tgt], c[tgt])
+    # surplus blocks released: 2 + 1 of them
+    assert sorted(res.plan.freed.tolist()) == sorted(case.tables[1, 4:6].tolist()
+                                                    + case.tables[2, 4:5].tolist())
