@@ -97,7 +97,8 @@ class _CompressArgs(ctypes.Structure):
                 ("window_lse", ctypes.POINTER(ctypes.c_void_p)), ("workspace", ctypes.c_void_p),
                 ("workspace_bytes", ctypes.c_size_t), ("freed_ids", ctypes.POINTER(ctypes.c_int32)),
                 ("num_freed", ctypes.POINTER(ctypes.c_int32)), ("stream", ctypes.c_void_p),
-                ("debug", ctypes.POINTER(_Debug)), ("flags", ctypes.c_uint32)]
+                ("debug", ctypes.POINTER(_Debug)), ("flags", ctypes.c_uint32),
+                ("num_blocks", ctypes.POINTER(ctypes.c_int32))]
 
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
@@ -428,7 +429,7 @@ def compress_query(cache: KVCache, num_reqs: int, n_max: int, window: int,
 def compress(cache: KVCache, pool: BlockPool, n_max: int, window: int, tables: np.ndarray,
              window_q: List, workspace, stream=None, debug: Optional[dict] = None,
              window_lse: Optional[List] = None, keep_prefix: bool = False,
-             device_tables=None) -> np.ndarray:
+             device_tables=None, num_blocks=None) -> np.ndarray:
     """zp_compress (zp_compress_lse when ``window_lse``, per-layer float
     tensors [R][w][Hq] of the window rows' normalisers, is given;
     zp_compress_n when ``tables`` has n_src > n_max columns).  ``tables``
@@ -436,7 +437,10 @@ def compress(cache: KVCache, pool: BlockPool, n_max: int, window: int, tables: n
     ids.  ``keep_prefix``: zp_compress_keep_prefix (shared blocks the
     compaction leaves unchanged stay shared).  ``device_tables`` (device
     int32 [R][n_src], the same ids as ``tables``): zp_compress_ex with the
-    caller's device copy, so an in-place plan uploads nothing."""
+    caller's device copy, so an in-place plan uploads nothing.  ``num_blocks``
+    (host int32 [R]): the blocks each request holds, its row padded with -1
+    (zp_compress_ex: requests past the cap by different amounts in one
+    call)."""
     import torch
     if not (isinstance(tables, np.ndarray) and tables.dtype == np.int32 and tables.ndim == 2
             and tables.flags.c_contiguous):
@@ -474,14 +478,21 @@ def compress(cache: KVCache, pool: BlockPool, n_max: int, window: int, tables: n
     if debug:
         dbg = _Debug(_dptr(debug.get("importance")), _dptr(debug.get("redundancy")),
                      _dptr(debug.get("score")), _dptr(debug.get("kept")))
-    if device_tables is not None:
-        a = _CompressArgs(n_src, n_max, window, R, _i32(tables), device_tables.data_ptr(),
+    nbk = None
+    if num_blocks is not None:
+        nbk = np.ascontiguousarray(num_blocks, dtype=np.int32)
+        if nbk.shape != (R,):
+            raise ValueError(f"num_blocks: shape {nbk.shape}, expected ({R},)")
+    if device_tables is not None or nbk is not None:
+        a = _CompressArgs(n_src, n_max, window, R, _i32(tables),
+                          device_tables.data_ptr() if device_tables is not None else None,
                           ctypes.cast(wq, ctypes.POINTER(_vp)),
                           ctypes.cast(wl, ctypes.POINTER(_vp)) if wl is not None else None,
                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                           _i32(freed), _i32(n), _stream_handle(stream),
                           ctypes.pointer(dbg) if dbg else None,
-                          ZP_COMPRESS_KEEP_PREFIX if keep_prefix else 0)
+                          ZP_COMPRESS_KEEP_PREFIX if keep_prefix else 0,
+                          _i32(nbk) if nbk is not None else None)
         st = lib().zp_compress_ex(cache.ref, pool.handle, ctypes.byref(a))
     elif keep_prefix:
         st = lib().zp_compress_keep_prefix(

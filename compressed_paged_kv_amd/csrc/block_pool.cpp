@@ -71,7 +71,7 @@ void add_pending(zp_block_pool* pool, std::vector<int32_t> ids, hipEvent_t event
 
 zp_status plan_compression(zp_block_pool* pool, int32_t n_src, int32_t n_max, int32_t num_reqs,
                            int32_t* block_tables, PlanResult* out, const int32_t* first_evict,
-                           int32_t block_size, bool dry_run) {
+                           int32_t block_size, bool dry_run, const int32_t* num_blocks) {
   // shared block n of request r that stays: every slot of it lies below the
   // request's first eviction in every layer and head
   auto kept_shared = [&](int32_t r, int32_t n) {
@@ -83,6 +83,21 @@ zp_status plan_compression(zp_block_pool* pool, int32_t n_src, int32_t n_max, in
   if (n_src < n_max) { set_error("n_src (%d) must be >= n_max (%d)", n_src, n_max); return ZP_ERR_INVALID; }
   if (num_reqs < 0) { set_error("num_reqs < 0"); return ZP_ERR_INVALID; }
   if (num_reqs > 0 && !block_tables) { set_error("block_tables is NULL"); return ZP_ERR_INVALID; }
+  // blocks request r holds: num_blocks[r] (the rest of its row is -1), or n_src
+  auto held = [&](int32_t r) { return num_blocks ? num_blocks[r] : n_src; };
+  if (num_blocks)
+    for (int32_t r = 0; r < num_reqs; r++) {
+      if (num_blocks[r] < n_max || num_blocks[r] > n_src) {
+        set_error("request %d holds %d blocks, not in [n_max=%d, n_src=%d]", r, num_blocks[r],
+                  n_max, n_src);
+        return ZP_ERR_INVALID;
+      }
+      for (int32_t n = num_blocks[r]; n < n_src; n++)
+        if (block_tables[(size_t)r * n_src + n] != -1) {
+          set_error("request %d: entry %d past its %d blocks is not -1", r, n, num_blocks[r]);
+          return ZP_ERR_INVALID;
+        }
+    }
   const int32_t nb = pool->num_blocks;
   const std::vector<int32_t>& rc0 = pool->rc;  // counts at the start of the call
   std::vector<int32_t> seen(nb, 0);
@@ -90,7 +105,7 @@ zp_status plan_compression(zp_block_pool* pool, int32_t n_src, int32_t n_max, in
   int64_t need = 0;
   for (int32_t r = 0; r < num_reqs; r++) {
     const int32_t* row = block_tables + (size_t)r * n_src;
-    for (int32_t n = 0; n < n_src; n++) {
+    for (int32_t n = 0; n < held(r); n++) {
       const int32_t id = row[n];
       if (id < 0 || id >= nb) {
         set_error("request %d block %d: id %d out of range [0, %d)", r, n, id, nb);
@@ -128,7 +143,7 @@ zp_status plan_compression(zp_block_pool* pool, int32_t n_src, int32_t n_max, in
   out->freed.clear();
   for (int32_t r = 0; r < num_reqs; r++) {
     int32_t* row = block_tables + (size_t)r * n_src;
-    for (int32_t n = 0; n < n_src; n++) {
+    for (int32_t n = 0; n < held(r); n++) {
       const int32_t s = row[n];
       if (n >= n_max) {
         if (--pool->rc[s] == 0) out->freed.push_back(s);

@@ -55,10 +55,14 @@ struct PlanResult {
 // keeps its place and contents in every layer and head, so it stays in the
 // table, shared, instead of being re-targeted.  With dry_run, only the
 // checks of the tables run (not the free-block count; nothing changes).
+//
+// num_blocks (optional, [R]): request r holds only the first num_blocks[r]
+// entries of its row (n_max <= num_blocks[r] <= n_src); the rest of the row
+// must be -1 and is left so.
 zp_status plan_compression(zp_block_pool* pool, int32_t n_src, int32_t n_max, int32_t num_reqs,
                            int32_t* block_tables, PlanResult* out,
                            const int32_t* first_evict = nullptr, int32_t block_size = 0,
-                           bool dry_run = false);
+                           bool dry_run = false, const int32_t* num_blocks = nullptr);
 
 // Attach freed ids to a pending group released by `event` (or by a fence
 // when event is null).  Takes ownership of the event.

@@ -59,11 +59,21 @@ __global__ __launch_bounds__(kThreads, 4) void k_compact(CompactParams p) {
   __shared__ int dstb[kMaxBlocks];
   __shared__ unsigned short kept[kMaxSlots];
   __shared__ int s_first;
-  const int32_t* ev = p.evicted + unit * p.E;
-  for (int i = tid; i < p.E; i += kThreads) f[i] = ev[i] - i;
-  for (int n = tid; n < p.n_src; n += kThreads) srcb[n] = p.src[(size_t)r * p.src_stride + n];
-  for (int n = tid; n < p.n_max - 1; n += kThreads) dstb[n] = p.dst[(size_t)r * p.dst_stride + n];
-  if (tid == 0) s_first = p.E > 0 ? ev[0] : p.K_keep;  // rows below the first eviction stay put
+  // this request's blocks (the call's largest unless rows are ragged) and evictions
+  const int n_src = unit_blocks(p.src, p.src_stride, r, p.n_src, p.n_max, p.ragged);
+  const int E = n_src * b - p.K_keep;
+  const int32_t* ev = p.evicted + unit * p.E;  // stride: the call's largest E
+  for (int i = tid; i < E; i += kThreads) f[i] = ev[i] - i;
+  // an id outside the pool is read as block 0 and never written
+  for (int n = tid; n < n_src; n += kThreads) {
+    const int id = p.src[(size_t)r * p.src_stride + n];
+    srcb[n] = (unsigned)id < (unsigned)p.num_blocks ? id : 0;
+  }
+  for (int n = tid; n < p.n_max - 1; n += kThreads) {
+    const int id = p.dst[(size_t)r * p.dst_stride + n];
+    dstb[n] = (unsigned)id < (unsigned)p.num_blocks ? id : -1;
+  }
+  if (tid == 0) s_first = E > 0 ? ev[0] : p.K_keep;  // rows below the first eviction stay put
   __syncthreads();
   // ... unless their block is re-targeted (a new block for a shared source)
   for (int n = tid; n < p.n_max - 1; n += kThreads)
@@ -72,7 +82,7 @@ __global__ __launch_bounds__(kThreads, 4) void k_compact(CompactParams p) {
   const int first = min(s_first, p.K_keep);
   // survivor list, once per workgroup: kept[r] = r + #{i : f_i <= r}
   for (int row = tid; row < p.K_keep; row += kThreads) {
-    int lo = 0, hi = p.E;
+    int lo = 0, hi = E;
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
       if (f[mid] <= row) lo = mid + 1; else hi = mid;
@@ -96,9 +106,10 @@ __global__ __launch_bounds__(kThreads, 4) void k_compact(CompactParams p) {
       const int row = min(t0 + rsub + u * kRowsPerPass, p.K_keep - 1);
       const int j = kept[row];
       const int from = row_of(srcb[j / b], j % b);
-      const int dst = row_of(dstb[row / b], row % b);
+      const int db = dstb[row / b];
+      const int dst = row_of(db, row % b);
       buf[u] = ZP_COMPACT_STREAM >= 2 ? ldg16_stream(addr(from)) : ldg16(addr(from));
-      to[u] = (dst != from && t0 + rsub + u * kRowsPerPass < p.K_keep) ? dst : -1;
+      to[u] = (db >= 0 && dst != from && t0 + rsub + u * kRowsPerPass < p.K_keep) ? dst : -1;
     }
   };
   if (first >= p.K_keep) return;  // nothing moves (uniform across the workgroup)

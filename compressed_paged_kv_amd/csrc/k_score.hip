@@ -186,9 +186,10 @@ struct SelectLds {
 // s_f (LDS, may be null) also gets f_i = e_i - i for the i-th evicted slot.
 template <int PER, int NW>
 __device__ inline void select_evicted(const float* s_sc, SelectLds& L, int* s_scr,
-                                      const ScoreParams& p, size_t unit, int* s_f) {
+                                      const ScoreParams& p, size_t unit, int* s_f, const int T,
+                                      const int C, const int E) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int per = (p.T + 64 * NW - 1) / (64 * NW);
+  const int per = (T + 64 * NW - 1) / (64 * NW);
   const int j0 = tid * per;
   uint32_t key[PER];
   if (per == PER) {  // 16-byte groups; a range past T stays inside s_buf (threads * PER floats)
@@ -202,9 +203,9 @@ __device__ inline void select_evicted(const float* s_sc, SelectLds& L, int* s_sc
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < PER; i++) key[i] = (i < per && j0 + i < p.T) ? order_key(s_sc[j0 + i]) : 0u;
+    for (int i = 0; i < PER; i++) key[i] = (i < per && j0 + i < T) ? order_key(s_sc[j0 + i]) : 0u;
   }
-  auto valid = [&](int i) { return i < per && j0 + i < p.C; };
+  auto valid = [&](int i) { return i < per && j0 + i < C; };
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
   for (int i = 0; i < PER; i++)
@@ -231,8 +232,8 @@ __device__ inline void select_evicted(const float* s_sc, SelectLds& L, int* s_sc
   int done = diff ? __clz((int)diff) : 32;  // leading bits every candidate key shares
   uint32_t mask = done == 0 ? 0u : done == 32 ? 0xFFFFFFFFu : 0xFFFFFFFFu << (32 - done);
   uint32_t prefix = kmin & mask;
-  int rank = p.E;   // the E-th smallest key is the rank-th smallest of the bin
-  int cnt = p.C;    // candidates in the bin
+  int rank = E;     // the E-th smallest key is the rank-th smallest of the bin
+  int cnt = C;      // candidates in the bin
   int pass = 0;
   while (cnt > kSelList && done < 32) {
     const int nb = min(8, 32 - done), shift = 32 - done - nb;
@@ -323,13 +324,13 @@ __device__ inline void select_evicted(const float* s_sc, SelectLds& L, int* s_sc
   int tie_idx = excl >> 16;
   int pos = (excl & 0xFFFF) + (listed ? 0 : max(0, tie_idx - tie_from));
   int kept_pos = j0 - pos;  // survivors below j0
-  int32_t* out = p.evicted + unit * p.E;
+  int32_t* out = p.evicted + unit * p.E;   // stride: the call's largest E
 #pragma unroll
   for (int i = 0; i < PER; i++) {
     const int j = j0 + i;
-    if (i >= per || j >= p.T) continue;
+    if (i >= per || j >= T) continue;
     bool ev = false;
-    if (j < p.C) {
+    if (j < C) {
       if (key[i] < prefix) {
         ev = true;
       } else if ((key[i] & mask) == prefix) {
@@ -342,7 +343,7 @@ __device__ inline void select_evicted(const float* s_sc, SelectLds& L, int* s_sc
       }
     }
     if (ev) {
-      if (pos < p.E) {
+      if (pos < E) {
         out[pos] = j;
         if (s_f) s_f[pos] = j - pos;
       }
@@ -374,7 +375,7 @@ __device__ inline void select_evicted(const float* s_sc, SelectLds& L, int* s_sc
 // the selection, then kept, and the request's source and target block ids.
 template <int VPR, int B, int NTH, int U, bool KCACHED>
 __device__ inline void compact_unit(const ScoreParams& p, float* lds, int* s_first, int l, int r,
-                                    int h) {
+                                    int h, const int n_src, const int E) {
   constexpr int kRowsPerPass = NTH / VPR;
   constexpr int kRowsPerTile = kRowsPerPass * U;
   constexpr size_t kRowBytes = (size_t)VPR * 16;
@@ -384,15 +385,22 @@ __device__ inline void compact_unit(const ScoreParams& p, float* lds, int* s_fir
   unsigned short* kept = reinterpret_cast<unsigned short*>(lds + kMaxEvicted);
   int* srcb = reinterpret_cast<int*>(lds + kMaxEvicted + kMaxScoreSlots / 2);
   int* dstb = srcb + kMaxScoreSlots / 16;
-  for (int n = tid; n < p.n_src; n += NTH) srcb[n] = p.src[(size_t)r * p.src_stride + n];
-  for (int n = tid; n < p.n_max - 1; n += NTH) dstb[n] = p.dst[(size_t)r * p.dst_stride + n];
+  // an id outside the pool is read as block 0 and never written
+  for (int n = tid; n < n_src; n += NTH) {
+    const int id = p.src[(size_t)r * p.src_stride + n];
+    srcb[n] = (unsigned)id < (unsigned)p.num_blocks ? id : 0;
+  }
+  for (int n = tid; n < p.n_max - 1; n += NTH) {
+    const int id = p.dst[(size_t)r * p.dst_stride + n];
+    dstb[n] = (unsigned)id < (unsigned)p.num_blocks ? id : -1;
+  }
   if (tid == 0) *s_first = p.K_keep;
   __syncthreads();  // f (written by the selection) and the block ids are in LDS
   // the first re-targeted block (a new block for a shared source) ...
   for (int n = tid; n < p.n_max - 1; n += NTH)
     if (dstb[n] != srcb[n]) atomicMin(s_first, n * B);
   for (int row = tid; row < p.K_keep; row += NTH) {
-    int lo = 0, hi = p.E;
+    int lo = 0, hi = E;
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
       if (f[mid] <= row) lo = mid + 1; else hi = mid;
@@ -401,7 +409,7 @@ __device__ inline void compact_unit(const ScoreParams& p, float* lds, int* s_fir
   }
   __syncthreads();
   // ... and the first evicted slot (f_0 = e_0): nothing below both moves
-  const int first = min(min(*s_first, p.E > 0 ? f[0] : p.K_keep), p.K_keep);
+  const int first = min(min(*s_first, E > 0 ? f[0] : p.K_keep), p.K_keep);
   if (first >= p.K_keep) return;  // nothing moves (uniform)
 
   char* const kbase = static_cast<char*>(p.layers[l - p.layer0].k) + vec * 16;
@@ -421,10 +429,11 @@ __device__ inline void compact_unit(const ScoreParams& p, float* lds, int* s_fir
       const int row = min(t0 + rsub + u * kRowsPerPass, p.K_keep - 1);
       const int j = kept[row];
       const int from = row_of(srcb[j / B], j % B);
-      const int dst = row_of(dstb[row / B], row % B);
+      const int db = dstb[row / B];
+      const int dst = row_of(db, row % B);
       kb[u] = KCACHED ? ldg16(kbase + off_of(from)) : ldg16_stream(kbase + off_of(from));
       vb[u] = ldg16_stream(vbase + off_of(from));
-      to[u] = (dst != from && t0 + rsub + u * kRowsPerPass < p.K_keep) ? dst : -1;
+      to[u] = (db >= 0 && dst != from && t0 + rsub + u * kRowsPerPass < p.K_keep) ? dst : -1;
     }
   };
   uint4 ck[U], cv[U], nk[U], nv[U];
@@ -500,6 +509,9 @@ __device__ __forceinline__ void score_unit(const ScoreParams& p) {
   const int rg = wave / WPG, wl = wave - rg * WPG;
   const char* kbase = static_cast<const char*>(p.layers[l - p.layer0].k);
   const char* qbase = static_cast<const char*>(p.layers[l - p.layer0].q);
+  // this request's blocks and slots (the call's largest unless rows are ragged)
+  const int n_src = unit_blocks(p.src, p.src_stride, r, p.n_src, p.n_max, p.ragged);
+  const int T = n_src * B, C = T - p.w, E = T - p.K_keep;
 
   __shared__ __align__(16) float s_buf[lds_floats<RG>()];
   __shared__ float s_wst[kWaves][RPW][2];
@@ -531,11 +543,11 @@ __device__ __forceinline__ void score_unit(const ScoreParams& p) {
   // -1 for padding rows.  Only the last block needs it, so it is not kept.
   auto lim = [&](int rt, int i) {
     const int row = rg * RPW + rt * 16 + 4 * grp + i;
-    return row < p.rows ? p.T - p.w + row / p.G : -1;
+    return row < p.rows ? T - p.w + row / p.G : -1;
   };
 
   // this wave's blocks are wl + WPG*k; lane k holds the physical id of the k-th
-  const int nbw = p.n_src > wl ? (p.n_src - wl + WPG - 1) / WPG : 0;
+  const int nbw = n_src > wl ? (n_src - wl + WPG - 1) / WPG : 0;
   // (a wave has at most 128 blocks: n_src <= 512 at four waves per row group)
   const int32_t* tab = p.src + (size_t)r * p.src_stride + wl;
   const int ids0 = lane < nbw ? tab[WPG * lane] : 0;
@@ -547,7 +559,8 @@ __device__ __forceinline__ void score_unit(const ScoreParams& p) {
   // wave loads fragments [rg*FL, rg*FL + FL).
   auto fetch = [&](int k, uint4 (&kd)[FL]) {
     const int kc = max(min(k, nbw - 1), 0);
-    const int pblk = kc < 64 ? __builtin_amdgcn_readlane(ids0, kc) : __builtin_amdgcn_readlane(ids1, kc - 64);
+    int pblk = kc < 64 ? __builtin_amdgcn_readlane(ids0, kc) : __builtin_amdgcn_readlane(ids1, kc - 64);
+    pblk = (unsigned)pblk < (unsigned)p.num_blocks ? pblk : 0;  // never outside the pool
     const char* tile = kbase + ((size_t)pblk * p.H + h) * B * ROWB + row_off;
 #pragma unroll
     for (int q = 0; q < FL; q++) {
@@ -565,7 +578,7 @@ __device__ __forceinline__ void score_unit(const ScoreParams& p) {
   auto ring = [&](auto reverse, auto body) {
     constexpr bool REV = decltype(reverse)::value;
     auto kof = [&](int it) { return REV ? nbw - 1 - it : it; };
-    const int iters = SH ? (p.n_src + WPG - 1) / WPG : nbw;
+    const int iters = SH ? (n_src + WPG - 1) / WPG : nbw;
     if (iters == 0) return;
     uint4 kb[kPrefetch][FL];
     // the prologue keeps slot order (the scheduler may not interleave the
@@ -641,7 +654,7 @@ __device__ __forceinline__ void score_unit(const ScoreParams& p) {
       }
     ring(BoolC<false>{}, [&](int k, const uint4 (&kt)[NST][NV]) {
       const int n = wl + WPG * k;
-      const bool last = n == p.n_src - 1;  // only the last block meets the causal limit
+      const bool last = n == n_src - 1;  // only the last block meets the causal limit
 #pragma unroll
       for (int st = 0; st < NST; st++) {
         const int j = n * B + st * 16 + col;
@@ -734,7 +747,7 @@ __device__ __forceinline__ void score_unit(const ScoreParams& p) {
   };
   ring(BoolC<kReversePass2>{}, [&](int k, const uint4 (&kt)[NST][NV]) {
     const int n = wl + WPG * k;
-    const bool last = n == p.n_src - 1;
+    const bool last = n == n_src - 1;
     float A[NST];
 #pragma unroll
     for (int st = 0; st < NST; st++) {
@@ -813,7 +826,7 @@ __device__ __forceinline__ void score_unit(const ScoreParams& p) {
             const size_t o = unit * p.T + j;
             if (p.dbg_importance) p.dbg_importance[o] = a;
             if (p.dbg_redundancy) p.dbg_redundancy[o] = Rd[st];
-            if (p.dbg_score && j < p.C) p.dbg_score[o] = s;
+            if (p.dbg_score && j < C) p.dbg_score[o] = s;
           } else {
             s_rr[j] = Rd[st];
           }
@@ -823,30 +836,30 @@ __device__ __forceinline__ void score_unit(const ScoreParams& p) {
   });
   __syncthreads();
   if (RG == 2) {
-    for (int j = tid; j < p.T; j += kThreads) {
+    for (int j = tid; j < T; j += kThreads) {
       const float a = (s_sc[j] + s_aux[j]) * inv_rows;
       const float s = a * (1.0f - s_rr[j]);
       const size_t o = unit * p.T + j;
       if (p.dbg_importance) p.dbg_importance[o] = a;
       if (p.dbg_redundancy) p.dbg_redundancy[o] = s_rr[j];
-      if (p.dbg_score && j < p.C) p.dbg_score[o] = s;
+      if (p.dbg_score && j < C) p.dbg_score[o] = s;
       s_sc[j] = s;
     }
     __syncthreads();
   }
 
   // ---------------------------------------------------------------- select
-  const int per = (p.T + kThreads - 1) / kThreads;
+  const int per = (T + kThreads - 1) / kThreads;
   int* s_f = FUSE ? reinterpret_cast<int*>(s_buf) : nullptr;  // the scores are in registers by then
-  if (per <= 8) select_evicted<8, kWaves>(s_sc, s_sel, s_scr, p, unit, s_f);
-  else if (per <= 16) select_evicted<16, kWaves>(s_sc, s_sel, s_scr, p, unit, s_f);
-  else select_evicted<32, kWaves>(s_sc, s_sel, s_scr, p, unit, s_f);
+  if (per <= 8) select_evicted<8, kWaves>(s_sc, s_sel, s_scr, p, unit, s_f, T, C, E);
+  else if (per <= 16) select_evicted<16, kWaves>(s_sc, s_sel, s_scr, p, unit, s_f, T, C, E);
+  else select_evicted<32, kWaves>(s_sc, s_sel, s_scr, p, unit, s_f, T, C, E);
   if constexpr (FUSE) {
     __shared__ int s_first;
     if (p.k_cached)  // uniform: one tile loop or the other, each straight-line
-      compact_unit<ROWB / 16, B, kThreads, kFusedUnroll, true>(p, s_buf, &s_first, l, r, h);
+      compact_unit<ROWB / 16, B, kThreads, kFusedUnroll, true>(p, s_buf, &s_first, l, r, h, n_src, E);
     else
-      compact_unit<ROWB / 16, B, kThreads, kFusedUnroll, false>(p, s_buf, &s_first, l, r, h);
+      compact_unit<ROWB / 16, B, kThreads, kFusedUnroll, false>(p, s_buf, &s_first, l, r, h, n_src, E);
   }
 }
 

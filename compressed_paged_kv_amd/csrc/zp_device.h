@@ -38,4 +38,24 @@ __device__ inline void stg16_stream(void* p, uint4 v) {
   __builtin_nontemporal_store(w, (g_u32x4*)(p));
 }
 
+// Blocks request r holds when rows are ragged: the index of the first
+// negative entry of its source row, clamped to [n_max, n_src]; otherwise
+// n_src.  Every lane of a wave gets the same value.
+__device__ inline int unit_blocks(const int32_t* src, int src_stride, int r, int n_src, int n_max,
+                                  int ragged) {
+  if (!ragged) return n_src;
+  const int32_t* row = src + (size_t)r * src_stride;
+  const int lane = threadIdx.x & 63;
+  int first = n_src;
+  for (int k0 = 0; k0 < n_src; k0 += 64) {
+    const int k = k0 + lane;
+    const unsigned long long neg = __ballot(k < n_src && row[k] < 0);
+    if (neg) {
+      first = k0 + __builtin_ctzll(neg);
+      break;
+    }
+  }
+  return first < n_max ? n_max : first;
+}
+
 }  // namespace zp

@@ -74,6 +74,11 @@ struct ScoreParams {
   int32_t* dbg_kept;        // optional [L*R*H][K_keep]
   const int32_t* dst;       // device, row r at dst + r*dst_stride: the n_max-1 target blocks; compact in the same kernel; null: select only
   int32_t k_cached;         // fused compaction: load K normally (1) or non-temporally (0)
+  // ragged: request r holds the blocks of its source row up to its first -1
+  // (at least n_max); n_src, T, C and E are then the call's largest, and the
+  // strides of evicted and of the debug arrays
+  int32_t ragged;
+  int32_t num_blocks;       // pool size: ids outside [0, num_blocks) are never followed
   int32_t R, H, Hq, G, w, n_src, n_max, T, C, E, K_keep, rows;  // T = n_src * b
   float scale_log2;  // log2(e) / sqrt(d)
 };
@@ -85,8 +90,11 @@ struct CompactParams {
   const int32_t* dst;       // device, row r at dst + r*dst_stride (n_max-1 entries)
   int32_t src_stride, dst_stride;
   const int32_t* evicted;   // [L*R*H][E]
+  int32_t ragged;           // as ScoreParams::ragged (E = the stride of evicted)
+  int32_t num_blocks;
   int32_t R, H, n_src, n_max, E, K_keep;
 };
+
 
 struct DecodeParams {
   const void* k;

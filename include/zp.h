@@ -292,8 +292,22 @@ zp_status zp_compress_n(const zp_kv_cache* cache, zp_block_pool* pool, int32_t n
  *                   a plan that re-targets blocks the caller refreshes it
  *                   from the rewritten host tables.
  *   flags           0, or ZP_COMPRESS_KEEP_PREFIX (zp_compress_keep_prefix).
- * Rejects what the named entry points reject, unknown flags and a
- * misaligned device_tables.
+ *   num_blocks      NULL (every request holds n_src blocks), or HOST int32
+ *                   [num_reqs]: request r holds the first num_blocks[r]
+ *                   entries of its row, n_max <= num_blocks[r] <= n_src, and
+ *                   the rest of the row is -1 (in block_tables and in
+ *                   device_tables alike: the kernels read each request's
+ *                   count off its row).  Requests past the cap by different
+ *                   amounts -- prompts compressed after chunks of their
+ *                   prefill, say -- then share one call; each is scored on
+ *                   its own T = num_blocks[r]*b slots and evicts
+ *                   (num_blocks[r] - n_max + 1)*b per head.  Debug outputs
+ *                   keep the row stride T = n_src*b; slots past a request's
+ *                   own T are left as they were.
+ * Rejects what the named entry points reject, unknown flags, a misaligned
+ * device_tables, and num_blocks outside [n_max, n_src] or rows not padded
+ * with -1.  Kernels never follow an id outside the pool: a device table that
+ * holds one reads that block as block 0 and never writes it.
  * ---------------------------------------------------------------------- */
 #define ZP_COMPRESS_KEEP_PREFIX 1u
 
@@ -313,6 +327,7 @@ typedef struct zp_compress_args {
   void* stream;
   const zp_compress_debug* debug;
   uint32_t flags;
+  const int32_t* num_blocks;
 } zp_compress_args;
 
 zp_status zp_compress_ex(const zp_kv_cache* cache, zp_block_pool* pool,

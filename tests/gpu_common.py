@@ -55,11 +55,14 @@ class GpuRun:
 def window_lse_on_gpu(cache, case, kp_tensors, wq_tensors, device="cuda"):
     """Normalisers of the window rows as the decode steps that produced the
     window queries record them: for window position i, zp_paged_decode_lse
-    of query i over slots 0..T-w+i, written to row r*w + i of a [R*w][Hq]
+    of query i over slots 0..T_r-w+i, written to row r*w + i of a [R*w][Hq]
     buffer per layer (returned as [R][w][Hq] views)."""
     g = case.geom
     R, w, n_src, b = case.num_reqs, case.window, case.n_src, g.block_size
-    T = n_src * b
+    counts = getattr(case, "num_blocks", None)
+    # each request's own length T_r (requests may hold different block counts)
+    T = torch.from_numpy((np.full(R, n_src) if counts is None else counts).astype(np.int32) * b)
+    T = T.to(device)
     tab_t = torch.from_numpy(np.ascontiguousarray(case.tables)).to(device)
     dws = torch.empty(max(zp.paged_decode_workspace_bytes(cache, R, n_src), 16),
                       dtype=torch.uint8, device=device)
@@ -68,7 +71,7 @@ def window_lse_on_gpu(cache, case, kp_tensors, wq_tensors, device="cuda"):
     for layer in range(g.num_layers):
         buf = torch.full((R * w, g.num_q_heads), float("nan"), dtype=torch.float32, device=device)
         for i in range(w):
-            seq = torch.full((R,), T - w + i + 1, dtype=torch.int32, device=device)
+            seq = (T - w + i + 1).to(torch.int32).contiguous()
             rows = (torch.arange(R, dtype=torch.int32, device=device) * w + i).contiguous()
             q_i = wq_tensors[layer][:, i].contiguous()
             zp.paged_decode(cache, layer, q_i, tab_t, seq, 1.0 / np.sqrt(g.head_dim), out, dws,
@@ -103,7 +106,8 @@ def run_case(case, device="cuda", decode=True, recorded_lse=False, keep_prefix=F
     wl = window_lse_on_gpu(cache, case, kp, wq, device) if recorded_lse else None
     dtab = torch.from_numpy(np.ascontiguousarray(case.tables)).to(device) if device_tables else None
     freed = zp.compress(cache, pool, n_max, w, tables, wq, ws, debug=dbg, window_lse=wl,
-                        keep_prefix=keep_prefix, device_tables=dtab)
+                        keep_prefix=keep_prefix, device_tables=dtab,
+                        num_blocks=getattr(case, "num_blocks", None))
     torch.cuda.synchronize()
     run = GpuRun(tables=tables.copy(), refcounts=pool.refcounts(), freed=freed.copy(),
                  A=dbg["importance"].cpu().numpy(), R=dbg["redundancy"].cpu().numpy(),
@@ -164,34 +168,17 @@ def check_case(case, run: GpuRun, *, check_decode=True, layers=None, keep_prefix
     np.testing.assert_array_equal(np.sort(run.freed), np.sort(ref.plan.freed))
     stats = dict(max_rel_A=0.0, max_abs_R=0.0, max_rel_s=0.0, near_tie_diffs=0, max_abs_out=0.0)
     dst_blocks = set(ref.plan.dst.reshape(-1).tolist())
+    nbk = getattr(case, "num_blocks", None)
     for li, layer in enumerate(layers):
         A, Rr, s = run.A[layer], run.R[layer], run.s[layer]
         Ao, Ro, so = ref.A[li], ref.R[li], ref.s[li]
-        assert np.isfinite(A).all() and np.isfinite(Rr).all()
-        okA = rel_ok(A, Ao, A_RTOL)
-        assert okA.all(), f"layer {layer}: importance off at {np.argwhere(~okA)[:5]}"
-        okR = np.abs(Rr - Ro) <= R_ATOL
-        assert okR.all(), f"layer {layer}: redundancy off at {np.argwhere(~okR)[:5]}"
-        okS = rel_ok(s[..., :C], so[..., :C], S_RTOL)
-        assert okS.all(), f"layer {layer}: score off at {np.argwhere(~okS)[:5]}"
-        stats["max_rel_A"] = max(stats["max_rel_A"], float(np.max(np.abs(A - Ao) / np.abs(Ao))))
-        stats["max_abs_R"] = max(stats["max_abs_R"], float(np.max(np.abs(Rr - Ro))))
-        stats["max_rel_s"] = max(stats["max_rel_s"],
-                                 float(np.max(np.abs(s[..., :C] - so[..., :C]) / np.abs(so[..., :C]))))
+        if nbk is not None:
+            _check_ragged_unit_scores(A, Rr, s, Ao, Ro, so, run.kept[layer], ref.kept[li],
+                                      nbk * b, w, k_sel, layer, stats)
+        else:
+            _check_unit_scores_uniform(A, Rr, s, Ao, Ro, so, run.kept[layer], ref.kept[li], C, w,
+                                       k_sel, layer, stats)
         kept = run.kept[layer]
-        # the GPU decision is exactly the selection rule applied to its own scores
-        own = np.full(s.shape, np.nan)
-        own[..., :C] = s[..., :C].astype(np.float64)
-        np.testing.assert_array_equal(kept, oracle.select(own, w, k_sel))
-        # and differs from the oracle's decision only at near-ties
-        ko = ref.kept[li]
-        for r, h in zip(*np.nonzero(np.any(kept != ko, axis=-1))):
-            gs, os_ = set(kept[r, h].tolist()), set(ko[r, h].tolist())
-            tau = np.sort(so[r, h, :C])[::-1][k_sel - 1]
-            for j in gs ^ os_:
-                assert abs(so[r, h, j] - tau) <= TIE_RTOL * abs(tau), \
-                    f"layer {layer} req {r} head {h}: slot {j} differs, not a near tie"
-            stats["near_tie_diffs"] += len(gs ^ os_)
         # compacted bytes: GPU rows == source rows at the GPU's own kept slots
         ri = np.arange(kept.shape[0])[:, None, None]
         hi = np.arange(kept.shape[1])[None, :, None]
@@ -207,22 +194,85 @@ def check_case(case, run: GpuRun, *, check_decode=True, layers=None, keep_prefix
             # every block that is not a compaction target is untouched
             assert np.array_equal(pa[others], pb[others]), f"layer {layer}: a non-target block changed"
         if check_decode and run.out is not None:
-            # oracle decode on the GPU-compacted, GPU-appended cache
-            seq = np.full(run.tables.shape[0], k_keep + 1, dtype=np.int32)
-            kp, vp = run.k_pool[layer].copy(), run.v_pool[layer].copy()
-            slot = (run.tables[:, k_keep // b] * b + k_keep % b).astype(np.int32)
-            oracle.append(kp, vp, case.k_new[layer], case.v_new[layer], slot)
-            # run_case poisoned the reserved blocks' slots past the appended one
-            res = run.tables[:, n_max - 1]
-            kp[res, :, 1:, :] = run.appended_k[layer][res, :, 1:, :]
-            vp[res, :, 1:, :] = run.appended_v[layer][res, :, 1:, :]
-            assert np.array_equal(words(run.appended_k[layer]), words(kp))
-            assert np.array_equal(words(run.appended_v[layer]), words(vp))
-            want = oracle.decode(kp, vp, case.q_new[layer],
-                                 np.ascontiguousarray(run.tables[:, :n_max]), seq,
-                                 num_q_heads=g.num_q_heads)
-            err = np.abs(run.out[layer] - want)
-            assert np.isfinite(run.out[layer]).all()
-            assert err.max() <= DECODE_ATOL, f"layer {layer}: decode error {err.max()}"
-            stats["max_abs_out"] = max(stats["max_abs_out"], float(err.max()))
+            _check_decode(case, run, layer, stats)
     return stats
+
+
+def _check_unit_scores_uniform(A, Rr, s, Ao, Ro, so, kept, ko, C, w, k_sel, layer, stats):
+    """Scores and survivors when every request holds the same block count."""
+    assert np.isfinite(A).all() and np.isfinite(Rr).all()
+    okA = rel_ok(A, Ao, A_RTOL)
+    assert okA.all(), f"layer {layer}: importance off at {np.argwhere(~okA)[:5]}"
+    okR = np.abs(Rr - Ro) <= R_ATOL
+    assert okR.all(), f"layer {layer}: redundancy off at {np.argwhere(~okR)[:5]}"
+    okS = rel_ok(s[..., :C], so[..., :C], S_RTOL)
+    assert okS.all(), f"layer {layer}: score off at {np.argwhere(~okS)[:5]}"
+    stats["max_rel_A"] = max(stats["max_rel_A"], float(np.max(np.abs(A - Ao) / np.abs(Ao))))
+    stats["max_abs_R"] = max(stats["max_abs_R"], float(np.max(np.abs(Rr - Ro))))
+    stats["max_rel_s"] = max(stats["max_rel_s"],
+                             float(np.max(np.abs(s[..., :C] - so[..., :C]) / np.abs(so[..., :C]))))
+    # the GPU decision is exactly the selection rule applied to its own scores
+    own = np.full(s.shape, np.nan)
+    own[..., :C] = s[..., :C].astype(np.float64)
+    np.testing.assert_array_equal(kept, oracle.select(own, w, k_sel))
+    # and differs from the oracle's decision only at near-ties
+    for r, h in zip(*np.nonzero(np.any(kept != ko, axis=-1))):
+        gs, os_ = set(kept[r, h].tolist()), set(ko[r, h].tolist())
+        tau = np.sort(so[r, h, :C])[::-1][k_sel - 1]
+        for j in gs ^ os_:
+            assert abs(so[r, h, j] - tau) <= TIE_RTOL * abs(tau), \
+                f"layer {layer} req {r} head {h}: slot {j} differs, not a near tie"
+        stats["near_tie_diffs"] += len(gs ^ os_)
+
+
+def _check_ragged_unit_scores(A, Rr, s, Ao, Ro, so, kept, ko, Ts, w, k_sel, layer, stats):
+    """Scores and survivors of requests holding different block counts: each
+    request against the oracle on its own T; the debug rows past its T left
+    as they were (NaN)."""
+    for r, T in enumerate(Ts.tolist()):
+        C = T - w
+        a, rr, ss = A[r, :, :T], Rr[r, :, :T], s[r, :, :T]
+        assert np.isnan(A[r, :, T:]).all() and np.isnan(s[r, :, T:]).all()
+        assert np.isfinite(a).all() and np.isfinite(rr).all()
+        okA = rel_ok(a, Ao[r, :, :T], A_RTOL)
+        assert okA.all(), f"layer {layer} req {r}: importance off at {np.argwhere(~okA)[:5]}"
+        okR = np.abs(rr - Ro[r, :, :T]) <= R_ATOL
+        assert okR.all(), f"layer {layer} req {r}: redundancy off at {np.argwhere(~okR)[:5]}"
+        okS = rel_ok(ss[:, :C], so[r, :, :C], S_RTOL)
+        assert okS.all(), f"layer {layer} req {r}: score off at {np.argwhere(~okS)[:5]}"
+        stats["max_rel_A"] = max(stats["max_rel_A"], float(np.max(np.abs(a - Ao[r, :, :T]) / np.abs(Ao[r, :, :T]))))
+        stats["max_abs_R"] = max(stats["max_abs_R"], float(np.max(np.abs(rr - Ro[r, :, :T]))))
+        own = np.full(ss.shape, np.nan)
+        own[:, :C] = ss[:, :C].astype(np.float64)
+        np.testing.assert_array_equal(kept[r], oracle.select(own, w, k_sel))
+        for h in np.nonzero(np.any(kept[r] != ko[r], axis=-1))[0]:
+            gs, os_ = set(kept[r, h].tolist()), set(ko[r, h].tolist())
+            tau = np.sort(so[r, h, :C])[::-1][k_sel - 1]
+            for j in gs ^ os_:
+                assert abs(so[r, h, j] - tau) <= TIE_RTOL * abs(tau), \
+                    f"layer {layer} req {r} head {h}: slot {j} differs, not a near tie"
+            stats["near_tie_diffs"] += len(gs ^ os_)
+
+
+def _check_decode(case, run, layer, stats):
+    g = case.geom
+    b, n_max = g.block_size, case.n_max
+    k_keep = (n_max - 1) * b
+    # oracle decode on the GPU-compacted, GPU-appended cache
+    seq = np.full(run.tables.shape[0], k_keep + 1, dtype=np.int32)
+    kp, vp = run.k_pool[layer].copy(), run.v_pool[layer].copy()
+    slot = (run.tables[:, k_keep // b] * b + k_keep % b).astype(np.int32)
+    oracle.append(kp, vp, case.k_new[layer], case.v_new[layer], slot)
+    # run_case poisoned the reserved blocks' slots past the appended one
+    res = run.tables[:, n_max - 1]
+    kp[res, :, 1:, :] = run.appended_k[layer][res, :, 1:, :]
+    vp[res, :, 1:, :] = run.appended_v[layer][res, :, 1:, :]
+    assert np.array_equal(words(run.appended_k[layer]), words(kp))
+    assert np.array_equal(words(run.appended_v[layer]), words(vp))
+    want = oracle.decode(kp, vp, case.q_new[layer],
+                         np.ascontiguousarray(run.tables[:, :n_max]), seq,
+                         num_q_heads=g.num_q_heads)
+    err = np.abs(run.out[layer] - want)
+    assert np.isfinite(run.out[layer]).all()
+    assert err.max() <= DECODE_ATOL, f"layer {layer}: decode error {err.max()}"
+    stats["max_abs_out"] = max(stats["max_abs_out"], float(err.max()))

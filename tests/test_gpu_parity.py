@@ -96,6 +96,20 @@ CASES = {
     "layers_50_two_launches": lambda: _case("m7", 228, num_reqs=2, num_layers=50, num_kv_heads=1,
                                             num_q_heads=2, head_dim=64, n_max=4, window=4,
                                             num_blocks=12),
+    # one call over requests holding different block counts (rows padded
+    # with -1): at the cap and past it side by side, with a shared prefix and
+    # two layers; b=32 with two row groups; fp32 from 6 to 60 blocks; and
+    # 1024 evictions next to a request at the cap
+    "mixed_counts_prefix_2layers": lambda: _case("x1", 230, num_reqs=4, num_layers=2, n_max=10,
+                                                 n_src=[10, 13, 11, 16], num_blocks=90,
+                                                 shared_prefix_blocks=2),
+    "mixed_counts_b32_rows128": lambda: _case("x2", 231, head_dim=64, block_size=32, window=32,
+                                              num_reqs=3, num_q_heads=8, n_max=8,
+                                              n_src=[8, 20, 9], num_blocks=64),
+    "mixed_counts_f32_d64": lambda: _case("x3", 232, dtype="f32", head_dim=64, num_reqs=3,
+                                          n_max=6, n_src=[60, 6, 30], num_blocks=120),
+    "mixed_counts_max_evictions": lambda: _case("x4", 233, head_dim=64, n_max=20, n_src=[83, 20],
+                                                num_blocks=140),
     # 16 keys per selecting thread: 4096 slots exactly, and a ragged 3200
     "slots_4096_rows64": lambda: _case("m4", 224, num_reqs=2, num_kv_heads=1, num_q_heads=4,
                                        n_max=256, num_blocks=520),
@@ -420,7 +434,8 @@ def test_keep_prefix_leaves_a_clean_shared_prefix_shared():
     check_case(c, run, keep_prefix=True)
 
 
-@pytest.mark.parametrize("name", ["shared_prefix_2layers", "over_cap_prefix_2layers"])
+@pytest.mark.parametrize("name", ["shared_prefix_2layers", "over_cap_prefix_2layers",
+                                  "mixed_counts_prefix_2layers"])
 def test_keep_prefix_matches_oracle_on_random_prefixes(name):
     case = CASES[name]()
     say(f"[gpu parity] keep-prefix on {name}")
@@ -465,6 +480,43 @@ def _random_configs(n, seed):
 def test_random_shapes_match_oracle(i, cfg):
     case = synth.make_case(f"rand{i}", 5000 + i, **cfg)
     say(f"[gpu parity] random shape {i}: {cfg}")
+    run = run_case(case)
+    check_case(case, run)
+
+
+def _random_mixed_configs(n, seed):
+    """Seeded calls over requests holding different block counts, inside
+    the host's limits for the largest of them."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        b = int(rng.choice([16, 32]))
+        w = int(rng.integers(1, b + 1))
+        G = int(rng.choice([1, 2, 4, 8]))
+        H = int(rng.integers(1, 3))
+        n_max = int(rng.integers(2, 25))
+        R = int(rng.integers(2, 5))
+        counts = [n_max + (int(rng.integers(0, 8)) if rng.random() < 0.6 else 0) for _ in range(R)]
+        if max(counts) == n_max:
+            counts[int(rng.integers(0, R))] += 1
+        if G * w > 128 or (G * w > 64 and max(counts) * b > 4096):
+            continue
+        if (max(counts) - n_max + 1) * b > 1024:
+            continue
+        P = int(rng.integers(0, min(n_max - 1, 3) + 1)) if rng.random() < 0.4 else 0
+        nb = P + sum(c - P for c in counts) + R * n_max + 4
+        out.append(dict(num_reqs=R, num_layers=int(rng.integers(1, 3)), num_kv_heads=H,
+                        num_q_heads=H * G, head_dim=int(rng.choice([64, 128])), block_size=b,
+                        n_max=n_max, window=w, num_blocks=nb,
+                        dtype=str(rng.choice(["bf16", "f32"])), shared_prefix_blocks=P,
+                        n_src=counts))
+    return out
+
+
+@pytest.mark.parametrize("i,cfg", list(enumerate(_random_mixed_configs(10, 5151))))
+def test_random_mixed_block_counts_match_oracle(i, cfg):
+    case = synth.make_case(f"mixed{i}", 5200 + i, **cfg)
+    say(f"[gpu parity] random mixed counts {i}: {cfg}")
     run = run_case(case)
     check_case(case, run)
 
@@ -535,7 +587,8 @@ def _fused_equals_standalone(case, want_k_cached):
 
 
 @pytest.mark.parametrize("name", ["bf16_d128_b16_ragged", "bf16_d64_b32_rows128",
-                                  "f32_d128_b32_w5", "over_cap_bf16_3_extra"])
+                                  "f32_d128_b32_w5", "over_cap_bf16_3_extra",
+                                  "mixed_counts_b32_rows128", "mixed_counts_f32_d64"])
 def test_fused_compaction_equals_the_standalone_kernel(name):
     """Without shared blocks the prefix-keeping call makes the same plan as
     the plain one, but runs the selection and the compaction as two kernels
@@ -579,6 +632,9 @@ def test_fused_compaction_streaming_k_equals_the_standalone_kernel():
     ("layers_50_two_launches", False),        # two launches of layer chunks
     ("shared_prefix_2layers", True),          # prefix keeping with device sources
     ("bf16_d128_b16_ragged", True),
+    ("mixed_counts_prefix_2layers", False),   # requests holding different block counts
+    ("mixed_counts_prefix_2layers", True),
+    ("mixed_counts_f32_d64", False),
 ])
 def test_device_tables_equal_the_uploaded_tables(name, keep_prefix):
     """zp_compress_ex with the caller's device copy of the tables: the same

@@ -2,11 +2,12 @@
 
 Long prompts (up to 470 tokens against a budget of 128) are written one
 chunk per step with zp_append_kv (one row per token).  When a chunk carries
-a request past the cap, the request is compressed in the same step with
-zp_compress_n (n_src = the blocks it holds, window = the chunk's last w
-queries); a final chunk that ends inside the window band records its window
-queries in a query slot, and decode records the rest, so the compression at
-the cap then uses rows from both.  Every compression (past the cap after a
+a request past the cap, the request is compressed in the same step
+(window = the chunk's last w queries), in one call with the step's other
+compressions, each request with the block count it holds; a final chunk
+that ends inside the window band records its window queries in a query
+slot, and decode records the rest, so the compression at the cap then uses
+rows from both.  Every compression (past the cap after a
 chunk, and at the cap after decode) is checked against the oracle on the
 cache as it stood, to the parity bar of the other GPU tests, and decode
 steps against the oracle's decode.
@@ -56,7 +57,8 @@ def test_chunked_prefill_through_compression_and_decode():
     lse_store = torch.zeros((S * w, Hq), dtype=torch.float32, device=dev)
     dws = torch.empty(max(max(zp.paged_decode_workspace_bytes(cache, r, n_max) for r in range(1, 5)),
                           16), dtype=torch.uint8, device=dev)
-    stats = dict(chunks=0, chunk_compressions=0, cap_compressions=0, band_rows=0, decode_checks=0)
+    stats = dict(chunks=0, chunk_compressions=0, cap_compressions=0, band_rows=0, decode_checks=0,
+                 mixed_calls=0)
     chunks_per_req = {rid: 0 for rid in prompts}
     n_src_seen = set()
     for step in range(140):
@@ -98,33 +100,38 @@ def test_chunked_prefill_through_compression_and_decode():
             chunks_per_req[rid] += 1
             stats["chunks"] += 1
         torch.cuda.synchronize()
-        # ---- compressions, one call per distinct n_src
+        # ---- compressions: one call over every request the step compresses,
+        # each with its own block count (rows padded with -1)
         news = {}
-        groups = {}
-        for i, rid in enumerate(plan["compress_ids"].tolist()):
-            groups.setdefault(int(plan["compress_n_src"][i]), []).append((rid, int(plan["compress_qslot"][i])))
-        for n_src, members in sorted(groups.items()):
-            ids = [m[0] for m in members]
-            tab, lens = sched.tables(ids, width=n_src)
-            assert np.all(lens == n_src * b) and np.all(tab >= 0)
+        ids = plan["compress_ids"].tolist()
+        if ids:
+            counts = plan["compress_n_src"].astype(np.int32)
+            qslots = plan["compress_qslot"].tolist()
+            width = int(counts.max())
+            tab, lens = sched.tables(ids, width=width)
+            assert np.array_equal(lens, counts * b)
+            for k in range(len(ids)):
+                assert np.all(tab[k, :counts[k]] >= 0) and np.all(tab[k, counts[k]:] == -1)
             wq_h = np.empty((len(ids), w, Hq, d), dtype=np.uint16)
-            for k, (rid, qs) in enumerate(members):
+            for k, (rid, qs) in enumerate(zip(ids, qslots)):
                 if qs >= 0:     # at the cap: the rows recorded in its query slot
                     wq_h[k] = to_numpy(q_store[qs * w:(qs + 1) * w])
                 else:           # right after a chunk: its last w queries
                     assert chunk_wq[rid] is not None
                     wq_h[k] = chunk_wq[rid]
-            case = synth.CompressCase(f"step{step}_n{n_src}", 0, geom, n_max, w, tab.copy(),
+            mixed = int(counts.min()) != width
+            case = synth.CompressCase(f"step{step}", 0, geom, n_max, w, tab.copy(),
                                       pool.refcounts(), [to_numpy(kp)], [to_numpy(vp)], [wq_h],
-                                      [], [], [])
+                                      [], [], [], num_blocks=counts.copy() if mixed else None)
             R_c = len(ids)
-            dbg = dict(importance=torch.full((1, R_c, H, n_src * b), float("nan"), device=dev),
-                       redundancy=torch.full((1, R_c, H, n_src * b), float("nan"), device=dev),
-                       score=torch.full((1, R_c, H, n_src * b), float("nan"), device=dev),
+            dbg = dict(importance=torch.full((1, R_c, H, width * b), float("nan"), device=dev),
+                       redundancy=torch.full((1, R_c, H, width * b), float("nan"), device=dev),
+                       score=torch.full((1, R_c, H, width * b), float("nan"), device=dev),
                        kept=torch.full((1, R_c, H, k_keep), -1, dtype=torch.int32, device=dev))
-            ws = torch.empty(zp.compress_workspace_bytes(cache, R_c, n_max, w, n_src=n_src),
+            ws = torch.empty(zp.compress_workspace_bytes(cache, R_c, n_max, w, n_src=width),
                              dtype=torch.uint8, device=dev)
-            freed = zp.compress(cache, pool, n_max, w, tab, [to_tensor(wq_h, dev)], ws, debug=dbg)
+            freed = zp.compress(cache, pool, n_max, w, tab, [to_tensor(wq_h, dev)], ws, debug=dbg,
+                                num_blocks=counts if mixed else None)
             torch.cuda.synchronize()
             run = GpuRun(tables=tab.copy(), refcounts=pool.refcounts(), freed=freed.copy(),
                          A=dbg["importance"].cpu().numpy(), R=dbg["redundancy"].cpu().numpy(),
@@ -132,14 +139,16 @@ def test_chunked_prefill_through_compression_and_decode():
                          k_pool=[to_numpy(kp)], v_pool=[to_numpy(vp)], out=None,
                          appended_k=None, appended_v=None)
             check_case(case, run, check_decode=False)
+            stats["mixed_calls"] += int(mixed)
             for k, rid in enumerate(ids):
                 news[rid] = tab[k, :n_max].copy()
-            if n_src > n_max:
-                stats["chunk_compressions"] += R_c
-                n_src_seen.add(n_src)
-            else:
-                stats["cap_compressions"] += sum(1 for _, qs in members if qs >= 0)
-                stats["chunk_compressions"] += sum(1 for _, qs in members if qs < 0)
+                if counts[k] > n_max:
+                    stats["chunk_compressions"] += 1
+                    n_src_seen.add(int(counts[k]))
+                elif qslots[k] >= 0:
+                    stats["cap_compressions"] += 1
+                else:
+                    stats["chunk_compressions"] += 1
         if plan["compress_ids"].size:
             sched.compress_commit(np.stack([news[r] for r in plan["compress_ids"].tolist()]))
         pool.sync()
@@ -153,3 +162,4 @@ def test_chunked_prefill_through_compression_and_decode():
     assert len(n_src_seen) >= 2          # compressions past the cap by different amounts
     assert stats["cap_compressions"] >= 2 and stats["band_rows"] > 0
     assert stats["decode_checks"] >= 5
+    assert stats["mixed_calls"] >= 1     # one call over requests holding different counts

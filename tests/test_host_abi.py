@@ -199,7 +199,8 @@ class _FakeTensor:
         self.shape = tuple(shape)
         self.dtype = getattr(torch, dtype_name.split(".")[-1])
         self.device = torch.device("cuda", 0)
-        self._buf = ctypes.create_string_buffer(max(nbytes, 64) + 256)
+        self._nbytes = max(nbytes, 64)
+        self._buf = ctypes.create_string_buffer(self._nbytes + 256)
         self._ptr = (ctypes.addressof(self._buf) + 255) // 256 * 256
 
     def data_ptr(self):
@@ -209,7 +210,7 @@ class _FakeTensor:
         return True
 
     def numel(self):
-        return 64
+        return self._nbytes
 
     def element_size(self):
         return 1
@@ -259,6 +260,43 @@ def test_compress_rejects_bad_arguments_before_any_work():
     mpool = zp.BlockPool(16, manual_fence=True)
     with pytest.raises(zp.ZpError):
         zp.compress(cache, mpool, n_max, 8, tables.copy(), wq, ws, stream=0)
+
+
+def test_compress_rejects_malformed_block_counts_before_any_work():
+    """Requests holding different block counts: each count must lie in
+    [n_max, n_src] and the rest of the row must be -1; otherwise the call
+    fails in planning, with tables and refcounts unchanged."""
+    cache = _fake_cache()
+    n_max, n_src = 8, 11
+    pool = zp.BlockPool(16)
+    ids = pool.alloc(8 + 11 - 8)
+    tables = np.full((2, n_src), -1, dtype=np.int32)
+    tables[0, :8] = ids[:8]          # request 0 at the cap
+    tables[1, :3] = ids[8:]          # request 1 needs 11 -> shares 8 of request 0's ids
+    tables[1, 3:11] = ids[:8]
+    for i in ids[:8]:
+        pool.share([int(i)])
+    rc0 = [pool.refcount(i) for i in range(16)]
+    wq = [_FakeTensor((2, 8, 4, 64), "torch.float32")]
+    need = zp.compress_workspace_bytes(cache, 2, n_max, 8, n_src=n_src)
+    ws = _FakeTensor((need,), "torch.uint8", nbytes=need)
+    bad = {
+        "count below n_max": (np.array([7, 11], np.int32), tables),
+        "count past n_src": (np.array([8, 12], np.int32), tables),
+        "padding not -1": (np.array([8, 11], np.int32),
+                           np.where(np.arange(n_src)[None] == 9, 3, tables).astype(np.int32)),
+        "hole inside the count": (np.array([9, 11], np.int32), tables),
+    }
+    for what, (counts, tab) in bad.items():
+        t = np.ascontiguousarray(tab).copy()
+        with pytest.raises(zp.ZpError) as e:
+            zp.compress(cache, pool, n_max, 8, t, wq, ws, stream=0, num_blocks=counts)
+        assert e.value.status == zp.ZP_ERR_INVALID, (what, str(e.value))
+        np.testing.assert_array_equal(t, tab)
+        assert [pool.refcount(i) for i in range(16)] == rc0, what
+    with pytest.raises(ValueError):       # the binding checks the shape itself
+        zp.compress(cache, pool, n_max, 8, tables.copy(), wq, ws, stream=0,
+                    num_blocks=np.array([8], np.int32))
 
 
 def test_binding_rejects_tensors_the_kernels_cannot_take():
