@@ -37,10 +37,12 @@
  *     ascending slot order.
  *
  * Parity note: every function here is pinned by CPU tests against brute
- * force, closed forms, library routines or invariants, except the choices
- * of combination (s = A(1-R)), aggregation (mean over the group) and LRS
- * reduction (mean cosine), which the pages leave open and which are pinned
- * only by their definitions: parity unpinned for those three choices.
+ * force, closed forms, library routines or invariants, the three readings
+ * above included (combination s = A(1-R), mean over the group, mean
+ * cosine: a hand-worked example with exact rational values, SciPy's softmax,
+ * scikit-learn's cosine).  What no test can pin is that the pages meant
+ * these readings: they print no number for them, so the choices themselves
+ * are fixed here and in the library header, not confirmed.
  */
 #include <math.h>
 #include <stdint.h>
