@@ -194,12 +194,13 @@ def summarize_counters(dirs) -> int:
     return 0
 
 
-def summarize(kt_dir: str, fetch_dir: str, write_dir: str, req_dir: str = None,
+def summarize(kt_dir: str, fetch_dir: str = None, write_dir: str = None, req_dir: str = None,
               dram_dir: str = None) -> int:
     """Summary text of rocprofv3 outputs: kernel-trace statistics of the
     bench run, and bytes per dispatch of each hot-path kernel leaving L2 for
-    the memory fabric, from the FETCH_SIZE / WRITE_SIZE runs scaled by what
-    the same counters read for the calibration copy (1 GiB each way).  With
+    the memory fabric, from the FETCH_SIZE / WRITE_SIZE runs (when given)
+    scaled by what the same counters read for the calibration copy (1 GiB
+    each way).  With
     ``req_dir`` (TCC_EA0_RDREQ, TCC_BUBBLE, TCC_EA0_RDREQ_32B and
     TCC_EA0_RDREQ_128B) the read bytes are also derived from the request
     sizes, which explains the copy's scale factor; with ``dram_dir``
@@ -213,6 +214,8 @@ def summarize(kt_dir: str, fetch_dir: str, write_dir: str, req_dir: str = None,
     for r in stats:
         print(f"{r['Name'][:70]:70s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
               f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f}")
+    if fetch_dir is None or write_dir is None:  # a kernel trace alone
+        return 0
     phases = HOT_PHASES
 
     def per_kernel(d, counter):
@@ -1039,12 +1042,39 @@ def run_mix(args):
     out = torch.empty((Rd, Hq, d), dtype=torch.float32, device=dev)
     scale = 1.0 / float(np.sqrt(d))
     s_c, s_d = torch.cuda.Stream(), torch.cuda.Stream()
+    # Every step compresses the same requests in place.  To keep the steps
+    # alike (as the single-layer step does), each compression is preceded by
+    # a refill of those requests' reserved blocks -- the window, w = b -- with
+    # fresh seeded rows (keys at each layer's per-head scale), the rows the
+    # decode steps before the cap would have appended, and takes the next of
+    # a few window-query sets.  The refill runs on the compression stream and
+    # is counted in its time.
+    n_sets = 8
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1107)
+    slot_c = torch.from_numpy((tables_c[:, k_keep // b, None] * b + np.arange(b)[None, :])
+                              .reshape(-1).astype(np.int32)).to(dev)
+    used_c = torch.from_numpy(tables_c[: min(Rc, 8), : n_max - 1].reshape(-1).astype(np.int64)).to(dev)
+    sig = [kp.index_select(0, used_c).float().transpose(0, 1).reshape(H, -1).std(dim=1)
+           for kp in case.k_pool]
+    fills = [[((torch.randn((Rc * b, H, d), generator=gen, device=dev) * sig[l][None, :, None])
+               .to(case.k_pool[l].dtype),
+               torch.randn((Rc * b, H, d), generator=gen, device=dev).to(case.k_pool[l].dtype))
+              for l in range(L)] for _ in range(n_sets)]
+    wq_sets = [wq] + [[torch.randn(q.shape, generator=gen, device=dev).to(q.dtype) for q in wq]
+                      for _ in range(n_sets - 1)]
+    rot = [0]
     torch.cuda.synchronize()
 
     tab_c_dev = torch.from_numpy(tables_c).to(dev)
 
-    def compress():
-        zp.compress(cache, pool, n_max, w, tables_c, wq, ws, stream=s_c, device_tables=tab_c_dev)
+    def compress(debug=None):
+        k = rot[0] % n_sets
+        rot[0] += 1
+        for l in range(L):
+            zp.append_kv(cache, l, fills[k][l][0], fills[k][l][1], slot_c, stream=s_c)
+        zp.compress(cache, pool, n_max, w, tables_c, wq_sets[k], ws, stream=s_c,
+                    device_tables=tab_c_dev, debug=debug)
 
     def decode():
         for l in range(L):
@@ -1070,25 +1100,38 @@ def run_mix(args):
         decode()
 
     kept = torch.empty((L, Rc, H, k_keep), dtype=torch.int32, device=dev)
-    zp.compress(cache, pool, n_max, w, tables_c, wq, ws, stream=s_c, debug={"kept": kept})
-    torch.cuda.synchronize()
-    moved = int(np.count_nonzero(kept.cpu().numpy() != np.arange(k_keep)[None, None, None, :]))
-    del kept
+    ar = torch.arange(k_keep, dtype=torch.int32, device=dev)
+
+    def moved_rows() -> int:
+        """Rows one compression step moves (from the kept lists), counted
+        right around the event-timed region: what drift the refill leaves
+        shows as the difference of the two counts."""
+        compress(debug={"kept": kept})
+        torch.cuda.synchronize()
+        return int((kept != ar).sum().item())
+
+    moved_first = moved_rows()
     for i in range(args.warmup):
         overlapped(i)
     log(f"timing {args.steps} steps: compression alone, decode alone, overlapped")
     t_c = timed(lambda i: compress(), args.steps)
     t_d = timed(lambda i: decode(), args.steps)
     t_o = timed(overlapped, args.steps)
+    moved_pre = moved_rows()
     zp.profile_enable(True)
     zp.profile_read()
     timed(overlapped, args.steps)
     prof = zp.profile_read()
     zp.profile_enable(False)
+    moved_post = moved_rows()
+    moved = 0.5 * (moved_pre + moved_post)
+    del kept
     assert np.isfinite(out.cpu().numpy()).all()
     dec_tokens = int((ld + 1).sum())
     nsplit = zp.paged_decode_workspace_bytes(cache, Rd, n_max) // (Rd * Hq * (d + 2) * 4)
-    alg, flops = _alg_bytes(Rc, Rd, L, H, Hq, d, b, n_max, w, moved, dec_tokens, nsplit=nsplit)
+    # append launches: the decode's (Rd rows) and the refill's (Rc*b rows), one of each per layer
+    alg, flops = _alg_bytes(Rc, Rd, L, H, Hq, d, b, n_max, w, moved, dec_tokens, nsplit=nsplit,
+                            append_rows=(Rd + Rc * b) / 2)
     kernels = _kernel_rows(prof, alg, flops)
     eff = (t_c + t_d - t_o) / min(t_c, t_d)
     return {
@@ -1106,6 +1149,8 @@ def run_mix(args):
         "decode_tok_s": round(Rd / (t_d * 1e-3), 1),
         "step_decode_tok_s": round(Rd / (t_o * 1e-3), 1),
         "moved_rows_per_step": moved,
+        "moved_rows_before_after": [moved_pre, moved_post],
+        "moved_rows_first": moved_first,
         "kernels_overlapped": kernels,
     }
 
