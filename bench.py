@@ -825,8 +825,9 @@ def run_continuous(args):
     stream 1 the append and the paged decode of every decoding request in all
     36 layers, the decode recording the query and its log-sum-exp into the
     request's query-slot row while it is in its observation window; on
-    stream 2 the compression of the requests at the cap (zp_compress_lse with
-    the recorded window rows), which rejoin decoding in the next step.  The
+    stream 2 the compression of the requests at the cap from the recorded
+    window rows and normalisers, read in place from the query-slot stores
+    (zp_compress_ex with window_slots), which rejoin decoding in the next step.  The
     caches are filled with N(0,1) rows once (a prompt's rows are whatever its
     blocks hold).  Reported: decode tokens and compressions per second of the
     whole run, batch sizes, preemptions and slot waits."""
@@ -929,10 +930,10 @@ def run_continuous(args):
             if R_c:
                 s2.wait_event(ev_dec[1 - par])  # window rows recorded up to step t-1
                 tab_c, _ = sched.tables(plan["compress_ids"])
-                rows = torch.from_numpy(plan["compress_qslot"].astype(np.int64)).to(dev, non_blocking=True)
-                wq = [q_store[l].view(S, w, Hq, d).index_select(0, rows) for l in range(L)]
-                wl = [lse_store[l].view(S, w, Hq).index_select(0, rows) for l in range(L)]
-                zp.compress(cache, pool, n_max, w, tab_c, wq, ws, stream=s2, window_lse=wl)
+                # the window rows are read in place from the query-slot stores
+                slots = torch.from_numpy(plan["compress_qslot"].astype(np.int32)).to(dev, non_blocking=True)
+                zp.compress(cache, pool, n_max, w, tab_c, q_store, ws, stream=s2, window_lse=lse_store,
+                            window_slots=slots)
                 sched.compress_commit(tab_c)
             ev_cmp[par].record(s2)
         # blocks given back by this plan were last read by step t-1

@@ -98,7 +98,8 @@ class _CompressArgs(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_size_t), ("freed_ids", ctypes.POINTER(ctypes.c_int32)),
                 ("num_freed", ctypes.POINTER(ctypes.c_int32)), ("stream", ctypes.c_void_p),
                 ("debug", ctypes.POINTER(_Debug)), ("flags", ctypes.c_uint32),
-                ("num_blocks", ctypes.POINTER(ctypes.c_int32))]
+                ("num_blocks", ctypes.POINTER(ctypes.c_int32)), ("window_slots", ctypes.c_void_p),
+                ("window_store_slots", ctypes.c_int32)]
 
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
@@ -429,7 +430,7 @@ def compress_query(cache: KVCache, num_reqs: int, n_max: int, window: int,
 def compress(cache: KVCache, pool: BlockPool, n_max: int, window: int, tables: np.ndarray,
              window_q: List, workspace, stream=None, debug: Optional[dict] = None,
              window_lse: Optional[List] = None, keep_prefix: bool = False,
-             device_tables=None, num_blocks=None) -> np.ndarray:
+             device_tables=None, num_blocks=None, window_slots=None) -> np.ndarray:
     """zp_compress (zp_compress_lse when ``window_lse``, per-layer float
     tensors [R][w][Hq] of the window rows' normalisers, is given;
     zp_compress_n when ``tables`` has n_src > n_max columns).  ``tables``
@@ -440,7 +441,10 @@ def compress(cache: KVCache, pool: BlockPool, n_max: int, window: int, tables: n
     caller's device copy, so an in-place plan uploads nothing.  ``num_blocks``
     (host int32 [R]): the blocks each request holds, its row padded with -1
     (zp_compress_ex: requests past the cap by different amounts in one
-    call)."""
+    call).  ``window_slots`` (device int32 [R]): zp_compress_ex reading the
+    window rows in place from query-slot stores -- ``window_q[l]`` is then
+    [S*w][Hq][d] and ``window_lse[l]`` [S*w][Hq], request r's rows those of
+    slot window_slots[r]."""
     import torch
     if not (isinstance(tables, np.ndarray) and tables.dtype == np.int32 and tables.ndim == 2
             and tables.flags.c_contiguous):
@@ -451,13 +455,23 @@ def compress(cache: KVCache, pool: BlockPool, n_max: int, window: int, tables: n
     dev = cache.device
     if len(window_q) != L:
         raise ValueError(f"window_q: {len(window_q)} entries for {L} layers")
+    S = 0
+    if window_slots is not None:
+        _want(window_slots, "window_slots", dev, torch.int32, (R,))
+        rows = int(window_q[0].shape[0]) if len(window_q[0].shape) == 3 else -1
+        if rows < window or rows % window:
+            raise ValueError(f"window_q[0]: expected a query-slot store [S*{window}][Hq][d], "
+                             f"got shape {tuple(window_q[0].shape)}")
+        S = rows // window
     for l, t in enumerate(window_q):
-        _want(t, f"window_q[{l}]", dev, cache.torch_dtype, (R, window, Hq, d))
+        _want(t, f"window_q[{l}]", dev, cache.torch_dtype,
+              (S * window, Hq, d) if S else (R, window, Hq, d))
     if window_lse is not None:
         if len(window_lse) != L:
             raise ValueError(f"window_lse: {len(window_lse)} entries for {L} layers")
         for l, t in enumerate(window_lse):
-            _want(t, f"window_lse[{l}]", dev, torch.float32, (R, window, Hq))
+            _want(t, f"window_lse[{l}]", dev, torch.float32,
+                  (S * window, Hq) if S else (R, window, Hq))
     _want(workspace, "workspace", dev, None, None)
     if device_tables is not None:
         _want(device_tables, "device_tables", dev, torch.int32, (R, n_src))
@@ -483,7 +497,7 @@ def compress(cache: KVCache, pool: BlockPool, n_max: int, window: int, tables: n
         nbk = np.ascontiguousarray(num_blocks, dtype=np.int32)
         if nbk.shape != (R,):
             raise ValueError(f"num_blocks: shape {nbk.shape}, expected ({R},)")
-    if device_tables is not None or nbk is not None:
+    if device_tables is not None or nbk is not None or window_slots is not None:
         a = _CompressArgs(n_src, n_max, window, R, _i32(tables),
                           device_tables.data_ptr() if device_tables is not None else None,
                           ctypes.cast(wq, ctypes.POINTER(_vp)),
@@ -492,7 +506,8 @@ def compress(cache: KVCache, pool: BlockPool, n_max: int, window: int, tables: n
                           _i32(freed), _i32(n), _stream_handle(stream),
                           ctypes.pointer(dbg) if dbg else None,
                           ZP_COMPRESS_KEEP_PREFIX if keep_prefix else 0,
-                          _i32(nbk) if nbk is not None else None)
+                          _i32(nbk) if nbk is not None else None,
+                          window_slots.data_ptr() if window_slots is not None else None, S)
         st = lib().zp_compress_ex(cache.ref, pool.handle, ctypes.byref(a))
     elif keep_prefix:
         st = lib().zp_compress_keep_prefix(

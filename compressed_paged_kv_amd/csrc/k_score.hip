@@ -509,6 +509,12 @@ __device__ __forceinline__ void score_unit(const ScoreParams& p) {
   const int rg = wave / WPG, wl = wave - rg * WPG;
   const char* kbase = static_cast<const char*>(p.layers[l - p.layer0].k);
   const char* qbase = static_cast<const char*>(p.layers[l - p.layer0].q);
+  // the request's window rows: its own (r) or those of its query slot
+  int qr = r;
+  if (p.qslot) {
+    qr = p.qslot[r];
+    qr = (unsigned)qr < (unsigned)p.qslots ? qr : 0;
+  }
   // this request's blocks and slots (the call's largest unless rows are ragged)
   const int n_src = unit_blocks(p.src, p.src_stride, r, p.n_src, p.n_max, p.ragged);
   const int T = n_src * B, C = T - p.w, E = T - p.K_keep;
@@ -531,7 +537,7 @@ __device__ __forceinline__ void score_unit(const ScoreParams& p) {
     const int row = rg * RPW + rt * 16 + col;
     if (row < p.rows) {
       const int i = row / p.G, g = row - i * p.G;
-      const char* ptr = qbase + ((size_t)(r * p.w + i) * p.Hq + (size_t)h * p.G + g) * ROWB + grp * 16;
+      const char* ptr = qbase + ((size_t)(qr * p.w + i) * p.Hq + (size_t)h * p.G + g) * ROWB + grp * 16;
 #pragma unroll
       for (int v = 0; v < NV; v++) qf[rt][v] = ld16(ptr + v * 64);
     } else {
@@ -638,7 +644,7 @@ __device__ __forceinline__ void score_unit(const ScoreParams& p) {
       float o = 1.0e30f;  // padding rows: probability 0
       if (tid < p.rows) {
         const int i = tid / p.G, g = tid - i * p.G;
-        const float v = lse[((size_t)r * p.w + i) * p.Hq + (size_t)h * p.G + g];
+        const float v = lse[((size_t)qr * p.w + i) * p.Hq + (size_t)h * p.G + g];
         o = isfinite(v) ? v * 1.4426950408889634f : 1.0e30f;
       }
       s_off[tid] = o;

@@ -79,6 +79,11 @@ struct ScoreParams {
   // strides of evicted and of the debug arrays
   int32_t ragged;
   int32_t num_blocks;       // pool size: ids outside [0, num_blocks) are never followed
+  // window rows from a query-slot store: request r's window position i is row
+  // qslot[r]*w + i of the layer's q (and lse) arrays, a slot outside
+  // [0, qslots) read as slot 0; null: row r*w + i
+  const int32_t* qslot;
+  int32_t qslots;
   int32_t R, H, Hq, G, w, n_src, n_max, T, C, E, K_keep, rows;  // T = n_src * b
   float scale_log2;  // log2(e) / sqrt(d)
 };

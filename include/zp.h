@@ -304,9 +304,23 @@ zp_status zp_compress_n(const zp_kv_cache* cache, zp_block_pool* pool, int32_t n
  *                   (num_blocks[r] - n_max + 1)*b per head.  Debug outputs
  *                   keep the row stride T = n_src*b; slots past a request's
  *                   own T are left as they were.
+ *   window_slots    NULL (window_q[l] is [num_reqs][window][Hq][d] and
+ *                   window_lse[l] [num_reqs][window][Hq]), or DEVICE int32
+ *                   [num_reqs]: the query slot of each request.  window_q[l]
+ *                   and window_lse[l] are then the query-slot stores the
+ *                   decode records into (zp_paged_decode_lse's q_out and
+ *                   lse_out), [window_store_slots*window][Hq][d] and
+ *                   [window_store_slots*window][Hq], and request r's window
+ *                   position i is their row window_slots[r]*window + i --
+ *                   the hybrid scheduler's query slots (nl page Methodologie
+ *                   item 2, ko page section 2.B) read in place, with nothing
+ *                   gathered first.  A slot outside [0, window_store_slots)
+ *                   is read as slot 0 (never outside the store); its
+ *                   request's results are then meaningless.
+ *   window_store_slots  slots in those stores (>= 1 when window_slots is set).
  * Rejects what the named entry points reject, unknown flags, a misaligned
- * device_tables, and num_blocks outside [n_max, n_src] or rows not padded
- * with -1.  Kernels never follow an id outside the pool: a device table that
+ * device_tables or window_slots, window_store_slots < 1 with window_slots,
+ * and num_blocks outside [n_max, n_src] or rows not padded with -1.  Kernels never follow an id outside the pool: a device table that
  * holds one reads that block as block 0 and never writes it.
  * ---------------------------------------------------------------------- */
 #define ZP_COMPRESS_KEEP_PREFIX 1u
@@ -328,6 +342,8 @@ typedef struct zp_compress_args {
   const zp_compress_debug* debug;
   uint32_t flags;
   const int32_t* num_blocks;
+  const int32_t* window_slots;
+  int32_t window_store_slots;
 } zp_compress_args;
 
 zp_status zp_compress_ex(const zp_kv_cache* cache, zp_block_pool* pool,

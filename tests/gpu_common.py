@@ -82,11 +82,14 @@ def window_lse_on_gpu(cache, case, kp_tensors, wq_tensors, device="cuda"):
 
 
 def run_case(case, device="cuda", decode=True, recorded_lse=False, keep_prefix=False,
-             device_tables=False) -> GpuRun:
+             device_tables=False, slot_store=None) -> GpuRun:
     """``recorded_lse``: compress with the window rows' normalisers taken
     from zp_paged_decode_lse (the single-read scoring) instead of the
     self-contained two-pass scoring.  ``device_tables``: zp_compress_ex with
-    a device copy of the tables (no upload when the plan is in place)."""
+    a device copy of the tables (no upload when the plan is in place).
+    ``slot_store`` (a seed): the window rows (and normalisers) sit in
+    query-slot stores of R + 3 slots, request r's at a seeded permuted slot,
+    every other slot NaN, and the call reads them in place (window_slots)."""
     g = case.geom
     L, H, b, n_max, w = g.num_layers, g.num_kv_heads, g.block_size, case.n_max, case.window
     R, n_src = case.num_reqs, case.n_src
@@ -105,9 +108,28 @@ def run_case(case, device="cuda", decode=True, recorded_lse=False, keep_prefix=F
                kept=torch.full((L, R, H, k_keep), -1, dtype=torch.int32, device=device))
     wl = window_lse_on_gpu(cache, case, kp, wq, device) if recorded_lse else None
     dtab = torch.from_numpy(np.ascontiguousarray(case.tables)).to(device) if device_tables else None
+    slots_t = None
+    if slot_store is not None:
+        S = R + 3
+        slots = np.random.default_rng(slot_store).permutation(S)[:R].astype(np.int32)
+        slots_t = torch.from_numpy(slots).to(device)
+        idx = torch.from_numpy(slots.astype(np.int64)).to(device)
+        stores = []
+        for q in wq:
+            st = torch.full((S, w, g.num_q_heads, g.head_dim), float("nan"), device=device).to(q.dtype)
+            st.index_copy_(0, idx, q)
+            stores.append(st.view(S * w, g.num_q_heads, g.head_dim))
+        wq = stores
+        if wl is not None:
+            lstores = []
+            for x in wl:
+                st = torch.full((S, w, g.num_q_heads), float("nan"), dtype=torch.float32, device=device)
+                st.index_copy_(0, idx, x.contiguous())
+                lstores.append(st.view(S * w, g.num_q_heads))
+            wl = lstores
     freed = zp.compress(cache, pool, n_max, w, tables, wq, ws, debug=dbg, window_lse=wl,
                         keep_prefix=keep_prefix, device_tables=dtab,
-                        num_blocks=getattr(case, "num_blocks", None))
+                        num_blocks=getattr(case, "num_blocks", None), window_slots=slots_t)
     torch.cuda.synchronize()
     run = GpuRun(tables=tables.copy(), refcounts=pool.refcounts(), freed=freed.copy(),
                  A=dbg["importance"].cpu().numpy(), R=dbg["redundancy"].cpu().numpy(),

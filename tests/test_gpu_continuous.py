@@ -3,11 +3,12 @@
 A small continuous-batching run: the scheduler plans every step; decode
 appends each request's token and records, while the request is in its
 observation window, its query and log-sum-exp into its query-slot rows;
-requests at the cap are compressed with zp_compress_lse from exactly those
-recorded rows.  Every compression is checked against the oracle run on the
-cache as it stood (the window queries read back from the slots) to the
-parity bar of the other GPU tests, and sampled decode steps against the
-oracle's decode.
+requests at the cap are compressed from exactly those recorded rows and
+normalisers, on alternate calls read in place from the query-slot stores
+(window_slots) or gathered per request first.  Every compression is
+checked against the oracle run on the cache as it stood (the window queries
+read back from the slots) to the parity bar of the other GPU tests, and
+sampled decode steps against the oracle's decode.
 """
 import numpy as np
 import pytest
@@ -57,7 +58,7 @@ def test_scheduler_driven_run_matches_oracle(w, nb):
                      device=dev)
     dws = torch.empty(max(max(zp.paged_decode_workspace_bytes(cache, r, n_max)
                               for r in range(1, 7)), 16), dtype=torch.uint8, device=dev)
-    n_compressions = n_decode_checks = 0
+    n_compressions = n_decode_checks = n_in_place = n_calls = 0
     for step in range(160):
         plan = sched.plan()
         n_preempted += plan["preempted"].size
@@ -76,7 +77,14 @@ def test_scheduler_driven_run_matches_oracle(w, nb):
                        redundancy=torch.full((1, R_c, H, T), float("nan"), device=dev),
                        score=torch.full((1, R_c, H, T), float("nan"), device=dev),
                        kept=torch.full((1, R_c, H, k_keep), -1, dtype=torch.int32, device=dev))
-            freed = zp.compress(cache, pool, n_max, w, tab, [wq], ws, debug=dbg, window_lse=[wl])
+            if n_calls % 2:   # the window rows gathered per request
+                freed = zp.compress(cache, pool, n_max, w, tab, [wq], ws, debug=dbg, window_lse=[wl])
+            else:          # read in place from the query-slot stores
+                slots = torch.from_numpy(plan["compress_qslot"].astype(np.int32)).to(dev)
+                freed = zp.compress(cache, pool, n_max, w, tab, [q_store], ws, debug=dbg,
+                                    window_lse=[lse_store], window_slots=slots)
+                n_in_place += 1
+            n_calls += 1
             torch.cuda.synchronize()
             run = GpuRun(tables=tab.copy(), refcounts=pool.refcounts(), freed=freed.copy(),
                          A=dbg["importance"].cpu().numpy(), R=dbg["redundancy"].cpu().numpy(),
@@ -111,5 +119,5 @@ def test_scheduler_driven_run_matches_oracle(w, nb):
         pool.fence()
     say(f"[gpu continuous] w={w}, pool {nb}: {n_compressions} compressions and "
         f"{n_decode_checks} decode steps matched the oracle, {n_preempted} preemptions")
-    assert n_compressions >= 3 and n_decode_checks >= 10
+    assert n_compressions >= 3 and n_decode_checks >= 10 and n_in_place >= 1
     assert (n_preempted > 0) == (nb < 30)

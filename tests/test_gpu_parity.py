@@ -767,3 +767,35 @@ def test_decode_bfloat16_output_is_the_rounded_float32_output(dtype, d, b, G, R,
     got = o16.cpu().view(torch.int16).numpy().view(np.uint16)
     np.testing.assert_array_equal(got, want)
     np.testing.assert_array_equal(l16.cpu().numpy().view(np.uint32), l32.cpu().numpy().view(np.uint32))
+
+
+@pytest.mark.parametrize("name,recorded,keep_prefix", [
+    ("bf16_d128_b16_ragged", False, False),
+    ("bf16_d64_b32_rows128", False, False),   # two row groups
+    ("shared_prefix_2layers", False, False),  # re-targets
+    ("shared_prefix_2layers", False, True),   # prefix keeping: the selection kernel alone
+    ("over_cap_bf16_3_extra", True, False),   # recorded normalisers, past the cap
+    ("mixed_counts_prefix_2layers", True, False),
+    ("f32_d128_b32_w5", True, False),
+])
+def test_window_rows_read_in_place_from_query_slots(name, recorded, keep_prefix):
+    """zp_compress_ex with window_slots: the window rows (and recorded
+    normalisers) read in place from query-slot stores, each request at a
+    permuted slot and every other slot NaN, give bit for bit the results of
+    the call that takes them gathered per request, and the oracle's."""
+    case = CASES[name]()
+    say(f"[gpu parity] window rows from query slots: {name}, recorded={recorded}, "
+        f"keep_prefix={keep_prefix}")
+    ref = run_case(case, recorded_lse=recorded, keep_prefix=keep_prefix)
+    got = run_case(case, recorded_lse=recorded, keep_prefix=keep_prefix, slot_store=77)
+    np.testing.assert_array_equal(ref.tables, got.tables)
+    np.testing.assert_array_equal(ref.refcounts, got.refcounts)
+    np.testing.assert_array_equal(ref.kept, got.kept)
+    for a, b in ((ref.A, got.A), (ref.R, got.R), (ref.s, got.s)):
+        np.testing.assert_array_equal(a.view(np.uint32), b.view(np.uint32))
+    for a, b in zip(ref.appended_k + ref.appended_v, got.appended_k + got.appended_v):
+        assert np.array_equal(np.ascontiguousarray(a).view(np.uint8),
+                              np.ascontiguousarray(b).view(np.uint8))
+    np.testing.assert_array_equal(ref.out.view(np.uint32), got.out.view(np.uint32))
+    check_case(case, got, keep_prefix=keep_prefix)
+

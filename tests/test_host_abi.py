@@ -299,6 +299,39 @@ def test_compress_rejects_malformed_block_counts_before_any_work():
                     num_blocks=np.array([8], np.int32))
 
 
+def test_compress_rejects_a_query_slot_store_without_slots():
+    """window_slots needs window_store_slots >= 1 and 4-byte alignment; the
+    binding needs the stores shaped [S*w][Hq][d] (and [S*w][Hq])."""
+    import torch
+    cache = _fake_cache()
+    n_max = 8
+    pool = zp.BlockPool(16)
+    tables = np.arange(8, dtype=np.int32)[None].copy()
+    pool.alloc(8)
+    need = zp.compress_workspace_bytes(cache, 1, n_max, 8)
+    ws = _FakeTensor((need,), "torch.uint8", nbytes=need)
+    store = [_FakeTensor((3 * 8, 4, 64), "torch.float32")]
+    slots = _FakeTensor((1,), "torch.int32")
+    lib = zp.lib()
+    wq = (ctypes.c_void_p * 1)(store[0].data_ptr())
+    freed = np.zeros(8, dtype=np.int32)
+    n = np.zeros(1, dtype=np.int32)
+    i32 = ctypes.POINTER(ctypes.c_int32)
+    for ptr, count in ((slots.data_ptr(), 0), (slots.data_ptr() + 2, 3)):
+        t = tables.copy()
+        a = zp._binding._CompressArgs(8, n_max, 8, 1, t.ctypes.data_as(i32), None,
+                                      ctypes.cast(wq, ctypes.POINTER(ctypes.c_void_p)), None,
+                                      ws.data_ptr(), need, freed.ctypes.data_as(i32),
+                                      n.ctypes.data_as(i32), None, None, 0, None, ptr, count)
+        assert lib.zp_compress_ex(cache.ref, pool.handle, ctypes.byref(a)) == zp.ZP_ERR_INVALID
+        assert "window_slots" in zp.last_error()
+        np.testing.assert_array_equal(t, tables)
+    with pytest.raises(ValueError):       # a dense [R][w][Hq][d] array is not a store
+        zp.compress(cache, pool, n_max, 8, tables.copy(), [_FakeTensor((1, 8, 4, 64), "torch.float32")],
+                    ws, stream=0, window_slots=slots)
+    assert [pool.refcount(i) for i in range(8)] == [1] * 8
+
+
 def test_binding_rejects_tensors_the_kernels_cannot_take():
     """The binding checks device, element type, contiguity and shape of every
     tensor before a pointer reaches the library (the C layer sees only
