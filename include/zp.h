@@ -691,6 +691,8 @@ int32_t zp_prefix_size(const zp_prefix_index* index);  /* listed entries */
  *                      (one host synchronisation with the call's stream) and
  *                      returns ZP_ERR_INVALID, changing nothing, when it
  *                      differs from block_tables.
+ * POISON fills with memset nodes and VALIDATE synchronises the host: keep
+ * both off for calls made under HIP graph capture.
  * ---------------------------------------------------------------------- */
 #define ZP_DEBUG_TRACE 1u
 #define ZP_DEBUG_POISON 2u
