@@ -286,9 +286,10 @@ zp_status zp_compress_n(const zp_kv_cache* cache, zp_block_pool* pool, int32_t n
  *                   stream, debug (may be NULL): as zp_compress_n.
  *   device_tables   NULL, or DEVICE int32 [num_reqs][n_src] (row stride
  *                   n_src, 4-byte aligned) holding the same ids as
- *                   block_tables at the call.  The library cannot compare
- *                   the two: a copy that differs gives wrong results (every
- *                   id is read as a block of the pool).  Not written; after
+ *                   block_tables at the call.  The library compares the
+ *                   two only under ZP_DEBUG_VALIDATE: a copy that differs
+ *                   gives wrong results (every id is still read as a block
+ *                   of the pool).  Not written; after
  *                   a plan that re-targets blocks the caller refreshes it
  *                   from the rewritten host tables.
  *   flags           0, or ZP_COMPRESS_KEEP_PREFIX (zp_compress_keep_prefix).
