@@ -483,6 +483,27 @@ def cold_decode_us(cache, q, tab_t, seq_t, scale, out, dws, reps: int = 10) -> f
     return float(np.median(times))
 
 
+def phase_summary(t, khz: int) -> dict:
+    """Per-unit phase durations (µs) of one compression call from the
+    stamps of zp_compress_debug.phase_times ([units][5], device wall clock
+    at ``khz``): pass 1 (softmax statistics), pass 2 (scores), selection and
+    compaction, plus the call's span and how far apart the units started."""
+    import numpy as np
+    if khz <= 0 or t.size == 0:
+        return None
+    us = (t - t[:, 0].min()) * (1e3 / khz)
+    d = np.diff(us, axis=1)
+    out = {"what": "per (layer, request, head) workgroup: durations of its phases in one call, "
+                   "from wall-clock stamps at the phase boundaries (debug phase_times)",
+           "units": int(t.shape[0]), "span_us": round(float(us[:, 4].max()), 1),
+           "start_spread_us": round(float(us[:, 0].max()), 1)}
+    for k, name in enumerate(("pass1_us", "pass2_us", "select_us", "compact_us")):
+        x = d[:, k]
+        out[name] = {"mean": round(float(x.mean()), 1), "p10": round(float(np.percentile(x, 10)), 1),
+                     "p90": round(float(np.percentile(x, 90)), 1), "max": round(float(x.max()), 1)}
+    return out
+
+
 def window_query_sets(first, n: int, seed: int, dev) -> list:
     """Window queries for successive steps: the workload's own set, then
     seeded N(0,1) sets (bf16) drawn on the device.  Every step compresses the
@@ -681,6 +702,15 @@ def run_single_stream(args, workload, cache, pool, tables, wq_sets, q_new, k_new
         rec = recorded_lse_compress(args.steps, cache, pool, tables, next_wq, n_max, w, R, Hq, d,
                                     dev, ws, dws, step)
     moved_after = moved_rows()
+    # where the fused kernel's time goes: one more step with every unit's
+    # phase boundaries stamped on the device wall clock
+    phases = None
+    if not args.headline_only:
+        stamps = torch.zeros((1, R, H, 5), dtype=torch.int64, device=dev)
+        step(0, debug={"phase_times": stamps})
+        torch.cuda.synchronize()
+        khz = zp.compress_query(cache, R, n_max, w)["wall_clock_khz"]
+        phases = phase_summary(stamps.cpu().numpy().reshape(-1, 5), khz)
     assert tables.tolist() == tables0.tolist(), "in-place compression changed the tables"
     assert np.isfinite(out.cpu().numpy()).all()
 
@@ -786,6 +816,7 @@ def run_single_stream(args, workload, cache, pool, tables, wq_sets, q_new, k_new
     rec_us = {k["phase"]: k["avg_us"] for k in _kernel_rows(rec, alg, flops)}
     rec_comp = sum(rec_us.get(p, 0.0) for p in COMPRESS_PHASES)
     rec_bytes = sum(alg[p] for p in COMPRESS_PHASES if p in rec_us)
+    result["fused_kernel_phases"] = phases
     result["recorded_lse"] = {
         "what": "compression with the window rows' softmax normalisers recorded by the decode "
                 "steps that produced the window queries (zp_compress_lse): the scoring reads K "

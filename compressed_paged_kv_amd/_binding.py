@@ -69,12 +69,13 @@ class _SchedStep(ctypes.Structure):
 class _CompressInfo(ctypes.Structure):
     _fields_ = [("units", ctypes.c_int32), ("threads", ctypes.c_int32),
                 ("resident_per_cu", ctypes.c_int32), ("compute_units", ctypes.c_int32),
-                ("k_cached", ctypes.c_int32)]
+                ("k_cached", ctypes.c_int32), ("wall_clock_khz", ctypes.c_int32)]
 
 
 class _Debug(ctypes.Structure):
     _fields_ = [("importance", ctypes.c_void_p), ("redundancy", ctypes.c_void_p),
-                ("score", ctypes.c_void_p), ("kept", ctypes.c_void_p)]
+                ("score", ctypes.c_void_p), ("kept", ctypes.c_void_p),
+                ("phase_times", ctypes.c_void_p)]
 
 
 ZP_COMPRESS_KEEP_PREFIX = 1
@@ -482,6 +483,8 @@ def compress(cache: KVCache, pool: BlockPool, n_max: int, window: int, tables: n
                 _want(debug[key], f"debug[{key!r}]", dev, torch.float32, (L, R, H, T))
         if debug.get("kept") is not None:
             _want(debug["kept"], "debug['kept']", dev, torch.int32, (L, R, H, k_keep))
+        if debug.get("phase_times") is not None:
+            _want(debug["phase_times"], "debug['phase_times']", dev, torch.int64, (L, R, H, 5))
     wq = (_vp * cache.num_layers)(*[t.data_ptr() for t in window_q])
     wl = None
     if window_lse is not None:
@@ -491,7 +494,8 @@ def compress(cache: KVCache, pool: BlockPool, n_max: int, window: int, tables: n
     dbg = None
     if debug:
         dbg = _Debug(_dptr(debug.get("importance")), _dptr(debug.get("redundancy")),
-                     _dptr(debug.get("score")), _dptr(debug.get("kept")))
+                     _dptr(debug.get("score")), _dptr(debug.get("kept")),
+                     _dptr(debug.get("phase_times")))
     nbk = None
     if num_blocks is not None:
         nbk = np.ascontiguousarray(num_blocks, dtype=np.int32)

@@ -633,6 +633,12 @@ __device__ __forceinline__ void score_unit(const ScoreParams& p) {
     }
   };
 
+  // phase boundaries on the device wall clock (debug only; thread 0)
+  int64_t* const times = p.dbg_times ? p.dbg_times + unit * 5 : nullptr;
+  auto stamp = [&](int k) {
+    if (times && threadIdx.x == 0) times[k] = (int64_t)wall_clock64();
+  };
+  stamp(0);
   // ---------------------------------------------------------------- pass 1
   // Skipped when the caller supplies the normalisers of the window rows
   // (the log-sum-exp the decode steps of those rows computed over the same
@@ -731,6 +737,7 @@ __device__ __forceinline__ void score_unit(const ScoreParams& p) {
 #pragma unroll
     for (int i = 0; i < 4; i++) off[rt][i] = s_off[rg * RPW + rt * 16 + 4 * grp + i];
 
+  stamp(1);
   // ---------------------------------------------------------------- pass 2
   const float inv_rows = 1.0f / (float)p.rows;
   const float inv_bm1 = 1.0f / (float)(B - 1);
@@ -854,18 +861,24 @@ __device__ __forceinline__ void score_unit(const ScoreParams& p) {
     __syncthreads();
   }
 
+  stamp(2);
   // ---------------------------------------------------------------- select
   const int per = (T + kThreads - 1) / kThreads;
   int* s_f = FUSE ? reinterpret_cast<int*>(s_buf) : nullptr;  // the scores are in registers by then
   if (per <= 8) select_evicted<8, kWaves>(s_sc, s_sel, s_scr, p, unit, s_f, T, C, E);
   else if (per <= 16) select_evicted<16, kWaves>(s_sc, s_sel, s_scr, p, unit, s_f, T, C, E);
   else select_evicted<32, kWaves>(s_sc, s_sel, s_scr, p, unit, s_f, T, C, E);
+  stamp(3);
   if constexpr (FUSE) {
     __shared__ int s_first;
     if (p.k_cached)  // uniform: one tile loop or the other, each straight-line
       compact_unit<ROWB / 16, B, kThreads, kFusedUnroll, true>(p, s_buf, &s_first, l, r, h, n_src, E);
     else
       compact_unit<ROWB / 16, B, kThreads, kFusedUnroll, false>(p, s_buf, &s_first, l, r, h, n_src, E);
+  }
+  if (times) {
+    __syncthreads();  // every wave done (uniform: the pointer is a kernel argument)
+    stamp(4);
   }
 }
 

@@ -72,6 +72,7 @@ struct ScoreParams {
   float* dbg_redundancy;    // optional [L*R*H][T]
   float* dbg_score;         // optional [L*R*H][T]
   int32_t* dbg_kept;        // optional [L*R*H][K_keep]
+  int64_t* dbg_times;       // optional [L*R*H][5]: wall clock at the phase boundaries
   const int32_t* dst;       // device, row r at dst + r*dst_stride: the n_max-1 target blocks; compact in the same kernel; null: select only
   int32_t k_cached;         // fused compaction: load K normally (1) or non-temporally (0)
   // ragged: request r holds the blocks of its source row up to its first -1

@@ -169,6 +169,13 @@ typedef struct zp_compress_debug {
   float* redundancy;  /* [L][R][H][T]: Lightning Redundancy Score R */
   float* score;       /* [L][R][H][T]: s = A*(1-R); slots >= T-w are not scored */
   int32_t* kept;      /* [L][R][H][K_keep]: surviving old slots, ascending */
+  /* [L][R][H][5]: the device wall clock (zp_compress_info.wall_clock_khz)
+   * read by each (layer, request, head) workgroup at its start, after the
+   * softmax statistics (pass 1; right after the start when the
+   * normalisers are supplied), after the scores (pass 2), after the selection, and at
+   * its end (after its compaction when the same kernel compacts) -- where
+   * the time of a compression goes, unit by unit. */
+  int64_t* phase_times;
 } zp_compress_debug;
 
 /* Device workspace (caller-owned) needed by zp_compress / zp_compress_lse,
@@ -362,6 +369,7 @@ typedef struct zp_compress_info {
   int32_t resident_per_cu;  /* such workgroups one compute unit holds at once */
   int32_t compute_units;    /* of the current device */
   int32_t k_cached;         /* 1: K loaded normally by the compaction; 0: streamed */
+  int32_t wall_clock_khz;   /* rate of the clock in zp_compress_debug.phase_times */
 } zp_compress_info;
 
 /* Rejects (ZP_ERR_INVALID) the shapes zp_compress_n rejects; ZP_ERR_HIP

@@ -50,6 +50,7 @@ class GpuRun:
     out: np.ndarray      # decode output [L][R][Hq][d]
     appended_k: list     # host pools after the append (for the decode check)
     appended_v: list
+    times: np.ndarray = None  # [L][R][H][5] phase wall-clock stamps, when asked for
 
 
 def window_lse_on_gpu(cache, case, kp_tensors, wq_tensors, device="cuda"):
@@ -82,7 +83,7 @@ def window_lse_on_gpu(cache, case, kp_tensors, wq_tensors, device="cuda"):
 
 
 def run_case(case, device="cuda", decode=True, recorded_lse=False, keep_prefix=False,
-             device_tables=False, slot_store=None) -> GpuRun:
+             device_tables=False, slot_store=None, phase_times=False) -> GpuRun:
     """``recorded_lse``: compress with the window rows' normalisers taken
     from zp_paged_decode_lse (the single-read scoring) instead of the
     self-contained two-pass scoring.  ``device_tables``: zp_compress_ex with
@@ -106,6 +107,8 @@ def run_case(case, device="cuda", decode=True, recorded_lse=False, keep_prefix=F
                redundancy=torch.full((L, R, H, T), float("nan"), device=device),
                score=torch.full((L, R, H, T), float("nan"), device=device),
                kept=torch.full((L, R, H, k_keep), -1, dtype=torch.int32, device=device))
+    if phase_times:
+        dbg["phase_times"] = torch.zeros((L, R, H, 5), dtype=torch.int64, device=device)
     wl = window_lse_on_gpu(cache, case, kp, wq, device) if recorded_lse else None
     dtab = torch.from_numpy(np.ascontiguousarray(case.tables)).to(device) if device_tables else None
     slots_t = None
@@ -135,7 +138,8 @@ def run_case(case, device="cuda", decode=True, recorded_lse=False, keep_prefix=F
                  A=dbg["importance"].cpu().numpy(), R=dbg["redundancy"].cpu().numpy(),
                  s=dbg["score"].cpu().numpy(), kept=dbg["kept"].cpu().numpy(),
                  k_pool=[to_numpy(t) for t in kp], v_pool=[to_numpy(t) for t in vp],
-                 out=None, appended_k=None, appended_v=None)
+                 out=None, appended_k=None, appended_v=None,
+                 times=dbg["phase_times"].cpu().numpy() if phase_times else None)
     if decode:
         # poison the reserved blocks' slots past the one about to be appended:
         # a decode that strayed past the length would turn its output NaN

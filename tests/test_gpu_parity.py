@@ -799,3 +799,40 @@ def test_window_rows_read_in_place_from_query_slots(name, recorded, keep_prefix)
     np.testing.assert_array_equal(ref.out.view(np.uint32), got.out.view(np.uint32))
     check_case(case, got, keep_prefix=keep_prefix)
 
+
+@pytest.mark.parametrize("name,keep_prefix,recorded", [
+    ("bf16_d128_b16_ragged", False, False),   # fused: start, pass 1, pass 2, selection, compaction
+    ("bf16_d64_b32_rows128", False, True),    # two row groups, recorded normalisers (no pass 1)
+    ("shared_prefix_2layers", True, False),   # the selection-only kernel
+])
+def test_phase_times_are_stamped_in_order_and_change_nothing(name, keep_prefix, recorded):
+    """debug phase_times: every unit's five wall-clock stamps are set and
+    non-decreasing, within the call, and asking for them leaves every other
+    result bit-identical."""
+    import compressed_paged_kv_amd as zp
+    case = CASES[name]()
+    say(f"[gpu parity] phase times: {name}, keep_prefix={keep_prefix}, recorded={recorded}")
+    ref = run_case(case, decode=False, keep_prefix=keep_prefix, recorded_lse=recorded)
+    got = run_case(case, decode=False, keep_prefix=keep_prefix, recorded_lse=recorded,
+                   phase_times=True)
+    np.testing.assert_array_equal(ref.tables, got.tables)
+    np.testing.assert_array_equal(ref.kept, got.kept)
+    for a, b in zip(ref.k_pool + ref.v_pool, got.k_pool + got.v_pool):
+        assert np.array_equal(np.ascontiguousarray(a).view(np.uint8),
+                              np.ascontiguousarray(b).view(np.uint8))
+    for a, b in ((ref.A, got.A), (ref.R, got.R), (ref.s, got.s)):
+        np.testing.assert_array_equal(a.view(np.uint32), b.view(np.uint32))
+    t = got.times.reshape(-1, 5)
+    assert (t > 0).all(), "a unit left a stamp unset"
+    assert (np.diff(t, axis=1) >= 0).all(), "stamps out of order"
+    from synth.device import to_tensor
+    g = case.geom
+    cache = zp.KVCache([to_tensor(case.k_pool[0], "cuda")] * g.num_layers,
+                       [to_tensor(case.v_pool[0], "cuda")] * g.num_layers, g.num_q_heads)
+    khz = zp.compress_query(cache, case.num_reqs, case.n_max, case.window,
+                            n_src=case.n_src)["wall_clock_khz"]
+    assert khz > 0
+    span_ms = (t[:, 4].max() - t[:, 0].min()) / khz
+    say(f"[gpu parity]   clock {khz} kHz, span {span_ms * 1e3:.1f} us")
+    assert span_ms < 1000.0
+
