@@ -15,17 +15,25 @@
 // Phases, all inside the workgroup:
 //   1. softmax statistics: each wave runs over its share of the unit's
 //      blocks keeping, per window row, a running (max, sum of 2^(x - max))
-//      that is rescaled only when the max grows by more than 64 (log2 units); lanes and
-//      waves are then merged in LDS into one exponent offset per row,
-//      M + log2(Z), so a probability is a single 2^(x - offset);
-//   2. the same blocks again (now in cache): probabilities summed over the
+//      that is rescaled only when the max grows by more than 64 (log2
+//      units); lanes and waves are then merged in LDS into one exponent
+//      offset per row, M + log2(Z), so a probability is a single
+//      2^(x - offset)
+//      (skipped when the caller supplies each window row's log-sum-exp);
+//   2. the same blocks again, in reverse order so the first ones are those
+//      pass 1 read last, still in cache: probabilities summed over the
 //      rows in a fixed order (so equal inputs give bit-equal importances),
 //      the in-block Gram matrix for the cosines, and s into LDS;
 //   3. the selection (select_evicted): radix passes over order-preserving
 //      32-bit keys, starting below the prefix all keys share, narrow the bin
 //      of the E-th smallest score; a small bin is ranked exactly, a large
 //      bin of equal keys gives up its highest slots; one prefix sum in slot
-//      order places the ascending evicted list.
+//      order places the ascending evicted list;
+//   4. (k_score_compact) the in-place compaction of the unit's K and V
+//      rows (compact_unit).
+// A request may hold more blocks than the cap, its own number when table
+// rows are padded with -1; its window rows are its own or, with query
+// slots, those of its slot in the decode's query store.
 // The rows x b logit tiles and the b x b Gram tiles are 16x16 MFMA tiles:
 // v_mfma_f32_16x16x32_bf16 for bfloat16 caches, v_mfma_f32_16x16x4f32 for
 // float32 ones.  A lane holds operand row (lane % 16) and a 16-byte slice of
