@@ -836,3 +836,30 @@ def test_phase_times_are_stamped_in_order_and_change_nothing(name, keep_prefix, 
     say(f"[gpu parity]   clock {khz} kHz, span {span_ms * 1e3:.1f} us")
     assert span_ms < 1000.0
 
+
+def _random_feature_configs(n, seed):
+    """Seeded shapes (uniform or mixed block counts, optional shared prefix)
+    each with a seeded choice of the call's options."""
+    rng = np.random.default_rng(seed)
+    out = []
+    shapes = _random_mixed_configs(n, seed + 1) + _random_configs(n, seed + 2)
+    for i in range(n):
+        cfg = dict(shapes[rng.integers(0, len(shapes))])
+        opts = dict(recorded_lse=bool(rng.random() < 0.5), keep_prefix=bool(rng.random() < 0.3),
+                    device_tables=bool(rng.random() < 0.5),
+                    slot_store=int(rng.integers(1, 1000)) if rng.random() < 0.5 else None)
+        out.append((cfg, opts))
+    return out
+
+
+@pytest.mark.parametrize("i,cfg,opts", [(i, c, o) for i, (c, o) in
+                                         enumerate(_random_feature_configs(16, 6161))])
+def test_random_feature_combinations_match_oracle(i, cfg, opts):
+    """Random shapes with a random mix of the call's options (per-request
+    block counts, device tables, prefix keeping, recorded normalisers, window
+    rows read in place from query slots), each against the oracle."""
+    case = synth.make_case(f"combo{i}", 5400 + i, **cfg)
+    say(f"[gpu parity] feature combination {i}: {cfg} {opts}")
+    run = run_case(case, **opts)
+    check_case(case, run, keep_prefix=opts["keep_prefix"])
+
