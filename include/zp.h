@@ -33,8 +33,11 @@
  *                             of a request lives in block table[j / b] at
  *                             offset j % b.
  *   window queries .......... [R][w][Hq][d] per layer, the queries of the
- *                             last w cached slots (the "query slots").
- *   decode query ............ [R][Hq][d]; output float32 [R][Hq][d].
+ *                             last w cached slots, or a query-slot store
+ *                             [S*w][Hq][d] the decode records into, read in
+ *                             place (zp_compress_ex, window_slots).
+ *   decode query ............ [R][Hq][d]; output float32 [R][Hq][d]
+ *                             (bfloat16 through zp_paged_decode_ex).
  * Query head hq belongs to KV head hq / G with G = Hq / H (grouped queries).
  * Element type: float32 or bfloat16 for caches and queries alike.
  */
