@@ -1053,6 +1053,9 @@ def run_mix(args):
     lens = case.seq_lens
     comp = np.nonzero(lens == n_max * b)[0]
     dec = np.nonzero(lens < n_max * b)[0]
+    # the decoding requests longest first, as the scheduler lists them (a
+    # ragged batch finishes sooner when its long requests start first)
+    dec = dec[np.argsort(-lens[dec], kind="stable")]
     Rc, Rd = len(comp), len(dec)
     cache = zp.KVCache(case.k_pool, case.v_pool, Hq)
     pool = zp.BlockPool.from_refcounts(case.refcounts)

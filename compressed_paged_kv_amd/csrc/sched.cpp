@@ -467,6 +467,24 @@ zp_status zp_sched_plan(zp_sched* s, zp_sched_step* out) {
     s->compress_qslot.push_back(s->reqs[id].qslot);
     s->compress_n_src.push_back(s->reqs[id].compress_n_src);
   }
+  // decodes longest first: the paged decode dispatches its workgroups in
+  // request order, and a ragged batch finishes sooner when its long requests
+  // start first (equal lengths keep their order)
+  {
+    const size_t nd = s->decode_ids.size();
+    std::vector<size_t> order(nd);
+    for (size_t i = 0; i < nd; i++) order[i] = i;
+    std::stable_sort(order.begin(), order.end(),
+                     [&](size_t a, size_t c) { return s->decode_seq[a] > s->decode_seq[c]; });
+    auto permute = [&](auto& v) {
+      auto old = v;
+      for (size_t i = 0; i < nd; i++) v[i] = old[order[i]];
+    };
+    permute(s->decode_ids);
+    permute(s->decode_slot);
+    permute(s->decode_seq);
+    permute(s->decode_row);
+  }
   zp::add_pending(s->pool, s->to_release, nullptr);
   s->step++;
 

@@ -589,7 +589,10 @@ typedef struct zp_sched_step {
   int32_t num_admitted;  /* admitted this step: whole prompt in the request's blocks, or
                             (chunked prefill) its first chunk, listed with the prefills */
   const int64_t* admitted;
-  int32_t num_decode;    /* decode one token each */
+  int32_t num_decode;    /* decode one token each, listed longest first: the
+                            paged decode starts its workgroups in request
+                            order, and a ragged batch finishes sooner when its
+                            long requests start first */
   const int64_t* decode_ids;
   const int32_t* decode_slot;        /* physical slot (block*b + offset) of the new token */
   const int32_t* decode_seq_len;     /* length including the new token */
@@ -599,7 +602,7 @@ typedef struct zp_sched_step {
   const int32_t* compress_qslot;     /* their query slots, rows slot*w .. slot*w + w-1; -1 after
                                         a prefill chunk (window = the chunk's last w queries) */
   const int32_t* compress_n_src;     /* blocks each holds: N_max at the cap, more after a chunk
-                                        (zp_compress_n; one call per distinct value) */
+                                        (one zp_compress_ex call with these as num_blocks) */
   int32_t num_prefill;   /* prefill chunks of this step (after the decodes, before the
                             compressions of the requests that wrote them) */
   const int64_t* prefill_ids;

@@ -175,6 +175,13 @@ def test_random_workload_invariants_and_completion(seed):
                 nb = int((tab[i] >= 0).sum())
                 assert nb <= n_max
                 assert nb in ((lens[i] + b - 1) // b, n_max)
+        # decodes listed longest first, each entry's slot the token's place in its table
+        assert np.all(np.diff(p["decode_seq_len"]) <= 0)
+        if p["decode_ids"].size:
+            tab_d, _ = s.tables(p["decode_ids"], width=n_max)
+            pos = p["decode_seq_len"] - 1
+            want = tab_d[np.arange(len(pos)), pos // b] * b + pos % b
+            np.testing.assert_array_equal(p["decode_slot"], want)
         # query-slot rows: recorded in window order, exactly w before compression
         for r, row, seq in zip(p["decode_ids"].tolist(), p["decode_record_row"].tolist(),
                                p["decode_seq_len"].tolist()):
