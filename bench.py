@@ -733,6 +733,8 @@ def run_single_stream(args, workload, cache, pool, tables, wq_sets, q_new, k_new
     roofline = {"bound": "hbm", "kernel": dom["phase"], "achieved": dom["alg_GBs"],
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dom["hbm_frac"],
                 "traffic": traffic,
+                # the counters' bytes over the same HIP-event kernel time (L2 egress rate)
+                "traffic_GBs": round(traffic / (dom["avg_us"] * 1e-6) / 1e9, 1) if traffic else None,
                 # requests bound for DRAM (memory-side cache hits included)
                 "traffic_dram": read_counters(dom["phase"], workload, "dram"),
                 # the same achieved rate against the best plain copy of this GPU
