@@ -7,7 +7,6 @@ import subprocess
 import sys
 
 import numpy as np
-import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
@@ -40,7 +39,7 @@ def test_algorithmic_bytes_past_the_cap():
     assert alg["score"] == 64 * 8 * (T * 256 + 16 * 4 * 256 + 528 * 4)
 
 
-def _profile(tmp_path, kernel_src_sha, what="fetch"):
+def _profile(tmp_path, kernel_src_sha):
     text = ("# header\n"
             f"phase score_compact: fetch_bytes=1000 write_bytes=500 source_sha={kernel_src_sha} "
             "(raw ...)\n"
