@@ -12,11 +12,12 @@
 // dimension, as 16-byte vectors at byte offsets 16*LPT*v + 16*c of the row,
 // so one load instruction covers whole contiguous rows.  The steps of one
 // block go to different waves (wave w takes step w % SPB of the blocks
-// w / SPB, w / SPB + 8/SPB, ...), so all of a block's tile is requested at
-// about the same time.  All G query heads of the KV head are done together,
-// so K and V are read once for the group; the next block's K and V are
-// loaded before the current one is consumed.  V is loaded non-temporally:
-// nothing reads it again soon, whereas K stays cached for the scoring of a
+// w / SPB, w / SPB + 8/SPB, ... counted from the newest), so all of a
+// block's tile is requested at about the same time.  All G query heads of
+// the KV head are done together, so K and V are read once for the group;
+// blocks are walked newest first, and the next block's K and V are loaded
+// before the current one is consumed.  V is loaded non-temporally: nothing
+// reads it again soon, whereas K stays cached for the scoring of a
 // compression that follows the decode step (measured: both faster).  The
 // LPT lanes of a token add their partial dot products; every lane keeps its own
 // running softmax state (max m, sum l, accumulator) for the tokens it saw,
@@ -201,18 +202,26 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode(DecodeParams p) {
   const char* vb = static_cast<const char*>(p.v);
   const size_t tile_bytes = (size_t)B * ROW;
   // SPB waves share a block, one step each, so a block's tile is requested
-  // at once; the workgroup walks NWB blocks at a time.  This wave's blocks
-  // are blk_begin + wblk + NWB*i, always at step st.
+  // at once; the workgroup walks NWB blocks at a time, newest first: this
+  // wave's i-th block is blk_end - 1 - (wblk + NWB*i), always at step st.
+  // The newest rows are the likeliest to be still in the memory-side cache
+  // (appended tokens, and the tail of a compaction that has just rewritten
+  // the request), and the oldest blocks, read last, are where a following
+  // scoring pass starts.  The order changes nothing but rounding: every
+  // lane's softmax state is merged by log-sum-exp at the end.
   static_assert(NW % SPB == 0, "steps per block must divide the waves");
   constexpr int NWB = NW / SPB;
   const int wblk = wave / SPB, st = wave - wblk * SPB;
   const int lane_off = (st * TPS + tok) * ROW + c * 16;  // this lane's bytes inside a block
   const int my_blocks = blk_end - blk_begin - wblk > 0 ? (blk_end - blk_begin - wblk + NWB - 1) / NWB : 0;
+  // block of the wave's i-th item: wblk + NWB*i < blk_end - blk_begin for
+  // every i < my_blocks, so it stays inside [blk_begin, blk_end)
+  auto block_of = [&](int i) { return blk_end - 1 - (wblk + NWB * i); };
   for (int g0 = 0; g0 < my_blocks; g0 += 64) {
     const int nb_here = min(64, my_blocks - g0);
     int id = -1;
     if (lane < nb_here) {
-      id = p.tables[(size_t)r * p.max_blocks + blk_begin + wblk + NWB * (g0 + lane)];
+      id = p.tables[(size_t)r * p.max_blocks + block_of(g0 + lane)];
       if ((unsigned)id >= (unsigned)p.num_blocks) id = -1;
     }
     const int n_items = nb_here;
@@ -230,7 +239,7 @@ __global__ __launch_bounds__(kDecodeThreads) void k_decode(DecodeParams p) {
     auto item_live = [&](int item) -> bool {
       if (item >= n_items) return false;
       const int pid = __builtin_amdgcn_readlane(id, item);
-      return pid >= 0 && (blk_begin + wblk + NWB * (g0 + item)) * B + st * TPS + tok < seq;
+      return pid >= 0 && block_of(g0 + item) * B + st * TPS + tok < seq;
     };
     // ring of PD+1 register slots: item k lives in slot k % (PD+1) and is
     // loaded PD items before it is consumed
