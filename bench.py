@@ -34,6 +34,9 @@ sys.path.insert(0, ROOT)
 METRIC = "KV compressions/sec + decode tok/s at budget 2048; % of HBM peak GB/s"
 HBM_PEAK_GBS = 8000.0
 PREWARM_SECONDS = 0.5   # untimed steps between the warm-up and the timed region
+# seeded batches of the Qwen3-8B layer, one per timed step (1 GiB of K and V
+# each, and half that kept aside to restore them)
+MAX_FRESH_BATCHES = 64
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 # committed rocprofv3 summaries, one per workload: profiles/hot_path_kernels_<workload>.txt
 PROFILE_DIR = os.path.join(ROOT, "profiles")
@@ -542,15 +545,16 @@ def reserved_block_fills(cache, tables, k_new, v_new, n_max, n_sets, dev) -> lis
     return sets
 
 
-def recorded_lse_compress(steps, cache, pool, tables, next_wq, n_max, w, R, Hq, d, dev, ws, dws,
+def recorded_lse_compress(steps, cache_of, pool, tables, wq_of, n_max, w, R, Hq, d, dev, ws, dws,
                           step):
-    """Per step: the window normalisers on the current cache (decode calls,
-    untimed), then one full step whose compression takes them; returns the
-    per-phase event totals of the compressions."""
+    """Per step it: the window normalisers on step it's cache (``cache_of(it)``,
+    window queries ``wq_of(it)``; decode calls, untimed), then one full step
+    whose compression takes them; returns the per-phase event totals of the
+    compressions."""
     import numpy as np
     import torch
     import compressed_paged_kv_amd as zp
-    b = cache.block_size
+    b = cache_of(0).block_size
     T = n_max * b
     tab_t = torch.from_numpy(np.ascontiguousarray(tables)).to(dev)
     out = torch.empty((R, Hq, d), dtype=torch.float32, device=dev)
@@ -560,7 +564,7 @@ def recorded_lse_compress(steps, cache, pool, tables, next_wq, n_max, w, R, Hq, 
     zp.profile_enable(False)
     totals = {}
     for it in range(steps):
-        wq = next_wq()
+        cache, wq = cache_of(it), wq_of(it)
         for i in range(w):
             zp.paged_decode(cache, 0, wq[0][:, i].contiguous(), tab_t, seqs[i], 1.0 / np.sqrt(d),
                             out, dws, lse_out=lse[0], lse_rows=rows[i])
@@ -576,21 +580,56 @@ def recorded_lse_compress(steps, cache, pool, tables, next_wq, n_max, w, R, Hq, 
     return totals
 
 
-def run_single_stream(args, workload, cache, pool, tables, wq_sets, q_new, k_new, v_new, geom,
-                      n_max, w, cpu_case=None):
-    """One step = host plan + compression of every request's single layer +
-    append into the reserved block + paged decode over the compacted cache
-    and the pending token, all on one stream.
+class FreshBatches:
+    """Seeded batches of one workload, one per step of a measured region: the
+    "layers" of one device case, which share its block tables and each hold
+    their own pools, window queries, pending token and decode query.  A
+    compression compacts its batch in place, so the used blocks of every pool
+    are kept aside and ``restore()`` copies them back before each region."""
 
-    The compression is in place, so every step compresses the cache the
-    previous one left.  To keep the steps alike, the append writes the whole
-    reserved block: the pending token plus the b-1 tokens the following
-    decode steps would add before the next trigger, fresh rows from a
-    rotating set, so each step meets a full cache whose newest block (the
-    observation window) is new.  (Appending one token and compressing again
-    would leave the same b-1 stale rows in the window at every step; their
-    copies pile up among the candidates, are evicted as redundant, and the
-    compaction moves ever fewer rows.)"""
+    def __init__(self, case, dev):
+        import numpy as np
+        import torch
+        import compressed_paged_kv_amd as zp
+        self.case = case
+        self.ids = torch.from_numpy(case.tables.reshape(-1).astype(np.int64)).to(dev)
+        self.caches = [zp.KVCache([k], [v], case.geom.num_q_heads)
+                       for k, v in zip(case.k_pool, case.v_pool)]
+        self.pristine = [(k.index_select(0, self.ids), v.index_select(0, self.ids))
+                         for k, v in zip(case.k_pool, case.v_pool)]
+
+    def __len__(self) -> int:
+        return len(self.caches)
+
+    def restore(self) -> None:
+        import torch
+        for k, v, (pk, pv) in zip(self.case.k_pool, self.case.v_pool, self.pristine):
+            k.index_copy_(0, self.ids, pk)
+            v.index_copy_(0, self.ids, pv)
+        torch.cuda.synchronize()
+
+
+def run_single_stream(args, workload, cache, pool, tables, wq_sets, q_new, k_new, v_new, geom,
+                      n_max, w, cpu_case=None, fresh=None):
+    """One step = host plan + compression of every request's single layer +
+    append + paged decode over the compacted cache and the pending token,
+    all on one stream.
+
+    With ``fresh`` (FreshBatches) step i of a measured region takes batch i:
+    a full cache never compressed before, its own window queries, one
+    pending token appended at slot (N_max-1)*b and the decode of its query
+    over the N_max-1 compacted blocks and that token -- the workload as
+    stated, at every step; the batches are restored before every region.
+
+    Without it every step compresses, in place, the cache the previous one
+    left.  To keep those steps alike, the append writes the whole reserved
+    block: the pending token plus the b-1 tokens the following decode steps
+    would add before the next trigger, fresh rows from a rotating set, so
+    each step meets a full cache whose newest block (the observation window)
+    is new.  (Appending one token and compressing again would leave the same
+    b-1 stale rows in the window at every step; their copies pile up among
+    the candidates, are evicted as redundant, and the compaction moves ever
+    fewer rows.)"""
     import numpy as np
     import torch
     import compressed_paged_kv_amd as zp
@@ -607,11 +646,37 @@ def run_single_stream(args, workload, cache, pool, tables, wq_sets, q_new, k_new
         return wq_sets[(rot[0] - 1) % len(wq_sets)]
 
     tab_t = torch.from_numpy(tables).to(dev)
-    # the reserved block of every request, all b slots (slot k_keep first)
-    slot_t = torch.from_numpy((tables[:, k_keep // b, None] * b
-                               + np.arange(b)[None, :]).reshape(-1).astype(np.int32)).to(dev)
-    fills = reserved_block_fills(cache, tables, k_new, v_new, n_max, 96 if R * b <= 1024 else 24,
-                                 dev)
+    if fresh is not None:
+        P = len(fresh)
+        if P < max(args.steps, args.warmup):
+            log(f"note: {P} fresh batches for {args.steps} timed steps: later steps recompress "
+                f"batches an earlier step of the same region compacted")
+
+        def cache_of(i):
+            return fresh.caches[i % P]
+
+        def wq_of(i):
+            return [fresh.case.window_q[i % P]]
+
+        # the pending token of every request: slot 0 of its reserved block
+        slot_t = torch.from_numpy((tables[:, k_keep // b] * b).astype(np.int32)).to(dev)
+        cache = fresh.caches[0]
+        restore = fresh.restore
+    else:
+        def cache_of(i):
+            return cache
+
+        def wq_of(i):
+            return next_wq()
+
+        # the reserved block of every request, all b slots (slot k_keep first)
+        slot_t = torch.from_numpy((tables[:, k_keep // b, None] * b
+                                   + np.arange(b)[None, :]).reshape(-1).astype(np.int32)).to(dev)
+        fills = reserved_block_fills(cache, tables, k_new, v_new, n_max,
+                                     96 if R * b <= 1024 else 24, dev)
+
+        def restore():
+            pass
     seq_t = torch.full((R,), seq, dtype=torch.int32, device=dev)
     ws = torch.empty(zp.compress_workspace_bytes(cache, R, n_max, w), dtype=torch.uint8, device=dev)
     dws = torch.empty(max(zp.paged_decode_workspace_bytes(cache, R, n_max), 16), dtype=torch.uint8,
@@ -621,28 +686,41 @@ def run_single_stream(args, workload, cache, pool, tables, wq_sets, q_new, k_new
     torch.cuda.synchronize()
 
     def step(i: int, debug=None, compress=True):
-        # i is ignored: the window-query sets rotate over the whole run
+        c = cache_of(i)
         if compress:
             # the decode's device table doubles as the compression's device
             # copy: an in-place plan then uploads nothing
-            zp.compress(cache, pool, n_max, w, tables, next_wq(), ws, debug=debug,
+            zp.compress(c, pool, n_max, w, tables, wq_of(i), ws, debug=debug,
                         device_tables=tab_t)
-        kf, vf = fills[rot[0] % len(fills)]
-        zp.append_kv(cache, 0, kf, vf, slot_t)
-        zp.paged_decode(cache, 0, q_new, tab_t, seq_t, scale, out, dws)
+        if fresh is not None:
+            P = len(fresh)
+            zp.append_kv(c, 0, fresh.case.k_new[i % P], fresh.case.v_new[i % P], slot_t)
+            zp.paged_decode(c, 0, fresh.case.q_new[i % P], tab_t, seq_t, scale, out, dws)
+        else:
+            kf, vf = fills[rot[0] % len(fills)]
+            zp.append_kv(c, 0, kf, vf, slot_t)
+            zp.paged_decode(c, 0, q_new, tab_t, seq_t, scale, out, dws)
 
-    def moved_rows() -> float:
-        """Rows the compaction moves per step (from the kept lists), averaged
-        over a few steps."""
-        kept = torch.empty((1, R, H, k_keep), dtype=torch.int32, device=dev)
-        ar = torch.arange(k_keep, dtype=torch.int32, device=dev)
+    kept_buf = torch.empty((1, R, H, k_keep), dtype=torch.int32, device=dev)
+    ar_keep = torch.arange(k_keep, dtype=torch.int32, device=dev)
+
+    def moved_rows(n: int = 4) -> list:
+        """Rows the compaction moves in each of n steps (from the kept lists)."""
         counts = []
-        for i in range(4):
-            step(i, debug={"kept": kept})
-            counts.append(int((kept[0] != ar).sum().item()))
-        return float(np.mean(counts))
+        for i in range(n):
+            step(i, debug={"kept": kept_buf})
+            counts.append(int((kept_buf[0] != ar_keep).sum().item()))
+        return counts
 
-    moved_before = moved_rows()
+    fresh_counts = None
+    if fresh is not None:
+        # every batch a timed step takes: the exact rows of the timed region
+        restore()
+        fresh_counts = moved_rows(min(args.steps, len(fresh)))
+        moved_before = float(np.mean(fresh_counts))
+        restore()
+    else:
+        moved_before = float(np.mean(moved_rows()))
     log(f"warmup {args.warmup} steps")
     for i in range(args.warmup):
         step(i)
@@ -661,6 +739,7 @@ def run_single_stream(args, workload, cache, pool, tables, wq_sets, q_new, k_new
             torch.cuda.synchronize()
     torch.cuda.synchronize()
     log(f"pre-warm: {n_pre} untimed append + decode passes in {time.perf_counter() - t_pre:.2f} s")
+    restore()
     # 1) the timed region: K steps back to back, nothing else on the stream
     log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
@@ -675,9 +754,11 @@ def run_single_stream(args, workload, cache, pool, tables, wq_sets, q_new, k_new
     # 2) the same K steps again with HIP events recorded around every kernel
     #    on its launch stream, for per-kernel durations (the events add small
     #    gaps between kernels, so this region's wall time is reported apart)
-    # the rows the compaction moves drift slowly from step to step: count
-    # them right around the region the per-kernel durations come from
-    moved_pre = moved_rows()
+    # without fresh batches the rows the compaction moves drift slowly from
+    # step to step: count them right around the region the per-kernel
+    # durations come from
+    moved_pre = moved_before if fresh is not None else float(np.mean(moved_rows()))
+    restore()
     log(f"timing {args.steps} steps with per-kernel events")
     zp.profile_enable(True)
     zp.profile_read()
@@ -690,7 +771,7 @@ def run_single_stream(args, workload, cache, pool, tables, wq_sets, q_new, k_new
     prof = zp.profile_read()
     zp.profile_enable(False)
     ms_per_step_events = (t3 - t2) * 1e3 / args.steps
-    moved_post = moved_rows()
+    moved_post = moved_before if fresh is not None else float(np.mean(moved_rows()))
     # 3) the compression fed with recorded window normalisers (the scoring
     #    reads K once): before each step the normalisers of the step's window
     #    rows are computed on the current cache by zp_paged_decode_lse, as the
@@ -698,14 +779,16 @@ def run_single_stream(args, workload, cache, pool, tables, wq_sets, q_new, k_new
     #    (outside the events: that work belongs to the earlier decode steps)
     rec = None
     if not args.headline_only:
+        restore()
         log(f"timing {args.steps} compressions with recorded window normalisers")
-        rec = recorded_lse_compress(args.steps, cache, pool, tables, next_wq, n_max, w, R, Hq, d,
+        rec = recorded_lse_compress(args.steps, cache_of, pool, tables, wq_of, n_max, w, R, Hq, d,
                                     dev, ws, dws, step)
-    moved_after = moved_rows()
+    moved_after = moved_before if fresh is not None else float(np.mean(moved_rows()))
     # where the fused kernel's time goes: one more step with every unit's
     # phase boundaries stamped on the device wall clock
     phases = None
     if not args.headline_only:
+        restore()
         stamps = torch.zeros((1, R, H, 5), dtype=torch.int64, device=dev)
         step(0, debug={"phase_times": stamps})
         torch.cuda.synchronize()
@@ -725,7 +808,7 @@ def run_single_stream(args, workload, cache, pool, tables, wq_sets, q_new, k_new
     moved = 0.5 * (moved_pre + moved_post)
     nsplit = zp.paged_decode_workspace_bytes(cache, R, n_max) // (R * Hq * (d + 2) * 4)
     alg, flops = _alg_bytes(R, R, 1, H, Hq, d, b, n_max, w, moved, R * seq, nsplit=nsplit,
-                            append_rows=R * b)
+                            append_rows=R if fresh is not None else R * b)
     kernels = _kernel_rows(prof, alg, flops)
     gpu_kernels = [k for k in kernels if k["phase"] != "upload"]
     dom = max(gpu_kernels, key=lambda k: k["avg_us"] * k["launches"])
@@ -787,11 +870,23 @@ def run_single_stream(args, workload, cache, pool, tables, wq_sets, q_new, k_new
             if dec_cold_us else None,
         "ceilings": ceilings,
         "moved_rows_per_step": int(moved),
-        "moved_rows_before_after": [moved_pre, moved_post],
-        "moved_rows_first_last": [moved_before, moved_after],
         "kernels": kernels,
         "roofline": roofline,
     }
+    if fresh is not None:
+        # every timed step compresses a batch never compressed before: its
+        # moved rows, counted on each batch the timed region takes
+        result["fresh_batches"] = {
+            "what": "every timed step takes its own seeded batch (a full cache never compressed "
+                    "before, its window queries, pending token and decode query); the batches "
+                    "are restored before each measured region",
+            "batches": len(fresh),
+            "moved_rows_mean": round(moved_before, 1),
+            "moved_rows_min_max": [min(fresh_counts), max(fresh_counts)],
+        }
+    else:
+        result["moved_rows_before_after"] = [moved_pre, moved_post]
+        result["moved_rows_first_last"] = [moved_before, moved_after]
     # the pairwise redundancy the Lightning Redundancy Score replaces, on the
     # same cache (every pair of the T slots of each head on MFMA)
     ra_us = None
@@ -1411,12 +1506,10 @@ def main() -> int:
     if args.calibrate_copy:
         calibrate_copy()
 
-    import numpy as np
     import torch
 
     import compressed_paged_kv_amd as zp
     import synth
-    from synth.device import to_tensor
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -1441,16 +1534,19 @@ def main() -> int:
                                    case.q_new[0], case.k_new[0], case.v_new[0], case.geom,
                                    case.n_max, case.window)
     else:
-        log("generating the Qwen3-8B-shaped layer (64 requests, budget 2048)")
-        case = synth.case_qwen3_8b_layer()
-        wq_sets = window_query_sets(to_tensor(case.window_q[0], dev), 64, 1102, dev)
-        cache = zp.KVCache([to_tensor(case.k_pool[0], dev)], [to_tensor(case.v_pool[0], dev)],
-                           case.geom.num_q_heads)
-        pool = zp.BlockPool.from_refcounts(case.refcounts)
-        result = run_single_stream(args, args.workload, cache, pool, case.tables.copy(), wq_sets,
-                                   to_tensor(case.q_new[0], dev), to_tensor(case.k_new[0], dev),
-                                   to_tensor(case.v_new[0], dev), case.geom, case.n_max,
-                                   case.window, cpu_case=case)
+        from synth.device_gen import case_qwen3_8b_layer_batches
+        n_batches = min(max(args.steps, args.warmup, 1), MAX_FRESH_BATCHES)
+        log(f"generating {n_batches} seeded batches of the Qwen3-8B-shaped layer on the device "
+            f"(64 requests at budget 2048 each, one batch per timed step)")
+        dcase = case_qwen3_8b_layer_batches(dev, n_batches)
+        fresh = FreshBatches(dcase, dev)
+        pool = zp.BlockPool.from_refcounts(dcase.refcounts)
+        # the oracle's sample for the CPU baseline: the same recipe drawn on the host
+        case = None if args.no_cpu_baseline else synth.case_qwen3_8b_layer()
+        result = run_single_stream(args, args.workload, fresh.caches[0], pool, dcase.tables.copy(),
+                                   None, dcase.q_new[0], dcase.k_new[0], dcase.v_new[0],
+                                   dcase.geom, dcase.n_max, dcase.window, cpu_case=case,
+                                   fresh=fresh)
     print(json.dumps(result), flush=True)
     return 0
 

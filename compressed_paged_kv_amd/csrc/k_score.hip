@@ -68,8 +68,16 @@ constexpr float kMasked = -3.0e38f;   // logit of a causally masked slot: adds 2
 // scores (T <= 8192) with one row group; three T <= 4096 arrays with two
 template <int RG>
 constexpr int lds_floats() { return RG == 2 ? 3 * 4096 : 8192; }
+// Registers per lane for the K ring (blocks loaded ahead of the one being
+// scored).  One row group: 64, so four 4 KiB (block, head) tiles of a
+// b = 16, d = 128 bfloat16 cache are in flight per wave -- keys that come
+// cold from HBM need the depth, cached ones do not.  Two row groups (the
+// b = 32, 128-row shape, bound by issue rather than by loads): 32.
 #ifndef ZP_SCORE_RING_VGPRS
-#define ZP_SCORE_RING_VGPRS 32
+#define ZP_SCORE_RING_VGPRS 64
+#endif
+#ifndef ZP_SCORE_RING_VGPRS_2RG
+#define ZP_SCORE_RING_VGPRS_2RG 32
 #endif
 #ifndef ZP_SCORE_REVERSE
 #define ZP_SCORE_REVERSE 1
@@ -472,11 +480,18 @@ __device__ inline void compact_unit(const ScoreParams& p, float* lds, int* s_fir
   }
 }
 
-// Sixteen waves fit a CU when a wave's Q fragments and K ring stay small
-// (at most 128 registers a lane); otherwise eight.
-template <int DT, int D, int RTW, int B>
-constexpr int score_min_blocks() {
-  return (RTW * D * Mma<DT>::kElemBytes / 64 <= 8 && (B / 16) * D * Mma<DT>::kElemBytes / 64 <= 4) ? 2 : 1;
+// Workgroups a CU is to hold, from the 16-byte fragments a lane keeps per
+// block (the Q rows of its row tiles and one b x d key tile): sixteen waves
+// (128 registers a lane) when they stay small, a single four-wave workgroup
+// (the whole 512-register file) for the float32 shapes whose fragments
+// alone would fill most of 256, eight waves otherwise.
+template <int DT, int D, int B, int RT, int RG>
+constexpr int score_wgs_per_cu() {
+  constexpr int NV = D * Mma<DT>::kElemBytes / 64, F = (B / 16) * NV, RTW = RT / RG;
+  constexpr int waves = score_waves<RG>();
+  if (RG == 1 && B == 16 && (RTW + 1) * NV <= 8) return 16 / waves;
+  if (RG == 1 && RTW * NV + F > 24) return 1;
+  return kMaxWaves / waves;
 }
 
 // RG row groups: with two, waves 0-3 take the first half of the row tiles and
@@ -503,9 +518,10 @@ __device__ __forceinline__ void score_unit(const ScoreParams& p) {
   constexpr bool SH = RG == 2 && F <= 8;
   constexpr int FL = SH ? F / 2 : F;    // fragments a wave loads per block
   // K ring slots: as many block loads as fit the register budget, 2 to 4
-  constexpr int kPrefetch = ZP_SCORE_RING_VGPRS / (FL * 4) < 2   ? 2
-                            : ZP_SCORE_RING_VGPRS / (FL * 4) > 4 ? 4
-                                                                 : ZP_SCORE_RING_VGPRS / (FL * 4);
+  constexpr int kRingVgprs = RG == 2 ? ZP_SCORE_RING_VGPRS_2RG : ZP_SCORE_RING_VGPRS;
+  constexpr int kPrefetch = kRingVgprs / (FL * 4) < 2   ? 2
+                            : kRingVgprs / (FL * 4) > 4 ? 4
+                                                        : kRingVgprs / (FL * 4);
 
   const size_t unit = (size_t)p.layer0 * p.R * p.H + blockIdx.x;  // over the whole call
   const int h = (int)(unit % p.H);
@@ -878,11 +894,15 @@ __device__ __forceinline__ void score_unit(const ScoreParams& p) {
   else select_evicted<32, kWaves>(s_sc, s_sel, s_scr, p, unit, s_f, T, C, E);
   stamp(3);
   if constexpr (FUSE) {
+    // rows a thread moves per tile: half as many where sixteen waves share a
+    // CU (128 registers a lane), so the tile buffers fit beside the scoring's
+    constexpr int kU = score_wgs_per_cu<DT, D, B, RT, RG>() * kWaves > kMaxWaves ? kFusedUnroll / 2
+                                                                                : kFusedUnroll;
     __shared__ int s_first;
     if (p.k_cached)  // uniform: one tile loop or the other, each straight-line
-      compact_unit<ROWB / 16, B, kThreads, kFusedUnroll, true>(p, s_buf, &s_first, l, r, h, n_src, E);
+      compact_unit<ROWB / 16, B, kThreads, kU, true>(p, s_buf, &s_first, l, r, h, n_src, E);
     else
-      compact_unit<ROWB / 16, B, kThreads, kFusedUnroll, false>(p, s_buf, &s_first, l, r, h, n_src, E);
+      compact_unit<ROWB / 16, B, kThreads, kU, false>(p, s_buf, &s_first, l, r, h, n_src, E);
   }
   if (times) {
     __syncthreads();  // every wave done (uniform: the pointer is a kernel argument)
@@ -891,12 +911,12 @@ __device__ __forceinline__ void score_unit(const ScoreParams& p) {
 }
 
 template <int DT, int D, int B, int RT, int RG>
-__global__ __launch_bounds__(64 * score_waves<RG>(), (kMaxWaves / score_waves<RG>()) * (score_min_blocks<DT, D, RT / RG, B>())) void k_score_select(ScoreParams p) {
+__global__ __launch_bounds__(64 * score_waves<RG>(), (score_wgs_per_cu<DT, D, B, RT, RG>())) void k_score_select(ScoreParams p) {
   score_unit<DT, D, B, RT, RG, false>(p);
 }
 
 template <int DT, int D, int B, int RT, int RG>
-__global__ __launch_bounds__(64 * score_waves<RG>(), (kMaxWaves / score_waves<RG>()) * (score_min_blocks<DT, D, RT / RG, B>())) void k_score_compact(ScoreParams p) {
+__global__ __launch_bounds__(64 * score_waves<RG>(), (score_wgs_per_cu<DT, D, B, RT, RG>())) void k_score_compact(ScoreParams p) {
   score_unit<DT, D, B, RT, RG, true>(p);
 }
 

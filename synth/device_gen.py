@@ -159,6 +159,17 @@ def make_device_case(name: str, seed: int, device, *, num_reqs: int, num_layers:
 
 # --- the full-size workloads --------------------------------------------
 
+def case_qwen3_8b_layer_batches(device, n: int, seed: int = 102, num_reqs: int = 64) -> DeviceCase:
+    """n independent batches of the Qwen3-8B-shaped layer at budget 2048 (64
+    requests at N_max = 128, b = 16, w = 16, 8 KV / 32 query heads, d = 128,
+    bf16, per-head key scale U(0.5, 2), pool 16384), as the n "layers" of one
+    case: one seeded set of block tables, each batch its own pools, window
+    queries, pending token and decode query."""
+    return make_device_case("qwen3_8b_budget2048", seed, device, num_reqs=num_reqs, num_layers=n,
+                            num_kv_heads=8, num_q_heads=32, head_dim=128, block_size=16, n_max=128,
+                            window=16, num_blocks=16384)
+
+
 def case_mix_device(device, seed: int = 103, num_reqs: int = 256, num_layers: int = 36,
                     compress_frac: float = 0.1) -> DeviceCase:
     """Continuous-batching mix on the Qwen3-8B shape: 256 requests x 36 layers,
