@@ -648,7 +648,7 @@ def run_single_stream(args, workload, cache, pool, tables, wq_sets, q_new, k_new
     tab_t = torch.from_numpy(tables).to(dev)
     if fresh is not None:
         P = len(fresh)
-        if P < max(args.steps, args.warmup):
+        if P < args.steps:
             log(f"note: {P} fresh batches for {args.steps} timed steps: later steps recompress "
                 f"batches an earlier step of the same region compacted")
 
@@ -714,9 +714,11 @@ def run_single_stream(args, workload, cache, pool, tables, wq_sets, q_new, k_new
 
     fresh_counts = None
     if fresh is not None:
-        # every batch a timed step takes: the exact rows of the timed region
+        # the timed region's own sequence of steps from restored batches (a
+        # batch taken twice when there are more steps than batches counts as
+        # the recompression it is): its exact rows
         restore()
-        fresh_counts = moved_rows(min(args.steps, len(fresh)))
+        fresh_counts = moved_rows(args.steps)
         moved_before = float(np.mean(fresh_counts))
         restore()
     else:
@@ -881,6 +883,7 @@ def run_single_stream(args, workload, cache, pool, tables, wq_sets, q_new, k_new
                     "before, its window queries, pending token and decode query); the batches "
                     "are restored before each measured region",
             "batches": len(fresh),
+            "steps_per_batch": -(-args.steps // len(fresh)),
             "moved_rows_mean": round(moved_before, 1),
             "moved_rows_min_max": [min(fresh_counts), max(fresh_counts)],
         }
