@@ -53,7 +53,7 @@ namespace {
 // Waves per workgroup: four with one row group (two workgroups share a CU;
 // with more units than workgroup slots one selects while another streams
 // K); eight with two row groups, whose paired waves exchange K tiles
-// through LDS.
+// through LDS, each pair synchronising on its own.
 template <int RG>
 constexpr int score_waves() { return RG == 2 ? 8 : 4; }
 constexpr int kMaxWaves = 8;
@@ -550,6 +550,9 @@ __device__ __forceinline__ void score_unit(const ScoreParams& p) {
   __shared__ int s_scr[kWaves + 1];
   __shared__ __align__(16) SelectLds s_sel;
   __shared__ uint4 s_x[SH ? 2 : 1][SH ? WPG : 1][SH ? F : 1][64];  // [parity][pair][fragment][lane]
+  // with shared tiles: per (row group, pair) the last exchange step whose
+  // half that wave has written (steps numbered across both passes)
+  __shared__ int s_pair[2][WPG];
   float* s_sc = s_buf;          // scores (with two row groups: group 0's partial importance)
   float* s_aux = s_buf + 4096;  // group 1's partial importance (two row groups only)
   float* s_rr = s_buf + 8192;   // redundancy (two row groups only)
@@ -602,10 +605,17 @@ __device__ __forceinline__ void score_unit(const ScoreParams& p) {
   // register buffers: slot s is refilled right after it is consumed, so
   // PD - 1 blocks stay in flight.  Pass 2 walks the blocks in reverse, so it
   // starts on those pass 1 read last (still in L2 / the memory-side cache).
-  // With shared tiles every wave runs the same number of iterations (the
-  // largest block count of any wave), each with one workgroup barrier
-  // between the LDS writes of the own half and the reads of the partner's.
-  auto ring = [&](auto reverse, auto body) {
+  // With shared tiles only the two waves of a pair wait for each other: a
+  // wave writes its half of the block, publishes the exchange step in
+  // s_pair (release), and reads the partner's half once the partner has
+  // published the same step (acquire).  Parity buffers alternate; a wave
+  // overwrites one only after the partner has published the step after the
+  // one that read it, so no half is overwritten before it is read.  Steps
+  // are numbered from `base`, distinct per pass, so a pass never takes the
+  // previous pass's counts for its own.  Both waves of a pair hold the same
+  // blocks, so they run the same steps; the wait is bounded (2^16 sleeps)
+  // so a wave can never spin forever.
+  auto ring = [&](auto reverse, int base, auto body) {
     constexpr bool REV = decltype(reverse)::value;
     auto kof = [&](int it) { return REV ? nbw - 1 - it : it; };
     const int iters = SH ? (n_src + WPG - 1) / WPG : nbw;
@@ -630,8 +640,14 @@ __device__ __forceinline__ void score_unit(const ScoreParams& p) {
             if (live) {
 #pragma unroll
               for (int q = 0; q < FL; q++) xb[(rg * FL + q) * 64 + lane] = kb[s][q];
+              // publish this half, then wait for the partner's (bounded)
+              const int step = base + it + 1;
+              __hip_atomic_store(&s_pair[rg][wl], step, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+              for (int spin = 0; spin < (1 << 16) &&
+                   __hip_atomic_load(&s_pair[1 - rg][wl], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < step;
+                   spin++)
+                __builtin_amdgcn_s_sleep(1);
             }
-            __syncthreads();
             if (live) {
               uint4 kt[NST][NV];
 #pragma unroll
@@ -662,6 +678,10 @@ __device__ __forceinline__ void score_unit(const ScoreParams& p) {
   auto stamp = [&](int k) {
     if (times && threadIdx.x == 0) times[k] = (int64_t)wall_clock64();
   };
+  if constexpr (SH) {
+    if (tid < 2 * WPG) (&s_pair[0][0])[tid] = 0;
+    __syncthreads();
+  }
   stamp(0);
   // ---------------------------------------------------------------- pass 1
   // Skipped when the caller supplies the normalisers of the window rows
@@ -688,7 +708,7 @@ __device__ __forceinline__ void score_unit(const ScoreParams& p) {
         m[rt][i] = kInitMax;
         z[rt][i] = 0.f;
       }
-    ring(BoolC<false>{}, [&](int k, const uint4 (&kt)[NST][NV]) {
+    ring(BoolC<false>{}, 0, [&](int k, const uint4 (&kt)[NST][NV]) {
       const int n = wl + WPG * k;
       const bool last = n == n_src - 1;  // only the last block meets the causal limit
 #pragma unroll
@@ -782,7 +802,7 @@ __device__ __forceinline__ void score_unit(const ScoreParams& p) {
     }
     return sum_rows(cs);
   };
-  ring(BoolC<kReversePass2>{}, [&](int k, const uint4 (&kt)[NST][NV]) {
+  ring(BoolC<kReversePass2>{}, 1 << 16, [&](int k, const uint4 (&kt)[NST][NV]) {
     const int n = wl + WPG * k;
     const bool last = n == n_src - 1;
     float A[NST];
